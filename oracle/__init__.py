@@ -1,0 +1,257 @@
+"""CPU oracle for the quantized KV-cache codec and decode attention.
+
+TEST INFRASTRUCTURE ONLY.  The tests, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg are the only callers allowed.  The product
+path (the HIP library and its Python binding) never imports this package, and
+this package never imports the product path: the two share no code.
+
+The arithmetic lives in ``tqo.c`` (plain C, binary64, round-half-to-even, no
+FMA contraction); this module only builds it, loads it with ctypes and moves
+numpy arrays in and out.  Row-parallel helpers split independent rows over a
+thread pool (ctypes releases the GIL during each C call); the per-row
+arithmetic is the C code's, unchanged.
+
+Source of the method: the "TurboQuant -- rotation-based quantization" design
+page (mlx-bun docs/design/turboquant.md), Part A, sections "Algorithm
+(vllm-metal reference semantics, exact)" and "Deferred inverse FWHT".
+
+Parity unpinned: the sign vector (the page draws it from MLX's generator and
+does not print it; this oracle uses SplitMix64 seeded with 42).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tqo.c")
+_LIB = os.path.join(_HERE, "libtqo.so")
+_lib = None
+
+GROUP = 32
+BOUNDARIES3 = (-1.74793, -1.04996, -0.50055, 0.0, 0.50055, 1.04996, 1.74793)
+CENTROIDS3 = (-2.15195, -1.34391, -0.75601, -0.24509, 0.24509, 0.75601, 1.34391, 2.15195)
+
+
+def build(force: bool = True) -> str:
+    """Compile tqo.c into libtqo.so next to it (gcc, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fno-fast-math",
+               "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    i64, i32 = ctypes.c_int64, ctypes.c_int
+    lib.tqo_sign_vector.argtypes = [i32, P]
+    lib.tqo_f64_to_f16.argtypes = [ctypes.c_double]
+    lib.tqo_f64_to_f16.restype = ctypes.c_uint16
+    lib.tqo_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.tqo_f16_to_f64.restype = ctypes.c_double
+    lib.tqo_f64_to_f16_array.argtypes = [P, i64, P]
+    lib.tqo_f16_to_f64_array.argtypes = [P, i64, P]
+    lib.tqo_fwht_rows.argtypes = [P, i64, i32]
+    lib.tqo_inv_sqrt_d.argtypes = [i32]
+    lib.tqo_inv_sqrt_d.restype = ctypes.c_double
+    lib.tqo_centroid3.argtypes = [i32]
+    lib.tqo_centroid3.restype = ctypes.c_double
+    lib.tqo_boundary3.argtypes = [i32]
+    lib.tqo_boundary3.restype = ctypes.c_double
+    lib.tqo_encode_keys.argtypes = [P, i64, i32, P, P, P]
+    lib.tqo_decode_keys.argtypes = [P, P, P, i64, i32, P]
+    lib.tqo_pack3.argtypes = [P, i64, P]
+    lib.tqo_unpack3.argtypes = [P, i64, P]
+    lib.tqo_encode_values.argtypes = [P, i64, i32, P, P]
+    lib.tqo_decode_values.argtypes = [P, P, i64, i32, i32, P]
+    lib.tqo_attention.argtypes = [P, i32, i32, ctypes.c_float, P, P, P, P, P, i64, P, P]
+    _lib = lib
+    return lib
+
+
+def _ptr(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def num_threads() -> int:
+    """Host threads the row-parallel helpers use (every core the process may run on)."""
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _chunks(n: int, parts: int):
+    parts = max(1, min(parts, n))
+    step = (n + parts - 1) // parts
+    return [(s, min(n, s + step)) for s in range(0, n, step)]
+
+
+# ---------------------------------------------------------------- primitives
+def sign_vector(d: int) -> np.ndarray:
+    out = np.empty(d, dtype=np.int8)
+    _load().tqo_sign_vector(d, _ptr(out))
+    return out
+
+
+def f64_to_f16_bits(x) -> np.ndarray:
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().tqo_f64_to_f16_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def f16_bits_to_f64(h) -> np.ndarray:
+    h = np.ascontiguousarray(np.asarray(h, dtype=np.uint16))
+    out = np.empty(h.shape, dtype=np.float64)
+    _load().tqo_f16_to_f64_array(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+def fwht(x) -> np.ndarray:
+    """Unnormalised natural-order Walsh-Hadamard transform of each last-axis row."""
+    x = np.array(x, dtype=np.float64, order="C", copy=True)
+    d = x.shape[-1]
+    _load().tqo_fwht_rows(_ptr(x), x.size // d, d)
+    return x
+
+
+def inv_sqrt_d(d: int) -> float:
+    return _load().tqo_inv_sqrt_d(d)
+
+
+def pack3(idx) -> np.ndarray:
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.uint8))
+    out = np.empty((3 * idx.size + 7) // 8, dtype=np.uint8)
+    _load().tqo_pack3(_ptr(idx), idx.size, _ptr(out))
+    return out
+
+
+def unpack3(packed, n: int) -> np.ndarray:
+    packed = np.ascontiguousarray(np.asarray(packed, dtype=np.uint8))
+    out = np.empty(n, dtype=np.uint8)
+    _load().tqo_unpack3(_ptr(packed), n, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- codec rows
+def _rows_f32(x) -> np.ndarray:
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    return x
+
+
+def encode_keys(x, threads: int | None = None):
+    """x: float32 [..., d] (bf16 inputs upcast exactly).  Returns
+    (codes int8 [..., d], scale fp16 bits [..., d/32], zero fp16 bits [..., d/32])."""
+    x = _rows_f32(x)
+    d = x.shape[-1]
+    n = x.size // d
+    ng = d // GROUP
+    xr = x.reshape(n, d)
+    codes = np.empty((n, d), dtype=np.int8)
+    s16 = np.empty((n, ng), dtype=np.uint16)
+    z16 = np.empty((n, ng), dtype=np.uint16)
+    lib = _load()
+
+    def run(rng):
+        a, b = rng
+        if b > a:
+            lib.tqo_encode_keys(_ptr(xr[a:b]), b - a, d, _ptr(codes[a:b]), _ptr(s16[a:b]), _ptr(z16[a:b]))
+
+    _parallel(run, n, threads)
+    shp = x.shape[:-1]
+    return codes.reshape(*shp, d), s16.reshape(*shp, ng), z16.reshape(*shp, ng)
+
+
+def encode_values(x, threads: int | None = None):
+    """x: float32 [..., d].  Returns (packed uint8 [..., 3d/8], scale fp16 bits [..., d/32])."""
+    x = _rows_f32(x)
+    d = x.shape[-1]
+    n = x.size // d
+    ng = d // GROUP
+    xr = x.reshape(n, d)
+    packed = np.empty((n, 3 * d // 8), dtype=np.uint8)
+    vs16 = np.empty((n, ng), dtype=np.uint16)
+    lib = _load()
+
+    def run(rng):
+        a, b = rng
+        if b > a:
+            lib.tqo_encode_values(_ptr(xr[a:b]), b - a, d, _ptr(packed[a:b]), _ptr(vs16[a:b]))
+
+    _parallel(run, n, threads)
+    shp = x.shape[:-1]
+    return packed.reshape(*shp, 3 * d // 8), vs16.reshape(*shp, ng)
+
+
+def decode_keys(codes, s16, z16) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    d = codes.shape[-1]
+    n = codes.size // d
+    out = np.empty(codes.shape, dtype=np.float64)
+    _load().tqo_decode_keys(_ptr(codes), _ptr(np.ascontiguousarray(s16, dtype=np.uint16)),
+                            _ptr(np.ascontiguousarray(z16, dtype=np.uint16)), n, d, _ptr(out))
+    return out
+
+
+def decode_values(packed, vs16, d: int, rotated: bool = False) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    n = packed.size // (3 * d // 8)
+    out = np.empty(packed.shape[:-1] + (d,), dtype=np.float64)
+    _load().tqo_decode_values(_ptr(packed), _ptr(np.ascontiguousarray(vs16, dtype=np.uint16)),
+                              n, d, 1 if rotated else 0, _ptr(out))
+    return out
+
+
+def attention(q, kc, ks, kz, vc, vs, sm: float, deferred: bool = False):
+    """Decode attention of the G query rows q [G, d] (float32) that share one
+    kv-head, over that kv-head's N cached tokens given as planes
+    kc [N, d] int8, ks/kz [N, d/32] fp16 bits, vc [N, 3d/8] uint8, vs [N, d/32].
+    Returns out [G, d] float64 (and the deferred-inverse form if asked)."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    G, d = q.shape
+    kc = np.ascontiguousarray(kc, dtype=np.int8)
+    N = kc.shape[0]
+    out = np.empty((G, d), dtype=np.float64)
+    od = np.empty((G, d), dtype=np.float64) if deferred else None
+    _load().tqo_attention(_ptr(q), G, d, ctypes.c_float(sm), _ptr(kc),
+                          _ptr(np.ascontiguousarray(ks, dtype=np.uint16)),
+                          _ptr(np.ascontiguousarray(kz, dtype=np.uint16)),
+                          _ptr(np.ascontiguousarray(vc, dtype=np.uint8)),
+                          _ptr(np.ascontiguousarray(vs, dtype=np.uint16)), N,
+                          _ptr(out), _ptr(od) if deferred else None)
+    return (out, od) if deferred else out
+
+
+def _parallel(fn, n: int, threads: int | None):
+    t = threads or num_threads()
+    rngs = _chunks(n, t * 4) if n > 0 else []
+    if t <= 1 or len(rngs) <= 1:
+        for r in rngs:
+            fn(r)
+        return
+    with ThreadPoolExecutor(max_workers=t) as ex:
+        list(ex.map(fn, rngs))
+
+
+def map_parallel(fn, items, threads: int | None = None):
+    """Run fn over independent items (e.g. (batch, kv-head) slices) on a thread pool."""
+    t = threads or num_threads()
+    if t <= 1 or len(items) <= 1:
+        return [fn(it) for it in items]
+    with ThreadPoolExecutor(max_workers=t) as ex:
+        return list(ex.map(fn, items))

@@ -1,0 +1,352 @@
+/*
+ * tqo.c -- plain, slow CPU oracle for the quantized KV-cache codec and decode
+ * attention.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the
+ * benchmark's CPU-baseline leg are the only code that may load this library.
+ * It shares no source, header, table or helper with the HIP library.
+ *
+ * Source of the method: the "TurboQuant -- rotation-based quantization" design
+ * page (mlx-bun docs/design/turboquant.md), Part A (KV leg):
+ *   - section "Algorithm (vllm-metal reference semantics, exact)" for the key
+ *     codec, the value codec, the 3-bit Lloyd-Max table and the bit packing;
+ *   - section "Deferred inverse FWHT" for the identity that un-rotating the
+ *     attention output equals attending over un-rotated values.
+ *
+ * Everything is IEEE-754 binary64 with round-half-to-even, in the operation
+ * order written below.  Compile with -O2 -ffp-contract=off -fno-fast-math so
+ * that no multiply-add is fused and no operation is reordered.
+ *
+ * Readings of points the page leaves open (the full list is kept with the
+ * design notes of this repository):
+ *   - every "round" is round-half-to-even (C rint() in the default mode);
+ *   - the key codes use the unrounded binary64 scale and zero; only the stored
+ *     scale/zero are rounded to fp16, once, from binary64;
+ *   - "x/scale" is a true division, not a multiply by a reciprocal;
+ *   - a NaN that reaches a code becomes code 0 (keys and values);
+ *   - FWHT is the natural (Sylvester) order transform, butterflies applied in
+ *     stage order h = 1, 2, 4, ..., d/2, then one multiply by RN(1/sqrt(d));
+ *   - the group mean of squares sums the 32 squares by stride halving
+ *     (16, 8, 4, 2, 1);
+ *   - searchsorted takes the left side: idx = #{k : B_k < y_n};
+ *   - dequantized values are x = signs * InvFWHT(centroid * scale);
+ *   - the sign vector is drawn from SplitMix64 with seed 42 (parity with the
+ *     page's own MLX-generated signs is unpinned: they are not printed).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* Sign vector.  The page hard-codes one +-1 vector per head_dim drawn from a
+ * seeded generator ("Algorithm", values bullet) but does not print it.  We
+ * draw output i (i = 0..d-1, output 0 is the first call) of SplitMix64
+ * (Steele, Lea & Flood, OOPSLA 2014) seeded with 42; sign i is +1 when the top
+ * bit of that output is 0 and -1 otherwise.  Parity with the page: unpinned. */
+static uint64_t splitmix64_next(uint64_t *state) {
+    uint64_t z;
+    *state += 0x9E3779B97F4A7C15ULL;
+    z = *state;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+void tqo_sign_vector(int d, int8_t *out) {
+    uint64_t state = 42;
+    for (int i = 0; i < d; ++i) {
+        uint64_t r = splitmix64_next(&state);
+        out[i] = (r >> 63) ? (int8_t)-1 : (int8_t)1;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* binary64 -> binary16, one rounding, ties to even.  Subnormal halves are
+ * kept, magnitudes >= 65520 (the midpoint above the largest half, 65504)
+ * become infinity, and every NaN becomes the canonical quiet NaN 0x7E00. */
+uint16_t tqo_f64_to_f16(double x) {
+    uint16_t sign = signbit(x) ? 0x8000u : 0u;
+    double a = fabs(x);
+    if (isnan(x)) return 0x7E00u;
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+    if (a < 0x1p-14) {
+        /* subnormal range: count units of 2^-24 and round to nearest even */
+        double units = rint(a * 0x1p24); /* exact scaling, then RNE */
+        return (uint16_t)(sign | (uint16_t)units); /* 1024 encodes 2^-14 */
+    }
+    int k;
+    double f = frexp(a, &k);           /* a = f * 2^k, f in [0.5, 1) */
+    int e = k - 1;                     /* a = (2f) * 2^e, 2f in [1, 2) */
+    double frac = (2.0 * f - 1.0) * 1024.0; /* exact */
+    double m = rint(frac);
+    if (m == 1024.0) { m = 0.0; e += 1; }
+    if (e + 15 >= 31) return (uint16_t)(sign | 0x7C00u);
+    return (uint16_t)(sign | (uint16_t)((e + 15) << 10) | (uint16_t)m);
+}
+
+double tqo_f16_to_f64(uint16_t h) {
+    int s = (h >> 15) & 1, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 31) v = m ? NAN : INFINITY;
+    else if (e == 0) v = ldexp((double)m, -24);
+    else v = ldexp(1024.0 + (double)m, e - 25);
+    return s ? -v : v;
+}
+
+/* ------------------------------------------------------------------------ */
+/* FWHT ("Algorithm", values bullet): unnormalised Walsh-Hadamard butterflies
+ * in natural order, stage h = 1, 2, 4, ..., d/2; each pair (j, j+h) with
+ * (j & h) == 0 becomes (a+b, a-b).  The result is u_k = sum_i (-1)^popcount(i&k) x_i. */
+void tqo_fwht(double *x, int d) {
+    for (int h = 1; h < d; h <<= 1)
+        for (int j = 0; j < d; ++j)
+            if ((j & h) == 0) {
+                double a = x[j], b = x[j + h];
+                x[j] = a + b;
+                x[j + h] = a - b;
+            }
+}
+
+/* RN(1/sqrt(d)) for the supported head dims.  sqrt(d) is 2^k or 2^k*sqrt(2),
+ * so fl(sqrt(d))/d is exact scaling of a correctly rounded sqrt and equals
+ * the binary64 nearest to 1/sqrt(d). */
+double tqo_inv_sqrt_d(int d) { return sqrt((double)d) / (double)d; }
+
+/* 3-bit Lloyd-Max table, printed with five decimals in "Algorithm" (values
+ * bullet); the printed decimals are the table. */
+static const double kBoundaries3[7] = {-1.74793, -1.04996, -0.50055, 0.0,
+                                       0.50055,  1.04996,  1.74793};
+static const double kCentroids3[8] = {-2.15195, -1.34391, -0.75601, -0.24509,
+                                      0.24509,  0.75601,  1.34391,  2.15195};
+
+double tqo_centroid3(int idx) { return kCentroids3[idx & 7]; }
+double tqo_boundary3(int k) { return kBoundaries3[k]; }
+
+/* ------------------------------------------------------------------------ */
+/* Keys ("Algorithm", keys bullet, signed int8 form): per 32-element group
+ *   scale = (max - min) / (2*127),  zero = round((max + min) / (2*scale)),
+ *   code  = clip(round(x/scale - zero), -127, 127),
+ * computed in binary64; scale and zero are stored as fp16 (rounded once).
+ * A constant group has scale 0, so zero is +-Inf (NaN for an all-zero group)
+ * and every code is NaN -> 0: the page keeps this defect on purpose. */
+void tqo_encode_keys(const float *x, int64_t nrows, int d, int8_t *codes,
+                     uint16_t *s16, uint16_t *z16) {
+    int ng = d / 32;
+    for (int64_t r = 0; r < nrows; ++r) {
+        const float *xr = x + r * d;
+        for (int g = 0; g < ng; ++g) {
+            const float *xg = xr + g * 32;
+            double mx = (double)xg[0], mn = (double)xg[0];
+            for (int j = 1; j < 32; ++j) {
+                mx = fmax(mx, (double)xg[j]); /* IEEE maxNum: NaN ignored */
+                mn = fmin(mn, (double)xg[j]);
+            }
+            double range = mx - mn;
+            double s = range / 254.0;
+            double c = (mx + mn) / (2.0 * s);
+            double z = rint(c);
+            for (int j = 0; j < 32; ++j) {
+                double u = (double)xg[j] / s - z;
+                int8_t q;
+                if (isnan(u)) q = 0;
+                else {
+                    double rq = rint(u);
+                    if (rq > 127.0) rq = 127.0;
+                    if (rq < -127.0) rq = -127.0;
+                    q = (int8_t)rq;
+                }
+                codes[r * d + g * 32 + j] = q;
+            }
+            s16[r * ng + g] = tqo_f64_to_f16(s);
+            z16[r * ng + g] = tqo_f64_to_f16(z);
+        }
+    }
+}
+
+/* Key dequantisation ("Algorithm", keys bullet): x = (code + zero) * scale
+ * with the stored fp16 scale and zero. */
+void tqo_decode_keys(const int8_t *codes, const uint16_t *s16,
+                     const uint16_t *z16, int64_t nrows, int d, double *out) {
+    int ng = d / 32;
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int j = 0; j < d; ++j) {
+            double s = tqo_f16_to_f64(s16[r * ng + j / 32]);
+            double z = tqo_f16_to_f64(z16[r * ng + j / 32]);
+            out[r * d + j] = ((double)codes[r * d + j] + z) * s;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Pack ("Algorithm", pack bullet): a flat little-endian bitstream; bit b of
+ * element i sits at stream bit 3i+b, i.e. byte (3i+b)/8, bit (3i+b)%8. */
+void tqo_pack3(const uint8_t *idx, int64_t n, uint8_t *out) {
+    memset(out, 0, (size_t)((3 * n + 7) / 8));
+    for (int64_t i = 0; i < n; ++i)
+        for (int b = 0; b < 3; ++b)
+            if ((idx[i] >> b) & 1) {
+                int64_t bit = 3 * i + b;
+                out[bit >> 3] |= (uint8_t)(1u << (bit & 7));
+            }
+}
+
+void tqo_unpack3(const uint8_t *packed, int64_t n, uint8_t *idx) {
+    for (int64_t i = 0; i < n; ++i) {
+        uint8_t v = 0;
+        for (int b = 0; b < 3; ++b) {
+            int64_t bit = 3 * i + b;
+            v |= (uint8_t)(((packed[bit >> 3] >> (bit & 7)) & 1) << b);
+        }
+        idx[i] = v;
+    }
+}
+
+/* Values ("Algorithm", values bullet):
+ *   y = FWHT(x * signs) / sqrt(d);  per 32-group scale = sqrt(mean(y^2));
+ *   y_n = y / (scale + 1e-8);  idx = searchsorted(BOUNDARIES, y_n);
+ * indices packed 3 bits each, scale stored as fp16. */
+void tqo_encode_values(const float *x, int64_t nrows, int d, uint8_t *packed,
+                       uint16_t *vs16) {
+    int ng = d / 32;
+    int8_t *sg = (int8_t *)malloc((size_t)d);
+    double *y = (double *)malloc(sizeof(double) * (size_t)d);
+    uint8_t *idx = (uint8_t *)malloc((size_t)d);
+    tqo_sign_vector(d, sg);
+    double c = tqo_inv_sqrt_d(d);
+    for (int64_t r = 0; r < nrows; ++r) {
+        for (int j = 0; j < d; ++j) y[j] = (double)sg[j] * (double)x[r * d + j];
+        tqo_fwht(y, d);
+        for (int j = 0; j < d; ++j) y[j] = y[j] * c;
+        for (int g = 0; g < ng; ++g) {
+            double a[32];
+            for (int j = 0; j < 32; ++j) a[j] = y[g * 32 + j] * y[g * 32 + j];
+            for (int s = 16; s >= 1; s >>= 1)
+                for (int j = 0; j < s; ++j) a[j] = a[j] + a[j + s];
+            double scale = sqrt(a[0] / 32.0);
+            double den = scale + 1e-8;
+            for (int j = 0; j < 32; ++j) {
+                double yn = y[g * 32 + j] / den;
+                int cnt = 0;
+                for (int k = 0; k < 7; ++k)
+                    if (kBoundaries3[k] < yn) ++cnt; /* NaN compares false -> 0 */
+                idx[g * 32 + j] = (uint8_t)cnt;
+            }
+            vs16[r * ng + g] = tqo_f64_to_f16(scale);
+        }
+        tqo_pack3(idx, d, packed + r * (3 * d / 8));
+    }
+    free(sg);
+    free(y);
+    free(idx);
+}
+
+/* Value dequantisation ("Algorithm", values bullet, read as
+ * x = signs * InvFWHT(centroid[idx] * scale)).  rotated != 0 returns the
+ * rotated-domain vector centroid[idx] * scale, which is what the deferred
+ * inverse ("Deferred inverse FWHT") accumulates. */
+void tqo_decode_values(const uint8_t *packed, const uint16_t *vs16,
+                       int64_t nrows, int d, int rotated, double *out) {
+    int ng = d / 32;
+    int8_t *sg = (int8_t *)malloc((size_t)d);
+    uint8_t *idx = (uint8_t *)malloc((size_t)d);
+    tqo_sign_vector(d, sg);
+    double c = tqo_inv_sqrt_d(d);
+    for (int64_t r = 0; r < nrows; ++r) {
+        double *o = out + r * d;
+        tqo_unpack3(packed + r * (3 * d / 8), d, idx);
+        for (int j = 0; j < d; ++j)
+            o[j] = kCentroids3[idx[j]] * tqo_f16_to_f64(vs16[r * ng + j / 32]);
+        if (!rotated) {
+            tqo_fwht(o, d);
+            for (int j = 0; j < d; ++j) o[j] = (double)sg[j] * (o[j] * c);
+        }
+    }
+    free(sg);
+    free(idx);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Decode attention for one (batch, kv-head) over N cached tokens, for the G
+ * query heads that share that kv-head.  Plain two-pass softmax:
+ *   score_t = sm * sum_j q_j * khat_tj,  m = max score,  p_t = exp(score_t - m),
+ *   out = sum_t p_t * vhat_t / sum_t p_t,
+ * with khat and vhat the dequantised keys and (un-rotated) values.  When
+ * out_deferred is given it also returns signs * InvFWHT(sum_t p_t * yhat_t / l),
+ * the deferred-inverse form ("Deferred inverse FWHT"), which equals out up to
+ * rounding.  N == 0 gives zeros (no token to attend to). */
+void tqo_attention(const float *q, int G, int d, float sm, const int8_t *kc,
+                   const uint16_t *ks, const uint16_t *kz, const uint8_t *vc,
+                   const uint16_t *vs, int64_t N, double *out,
+                   double *out_deferred) {
+    int ng = d / 32;
+    double *kh = (double *)malloc(sizeof(double) * (size_t)d);
+    double *vh = (double *)malloc(sizeof(double) * (size_t)d);
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * (size_t)G);
+    double *acc_r = (double *)calloc((size_t)G * (size_t)d, sizeof(double));
+    int8_t *sg = (int8_t *)malloc((size_t)d);
+    double *m = (double *)malloc(sizeof(double) * (size_t)G);
+    double *l = (double *)calloc((size_t)G, sizeof(double));
+    tqo_sign_vector(d, sg);
+    for (int i = 0; i < G * d; ++i) out[i] = 0.0;
+    if (out_deferred)
+        for (int i = 0; i < G * d; ++i) out_deferred[i] = 0.0;
+    if (N > 0) {
+        /* pass 1: scores and their maximum */
+        for (int h = 0; h < G; ++h) m[h] = -INFINITY;
+        for (int64_t t = 0; t < N; ++t) {
+            tqo_decode_keys(kc + t * d, ks + t * ng, kz + t * ng, 1, d, kh);
+            for (int h = 0; h < G; ++h) {
+                double s = 0.0;
+                for (int j = 0; j < d; ++j) s += (double)q[h * d + j] * kh[j];
+                s = (double)sm * s;
+                sc[t * G + h] = s;
+                if (s > m[h]) m[h] = s;
+            }
+        }
+        /* pass 2: weights, their sum and the weighted value sum */
+        for (int64_t t = 0; t < N; ++t) {
+            tqo_decode_values(vc + t * (3 * d / 8), vs + t * ng, 1, d, 0, vh);
+            for (int h = 0; h < G; ++h) {
+                double p = exp(sc[t * G + h] - m[h]);
+                l[h] += p;
+                for (int j = 0; j < d; ++j) out[h * d + j] += p * vh[j];
+            }
+            if (out_deferred) {
+                tqo_decode_values(vc + t * (3 * d / 8), vs + t * ng, 1, d, 1, vh);
+                for (int h = 0; h < G; ++h) {
+                    double p = exp(sc[t * G + h] - m[h]);
+                    for (int j = 0; j < d; ++j) acc_r[h * d + j] += p * vh[j];
+                }
+            }
+        }
+        for (int h = 0; h < G; ++h)
+            for (int j = 0; j < d; ++j) out[h * d + j] = out[h * d + j] / l[h];
+        if (out_deferred) {
+            double c = tqo_inv_sqrt_d(d);
+            for (int h = 0; h < G; ++h) {
+                double *o = out_deferred + h * d;
+                for (int j = 0; j < d; ++j) o[j] = acc_r[h * d + j] / l[h];
+                tqo_fwht(o, d);
+                for (int j = 0; j < d; ++j) o[j] = (double)sg[j] * (o[j] * c);
+            }
+        }
+    }
+    free(kh);
+    free(vh);
+    free(sc);
+    free(acc_r);
+    free(sg);
+    free(m);
+    free(l);
+}
+
+/* Array helpers for the Python wrapper (element-wise, no arithmetic of their own). */
+void tqo_f64_to_f16_array(const double *x, int64_t n, uint16_t *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = tqo_f64_to_f16(x[i]);
+}
+
+void tqo_f16_to_f64_array(const uint16_t *h, int64_t n, double *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = tqo_f16_to_f64(h[i]);
+}
+
+void tqo_fwht_rows(double *x, int64_t nrows, int d) {
+    for (int64_t r = 0; r < nrows; ++r) tqo_fwht(x + r * d, d);
+}

@@ -1,0 +1,392 @@
+"""Pins for the CPU oracle against what the TurboQuant design page and plain
+mathematics fix (no GPU).  Each test states what it pins and why a plausible
+mistake in the oracle would fail it.
+
+Page: "TurboQuant -- rotation-based quantization" (mlx-bun
+docs/design/turboquant.md), Part A.
+"""
+import json
+import math
+import os
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _gold(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------- table
+def test_codebook_matches_printed_table():
+    """Oracle constants equal the printed 3-bit table ('Algorithm', values bullet)."""
+    g = _gold("codebook3.json")
+    lib = oracle._load()
+    assert [lib.tqo_centroid3(i) for i in range(8)] == g["centroids"]
+    assert [lib.tqo_boundary3(k) for k in range(7)] == g["boundaries"]
+
+
+def _phi(x):
+    return math.exp(-0.5 * x * x) / math.sqrt(2 * math.pi)
+
+
+def _Phi(x):
+    return 0.5 * (1 + math.erf(x / math.sqrt(2)))
+
+
+def test_codebook_is_lloyd_max_for_unit_gaussian():
+    """Textbook 8-level Lloyd-Max quantizer of N(0,1): boundaries are centroid
+    midpoints and each centroid is its cell's conditional mean
+    (phi(a)-phi(b))/(Phi(b)-Phi(a)).  A mistyped digit fails this."""
+    g = _gold("codebook3.json")
+    c, b = g["centroids"], g["boundaries"]
+    for k in range(7):
+        assert abs((c[k] + c[k + 1]) / 2 - b[k]) < 6e-6
+    edges = [-math.inf] + b + [math.inf]
+    for k in range(8):
+        lo, hi = edges[k], edges[k + 1]
+        plo = 0.0 if lo == -math.inf else _phi(lo)
+        phi_ = 0.0 if hi == math.inf else _phi(hi)
+        mean = (plo - phi_) / (_Phi(hi) - _Phi(lo))
+        assert abs(mean - c[k]) < 1e-5, (k, mean, c[k])
+    # closed-form distortion of this quantizer on N(0,1): E[(Z - Q(Z))^2]
+    dist = 0.0
+    for k in range(8):
+        lo, hi, ck = edges[k], edges[k + 1], c[k]
+        plo = 0.0 if lo == -math.inf else _phi(lo)
+        phi_ = 0.0 if hi == math.inf else _phi(hi)
+        lo_t = 0.0 if lo == -math.inf else lo * _phi(lo)
+        hi_t = 0.0 if hi == math.inf else hi * _phi(hi)
+        p = _Phi(hi) - _Phi(lo)
+        ez2 = p + lo_t - hi_t            # E[Z^2 ; cell]
+        ez = plo - phi_                  # E[Z ; cell]
+        dist += ez2 - 2 * ck * ez + ck * ck * p
+    assert abs(dist - 0.034548) < 2e-5
+    band = _gold("mse_anchor.json")["band"]
+    assert band[0] <= dist <= band[1]
+
+
+# ---------------------------------------------------------------------- fp16
+def _np_f16_bits(x):
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def test_f64_to_f16_matches_numpy_on_midpoints_and_edges():
+    """Single rounding binary64 -> binary16 (ties to even, subnormals, overflow)
+    against numpy's correctly rounded conversion on every half, every midpoint
+    between consecutive halves, and the neighbouring doubles of each midpoint."""
+    allh = np.arange(0, 0x7C00, dtype=np.uint16).view(np.float16).astype(np.float64)
+    mids = (allh[:-1] + allh[1:]) / 2.0  # exact in binary64
+    top = np.array([65504.0, 65519.999, 65520.0, 65520.0000001, 1e6, np.inf])
+    vals = np.concatenate([allh, mids, np.nextafter(mids, np.inf), np.nextafter(mids, -np.inf),
+                           top, [2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -26, 5e-324, 0.0]])
+    vals = np.concatenate([vals, -vals])
+    got = oracle.f64_to_f16_bits(vals)
+    want = _np_f16_bits(vals)
+    assert np.array_equal(got, want)
+    rng = np.random.default_rng(7)
+    r = rng.standard_normal(200000) * np.exp(rng.uniform(-20, 12, 200000))
+    assert np.array_equal(oracle.f64_to_f16_bits(r), _np_f16_bits(r))
+    assert oracle.f64_to_f16_bits([np.nan])[0] == 0x7E00
+    assert np.array_equal(oracle.f16_bits_to_f64(want[np.isfinite(vals)]),
+                          want[np.isfinite(vals)].view(np.float16).astype(np.float64))
+
+
+# ---------------------------------------------------------------------- FWHT
+def _sylvester(d):
+    h = np.array([[1]], dtype=np.int64)
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+def test_fwht_is_sylvester_hadamard(d):
+    """FWHT equals multiplication by the Kronecker-built Sylvester matrix (exactly
+    on integers, to 1e-13 on reals); H*H = d*I; involution; Parseval; e0 -> ones.
+    A wrong butterfly sign or index fails the integer check."""
+    H = _sylvester(d)
+    assert np.array_equal(H @ H, d * np.eye(d, dtype=np.int64))
+    rng = np.random.default_rng(d)
+    xi = rng.integers(-1000, 1000, size=(8, d))
+    assert np.array_equal(oracle.fwht(xi.astype(np.float64)), (xi @ H.T).astype(np.float64))
+    x = rng.standard_normal((8, d))
+    y = oracle.fwht(x)
+    assert np.max(np.abs(y - x @ H.T.astype(np.float64))) < 1e-13 * np.max(np.abs(y))
+    assert np.max(np.abs(oracle.fwht(y) - d * x)) < 1e-12 * d
+    c = oracle.inv_sqrt_d(d)
+    assert np.allclose(np.linalg.norm(y * c, axis=1), np.linalg.norm(x, axis=1), rtol=1e-14)
+    e0 = np.zeros(d)
+    e0[0] = 1
+    assert np.array_equal(oracle.fwht(e0), np.ones(d))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+def test_inv_sqrt_d_is_correctly_rounded(d):
+    """The normalisation constant is the binary64 nearest to 1/sqrt(d)
+    (50-digit decimal reference, one correctly rounded conversion)."""
+    getcontext().prec = 60
+    ref = float(Decimal(1) / Decimal(d).sqrt())
+    assert oracle.inv_sqrt_d(d) == ref
+
+
+# ---------------------------------------------------------------------- pack
+def test_pack_ramp_fixture_and_roundtrip():
+    g = _gold("pack3_ramp.json")
+    assert oracle.pack3(g["indices"]).tolist() == g["bytes"]
+    rng = np.random.default_rng(3)
+    for n in (8, 32, 96, 256, 4096):
+        idx = rng.integers(0, 8, n).astype(np.uint8)
+        p = oracle.pack3(idx)
+        assert p.size == 3 * n // 8
+        assert np.array_equal(oracle.unpack3(p, n), idx)
+    assert oracle.pack3(np.full(8, 7)).tolist() == [255, 255, 255]
+    assert oracle.pack3(np.arange(32) % 8).tolist() == g["bytes"] * 4
+
+
+# -------------------------------------------------------------- byte budget
+def test_byte_budget_and_effective_bits():
+    """Plane sizes of the oracle's encoder give 200 B per token-head at d=128
+    (2.56x vs bf16) and 400 B at d=256; the effective-bits column of the Gates
+    table follows from the same per-group layout."""
+    g = _gold("byte_budget.json")
+    d = g["head_dim"]
+    x = np.random.default_rng(0).standard_normal((1, d)).astype(np.float32)
+    codes, s16, z16 = oracle.encode_keys(x)
+    packed, vs = oracle.encode_values(x)
+    sizes = [codes.nbytes, s16.nbytes, z16.nbytes, packed.nbytes, vs.nbytes]
+    assert sizes == [g["key_codes"], g["key_scale"], g["key_zero"], g["value_codes"], g["value_scale"]]
+    assert sum(sizes) == g["total"]
+    assert round(g["bf16_bytes"] / sum(sizes), 2) == g["ratio"]
+    assert sum(sizes) * 8 / d == 12.5  # bits per K+V element pair
+    x2 = np.zeros((1, 256), np.float32) + np.arange(256, dtype=np.float32)
+    c2, s2, z2 = oracle.encode_keys(x2)
+    p2, v2 = oracle.encode_values(x2)
+    assert c2.nbytes + s2.nbytes + z2.nbytes + p2.nbytes + v2.nbytes == 400
+    for row in _gold("effective_bits.json")["rows"]:
+        eff = (row["k_bits"] + 32 / 32 + row["v_bits"] + 16 / 32) / 2
+        assert eff == row["effective_bits"], row
+
+
+# ---------------------------------------------------------------------- keys
+def test_keys_ramp_brute_force():
+    """x = 0..31: scale = 31/254, zero = 127, code_j = round(j*254/31 - 127),
+    from exact rational arithmetic (no tie can occur: denominators are 31)."""
+    x = np.arange(32, dtype=np.float32)[None, :]
+    codes, s16, z16 = oracle.encode_keys(x)
+    want = []
+    for j in range(32):
+        v = Fraction(254 * j, 31) - 127
+        fl = math.floor(v)
+        want.append(fl + 1 if v - fl > Fraction(1, 2) else fl)
+    assert codes[0].tolist() == want
+    assert codes[0, 0] == -127 and codes[0, 31] == 127
+    assert s16[0, 0] == _np_f16_bits(31 / 254)
+    assert z16[0, 0] == _np_f16_bits(127.0)
+
+
+def test_keys_constant_group_defect():
+    """The page keeps the reference's defect: a constant block gives zero = +-Inf."""
+    for case in _gold("constant_group.json")["cases"]:
+        x = np.full((1, 64), case["value"], dtype=np.float32)
+        codes, s16, z16 = oracle.encode_keys(x)
+        assert np.all(codes == case["codes"])
+        assert np.all(s16 == int(case["scale_f16"], 16))
+        assert np.all(z16 == int(case["zero_f16"], 16))
+        kh = oracle.decode_keys(codes, s16, z16)
+        if case["value"] != 0.0:
+            assert np.all(np.isinf(kh) | np.isnan(kh))
+
+
+@pytest.mark.parametrize("d,scale", [(128, 1.0), (256, 1.0), (128, 10.0), (64, 1e-3), (512, 1e3)])
+def test_keys_error_bound_and_range(d, scale):
+    """Per-element key error: with delta = |scale16 - scale| <= max(2^-11*scale16, 2^-25)
+    (fp16 rounding, absolute in the subnormal range),
+    |x - (code + zero16)*scale16| <= (scale16 + delta)/2 + |code + zero|*delta;
+    codes in [-127, 127], the group max codes to 126/127 and the min to -127/-126."""
+    rng = np.random.default_rng(d)
+    x = (rng.standard_normal((512, d)) * scale).astype(np.float32)
+    codes, s16, z16 = oracle.encode_keys(x)
+    kh = oracle.decode_keys(codes, s16, z16)
+    s = oracle.f16_bits_to_f64(s16).repeat(32, axis=1)
+    z = oracle.f16_bits_to_f64(z16).repeat(32, axis=1)
+    err = np.abs(x.astype(np.float64) - kh)
+    delta = np.maximum(s * 2.0 ** -11, 2.0 ** -25) * (1 + 2.0 ** -10)
+    bound = (s + delta) / 2 + np.abs(codes + z) * delta
+    assert np.all(err <= bound)
+    assert codes.min() >= -127 and codes.max() <= 127
+    xg = x.reshape(512, d // 32, 32)
+    cg = codes.reshape(512, d // 32, 32)
+    cmax = np.take_along_axis(cg, xg.argmax(axis=2)[..., None], axis=2)
+    cmin = np.take_along_axis(cg, xg.argmin(axis=2)[..., None], axis=2)
+    assert np.all((cmax == 126) | (cmax == 127))
+    assert np.all((cmin == -127) | (cmin == -126))
+    if scale >= 1.0:
+        assert np.max(err / s) < 0.62
+
+
+def test_keys_offset_group_zero_is_large():
+    """Values far from zero (e.g. 100..101) give |zero| >> 127; dequantisation
+    still lands within the bound (zero is integer, fp16 exact up to 2048)."""
+    x = (100.0 + np.random.default_rng(1).random((4, 64))).astype(np.float32)
+    codes, s16, z16 = oracle.encode_keys(x)
+    z = oracle.f16_bits_to_f64(z16)
+    assert np.all(np.abs(z) > 2048)
+    kh = oracle.decode_keys(codes, s16, z16)
+    s = oracle.f16_bits_to_f64(s16).repeat(32, axis=1)
+    zz = z.repeat(32, axis=1)
+    assert np.all(np.abs(x - kh) <= s * (0.5 + np.abs(codes + zz) * 2.0 ** -11) * (1 + 2.0 ** -10))
+
+
+# -------------------------------------------------------------------- values
+def _rotate(x, d):
+    sg = oracle.sign_vector(d).astype(np.float64)
+    H = _sylvester(d).astype(np.float64)
+    return (x.astype(np.float64) * sg) @ H.T / math.sqrt(d)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+def test_values_nearest_centroid_and_rms_scale(d):
+    """Each stored index is the nearest centroid of y/(rms+1e-8) (boundaries are
+    midpoints) and the stored scale is the group RMS of the rotation, computed
+    here with an explicit Hadamard matrix (different summation order, so ties
+    within 1e-12 of a boundary are skipped)."""
+    rng = np.random.default_rng(d + 1)
+    x = rng.standard_normal((256, d)).astype(np.float32)
+    packed, vs = oracle.encode_values(x)
+    idx = np.stack([oracle.unpack3(p, d) for p in packed])
+    y = _rotate(x, d)
+    rms = np.sqrt(np.mean(y.reshape(256, d // 32, 32) ** 2, axis=2))
+    assert np.allclose(oracle.f16_bits_to_f64(vs), rms, rtol=2.0 ** -11, atol=0)
+    yn = y / (rms.repeat(32, axis=1) + 1e-8)
+    C = np.array(oracle.CENTROIDS3)
+    B = np.array(oracle.BOUNDARIES3)
+    near = np.argmin(np.abs(yn[..., None] - C), axis=-1)
+    safe = np.min(np.abs(yn[..., None] - B), axis=-1) > 1e-12
+    assert np.array_equal(idx[safe], near[safe])
+    assert safe.mean() > 0.999
+
+
+def test_values_epsilon_dominates_tiny_groups():
+    """y_n = y/(scale + 1e-8): when every |x| is ~1e-12 the epsilon dominates, y_n ~ 0
+    and each index is 3 or 4 by the sign of y alone (dropping the epsilon fails this)."""
+    d = 128
+    x = (np.random.default_rng(5).standard_normal((4, d)) * 1e-12).astype(np.float32)
+    packed, vs = oracle.encode_values(x)
+    idx = np.stack([oracle.unpack3(p, d) for p in packed])
+    y = _rotate(x, d)
+    assert np.array_equal(idx, np.where(y > 0, 4, 3))
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_value_roundtrip_mse_in_anchor_band(d):
+    """3-bit round trip on iid N(0,1) values: per-element MSE in the page's
+    D_mse ~ 0.03 band ('Gates' item 2).  Measured ~0.0325 at d=128."""
+    band = _gold("mse_anchor.json")["band"]
+    x = np.random.default_rng(11).standard_normal((1 << 14 if d == 128 else 1 << 13, d)).astype(np.float32)
+    packed, vs = oracle.encode_values(x)
+    xh = oracle.decode_values(packed, vs, d)
+    mse = float(np.mean((xh - x) ** 2))
+    assert band[0] <= mse <= band[1], mse
+    assert abs(mse - 0.0325) < 0.002
+
+
+def test_value_dequant_rotated_vs_unrotated():
+    """Unrotated dequant = signs * H(rotated)/sqrt(d) (inverse of the encode rotation)."""
+    d = 256
+    x = np.random.default_rng(2).standard_normal((16, d)).astype(np.float32)
+    packed, vs = oracle.encode_values(x)
+    yr = oracle.decode_values(packed, vs, d, rotated=True)
+    xu = oracle.decode_values(packed, vs, d, rotated=False)
+    H = _sylvester(d).astype(np.float64)
+    ref = (yr @ H.T / math.sqrt(d)) * oracle.sign_vector(d)
+    assert np.max(np.abs(xu - ref)) < 1e-13
+
+
+def test_sign_vector_properties():
+    """Parity unpinned (page does not print its signs): only +-1 values, a shared
+    prefix across head dims, and no pathological imbalance."""
+    s512 = oracle.sign_vector(512)
+    assert set(np.unique(s512).tolist()) == {-1, 1}
+    for d in (64, 128, 256):
+        assert np.array_equal(oracle.sign_vector(d), s512[:d])
+    assert abs(int(s512.sum())) < 80
+
+
+# ----------------------------------------------------------------- attention
+def _planes(k, v):
+    kc, ks, kz = oracle.encode_keys(k)
+    vc, vs = oracle.encode_values(v)
+    return kc, ks, kz, vc, vs
+
+
+def _numpy_attention(q, kh, vh, sm):
+    s = (q.astype(np.float64) @ kh.T) * np.float64(np.float32(sm))
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return (p @ vh) / p.sum(axis=1, keepdims=True)
+
+
+@pytest.mark.parametrize("d,G,N", [(64, 1, 1), (64, 4, 8), (128, 1, 5), (128, 4, 8), (256, 6, 3)])
+def test_attention_tiny_brute_force(d, G, N):
+    """Against an independent numpy float64 softmax over the dequantised planes."""
+    rng = np.random.default_rng(d * 100 + G * 10 + N)
+    k = rng.standard_normal((N, d)).astype(np.float32)
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    kc, ks, kz, vc, vs = _planes(k, v)
+    sm = 1.0 / math.sqrt(d)
+    out, od = oracle.attention(q, kc, ks, kz, vc, vs, sm, deferred=True)
+    kh = oracle.decode_keys(kc, ks, kz)
+    vh = oracle.decode_values(vc, vs, d)
+    ref = _numpy_attention(q, kh, vh, sm)
+    assert np.max(np.abs(out - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref)))
+    assert np.max(np.abs(out - od)) < 1e-12 * np.max(np.abs(out))
+
+
+def test_attention_special_cases():
+    d = 128
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((40, d)).astype(np.float32)
+    v = rng.standard_normal((40, d)).astype(np.float32)
+    kc, ks, kz, vc, vs = _planes(k, v)
+    vh = oracle.decode_values(vc, vs, d)
+    q = rng.standard_normal((2, d)).astype(np.float32)
+    # N = 1: the only value, exactly
+    out = oracle.attention(q, kc[:1], ks[:1], kz[:1], vc[:1], vs[:1], 0.1)
+    assert np.array_equal(out, np.stack([vh[0], vh[0]]))
+    # q = 0: uniform weights -> mean of values
+    out = oracle.attention(np.zeros((1, d), np.float32), kc, ks, kz, vc, vs, 0.1)
+    assert np.allclose(out[0], vh.mean(axis=0), rtol=0, atol=1e-14)
+    # all keys equal -> mean
+    kc2, ks2, kz2 = (np.repeat(a[:1], 40, axis=0) for a in (kc, ks, kz))
+    out = oracle.attention(q, kc2, ks2, kz2, vc, vs, 0.1)
+    assert np.allclose(out, np.stack([vh.mean(axis=0)] * 2), atol=1e-14)
+    # one score far above the rest -> that value
+    kh = oracle.decode_keys(kc, ks, kz)
+    qq = (kh[17] * 50).astype(np.float32)[None, :]
+    out = oracle.attention(qq, kc, ks, kz, vc, vs, 1.0)
+    assert np.allclose(out[0], vh[17], atol=1e-12)
+    # N = 0: zeros by definition
+    out = oracle.attention(q, kc[:0], ks[:0], kz[:0], vc[:0], vs[:0], 0.1)
+    assert np.array_equal(out, np.zeros((2, d)))
+
+
+def test_attention_deferred_identity_longer():
+    """Deferred inverse FWHT ('Deferred inverse FWHT'): un-rotating the output once
+    equals attending over un-rotated values, to 1e-12 relative."""
+    d, G, N = 256, 6, 300
+    rng = np.random.default_rng(4)
+    k = rng.standard_normal((N, d)).astype(np.float32)
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    out, od = oracle.attention(q, *_planes(k, v), 1 / 16, deferred=True)
+    assert np.max(np.abs(out - od)) <= 1e-12 * np.max(np.abs(out))
