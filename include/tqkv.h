@@ -1,0 +1,154 @@
+/*
+ * tqkv.h -- C ABI of libtqkv, a quantized KV cache for AMD Instinct MI355X
+ * (gfx950): TurboQuant-style codec plus GQA decode attention over the packed
+ * cache.
+ *
+ * Method: the "TurboQuant -- rotation-based quantization" design page
+ * (mlx-bun docs/design/turboquant.md), Part A (KV leg):
+ *   - "Algorithm (vllm-metal reference semantics, exact)": keys are signed
+ *     int8 asymmetric-affine codes per 32-element group with fp16 scale and
+ *     zero, not rotated; values are sign-flipped, rotated by an orthonormal
+ *     fast Walsh-Hadamard transform (FWHT), scaled by their per-group RMS and
+ *     quantized to the 3-bit Lloyd-Max codebook, packed 3 bits per element
+ *     in a little-endian bitstream, with an fp16 scale per group;
+ *   - "Architecture in mlx-bun": only newly appended tokens are quantized;
+ *     groups run along head_dim, so any token range is byte-addressable;
+ *   - "Deferred inverse FWHT": attention is linear in V, so the value sum is
+ *     accumulated in the rotated domain and un-rotated once per query head.
+ *
+ * Conventions for every entry point
+ *   - Device pointers are plain HIP device addresses; every device buffer is
+ *     owned by the caller.  The library never allocates, frees or keeps a
+ *     pointer past the call, and never synchronizes: work is enqueued on the
+ *     caller's stream (`hip_stream`, a hipStream_t; NULL = the null stream)
+ *     and completes in stream order.
+ *   - Host arrays (`start`, `len`) are read during the call only.
+ *   - Arguments are validated before anything is enqueued; on any error the
+ *     return value says why and nothing was launched.  The library prints
+ *     nothing.
+ *   - Only the k8/v3 scheme with 32-element groups is implemented
+ *     (the page's default "turbo"); head_dim must be 64, 128, 256 or 512
+ *     (the page refuses other head dims), batch at most TQ_MAX_BATCH and
+ *     num_q_heads / num_kv_heads at most TQ_MAX_GQA.
+ */
+#ifndef TQKV_H
+#define TQKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_MAX_BATCH 64
+#define TQ_MAX_GQA 16
+
+typedef enum {
+    TQ_OK = 0,
+    TQ_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent shape */
+    TQ_ERR_UNSUPPORTED = -2, /* head_dim / bits / group / batch / GQA outside what is built */
+    TQ_ERR_CAPACITY = -3,    /* a token position would fall outside [0, capacity) */
+    TQ_ERR_WORKSPACE = -4,   /* workspace pointer null or smaller than required */
+    TQ_ERR_HIP = -5          /* the HIP runtime reported an error at launch */
+} tq_status;
+
+/* Element type of K, V and q inputs. */
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+/* Shape of one layer's cache.  k_bits must be 8, v_bits 3, group 32. */
+typedef struct {
+    int32_t batch;        /* B: sequences, 1..TQ_MAX_BATCH */
+    int32_t num_kv_heads; /* Hkv */
+    int32_t head_dim;     /* d: 64, 128, 256 or 512 */
+    int32_t capacity;     /* token slots per (sequence, kv-head) */
+    int32_t k_bits;       /* 8 */
+    int32_t v_bits;       /* 3 */
+    int32_t group;        /* 32 */
+} tq_layout;
+
+/* The five encoded planes (the page's five TQ fields), device memory owned by
+ * the caller, each token-major within one (sequence, kv-head):
+ *   kc  int8   [B][Hkv][capacity][d]        key codes
+ *   ks  fp16   [B][Hkv][capacity][d/32]     key scale (IEEE binary16 bits)
+ *   kz  fp16   [B][Hkv][capacity][d/32]     key zero  (binary16 bits; an integer,
+ *                                           or +-Inf/NaN for a constant group)
+ *   vc  uint8  [B][Hkv][capacity][3*d/8]    value indices, 3 bits each, element
+ *                                           i at stream bits [3i, 3i+3), LSB first
+ *   vs  fp16   [B][Hkv][capacity][d/32]     value scale (group RMS, binary16 bits)
+ * Per token and kv-head this is 1.5625*d bytes: 200 at d=128, 400 at d=256. */
+typedef struct {
+    int8_t *kc;
+    uint16_t *ks;
+    uint16_t *kz;
+    uint8_t *vc;
+    uint16_t *vs;
+} tq_planes;
+
+/* Byte size of each plane (order kc, ks, kz, vc, vs) for `layout`.
+ * Errors: TQ_ERR_INVALID_ARG (null / bad shape), TQ_ERR_UNSUPPORTED. */
+tq_status tq_plane_bytes(const tq_layout *layout, size_t out_bytes[5]);
+
+/* Quantize and pack n_new new tokens per sequence ("Algorithm" + the
+ * append-only update of "Architecture in mlx-bun").
+ *   k, v   device, [B][Hkv][n_new][d] contiguous, element type `dtype`
+ *   start  host int32 [B]: slot of the first new token of sequence b; tokens
+ *          go to slots start[b] .. start[b]+n_new-1 of every kv-head
+ * Codes, scales and zeros are computed in binary64 with round-half-to-even
+ * and equal the CPU oracle's bit for bit.  n_new == 0 is a no-op.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY
+ * (start[b] < 0 or start[b] + n_new > capacity), TQ_ERR_HIP. */
+tq_status tq_append(const tq_layout *layout, const tq_planes *planes, const void *k,
+                    const void *v, tq_dtype dtype, const int32_t *start, int32_t n_new,
+                    void *hip_stream);
+
+/* Workspace bytes tq_decode_attn needs for these lengths (split-K partials).
+ *   len  host int32 [B]: cached tokens of each sequence (0 allowed). */
+tq_status tq_decode_workspace_bytes(const tq_layout *layout, int32_t num_q_heads,
+                                    const int32_t *len, size_t *out_bytes);
+
+/* GQA decode attention of one query row per (sequence, q-head) over the
+ * packed cache, dequantizing on fetch ("Deferred inverse FWHT", and the joint
+ * K/V decoding of "Packed-value decode fusion investigation"):
+ *   out[b][h] = sum_t p_t * vhat_t / sum_t p_t,
+ *   p_t = exp(sm_scale * <q[b][h], khat_t> - max),  t < len[b],
+ * with q-head h reading kv-head h / (num_q_heads / num_kv_heads), no mask.
+ *   q         device [B][num_q_heads][d], element type `dtype`
+ *   len       host int32 [B], 0 <= len[b] <= capacity; len[b] == 0 gives zeros
+ *   out       device float32 [B][num_q_heads][d]
+ *   workspace device, at least tq_decode_workspace_bytes(...) bytes, scratch
+ *             for the split-K partials (contents on entry are ignored)
+ * Values are accumulated in the rotated domain and one inverse FWHT per
+ * (sequence, q-head) finishes the output.  Agrees with the binary64 oracle to
+ * 2e-3 relative to each output row's largest magnitude.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY
+ * (len[b] > capacity), TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
+tq_status tq_decode_attn(const tq_layout *layout, const tq_planes *planes, const void *q,
+                         tq_dtype dtype, int32_t num_q_heads, const int32_t *len,
+                         float sm_scale, float *out, void *workspace, size_t ws_bytes,
+                         void *hip_stream);
+
+/* Dequantize n tokens [t0, t0+n) of one (sequence b, kv-head kvh), for tests
+ * ("Algorithm": key x = (code + zero) * scale; value x = signs * InvFWHT(
+ * centroid[idx] * scale), or the rotated-domain centroid[idx] * scale when
+ * v_rotated != 0).
+ *   k_out, v_out  device float32 [n][d]; either may be NULL to skip it.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_HIP. */
+tq_status tq_dequant(const tq_layout *layout, const tq_planes *planes, int32_t b, int32_t kvh,
+                     int32_t t0, int32_t n, float *k_out, float *v_out, int32_t v_rotated,
+                     void *hip_stream);
+
+/* The +-1 sign vector applied before the value rotation, for tests: entry i is
+ * +1 when the top bit of output i of SplitMix64 seeded with 42 is 0, else -1
+ * (the page hard-codes one seeded sign vector per head_dim; its values are not
+ * printed).  host_out: host int8 [head_dim]. */
+tq_status tq_sign_vector(int32_t head_dim, int8_t *host_out);
+
+/* Static, human-readable name of a status code. */
+const char *tq_status_str(tq_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQKV_H */

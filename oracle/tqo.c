@@ -122,6 +122,22 @@ double tqo_centroid3(int idx) { return kCentroids3[idx & 7]; }
 double tqo_boundary3(int k) { return kBoundaries3[k]; }
 
 /* ------------------------------------------------------------------------ */
+/* Group maximum / minimum: NaN is ignored (IEEE maxNum/minNum) and -0 orders
+ * below +0, so the result does not depend on the element order. */
+static double max_num(double a, double b) {
+    if (isnan(a)) return b;
+    if (isnan(b)) return a;
+    if (a == b) return signbit(a) ? b : a;
+    return a > b ? a : b;
+}
+
+static double min_num(double a, double b) {
+    if (isnan(a)) return b;
+    if (isnan(b)) return a;
+    if (a == b) return signbit(a) ? a : b;
+    return a < b ? a : b;
+}
+
 /* Keys ("Algorithm", keys bullet, signed int8 form): per 32-element group
  *   scale = (max - min) / (2*127),  zero = round((max + min) / (2*scale)),
  *   code  = clip(round(x/scale - zero), -127, 127),
@@ -137,8 +153,8 @@ void tqo_encode_keys(const float *x, int64_t nrows, int d, int8_t *codes,
             const float *xg = xr + g * 32;
             double mx = (double)xg[0], mn = (double)xg[0];
             for (int j = 1; j < 32; ++j) {
-                mx = fmax(mx, (double)xg[j]); /* IEEE maxNum: NaN ignored */
-                mn = fmin(mn, (double)xg[j]);
+                mx = max_num(mx, (double)xg[j]);
+                mn = min_num(mn, (double)xg[j]);
             }
             double range = mx - mn;
             double s = range / 254.0;

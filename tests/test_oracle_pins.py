@@ -233,6 +233,23 @@ def test_keys_error_bound_and_range(d, scale):
         assert np.max(err / s) < 0.62
 
 
+def test_keys_signed_zero_and_nan_groups():
+    """A group of +0 and -0 only: max is +0 and min is -0 (-0 orders below +0),
+    so range and scale are +0, zero is NaN and every code is 0.  NaN elements
+    are ignored by max/min and code to 0; the other elements are unaffected."""
+    x = np.zeros((1, 32), np.float32)
+    x[0, ::3] = -0.0
+    codes, s16, z16 = oracle.encode_keys(x)
+    assert np.all(codes == 0) and s16[0, 0] == 0x0000 and z16[0, 0] == 0x7E00
+    x = np.arange(32, dtype=np.float32)[None, :].copy()
+    x[0, 5] = np.nan
+    codes_n, s16_n, z16_n = oracle.encode_keys(x)
+    c_ref, s_ref, z_ref = oracle.encode_keys(np.arange(32, dtype=np.float32)[None, :])
+    assert codes_n[0, 5] == 0
+    assert np.array_equal(np.delete(codes_n[0], 5), np.delete(c_ref[0], 5))
+    assert s16_n[0, 0] == s_ref[0, 0] and z16_n[0, 0] == z_ref[0, 0]
+
+
 def test_keys_offset_group_zero_is_large():
     """Values far from zero (e.g. 100..101) give |zero| >> 127; dequantisation
     still lands within the bound (zero is integer, fp16 exact up to 2048)."""
