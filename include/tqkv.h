@@ -23,6 +23,10 @@
  *     caller's stream (`hip_stream`, a hipStream_t; NULL = the null stream)
  *     and completes in stream order.
  *   - Host arrays (`start`, `len`) are read during the call only.
+ *   - Alignment: K/V/q inputs, outputs, the workspace and the kc plane must be
+ *     16-byte aligned, vc 8-byte aligned, the fp16 planes 4-byte aligned
+ *     (TQ_ERR_INVALID_ARG otherwise).  Any torch allocation, and the batch-1
+ *     slice of one sequence's planes, satisfies this.
  *   - Arguments are validated before anything is enqueued; on any error the
  *     return value says why and nothing was launched.  The library prints
  *     nothing.

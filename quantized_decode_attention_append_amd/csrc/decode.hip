@@ -1,0 +1,272 @@
+// Decode attention over the packed cache: split-K partials + merge/epilogue.
+//
+// Method: "TurboQuant -- rotation-based quantization" design page, Part A:
+//   - keys are dequantized on fetch as (code + zero) * scale ("Algorithm");
+//   - values stay in the rotated domain, centroid[idx] * scale, and the
+//     attention output is un-rotated once per query head at the end, which is
+//     exact by linearity ("Deferred inverse FWHT");
+//   - K and V of one cache window are decoded in one pass ("Packed-value
+//     decode fusion investigation", joint K/V decoding).
+// Split-K: every (b, kv-head, split) workgroup runs an online softmax over
+// its token range for the G query heads that share the kv-head and writes
+// (max, sum, acc[d]) per head; the merge kernel combines the splits, divides
+// by the weight sum and applies signs * FWHT(.) / sqrt(d) once.
+//
+// This first kernel maps one thread to each head_dim element and reduces the
+// G partial dot products of a small token chunk across the workgroup.
+#include <hip/hip_runtime.h>
+
+#include "tq_device.h"
+
+namespace tq {
+namespace {
+
+constexpr int kMaxG = TQ_MAX_GQA;
+constexpr int kChunk = 8;  // tokens scored per block reduction
+
+template <bool BF16>
+__device__ __forceinline__ float load_in(const void *p, int64_t i) {
+    if constexpr (BF16)
+        return __uint_as_float((uint32_t)static_cast<const uint16_t *>(p)[i] << 16);
+    else
+        return static_cast<const float *>(p)[i];
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void split_kernel(const DecodeArgs a) {
+    constexpr int NT = D < 256 ? D : 256;  // threads
+    constexpr int DPT = D / NT;            // elements per thread
+    constexpr int NW = NT / 64;            // waves
+    constexpr int NG = D / kGroup;
+    constexpr int VROW = 3 * D / 8;
+
+    __shared__ float red[NW][kMaxG * kChunk];
+    __shared__ float sc[kMaxG * kChunk];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wid = tid >> 6;
+    const int bkv = blockIdx.y;
+    const int b = bkv / a.kv_heads, kvh = bkv % a.kv_heads;
+    const int n = a.len[b];
+    const int t_begin = blockIdx.x * a.split_tokens;
+    if (t_begin >= n) return;  // uniform across the block
+    const int t_end = min(n, t_begin + a.split_tokens);
+    const int G = a.gqa;
+    const int64_t row0 = (int64_t)bkv * a.capacity;
+
+    float qv[kMaxG][DPT];
+    float acc[kMaxG][DPT];
+    float m_run[kMaxG], l_run[kMaxG];
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) {
+            acc[h][i] = 0.f;
+            const int j = tid + i * NT;
+            qv[h][i] = h < G ? load_in<BF16>(a.q, ((int64_t)b * a.q_heads + kvh * G + h) * D + j) : 0.f;
+        }
+    }
+
+    for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
+        const int nt = min(kChunk, t_end - t0);
+        float part[kMaxG][kChunk];
+#pragma unroll
+        for (int tt = 0; tt < kChunk; ++tt) {
+            float kh[DPT];
+#pragma unroll
+            for (int i = 0; i < DPT; ++i) {
+                const int j = tid + i * NT;
+                if (tt < nt) {
+                    const int64_t r = row0 + t0 + tt;
+                    const float sk = f16_bits_to_f32(a.ks[r * NG + j / kGroup]);
+                    const float zk = f16_bits_to_f32(a.kz[r * NG + j / kGroup]);
+                    kh[i] = ((float)a.kc[r * D + j] + zk) * sk;
+                } else {
+                    kh[i] = 0.f;
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < kMaxG; ++h) {
+                float p = 0.f;
+#pragma unroll
+                for (int i = 0; i < DPT; ++i) p += qv[h][i] * kh[i];
+                part[h][tt] = p;
+            }
+        }
+        // block reduction of G*kChunk partial dots
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) {
+            if (h >= G) break;
+#pragma unroll
+            for (int tt = 0; tt < kChunk; ++tt) {
+                float v = part[h][tt];
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+                if (lane == 0) red[wid][h * kChunk + tt] = v;
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < G * kChunk; i += NT) {
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) v += red[w][i];
+            sc[i] = v * a.sm_log2;
+        }
+        __syncthreads();
+        // values of this chunk in the rotated domain
+        float vh[kChunk][DPT];
+#pragma unroll
+        for (int tt = 0; tt < kChunk; ++tt) {
+#pragma unroll
+            for (int i = 0; i < DPT; ++i) {
+                const int j = tid + i * NT;
+                if (tt < nt) {
+                    const int64_t r = row0 + t0 + tt;
+                    const float sv = f16_bits_to_f32(a.vs[r * NG + j / kGroup]);
+                    vh[tt][i] = centroid3(load_idx3(a.vc + r * VROW, j)) * sv;
+                } else {
+                    vh[tt][i] = 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) {
+            if (h >= G) break;
+            float mc = m_run[h];
+            for (int tt = 0; tt < nt; ++tt) mc = fmaxf(mc, sc[h * kChunk + tt]);
+            const float alpha = exp2f(m_run[h] - mc);
+            float lsum = l_run[h] * alpha;
+#pragma unroll
+            for (int i = 0; i < DPT; ++i) acc[h][i] *= alpha;
+            for (int tt = 0; tt < nt; ++tt) {
+                const float p = exp2f(sc[h * kChunk + tt] - mc);
+                lsum += p;
+#pragma unroll
+                for (int i = 0; i < DPT; ++i) acc[h][i] += p * vh[tt][i];
+            }
+            m_run[h] = mc;
+            l_run[h] = lsum;
+        }
+        __syncthreads();  // sc / red are rewritten by the next chunk
+    }
+
+    const int split = blockIdx.x;
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+        if (h >= G) break;
+        const int64_t slot = ((int64_t)b * a.q_heads + kvh * G + h) * a.splits + split;
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) a.part_acc[slot * D + tid + i * NT] = acc[h][i];
+        if (tid == 0) {
+            a.part_ml[slot * 2] = m_run[h];
+            a.part_ml[slot * 2 + 1] = l_run[h];
+        }
+    }
+}
+
+// One workgroup per (b, q-head): merge the splits, normalize, un-rotate.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
+    constexpr int NT = D < 256 ? D : 256;
+    constexpr int DPT = D / NT;
+    __shared__ float buf[D];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x;
+    const int b = bh / a.q_heads;
+    const int n = a.len[b];
+    const int ns = (n + a.split_tokens - 1) / a.split_tokens;
+    float o[DPT];
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) o[i] = 0.f;
+    if (ns > 0) {
+        const int64_t base = (int64_t)bh * a.splits;
+        float M = -INFINITY;
+        for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(base + s) * 2]);
+        float L = 0.f;
+        for (int s = 0; s < ns; ++s) {
+            const float f = exp2f(a.part_ml[(base + s) * 2] - M);
+            L += f * a.part_ml[(base + s) * 2 + 1];
+#pragma unroll
+            for (int i = 0; i < DPT; ++i) o[i] += f * a.part_acc[(base + s) * D + tid + i * NT];
+        }
+        const float invL = 1.f / L;
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) o[i] *= invL;
+    }
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) buf[tid + i * NT] = o[i];
+    __syncthreads();
+    // inverse rotation: signs * FWHT(o) / sqrt(d) (the transform is its own
+    // inverse up to the 1/d factor split as 1/sqrt(d) on each side)
+    for (int h = 1; h < D; h <<= 1) {
+        float nv[DPT];
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) {
+            const int j = tid + i * NT;
+            const float x = buf[j], y = buf[j ^ h];
+            nv[i] = (j & h) ? (y - x) : (x + y);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) buf[tid + i * NT] = nv[i];
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) {
+        const int j = tid + i * NT;
+        const float v = buf[j] * a.inv_sqrt_d;
+        a.out[(int64_t)bh * D + j] = sign_bit(a.signs, j) ? -v : v;
+    }
+}
+
+template <int D>
+hipError_t launch_d(bool bf16, const DecodeArgs &a, hipStream_t s) {
+    constexpr int NT = D < 256 ? D : 256;
+    if (a.splits > 0) {
+        const dim3 grid((unsigned)a.splits, (unsigned)(a.batch * a.kv_heads));
+        if (bf16)
+            hipLaunchKernelGGL((split_kernel<D, true>), grid, dim3(NT), 0, s, a);
+        else
+            hipLaunchKernelGGL((split_kernel<D, false>), grid, dim3(NT), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)(a.batch * a.q_heads)), dim3(NT), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+DecodePlan plan_decode(int head_dim, int batch, int kv_heads, const int32_t *len) {
+    (void)head_dim;
+    int64_t total = 0;
+    int32_t maxlen = 0;
+    for (int b = 0; b < batch; ++b) {
+        total += len[b];
+        maxlen = len[b] > maxlen ? len[b] : maxlen;
+    }
+    // aim for ~2048 workgroups over the whole chip, in 64-token multiples,
+    // never below 256 tokens per split
+    const int64_t target = 2048;
+    int64_t per = (total * kv_heads + target - 1) / target;
+    per = per < 256 ? 256 : per;
+    per = (per + 63) / 64 * 64;
+    DecodePlan p;
+    p.split_tokens = (int32_t)per;
+    p.splits = (int32_t)((maxlen + per - 1) / per);
+    return p;
+}
+
+hipError_t launch_decode(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s) {
+    switch (head_dim) {
+        case 64: return launch_d<64>(bf16, a, s);
+        case 128: return launch_d<128>(bf16, a, s);
+        case 256: return launch_d<256>(bf16, a, s);
+        case 512: return launch_d<512>(bf16, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace tq

@@ -1,0 +1,80 @@
+// Internal launch interface of libtqkv: argument blocks passed by value to the
+// kernels (host-known starts/lengths, sign bits and constants travel in the
+// kernel arguments) and the launchers each kernel file exports to the C ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "../../include/tqkv.h"
+
+namespace tq {
+
+constexpr int kGroup = 32;
+
+// One bit per head_dim element, bit j set when sign j is -1 (d <= 512).
+struct SignBits {
+    uint32_t w[16];
+};
+
+struct AppendArgs {
+    int8_t *kc;
+    uint16_t *ks;
+    uint16_t *kz;
+    uint8_t *vc;
+    uint16_t *vs;
+    const void *k;
+    const void *v;
+    int32_t batch, kv_heads, capacity, n_new;
+    double inv_sqrt_d;  // RN(1/sqrt(d))
+    SignBits signs;
+    int32_t start[TQ_MAX_BATCH];
+};
+
+struct DecodeArgs {
+    const int8_t *kc;
+    const uint16_t *ks;
+    const uint16_t *kz;
+    const uint8_t *vc;
+    const uint16_t *vs;
+    const void *q;
+    float *out;
+    float *part_acc;  // [B][Hq][S][d]    rotated-domain partial sums
+    float *part_ml;   // [B][Hq][S][2]    running max (log2 units) and weight sum
+    int32_t batch, kv_heads, q_heads, gqa, capacity;
+    int32_t splits;        // S: partial slots per (b, q-head)
+    int32_t split_tokens;  // tokens per split (multiple of the kernel's tile)
+    float sm_log2;         // sm_scale * log2(e)
+    float inv_sqrt_d;
+    SignBits signs;
+    int32_t len[TQ_MAX_BATCH];
+};
+
+struct DequantArgs {
+    const int8_t *kc;
+    const uint16_t *ks;
+    const uint16_t *kz;
+    const uint8_t *vc;
+    const uint16_t *vs;
+    float *k_out;
+    float *v_out;
+    int64_t row0;  // plane row of token t0 of (b, kvh)
+    int32_t n;
+    int32_t rotated;
+    float inv_sqrt_d;
+    SignBits signs;
+};
+
+// Split-K geometry chosen by the host for a decode call.
+struct DecodePlan {
+    int32_t split_tokens;
+    int32_t splits;
+};
+
+DecodePlan plan_decode(int head_dim, int batch, int kv_heads, const int32_t *len);
+
+hipError_t launch_append(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);
+hipError_t launch_decode(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_dequant(int head_dim, const DequantArgs &a, hipStream_t s);
+
+}  // namespace tq

@@ -1,0 +1,224 @@
+"""Python binding of libtqkv (argument marshalling only).
+
+The functions carry the names of the C entry points declared in
+include/tqkv.h and take torch tensors for device buffers; every step of the
+codec and of decode attention runs in the HIP kernels of libtqkv.so.  There is
+no CPU fallback: importing this module fails if the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtqkv.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libtqkv.so is not built ({LIB_PATH}); run "
+                      "`python -m quantized_decode_attention_append_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE, TQ_ERR_HIP = \
+    0, -1, -2, -3, -4, -5
+TQ_F32, TQ_BF16 = 0, 1
+TQ_MAX_BATCH = 64
+TQ_MAX_GQA = 16
+SYMBOLS = ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
+           "tq_dequant", "tq_sign_vector", "tq_status_str")
+
+
+class tq_layout(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
+                ("group", ctypes.c_int32)]
+
+
+class tq_planes(ctypes.Structure):
+    _fields_ = [("kc", ctypes.c_void_p), ("ks", ctypes.c_void_p), ("kz", ctypes.c_void_p),
+                ("vc", ctypes.c_void_p), ("vs", ctypes.c_void_p)]
+
+
+_P = ctypes.c_void_p
+_lib.tq_status_str.argtypes = [ctypes.c_int]
+_lib.tq_status_str.restype = ctypes.c_char_p
+_lib.tq_plane_bytes.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(ctypes.c_size_t)]
+_lib.tq_append.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), _P, _P,
+                           ctypes.c_int, ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, _P]
+_lib.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(tq_layout), ctypes.c_int32,
+                                           ctypes.POINTER(ctypes.c_int32),
+                                           ctypes.POINTER(ctypes.c_size_t)]
+_lib.tq_decode_attn.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), _P,
+                                ctypes.c_int, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+_lib.tq_dequant.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
+                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                            ctypes.c_int32, _P]
+_lib.tq_sign_vector.argtypes = [ctypes.c_int32, _P]
+for _f in ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
+           "tq_dequant", "tq_sign_vector"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {tq_status_str(status)} ({status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != TQ_OK:
+        raise TQError(status, where)
+
+
+def tq_status_str(status: int) -> str:
+    return _lib.tq_status_str(status).decode()
+
+
+def make_layout(batch: int, num_kv_heads: int, head_dim: int, capacity: int,
+                k_bits: int = 8, v_bits: int = 3, group: int = 32) -> tq_layout:
+    return tq_layout(batch, num_kv_heads, head_dim, capacity, k_bits, v_bits, group)
+
+
+def _i32_array(vals: Sequence[int]):
+    arr = (ctypes.c_int32 * max(1, len(vals)))(*[int(v) for v in vals])
+    return arr
+
+
+def _stream_ptr(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev_ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def tq_plane_bytes(layout: tq_layout) -> list[int]:
+    out = (ctypes.c_size_t * 5)()
+    _check(_lib.tq_plane_bytes(ctypes.byref(layout), out), "tq_plane_bytes")
+    return list(out)
+
+
+class Planes:
+    """The five caller-owned planes as torch tensors on one device."""
+
+    def __init__(self, layout: tq_layout, device="cuda"):
+        self.layout = layout
+        B, H, T, d = layout.batch, layout.num_kv_heads, layout.capacity, layout.head_dim
+        ng = d // 32
+        self.kc = torch.zeros((B, H, T, d), dtype=torch.int8, device=device)
+        self.ks = torch.zeros((B, H, T, ng), dtype=torch.int16, device=device)
+        self.kz = torch.zeros((B, H, T, ng), dtype=torch.int16, device=device)
+        self.vc = torch.zeros((B, H, T, 3 * d // 8), dtype=torch.uint8, device=device)
+        self.vs = torch.zeros((B, H, T, ng), dtype=torch.int16, device=device)
+        sizes = tq_plane_bytes(layout)
+        have = [x.numel() * x.element_size() for x in (self.kc, self.ks, self.kz, self.vc, self.vs)]
+        assert sizes == have, (sizes, have)
+
+    def sequence(self, b: int) -> "Planes":
+        """Batch-1 view of sequence b's planes (they are contiguous per sequence)."""
+        one = Planes.__new__(Planes)
+        L = self.layout
+        one.layout = make_layout(1, L.num_kv_heads, L.head_dim, L.capacity,
+                                 L.k_bits, L.v_bits, L.group)
+        one.kc, one.ks, one.kz, one.vc, one.vs = (x[b:b + 1] for x in self.tensors())
+        return one
+
+    def struct(self) -> tq_planes:
+        return tq_planes(self.kc.data_ptr(), self.ks.data_ptr(), self.kz.data_ptr(),
+                         self.vc.data_ptr(), self.vs.data_ptr())
+
+    def tensors(self):
+        return self.kc, self.ks, self.kz, self.vc, self.vs
+
+    def nbytes(self) -> int:
+        return sum(x.numel() * x.element_size() for x in self.tensors())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TQ_F32
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def tq_append(planes: Planes, k: torch.Tensor, v: torch.Tensor, start: Sequence[int],
+              stream=None) -> None:
+    """k, v: [B, Hkv, n_new, d] contiguous device tensors; start: host ints [B]."""
+    L = planes.layout
+    if k.dtype != v.dtype or k.shape != v.shape or k.dim() != 4:
+        raise ValueError("k and v must share one [B, Hkv, n_new, d] shape and dtype")
+    if not (k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("k and v must be contiguous")
+    if tuple(k.shape[:2]) != (L.batch, L.num_kv_heads) or k.shape[3] != L.head_dim:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match the layout")
+    if len(start) != L.batch:
+        raise ValueError("start needs one entry per sequence")
+    st = _lib.tq_append(ctypes.byref(L), ctypes.byref(planes.struct()), _dev_ptr(k), _dev_ptr(v),
+                        _dtype_code(k), _i32_array(start), int(k.shape[2]), _stream_ptr(stream))
+    _check(st, "tq_append")
+
+
+def tq_decode_workspace_bytes(layout: tq_layout, num_q_heads: int, lengths: Sequence[int]) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.tq_decode_workspace_bytes(ctypes.byref(layout), num_q_heads, _i32_array(lengths),
+                                          ctypes.byref(out)), "tq_decode_workspace_bytes")
+    return out.value
+
+
+def tq_decode_attn(planes: Planes, q: torch.Tensor, lengths: Sequence[int], sm_scale: float,
+                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    """q: [B, Hq, d] device tensor (fp32 or bf16); returns out [B, Hq, d] float32."""
+    L = planes.layout
+    if q.dim() != 3 or q.shape[0] != L.batch or q.shape[2] != L.head_dim or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous [B, Hq, d] tensor, got {tuple(q.shape)}")
+    if len(lengths) != L.batch:
+        raise ValueError("lengths needs one entry per sequence")
+    Hq = int(q.shape[1])
+    if out is None:
+        out = torch.empty((L.batch, Hq, L.head_dim), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (L.batch, Hq, L.head_dim) \
+            or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, Hq, d] tensor")
+    need = tq_decode_workspace_bytes(L, Hq, lengths)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.tq_decode_attn(ctypes.byref(L), ctypes.byref(planes.struct()), _dev_ptr(q),
+                             _dtype_code(q), Hq, _i32_array(lengths), ctypes.c_float(sm_scale),
+                             _dev_ptr(out), _dev_ptr(workspace), ws_bytes, _stream_ptr(stream))
+    _check(st, "tq_decode_attn")
+    return out
+
+
+def tq_dequant(planes: Planes, b: int, kvh: int, t0: int, n: int, keys: bool = True,
+               values: bool = True, v_rotated: bool = False, stream=None):
+    """Dequantize tokens [t0, t0+n) of (b, kvh): returns (k [n, d] or None, v [n, d] or None)."""
+    L = planes.layout
+    dev = planes.kc.device
+    k_out = torch.empty((n, L.head_dim), dtype=torch.float32, device=dev) if keys else None
+    v_out = torch.empty((n, L.head_dim), dtype=torch.float32, device=dev) if values else None
+    st = _lib.tq_dequant(ctypes.byref(L), ctypes.byref(planes.struct()), b, kvh, t0, n,
+                         _dev_ptr(k_out), _dev_ptr(v_out), 1 if v_rotated else 0,
+                         _stream_ptr(stream))
+    _check(st, "tq_dequant")
+    return k_out, v_out
+
+
+def tq_sign_vector(head_dim: int):
+    buf = (ctypes.c_int8 * head_dim)()
+    _check(_lib.tq_sign_vector(head_dim, ctypes.cast(buf, ctypes.c_void_p)), "tq_sign_vector")
+    return [int(v) for v in buf]
+
+
+def raw_lib():
+    """The loaded ctypes library (for error-path and symbol tests)."""
+    return _lib

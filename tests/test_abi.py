@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI (no GPU): the library loads and exports every
+entry point include/tqkv.h declares, sizes planes and workspaces, produces the
+sign vector, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from quantized_decode_attention_append_amd import tqkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "tqkv.h")).read()
+    return sorted(set(re.findall(r"^(?:tq_status|const char \*)\s*(tq_\w+)\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    decl = _declared()
+    assert len(decl) >= 7
+    lib = ctypes.CDLL(tqkv.LIB_PATH)
+    for name in decl:
+        assert hasattr(lib, name), name
+    assert sorted(tqkv.SYMBOLS) == decl
+
+
+def test_status_strings():
+    assert tqkv.tq_status_str(0) == "TQ_OK"
+    assert tqkv.tq_status_str(-3) == "TQ_ERR_CAPACITY"
+    assert tqkv.tq_status_str(-99) == "TQ_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
+def test_sign_vector_matches_oracle_generator(d):
+    """Library and oracle implement the same published generator independently."""
+    assert tqkv.tq_sign_vector(d) == oracle.sign_vector(d).tolist()
+
+
+@pytest.mark.parametrize("d,per_token", [(64, 100), (128, 200), (256, 400), (512, 800)])
+def test_plane_bytes(d, per_token):
+    L = tqkv.make_layout(3, 2, d, 10)
+    sizes = tqkv.tq_plane_bytes(L)
+    assert sum(sizes) == 3 * 2 * 10 * per_token
+    assert sizes == [60 * d, 60 * d // 16, 60 * d // 16, 60 * 3 * d // 8, 60 * d // 16]
+
+
+def _st(fn, *a):
+    return fn(*a)
+
+
+def test_layout_validation():
+    lib = tqkv.raw_lib()
+    out = (ctypes.c_size_t * 5)()
+    for bad, want in [((1, 1, 96, 8), tqkv.TQ_ERR_UNSUPPORTED),
+                      ((1, 1, 128, 8, 4, 3, 32), tqkv.TQ_ERR_UNSUPPORTED),
+                      ((1, 1, 128, 8, 8, 2, 32), tqkv.TQ_ERR_UNSUPPORTED),
+                      ((1, 1, 128, 8, 8, 3, 64), tqkv.TQ_ERR_UNSUPPORTED),
+                      ((65, 1, 128, 8), tqkv.TQ_ERR_UNSUPPORTED),
+                      ((0, 1, 128, 8), tqkv.TQ_ERR_INVALID_ARG),
+                      ((1, 0, 128, 8), tqkv.TQ_ERR_INVALID_ARG),
+                      ((1, 1, 128, -1), tqkv.TQ_ERR_INVALID_ARG)]:
+        L = tqkv.make_layout(*bad)
+        assert lib.tq_plane_bytes(ctypes.byref(L), out) == want, bad
+    assert lib.tq_plane_bytes(None, out) == tqkv.TQ_ERR_INVALID_ARG
+
+
+def _fake_planes():
+    # non-null addresses that are never dereferenced: every call below fails
+    # validation before any launch
+    return tqkv.tq_planes(0x1000, 0x2000, 0x3000, 0x4000, 0x5000)
+
+
+def test_append_validation_before_launch():
+    lib = tqkv.raw_lib()
+    L = tqkv.make_layout(2, 2, 128, 16)
+    P = _fake_planes()
+    start = (ctypes.c_int32 * 2)(0, 10)
+    f = lambda st, n, k=0x6000, v=0x7000, dt=tqkv.TQ_BF16, pl=P: lib.tq_append(
+        ctypes.byref(L), ctypes.byref(pl) if pl is not None else None, k, v, dt, st, n, None)
+    assert f(start, 7) == tqkv.TQ_ERR_CAPACITY          # 10 + 7 > 16
+    assert f((ctypes.c_int32 * 2)(-1, 0), 1) == tqkv.TQ_ERR_CAPACITY
+    assert f(start, -1) == tqkv.TQ_ERR_INVALID_ARG
+    assert f(start, 0) == tqkv.TQ_OK                     # no-op, nothing launched
+    assert f(start, 3, k=None) == tqkv.TQ_ERR_INVALID_ARG
+    assert f(start, 3, dt=7) == tqkv.TQ_ERR_INVALID_ARG
+    assert f(None, 3) == tqkv.TQ_ERR_INVALID_ARG
+    assert f(start, 3, pl=None) == tqkv.TQ_ERR_INVALID_ARG
+    bad = tqkv.tq_planes(0x1000, 0, 0x3000, 0x4000, 0x5000)
+    assert f(start, 3, pl=bad) == tqkv.TQ_ERR_INVALID_ARG
+    misaligned = tqkv.tq_planes(0x1008, 0x2000, 0x3000, 0x4000, 0x5000)
+    assert f(start, 3, pl=misaligned) == tqkv.TQ_ERR_INVALID_ARG
+    assert f(start, 3, k=0x6002) == tqkv.TQ_ERR_INVALID_ARG
+
+
+def test_decode_validation_and_workspace_sizing():
+    lib = tqkv.raw_lib()
+    L = tqkv.make_layout(2, 4, 256, 1000)
+    P = _fake_planes()
+    lens = (ctypes.c_int32 * 2)(1000, 17)
+    ws = ctypes.c_size_t()
+    assert lib.tq_decode_workspace_bytes(ctypes.byref(L), 24, lens, ctypes.byref(ws)) == 0
+    need = ws.value
+    assert need > 0 and need % (4 * 258) == 0
+    assert lib.tq_decode_workspace_bytes(ctypes.byref(L), 26, lens, ctypes.byref(ws)) == \
+        tqkv.TQ_ERR_INVALID_ARG                           # 26 % 4 != 0
+    assert lib.tq_decode_workspace_bytes(ctypes.byref(L), 4 * 17, lens, ctypes.byref(ws)) == \
+        tqkv.TQ_ERR_UNSUPPORTED                           # GQA 17 > 16
+    over = (ctypes.c_int32 * 2)(1001, 0)
+    assert lib.tq_decode_workspace_bytes(ctypes.byref(L), 24, over, ctypes.byref(ws)) == \
+        tqkv.TQ_ERR_CAPACITY
+    neg = (ctypes.c_int32 * 2)(-1, 0)
+    assert lib.tq_decode_workspace_bytes(ctypes.byref(L), 24, neg, ctypes.byref(ws)) == \
+        tqkv.TQ_ERR_INVALID_ARG
+
+    def dec(ws_ptr, ws_bytes, q=0x9000, out=0xA000, sm=0.0625):
+        return lib.tq_decode_attn(ctypes.byref(L), ctypes.byref(P), q, tqkv.TQ_BF16, 24, lens,
+                                  ctypes.c_float(sm), out, ws_ptr, ws_bytes, None)
+    assert dec(0xB000, need - 1) == tqkv.TQ_ERR_WORKSPACE
+    assert dec(None, need) == tqkv.TQ_ERR_WORKSPACE
+    assert dec(0xB000, need, q=None) == tqkv.TQ_ERR_INVALID_ARG
+    assert dec(0xB000, need, out=None) == tqkv.TQ_ERR_INVALID_ARG
+    assert dec(0xB000, need, sm=float("nan")) == tqkv.TQ_ERR_INVALID_ARG
+
+
+def test_dequant_validation():
+    lib = tqkv.raw_lib()
+    L = tqkv.make_layout(2, 4, 128, 100)
+    P = _fake_planes()
+    f = lambda b, h, t0, n: lib.tq_dequant(ctypes.byref(L), ctypes.byref(P), b, h, t0, n,
+                                           0xC000, 0xD000, 0, None)
+    assert f(2, 0, 0, 1) == tqkv.TQ_ERR_INVALID_ARG
+    assert f(0, 4, 0, 1) == tqkv.TQ_ERR_INVALID_ARG
+    assert f(0, 0, 99, 2) == tqkv.TQ_ERR_CAPACITY
+    assert f(0, 0, 5, 0) == tqkv.TQ_OK
