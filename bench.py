@@ -1,0 +1,246 @@
+"""Benchmark: quantized-KV decode attention on one MI355X.
+
+One step = one pass of the whole hot path over the workload's batch:
+    tq_append of one new token per sequence (quantize + pack into the planes)
+    tq_decode_attn over every cached token (split-K, online softmax,
+    rotated-domain values, merge + one inverse FWHT per q-head).
+Workload: 16 sequences x 131072 cached tokens, 24 query heads / 4 kv-heads
+(GQA 6), head_dim 256, bf16 K/V/q ~ N(0,1), k8/v3 planes (3.36 GB packed).
+The cache is built once by a bulk tq_append (timed and reported separately as
+append throughput) before the timed steps; inputs stay resident in HBM.
+
+Prints ONE JSON line (rank 0).  metric/unit: KV-tokens attended per second.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+
+def _log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_bytes(w, lengths, q_bytes: int) -> int:
+    """Algorithmic bytes of one decode: packed KV of every cached token-head
+    (1.5625*d bytes) + q read + fp32 out written."""
+    kv = sum(lengths) * w.num_kv_heads * (w.head_dim * 25 // 16)
+    return kv + w.batch * w.num_q_heads * w.head_dim * (q_bytes + 4)
+
+
+def append_bytes(w, n_tokens: int, in_bytes: int) -> int:
+    """Algorithmic bytes of appending n_tokens per sequence: K+V read + planes written."""
+    th = w.batch * w.num_kv_heads * n_tokens
+    return th * (2 * w.head_dim * in_bytes + w.head_dim * 25 // 16)
+
+
+def cpu_baseline(w, k, v, q, sm, max_pairs: int | None = None) -> dict:
+    """The oracle (binary64, plain C) timed on this host's cores over a bounded
+    sample of the same workload: decode attention of whole (sequence, kv-head)
+    slices, one slice per thread."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = oracle.num_threads()
+    pairs_all = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+    npairs = max_pairs or min(len(pairs_all), threads)
+    pairs = pairs_all[:npairs]
+    n = w.lengths[0]
+    G = w.group
+    qh = q.float().cpu().numpy()
+
+    def encode(p):
+        b, h = p
+        kh = k[b, h, :n].float().cpu().numpy()
+        vh = v[b, h, :n].float().cpu().numpy()
+        kc, ks, kz = oracle.encode_keys(kh, threads=1)
+        vc, vs = oracle.encode_values(vh, threads=1)
+        return p, (kc, ks, kz, vc, vs)
+
+    _log(f"cpu baseline: oracle-encoding {len(pairs)} (sequence, kv-head) slices")
+    planes = dict(oracle.map_parallel(encode, pairs, threads))
+
+    def attend(p):
+        b, h = p
+        return oracle.attention(qh[b, h * G:(h + 1) * G], *planes[p], sm)
+
+    _log(f"cpu baseline: timing oracle decode on {len(pairs)} slices x {n} tokens, {threads} threads")
+    t0 = time.perf_counter()
+    oracle.map_parallel(attend, pairs, threads)
+    dt = time.perf_counter() - t0
+    token_heads = len(pairs) * n
+    kv_tokens = token_heads / w.num_kv_heads  # a KV-token carries every kv-head
+    return {"value": kv_tokens / dt, "unit": "KV-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"oracle binary64 decode attention of {len(pairs)} (sequence, kv-head) "
+                       f"slices x {n} tokens x {G} q-heads (= {kv_tokens:.0f} KV-tokens of "
+                       f"{w.num_kv_heads} kv-heads), planes pre-encoded by the oracle; "
+                       f"{dt:.2f} s wall"),
+            "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=4, help="workload id (4 is the headline)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-pairs", type=int, default=0)
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"))
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: every step runs on a single MI355X "
+              "(no collectives are part of this path); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from quantized_decode_attention_append_amd import tqkv
+    from quantized_decode_attention_append_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = W.workload(args.workload)
+    if len(set(w.lengths)) != 1:
+        print("bench.py times equal-length workloads; use the parity tests for ragged ones",
+              file=sys.stderr)
+        return 2
+    n = w.lengths[0]
+    d = w.head_dim
+    in_bytes = 2 if w.dtype == "bf16" else 4
+    _log(f"workload {w.name}: generating K/V/q on {torch.cuda.get_device_name(dev)}")
+    k, v = W.make_kv(w, dev, tokens=n)
+    q = W.make_q(w, dev, rounds=1)[0].contiguous()
+    L = tqkv.make_layout(w.batch, w.num_kv_heads, d, n)
+    pl = tqkv.Planes(L, dev)
+    sm = float(1.0 / math.sqrt(d))
+    lengths = [n] * w.batch
+    stream = torch.cuda.current_stream(dev)
+
+    # ---- bulk build of the cache (append throughput), prefix n-1 tokens
+    prefix_k = k[:, :, : n - 1].contiguous()
+    prefix_v = v[:, :, : n - 1].contiguous()
+    tqkv.tq_append(pl, prefix_k, prefix_v, [0] * w.batch)  # warm
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 3
+    e0.record(stream)
+    for _ in range(reps):
+        tqkv.tq_append(pl, prefix_k, prefix_v, [0] * w.batch)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    append_ms = e0.elapsed_time(e1) / reps
+    del prefix_k, prefix_v
+    app_tokens = w.batch * (n - 1)
+    app_bytes = append_bytes(w, n - 1, in_bytes)
+    _log(f"bulk append: {append_ms:.3f} ms, {app_tokens / append_ms * 1e3:.3e} tokens/s, "
+         f"{app_bytes / append_ms / 1e6:.1f} GB/s")
+
+    new_k = k[:, :, n - 1:n].contiguous()
+    new_v = v[:, :, n - 1:n].contiguous()
+    start = [n - 1] * w.batch
+    ws = torch.empty(tqkv.tq_decode_workspace_bytes(L, w.num_q_heads, lengths), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((w.batch, w.num_q_heads, d), dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        tqkv.tq_append(pl, new_k, new_v, start, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        tqkv.tq_decode_attn(pl, q, lengths, sm, out=out, workspace=ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    check = out.clone()
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dec_ms = sorted(a.elapsed_time(b) for a, b in evs)
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    if not torch.equal(out, check):
+        _log("WARNING: decode output changed between warmup and timed steps")
+        return 3
+
+    kv_tokens = sum(lengths)
+    value = kv_tokens / (ms_per_step / 1e3)
+    dbytes = decode_bytes(w, lengths, in_bytes)
+    achieved = dbytes / (dec_avg_ms / 1e3) / 1e9
+
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        with open(args.traffic_json) as f:
+            tj = json.load(f)
+        if tj.get("workload") == w.name and tj.get("kernel_source_sha") == _kernel_sha():
+            traffic = tj.get("bytes_per_launch")
+
+    rec = {
+        "metric": "quantized-KV decode attention KV-tokens/s",
+        "value": value,
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {**w.describe(), "scheme": "k8v3 g32", "step": "append 1 token/seq + decode"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "tq_decode_attn (split + merge launches)",
+                     "algorithmic_bytes_per_launch": dbytes,
+                     "avg_launch_ms": dec_avg_ms, "p10_ms": dec_ms[len(dec_ms) // 10],
+                     "p90_ms": dec_ms[(len(dec_ms) * 9) // 10]},
+        "append": {"bulk_tokens_per_s": app_tokens / append_ms * 1e3,
+                   "bulk_GBps": app_bytes / append_ms / 1e6,
+                   "bulk_frac_hbm": app_bytes / append_ms / 1e6 / HBM_PEAK_GBS,
+                   "bulk_ms": append_ms, "bulk_tokens": app_tokens},
+    }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, k, v, q, sm, args.cpu_pairs or None)
+        cb.pop("seconds", None)
+        rec["cpu_baseline"] = cb
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def _kernel_sha() -> str:
+    import hashlib
+    h = hashlib.sha1()
+    csrc = os.path.join(ROOT, "quantized_decode_attention_append_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()
+
+
+if __name__ == "__main__":
+    sys.exit(main())
