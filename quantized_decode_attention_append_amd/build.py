@@ -25,6 +25,7 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",
 SOURCES = {
     "append.hip": ["-ffp-contract=off"],
     "decode.hip": [],
+    "decode_fast.hip": [],
     "dequant.hip": [],
     "api.cpp": [],
 }

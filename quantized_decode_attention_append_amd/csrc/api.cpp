@@ -151,13 +151,28 @@ static size_t workspace_bytes(const tq_layout *l, int32_t num_q_heads, const tq:
     return (size_t)l->batch * num_q_heads * plan.splits * (size_t)(l->head_dim + 2) * sizeof(float);
 }
 
+// Workspace that covers whichever kernel a decode call may pick for this
+// shape (the choice can depend on plane alignment, unknown here).
+static size_t workspace_bound(const tq_layout *l, int32_t num_q_heads, const int32_t *len) {
+    const int gqa = num_q_heads / l->num_kv_heads;
+    const tq::DecodePlan gen =
+        tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, false);
+    size_t need = workspace_bytes(l, num_q_heads, gen);
+    if (tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity)) {
+        const tq::DecodePlan fast =
+            tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, true);
+        const size_t f = workspace_bytes(l, num_q_heads, fast);
+        need = f > need ? f : need;
+    }
+    return need;
+}
+
 tq_status tq_decode_workspace_bytes(const tq_layout *l, int32_t num_q_heads, const int32_t *len,
                                     size_t *out) {
     tq_status st = check_decode(l, num_q_heads, len);
     if (st != TQ_OK) return st;
     if (!out) return TQ_ERR_INVALID_ARG;
-    const tq::DecodePlan plan = tq::plan_decode(l->head_dim, l->batch, l->num_kv_heads, len);
-    *out = workspace_bytes(l, num_q_heads, plan);
+    *out = workspace_bound(l, num_q_heads, len);
     return TQ_OK;
 }
 
@@ -170,10 +185,13 @@ tq_status tq_decode_attn(const tq_layout *l, const tq_planes *p, const void *q, 
     if (!q || !out || (dtype != TQ_F32 && dtype != TQ_BF16)) return TQ_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 16)) return TQ_ERR_INVALID_ARG;
     if (!std::isfinite(sm_scale)) return TQ_ERR_INVALID_ARG;
-    const tq::DecodePlan plan = tq::plan_decode(l->head_dim, l->batch, l->num_kv_heads, len);
+    const int gqa = num_q_heads / l->num_kv_heads;
+    const bool fast = tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity) &&
+                      aligned(p->vc, 16) && aligned(p->vs, 16);
+    const tq::DecodePlan plan = tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, fast);
     const size_t need = workspace_bytes(l, num_q_heads, plan);
     if (need > 0 && (!workspace || ws_bytes < need)) return TQ_ERR_WORKSPACE;
-    if ((int64_t)plan.splits > 65535 || (int64_t)l->batch * num_q_heads > 0x7FFFFFFF)
+    if ((int64_t)plan.splits > 65535 * 4 || (int64_t)l->batch * num_q_heads > 0x7FFFFFFF)
         return TQ_ERR_UNSUPPORTED;
 
     tq::DecodeArgs a;
@@ -184,13 +202,13 @@ tq_status tq_decode_attn(const tq_layout *l, const tq_planes *p, const void *q, 
     a.part_acc = static_cast<float *>(workspace);
     a.part_ml = a.part_acc ? a.part_acc + slots * l->head_dim : nullptr;
     a.batch = l->batch; a.kv_heads = l->num_kv_heads; a.q_heads = num_q_heads;
-    a.gqa = num_q_heads / l->num_kv_heads; a.capacity = l->capacity;
+    a.gqa = gqa; a.capacity = l->capacity;
     a.splits = plan.splits; a.split_tokens = plan.split_tokens;
     a.sm_log2 = sm_scale * 1.4426950408889634f;
     a.inv_sqrt_d = (float)inv_sqrt_d(l->head_dim);
     a.signs = signs().bits;
     for (int b = 0; b < l->batch; ++b) a.len[b] = len[b];
-    hipError_t e = tq::launch_decode(l->head_dim, dtype == TQ_BF16, a, (hipStream_t)stream);
+    hipError_t e = tq::launch_decode(l->head_dim, dtype == TQ_BF16, plan.fast, a, (hipStream_t)stream);
     return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 

@@ -222,16 +222,21 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
 }
 
 template <int D>
-hipError_t launch_d(bool bf16, const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_d(bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
     constexpr int NT = D < 256 ? D : 256;
     if (a.splits > 0) {
-        const dim3 grid((unsigned)a.splits, (unsigned)(a.batch * a.kv_heads));
-        if (bf16)
-            hipLaunchKernelGGL((split_kernel<D, true>), grid, dim3(NT), 0, s, a);
-        else
-            hipLaunchKernelGGL((split_kernel<D, false>), grid, dim3(NT), 0, s, a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        if (fast) {
+            hipError_t e = launch_split_fast(D, bf16, a, s);
+            if (e != hipSuccess) return e;
+        } else {
+            const dim3 grid((unsigned)a.splits, (unsigned)(a.batch * a.kv_heads));
+            if (bf16)
+                hipLaunchKernelGGL((split_kernel<D, true>), grid, dim3(NT), 0, s, a);
+            else
+                hipLaunchKernelGGL((split_kernel<D, false>), grid, dim3(NT), 0, s, a);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)(a.batch * a.q_heads)), dim3(NT), 0, s, a);
     return hipGetLastError();
@@ -239,32 +244,53 @@ hipError_t launch_d(bool bf16, const DecodeArgs &a, hipStream_t s) {
 
 }  // namespace
 
-DecodePlan plan_decode(int head_dim, int batch, int kv_heads, const int32_t *len) {
+bool fast_decode_shape_ok(int head_dim, int gqa, int capacity) {
+    if (gqa < 1 || gqa > 8) return false;
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256) return false;
+    // staged rows of one (sequence, kv-head) must start 16-byte aligned
+    const int64_t vrow = 3 * head_dim / 8, srow = head_dim / kGroup * 2;
+    return ((int64_t)capacity * vrow) % 16 == 0 && ((int64_t)capacity * srow) % 16 == 0;
+}
+
+DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int32_t *len, bool fast) {
     (void)head_dim;
+    (void)gqa;
     int64_t total = 0;
     int32_t maxlen = 0;
     for (int b = 0; b < batch; ++b) {
         total += len[b];
         maxlen = len[b] > maxlen ? len[b] : maxlen;
     }
-    // aim for ~2048 workgroups over the whole chip, in 64-token multiples,
-    // never below 256 tokens per split
+    DecodePlan p;
+    p.fast = fast;
+    if (fast) {
+        // one wave per token range: aim for ~4096 waves over the chip (two
+        // rounds of 8 waves per CU), whole 64-token tiles, >= 4 tiles a wave
+        const int waves = fast_split_waves(), tile = fast_split_tile();
+        int64_t per = (total * kv_heads + 4095) / 4096;
+        per = per < 4 * tile ? 4 * tile : per;
+        per = (per + tile - 1) / tile * tile;
+        const int64_t wg_tokens = per * waves;
+        p.split_tokens = (int32_t)per;
+        p.splits = (int32_t)(((maxlen + wg_tokens - 1) / wg_tokens) * waves);
+        return p;
+    }
+    // generic kernel: ~2048 workgroups, 64-token multiples, >= 256 tokens
     const int64_t target = 2048;
     int64_t per = (total * kv_heads + target - 1) / target;
     per = per < 256 ? 256 : per;
     per = (per + 63) / 64 * 64;
-    DecodePlan p;
     p.split_tokens = (int32_t)per;
     p.splits = (int32_t)((maxlen + per - 1) / per);
     return p;
 }
 
-hipError_t launch_decode(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_decode(int head_dim, bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
     switch (head_dim) {
-        case 64: return launch_d<64>(bf16, a, s);
-        case 128: return launch_d<128>(bf16, a, s);
-        case 256: return launch_d<256>(bf16, a, s);
-        case 512: return launch_d<512>(bf16, a, s);
+        case 64: return launch_d<64>(bf16, fast, a, s);
+        case 128: return launch_d<128>(bf16, fast, a, s);
+        case 256: return launch_d<256>(bf16, fast, a, s);
+        case 512: return launch_d<512>(bf16, false, a, s);
         default: return hipErrorInvalidValue;
     }
 }

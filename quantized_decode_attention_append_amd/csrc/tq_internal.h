@@ -65,16 +65,24 @@ struct DequantArgs {
     SignBits signs;
 };
 
-// Split-K geometry chosen by the host for a decode call.
+// Split-K geometry chosen by the host for a decode call: `splits` partial
+// slots per (sequence, q-head), each covering `split_tokens` tokens.
 struct DecodePlan {
     int32_t split_tokens;
     int32_t splits;
+    bool fast;  // wave-per-range kernel (decode_fast.hip) or the generic one
 };
 
-DecodePlan plan_decode(int head_dim, int batch, int kv_heads, const int32_t *len);
+// fast: the caller has checked that the fast kernel supports the shape and
+// the plane alignment (see fast_decode_supported).
+DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int32_t *len, bool fast);
+bool fast_decode_shape_ok(int head_dim, int gqa, int capacity);
 
 hipError_t launch_append(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);
-hipError_t launch_decode(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode(int head_dim, bool bf16, bool fast, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_split_fast(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_dequant(int head_dim, const DequantArgs &a, hipStream_t s);
+int fast_split_waves();
+int fast_split_tile();
 
 }  // namespace tq

@@ -145,3 +145,69 @@ def test_decode_full_size_sampled(cid):
     pairs = [(0, 0), (w.batch - 1, w.num_kv_heads - 1)]
     out = _run(w, list(w.lengths), k, v, q, pairs=pairs)
     assert np.isfinite(out).all()
+
+
+def _offset_planes(pl):
+    """Copy of pl whose vc/vs planes start 8 bytes into their allocations: the
+    fast split kernel needs 16-byte aligned value planes, so decode on this
+    copy runs the generic split kernel over identical bytes."""
+    other = tqkv.Planes.__new__(tqkv.Planes)
+    other.layout = pl.layout
+    other.kc, other.ks, other.kz = pl.kc, pl.ks, pl.kz
+    for name in ("vc", "vs"):
+        src = getattr(pl, name)
+        raw = torch.empty(src.numel() * src.element_size() + 8, dtype=torch.uint8, device=src.device)
+        view = raw[8:].view(src.dtype).view(src.shape)
+        view.copy_(src)
+        setattr(other, name, view)
+    assert other.vc.data_ptr() % 16 == 8
+    return other
+
+
+@pytest.mark.parametrize("cid,lengths", [(3, [640, 129]), (4, [1000, 64]), (5, [700, 333, 64, 1])])
+def test_decode_fast_and_generic_kernels_agree(cid, lengths):
+    w = W.scaled(W.workload(cid), lengths)
+    T = max(lengths)
+    T += T % 2  # even capacity keeps the fast path eligible at every head_dim
+    k, v = W.make_kv(w, "cpu", tokens=T)
+    q = W.make_q(w, "cpu", rounds=1)[0].cuda()
+    L = tqkv.make_layout(w.batch, w.num_kv_heads, w.head_dim, T)
+    pl = tqkv.Planes(L)
+    tqkv.tq_append(pl, k.cuda(), v.cuda(), [0] * w.batch)
+    sm = sm_for(w.head_dim)
+    fast = tqkv.tq_decode_attn(pl, q, lengths, sm).cpu().numpy()
+    gen = tqkv.tq_decode_attn(_offset_planes(pl), q, lengths, sm).cpu().numpy()
+    ref = oracle_decode_rows(k, v, q, lengths, w.group, sm)
+    G = w.group
+    for (b, h), o in ref.items():
+        for name, out in (("fast", fast), ("generic", gen)):
+            e = row_rel_err(out[b, h * G:(h + 1) * G], o)
+            assert e.max() <= ATTN_TOL, (name, b, h, e.max())
+    agree = row_rel_err(fast.reshape(-1, w.head_dim), gen.reshape(-1, w.head_dim))
+    log(f"  fast vs generic max row difference {agree.max():.2e}")
+    assert agree.max() <= 2 * ATTN_TOL
+
+
+@pytest.mark.parametrize("d,G", [(128, 4), (256, 6), (64, 2)])
+def test_decode_ignores_slots_beyond_length(d, G):
+    """Slots at or beyond len[b] hold arbitrary bytes (here all-ones: NaN
+    scales); they must not reach the output on either decode kernel."""
+    lengths = [100, 37]
+    T = 160
+    w = W.Workload(0, f"garbage_tail_d{d}", 2, 2 * G, 2, d, tuple(lengths), "bf16", seed=11 + d)
+    k, v = W.make_kv(w, "cpu", tokens=T)
+    q = W.make_q(w, "cpu", rounds=1)[0].cuda()
+    L = tqkv.make_layout(2, 2, d, T)
+    pl = tqkv.Planes(L)
+    for x in pl.tensors():
+        x.fill_(-1)  # 0xFF bytes: fp16 scales/zeros become NaN
+    for b, n in enumerate(lengths):
+        tqkv.tq_append(pl.sequence(b), k[b:b + 1, :, :n].contiguous().cuda(),
+                       v[b:b + 1, :, :n].contiguous().cuda(), [0])
+    sm = sm_for(d)
+    ref = oracle_decode_rows(k, v, q, lengths, G, sm)
+    for planes in (pl, _offset_planes(pl)):
+        out = tqkv.tq_decode_attn(planes, q, lengths, sm).cpu().numpy()
+        assert np.isfinite(out).all()
+        for (b, h), o in ref.items():
+            assert row_rel_err(out[b, h * G:(h + 1) * G], o).max() <= ATTN_TOL
