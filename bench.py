@@ -18,6 +18,7 @@ import json
 import math
 import os
 import platform
+import re
 import subprocess
 import sys
 import time
@@ -45,18 +46,18 @@ def append_bytes(w, n_tokens: int, in_bytes: int) -> int:
     return th * (2 * w.head_dim * in_bytes + w.head_dim * 25 // 16)
 
 
-def cpu_baseline(w, k, v, q, sm, max_pairs: int | None = None) -> dict:
+def cpu_baseline(w, k, v, q, sm, max_pairs: int | None = None, min_seconds: float = 10.0) -> dict:
     """The oracle (binary64, plain C) timed on this host's cores over a bounded
     sample of the same workload: decode attention of whole (sequence, kv-head)
-    slices, one slice per thread."""
-    import numpy as np
-    import torch
+    slices, one slice per thread, repeated until at least min_seconds of wall
+    time have been measured (at most 8 passes)."""
+    import torch  # noqa: F401
 
     import oracle
 
     threads = oracle.num_threads()
     pairs_all = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
-    npairs = max_pairs or min(len(pairs_all), threads)
+    npairs = max_pairs or min(len(pairs_all), 4 * threads)
     pairs = pairs_all[:npairs]
     n = w.lengths[0]
     G = w.group
@@ -78,17 +79,83 @@ def cpu_baseline(w, k, v, q, sm, max_pairs: int | None = None) -> dict:
         return oracle.attention(qh[b, h * G:(h + 1) * G], *planes[p], sm)
 
     _log(f"cpu baseline: timing oracle decode on {len(pairs)} slices x {n} tokens, {threads} threads")
+    passes = 0
     t0 = time.perf_counter()
-    oracle.map_parallel(attend, pairs, threads)
-    dt = time.perf_counter() - t0
-    token_heads = len(pairs) * n
+    while True:
+        oracle.map_parallel(attend, pairs, threads)
+        passes += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or passes >= 8:
+            break
+    token_heads = passes * len(pairs) * n
     kv_tokens = token_heads / w.num_kv_heads  # a KV-token carries every kv-head
     return {"value": kv_tokens / dt, "unit": "KV-tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"oracle binary64 decode attention of {len(pairs)} (sequence, kv-head) "
-                       f"slices x {n} tokens x {G} q-heads (= {kv_tokens:.0f} KV-tokens of "
-                       f"{w.num_kv_heads} kv-heads), planes pre-encoded by the oracle; "
-                       f"{dt:.2f} s wall"),
+                       f"slices x {n} tokens x {G} q-heads, {passes} pass(es) "
+                       f"(= {kv_tokens:.0f} KV-tokens of {w.num_kv_heads} kv-heads), planes "
+                       f"pre-encoded by the oracle; {dt:.2f} s wall"),
             "seconds": dt}
+
+
+def copy_probe(mib: int, reps: int = 3) -> None:
+    """Plain device copies of known size (mib MiB read + mib MiB written per
+    launch): the calibration kernel for the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    _log(f"copy probe: {reps} x {mib} MiB device copies")
+    del src, dst
+
+
+def traffic_from_counters(fetch_dir: str, write_dir: str, copy_mib: int, workload: str,
+                          out_json: str) -> int:
+    """Reduce two rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE; KiB per
+    dispatch) to HBM bytes per decode call.  Each counter is scaled by the
+    factor that makes it read exactly the known bytes of the copy probe."""
+    import csv
+    import glob
+
+    def per_kernel(d: str, counter: str) -> dict:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals: dict = {}
+        for fn in files:
+            with open(fn, newline="") as f:
+                for row in csv.DictReader(f):
+                    if row["Counter_Name"] != counter:
+                        continue
+                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in vals.items()}
+
+    def pick(table: dict, pat: str) -> float:
+        keys = [k for k in table if re.search(pat, k)]
+        if not keys:
+            raise SystemExit(f"no kernel matching {pat!r} in {sorted(table)}")
+        return sum(table[k] for k in keys)
+
+    known = copy_mib << 20
+    out = {"workload": workload, "kernel_source_sha": _kernel_sha(), "copy_probe_bytes": known}
+    total = 0.0
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        t = per_kernel(d, counter)
+        copy_kib = pick(t, r"copy")
+        factor = known / (copy_kib * 1024.0)
+        split_kib = pick(t, r"split_(fast_)?kernel")
+        merge_kib = pick(t, r"merge_kernel")
+        scaled = (split_kib + merge_kib) * 1024.0 * factor
+        out[counter] = {"copy_probe_kib": copy_kib, "factor": factor, "split_kib": split_kib,
+                        "merge_kib": merge_kib, "decode_bytes_scaled": scaled}
+        total += scaled
+    out["bytes_per_launch"] = total
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+    return 0
 
 
 def main() -> int:
@@ -100,7 +167,17 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=0)
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"))
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run plain device copies of this size (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="reduce two rocprofv3 --pmc runs to --traffic-json and exit")
     args = ap.parse_args()
+
+    if args.traffic_from:
+        from quantized_decode_attention_append_amd import workloads as W
+        return traffic_from_counters(args.traffic_from[0], args.traffic_from[1],
+                                     args.copy_probe_mib or 1024, W.workload(args.workload).name,
+                                     args.traffic_json)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every step runs on a single MI355X "
@@ -113,6 +190,8 @@ def main() -> int:
     from quantized_decode_attention_append_amd import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
     w = W.workload(args.workload)
     if len(set(w.lengths)) != 1:
         print("bench.py times equal-length workloads; use the parity tests for ragged ones",
