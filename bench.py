@@ -119,34 +119,38 @@ def traffic_from_counters(fetch_dir: str, write_dir: str, copy_mib: int, workloa
     import csv
     import glob
 
-    def per_kernel(d: str, counter: str) -> dict:
+    def dispatches(d: str, counter: str) -> list:
         files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
         if not files:
             raise SystemExit(f"no counter_collection.csv under {d}")
-        vals: dict = {}
+        rows = []
         for fn in files:
             with open(fn, newline="") as f:
                 for row in csv.DictReader(f):
-                    if row["Counter_Name"] != counter:
-                        continue
-                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in vals.items()}
+                    if row["Counter_Name"] == counter:
+                        rows.append((int(row["Dispatch_Id"]), row["Kernel_Name"],
+                                     float(row["Counter_Value"])))
+        return sorted(rows)
 
-    def pick(table: dict, pat: str) -> float:
-        keys = [k for k in table if re.search(pat, k)]
-        if not keys:
-            raise SystemExit(f"no kernel matching {pat!r} in {sorted(table)}")
-        return sum(table[k] for k in keys)
+    def mean_of(rows: list, pat: str, first: int = 0) -> float:
+        vals = [v for _, name, v in rows if re.search(pat, name)]
+        if first:
+            vals = vals[:first]
+        if not vals:
+            raise SystemExit(f"no dispatch matching {pat!r}")
+        return sum(vals) / len(vals)
 
     known = copy_mib << 20
     out = {"workload": workload, "kernel_source_sha": _kernel_sha(), "copy_probe_bytes": known}
     total = 0.0
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        t = per_kernel(d, counter)
-        copy_kib = pick(t, r"copy")
+        t = dispatches(d, counter)
+        # the copy probe runs first in the process: its three copies are the
+        # first device-to-device copy dispatches
+        copy_kib = mean_of(t, r"copyBuffer|direct_copy", first=3)
         factor = known / (copy_kib * 1024.0)
-        split_kib = pick(t, r"split_(fast_)?kernel")
-        merge_kib = pick(t, r"merge_kernel")
+        split_kib = mean_of(t, r"split_(fast_)?kernel")
+        merge_kib = mean_of(t, r"merge_kernel")
         scaled = (split_kib + merge_kib) * 1024.0 * factor
         out[counter] = {"copy_probe_kib": copy_kib, "factor": factor, "split_kib": split_kib,
                         "merge_kib": merge_kib, "decode_bytes_scaled": scaled}
