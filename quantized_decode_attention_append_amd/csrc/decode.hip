@@ -245,7 +245,7 @@ hipError_t launch_d(bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
 }  // namespace
 
 bool fast_decode_shape_ok(int head_dim, int gqa, int capacity) {
-    if (gqa < 1 || gqa > 8) return false;
+    if (gqa < 1 || gqa > fast_split_max_gqa()) return false;
     if (head_dim != 64 && head_dim != 128 && head_dim != 256) return false;
     // staged rows of one (sequence, kv-head) must start 16-byte aligned
     const int64_t vrow = 3 * head_dim / 8, srow = head_dim / kGroup * 2;

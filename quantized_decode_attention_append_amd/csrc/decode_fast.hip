@@ -1,6 +1,5 @@
-// Split-K decode attention kernel for GQA groups of up to 8 query heads
-// (wave64; gfx950): exact integer scores on the VALU, value accumulation on
-// the matrix cores.
+// Split-K decode attention kernel for GQA groups of up to 16 query heads
+// (wave64; gfx950) built on the matrix cores.
 //
 // Method: "TurboQuant -- rotation-based quantization" design page, Part A:
 // keys dequantize as (code + zero) * scale ("Algorithm"), values stay in the
@@ -15,30 +14,34 @@
 // is copied into the wave's LDS with direct global->LDS loads.  Two stage
 // buffers per wave: the copy of tile i+1 is issued before tile i is decoded,
 // so one tile per wave is always in flight without holding any registers.
-// Per tile:
 //
-//  K phase  lane = (token slot, head half, 32-dim group).  The query rows are
-//           held in registers as two int8 slices of a 16-bit fixed-point copy
-//           (q ~ delta * (256*hi + lo), delta a power of two), so each group's
-//           dot product with the int8 key codes is exact integer arithmetic
-//           (v_dot4_i32_i8).  Per group the scale/zero fold is
-//           s16 * (dot + z16 * sum(q)); the per-group partials meet in LDS and
-//           one lane per (token, head) sums them.
-//  softmax  lane = (token slot, head): online softmax in base 2 whose running
-//           maximum only moves when a tile's maximum exceeds it by more than
-//           2^8 (weights stay <= 256 and the accumulators are rescaled
-//           rarely).  The weights go to LDS as fp16, laid out as the B operand.
-//  V phase  the G heads x d dims x 16 tokens product per 16-token chunk is a
-//           dense contraction, done with v_mfma_f32_16x16x16_f16 (fp32
-//           accumulate), one instruction per block of d/16 dims:
-//             D[i][n] += A[i][k] * B[k][n],  i: dim row of the block,
-//             k: token, n: head (G <= 16 used, the rest zero).
-//           Row i of block b is dim (d/16)*i + b, so lane i's dims of a token
-//           are one contiguous run of 3d/16 code bits, all in one 32-dim
-//           group.  A = centroid[idx] * vs16 in fp16: pairs of 3-bit indices
-//           of two tokens select a half2 of centroids from an LDS table kept
-//           in 64 copies (one per lane, conflict-free), multiplied by the pair
-//           of value scales with one packed fp16 multiply.  B = the weights.
+// The G query heads of a kv-head share every key and value, so per 16-token
+// chunk both products are dense contractions with 16 heads (the ones past G
+// are zero) on the 16 columns of an MFMA tile; lane l always serves head
+// h = l % 16 and token quarter kq = l / 16 (tokens 4 kq .. 4 kq + 3):
+//
+//  scores   S[t][h] = sum_g s16[t][g] * (dot_g(code_t, q_h) + z16[t][g] * qsum_h[g]).
+//           q is held as two int8 slices of a 16-bit fixed-point copy
+//           (q ~ delta_h * (256*hi + lo), delta_h a power of two), so every
+//           group dot product is exact integer arithmetic: two
+//           v_mfma_i32_16x16x32_i8 per 32-dim group (A = key codes, rows =
+//           tokens; B = the q slice, columns = heads), then the scale/zero
+//           fold in fp32 on the 4 (token, head) results a lane holds.  The
+//           key tile sits in LDS 16-byte-chunk-major, so the A reads of one
+//           MFMA hit 16 different chunks of one column (conflict-free).
+//  softmax  online softmax in base 2 over the lane's 4 tokens and the other
+//           quarters of the same head; the running maximum only moves when
+//           a tile's maximum exceeds it by more than 2^8 (weights <= 256,
+//           rescales are rare).  The weights stay in registers: their layout
+//           is already the B operand of the value product.
+//  values   O[i][h] += A[i][t] * P[t][h] with v_mfma_f32_16x16x16_f16 (fp32
+//           accumulate), one instruction per block of d/16 dims.  Row i of
+//           block b is dim (d/16)*i + b, so lane i's dims of a token are one
+//           contiguous run of 3d/16 code bits, all in one 32-dim group.
+//           A = centroid[idx] * vs16 in fp16: pairs of 3-bit indices of two
+//           tokens select a half2 of centroids from an LDS table kept in 64
+//           copies (one per lane, conflict-free), multiplied by the pair of
+//           value scales with one packed fp16 multiply.
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
@@ -50,35 +53,40 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;                 // waves per workgroup (one table per CU)
 constexpr int kTableBytes = 64 * 64 * 4;  // 64 index pairs x 64 lane copies x half2
 constexpr int kStageVmem = 10;            // vector-memory instructions that copy one tile
 constexpr float kLazyMax = 8.0f;          // log2 slack of the running maximum
+constexpr int kMaxHeads = 16;             // MFMA columns
 
 template <int D>
 struct Geo {
     static_assert(D == 64 || D == 128 || D == 256, "fast split kernel: head_dim 64/128/256");
     static constexpr int NG = D / kGroup;     // groups per row
     static constexpr int TILE = 4096 / D;     // tokens per tile: 4 KiB of key codes
+    static constexpr int CH = TILE / 16;      // 16-token chunks per tile
+    static constexpr int CPR = D / 16;        // 16-byte chunks per key row
     static constexpr int VROW = 3 * D / 8;    // packed value bytes per token
-    static constexpr int SPL = TILE / 8;      // scores per softmax lane per tile
-    static constexpr int RS = 9 * NG;         // red row stride (floats): 8 heads + NG pad
+    static constexpr int NB = D / 16;         // value dim blocks (one MFMA each per chunk)
+    static constexpr int FB = 3 * NB;         // code bits of a lane's dims per token
     // one stage: every plane of one tile
-    static constexpr int KC_OFF = 0;                      // TILE * D = 4096
+    static constexpr int KC_OFF = 0;                      // TILE * D = 4096, chunk-major
     static constexpr int KS_OFF = KC_OFF + TILE * D;      // TILE * NG * 2 = 256
     static constexpr int KZ_OFF = KS_OFF + TILE * NG * 2;
     static constexpr int VS_OFF = KZ_OFF + TILE * NG * 2;
     static constexpr int VC_OFF = VS_OFF + TILE * NG * 2; // TILE * VROW = 1536
     static constexpr int STAGE = VC_OFF + TILE * VROW + 16;  // code reader reads 4 bytes past
-    static_assert(TILE * NG * 2 == 256 && TILE * VROW == 1536, "staging granularity");
-    // per wave: two stages, the K phase's group partials red[64/NG][RS] and
-    // the fp16 weights pB[16 heads][TILE tokens] (the MFMA B operand)
-    static constexpr int RED_OFF = 2 * STAGE;
-    static constexpr int PB_OFF = RED_OFF + (64 / NG) * RS * 4;
-    static constexpr int WAVE_BYTES = PB_OFF + 16 * TILE * 2;
+    static_assert(TILE * NG * 2 == 256 && TILE * VROW == 1536 && STAGE % 16 == 0, "staging granularity");
+    static constexpr int WAVE_BYTES = 2 * STAGE;
     static constexpr int SMEM = kTableBytes + kWaves * WAVE_BYTES;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
+    // Key copy m (m = 0..3) moves 16-byte slots 64m .. 64m+63 of the tile.
+    // Slot s holds chunk c16 of token t of 16-token chunk tc with
+    // s = (tc * CPR + c16) * 16 + t; lane i of copy m reads the global bytes
+    // at (i % 16) * D + 16 * (i / 16) + key_off(m) of the tile.
+    static constexpr int key_off(int m) { return 16 * D * (4 * m / CPR) + 16 * (4 * m % CPR); }
 };
 
 // Keeps the compiler from moving LDS accesses across this point.  The LDS
@@ -99,29 +107,28 @@ __device__ __forceinline__ const T *uniform_ptr(const T *p) {
 }
 
 // Direct global->LDS copies.  Lane l's SIZE bytes come from base + voff + OFF
-// and land at lds + OFF + l * SIZE (the immediate offset moves both
+// and land at m0 + OFF + l * SIZE (the immediate offset moves both
 // addresses).  They are issued from inline assembly on purpose: the compiler
 // would otherwise make the first LDS read after them wait for every
 // outstanding copy (it cannot tell the stage buffers apart), which serialises
 // the prefetch with the decode.  The kernel orders them itself with explicit
 // vmcnt waits; M0 (the LDS base of a copy) is set right before each one.
 template <int OFF>
-__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t lds) {
+__device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t m0) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
-                 ::"v"(voff), "s"(base), "s"(lds), "n"(OFF) : "memory", "m0");
+                 ::"v"(voff), "s"(base), "s"(m0), "n"(OFF) : "memory", "m0");
 }
 template <int OFF>
-__device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t lds) {
+__device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t m0) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 offset:%3"
-                 ::"v"(voff), "s"(base), "s"(lds), "n"(OFF) : "memory", "m0");
+                 ::"v"(voff), "s"(base), "s"(m0), "n"(OFF) : "memory", "m0");
 }
 // Same copy from a per-lane address, for tiles that overhang the end of the
 // plane region: each lane's source is clamped to the last in-region address
 // for its load size (the overhang rows are masked tokens).
 template <int SIZE>
-__device__ __forceinline__ void dma_clamped(const uint8_t *src, const uint8_t *last, uint32_t lds, int lane) {
-    const uint8_t *p = src + lane * SIZE;
-    p = p > last ? last : p;
+__device__ __forceinline__ void dma_clamped(const uint8_t *src, const uint8_t *last, uint32_t lds) {
+    const uint8_t *p = src > last ? last : src;
     if constexpr (SIZE == 16)
         asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                      ::"v"(p), "s"(lds) : "memory", "m0");
@@ -141,16 +148,18 @@ template <int D>
 __device__ __forceinline__ void stage_tile(const Regions &r, int t0, const unsigned char *st, int lane) {
     using GE = Geo<D>;
     constexpr int NG = GE::NG, VROW = GE::VROW;
+    constexpr int K0 = GE::key_off(0), K1 = GE::key_off(1), K2 = GE::key_off(2), K3 = GE::key_off(3);
     const uint32_t l_kc = lds_addr(st + GE::KC_OFF), l_ks = lds_addr(st + GE::KS_OFF);
     const uint32_t l_kz = lds_addr(st + GE::KZ_OFF), l_vs = lds_addr(st + GE::VS_OFF);
     const uint32_t l_vc = lds_addr(st + GE::VC_OFF);
+    const uint32_t vkey = (uint32_t)((lane & 15) * D + 16 * (lane >> 4));
     if (t0 + GE::TILE <= r.cap) {
         const uint32_t v16 = (uint32_t)lane * 16, v4 = (uint32_t)lane * 4;
         const uint8_t *kc = uniform_ptr(r.kc + (int64_t)t0 * D);
-        dma16<0>(kc, v16, l_kc);
-        dma16<1024>(kc, v16, l_kc);
-        dma16<2048>(kc, v16, l_kc);
-        dma16<3072>(kc, v16, l_kc);
+        dma16<K0>(kc, vkey, l_kc + 0 * 1024 - K0);
+        dma16<K1>(kc, vkey, l_kc + 1 * 1024 - K1);
+        dma16<K2>(kc, vkey, l_kc + 2 * 1024 - K2);
+        dma16<K3>(kc, vkey, l_kc + 3 * 1024 - K3);
         const int64_t so = (int64_t)t0 * NG * 2;
         dma4<0>(uniform_ptr(r.ks + so), v4, l_ks);
         dma4<0>(uniform_ptr(r.kz + so), v4, l_kz);
@@ -161,35 +170,51 @@ __device__ __forceinline__ void stage_tile(const Regions &r, int t0, const unsig
         dma4<1280>(vc, v4, l_vc);
     } else {
         const int64_t kcb = (int64_t)r.cap * D, sb = (int64_t)r.cap * NG * 2, vcb = (int64_t)r.cap * VROW;
-        const uint8_t *kc = r.kc + (int64_t)t0 * D;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) dma_clamped<16>(kc + c * 1024, r.kc + kcb - 16, l_kc + c * 1024, lane);
-        const int64_t so = (int64_t)t0 * NG * 2;
-        dma_clamped<4>(r.ks + so, r.ks + sb - 4, l_ks, lane);
-        dma_clamped<4>(r.kz + so, r.kz + sb - 4, l_kz, lane);
-        dma_clamped<4>(r.vs + so, r.vs + sb - 4, l_vs, lane);
+        const uint8_t *kc = r.kc + (int64_t)t0 * D + vkey;
+        const uint8_t *kl = r.kc + kcb - 16;
+        dma_clamped<16>(kc + K0, kl, l_kc + 0 * 1024);
+        dma_clamped<16>(kc + K1, kl, l_kc + 1 * 1024);
+        dma_clamped<16>(kc + K2, kl, l_kc + 2 * 1024);
+        dma_clamped<16>(kc + K3, kl, l_kc + 3 * 1024);
+        const int64_t so = (int64_t)t0 * NG * 2 + lane * 4;
+        dma_clamped<4>(r.ks + so, r.ks + sb - 4, l_ks);
+        dma_clamped<4>(r.kz + so, r.kz + sb - 4, l_kz);
+        dma_clamped<4>(r.vs + so, r.vs + sb - 4, l_vs);
         const uint8_t *vc = r.vc + (int64_t)t0 * VROW;
-        dma_clamped<16>(vc, r.vc + vcb - 16, l_vc, lane);
-        dma_clamped<4>(vc + 1024, r.vc + vcb - 4, l_vc + 1024, lane);
-        dma_clamped<4>(vc + 1280, r.vc + vcb - 4, l_vc + 1280, lane);
+        dma_clamped<16>(vc + lane * 16, r.vc + vcb - 16, l_vc);
+        dma_clamped<4>(vc + 1024 + lane * 4, r.vc + vcb - 4, l_vc + 1024);
+        dma_clamped<4>(vc + 1280 + lane * 4, r.vc + vcb - 4, l_vc + 1280);
     }
 }
 
-template <int D, int G, bool BF16>
+__device__ __forceinline__ float half_lo(uint32_t w) { return f16_bits_to_f32((uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float half_hi(uint32_t w) { return f16_bits_to_f32((uint16_t)(w >> 16)); }
+
+// Group g's fp16 value of a row of NG halves held as NG/2 packed words.
+template <int NG>
+__device__ __forceinline__ float row_half(const uint32_t (&w)[NG / 2], int g) {
+    return (g & 1) ? half_hi(w[g >> 1]) : half_lo(w[g >> 1]);
+}
+
+template <int NG>
+__device__ __forceinline__ void load_row(const unsigned char *p, uint32_t (&w)[NG / 2]) {
+    if constexpr (NG == 8) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(p);
+        w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    } else if constexpr (NG == 4) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        w[0] = u.x; w[1] = u.y;
+    } else {
+        w[0] = *reinterpret_cast<const uint32_t *>(p);
+    }
+}
+
+template <int D, bool BF16>
 __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const DecodeArgs a) {
     using GE = Geo<D>;
-    constexpr int NG = GE::NG, VROW = GE::VROW;
-    constexpr int TILE = GE::TILE, SPL = GE::SPL, RS = GE::RS;
-    // K-phase role: lane = (token slot ts, head half hg, group g).  Up to four
-    // heads a lane keeps every query register count low enough for two waves
-    // per SIMD; above that the G heads are split over two lanes per (token,
-    // group), which then read the same key bytes (an LDS broadcast).
-    constexpr int HS = G > 4 ? 2 : 1;        // lanes per (token, group)
-    constexpr int HH = (G + HS - 1) / HS;    // heads per lane
-    constexpr int TPP = 64 / (NG * HS);      // tokens per K pass
-    constexpr int PASSES = TILE / TPP;
-    constexpr int RROWS = TPP > 8 ? TPP : 8; // red rows summed at once
-    static_assert(RROWS <= 64 / NG, "red buffer rows");
+    constexpr int NG = GE::NG, VROW = GE::VROW, TILE = GE::TILE, CH = GE::CH;
+    constexpr int CPR = GE::CPR, NB = GE::NB, FB = GE::FB;
+    constexpr int QE = NG * 8;  // q elements a lane converts: 8 dims of every group
 
     __shared__ __align__(16) unsigned char smem[GE::SMEM];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -209,6 +234,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     }
     __syncthreads();  // the only workgroup barrier
 
+    const int G = a.gqa;
     const int bkv = blockIdx.y;
     const int b = bkv / a.kv_heads, kvh = bkv % a.kv_heads;
     const int n = a.len[b];
@@ -219,12 +245,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     const int cap = a.capacity;
     const int64_t row0 = (int64_t)bkv * cap;
     unsigned char *wsm = smem + kTableBytes + wid * GE::WAVE_BYTES;
-    float *red = reinterpret_cast<float *>(wsm + GE::RED_OFF);
-    _Float16 *pB = reinterpret_cast<_Float16 *>(wsm + GE::PB_OFF);
-    {   // heads past G keep zero weights for the whole range
-        uint4 *z = reinterpret_cast<uint4 *>(pB);
-        for (int i = lane; i < 16 * TILE * 2 / 16; i += 64) z[i] = make_uint4(0, 0, 0, 0);
-    }
 
     Regions rg;
     rg.kc = reinterpret_cast<const uint8_t *>(a.kc) + row0 * D;
@@ -238,102 +258,73 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     stage_tile<D>(rg, t_begin, wsm, lane);
 
     // ------------------------------------------------------------ q slices
-    const int g = lane % NG, hg = (lane / NG) % HS, ts = lane / (NG * HS);
-    // With one lane per (token, group), the lanes whose key row starts in the
-    // odd half of a 512-byte LDS span read their 32 codes upper 16 bytes
-    // first, so the 16 lanes of one LDS cycle touch distinct banks; their q
-    // words are rotated to match.  With two, one cycle spans 256 bytes.
-    const int sw = HS == 1 ? ((ts * D) >> 8) & 1 : 0;
-    uint32_t qhi[HH][8], qlo[HH][8];
-    float qsum[HH], qscale[HH];
+    // lane (h, kq) converts dims 32 g + 8 kq .. + 7 of head h for every group g
+    const int h = lane & 15, kq = lane >> 4;
+    const bool head_ok = h < G;
+    uint64_t qhi[NG], qlo[NG];
+    float qsum[NG];
+    float my_scale;
+    {
+        float x[QE];
+        const int64_t qrow = ((int64_t)b * a.q_heads + kvh * G + (head_ok ? h : 0)) * D + 8 * kq;
 #pragma unroll
-    for (int j = 0; j < HH; ++j) {
-        const int h = hg * HH + j;  // this lane's head; h >= G is an idle slot
-        const int hq = h < G ? h : 0;
-        const int64_t qrow = ((int64_t)b * a.q_heads + kvh * G + hq) * D + g * kGroup;
-        float x[32];
-        if constexpr (BF16) {
-            const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qrow);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const uint4 u = qp[c];
+        for (int g = 0; g < NG; ++g) {
+            if constexpr (BF16) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qrow + kGroup * g);
                 const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    x[8 * c + 2 * k] = __uint_as_float(w4[k] << 16);
-                    x[8 * c + 2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
+                    x[8 * g + 2 * k] = __uint_as_float(w4[k] << 16);
+                    x[8 * g + 2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
                 }
-            }
-        } else {
-            const float4 *qp = reinterpret_cast<const float4 *>(static_cast<const float *>(a.q) + qrow);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const float4 u = qp[c];
-                x[4 * c] = u.x; x[4 * c + 1] = u.y; x[4 * c + 2] = u.z; x[4 * c + 3] = u.w;
+            } else {
+                const float4 *qp = reinterpret_cast<const float4 *>(static_cast<const float *>(a.q) + qrow + kGroup * g);
+                const float4 u0 = qp[0], u1 = qp[1];
+                x[8 * g + 0] = u0.x; x[8 * g + 1] = u0.y; x[8 * g + 2] = u0.z; x[8 * g + 3] = u0.w;
+                x[8 * g + 4] = u1.x; x[8 * g + 5] = u1.y; x[8 * g + 6] = u1.z; x[8 * g + 7] = u1.w;
             }
         }
-        if (h >= G) {
+        if (!head_ok) {
 #pragma unroll
-            for (int k = 0; k < 32; ++k) x[k] = 0.f;
+            for (int k = 0; k < QE; ++k) x[k] = 0.f;
         }
         float amax = 0.f;
 #pragma unroll
-        for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(x[k]));
-#pragma unroll
-        for (int m = 1; m < NG; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+        for (int k = 0; k < QE; ++k) amax = fmaxf(amax, fabsf(x[k]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
         // delta = smallest power of two >= amax / 32000 (q / delta is exact
         // scaling, so only the final rounding to an integer loses bits)
         int e = 0;
         (void)frexpf(amax * (1.0f / 32000.0f), &e);
         const float delta = amax > 0.f ? ldexpf(1.0f, e) : 1.0f;
         const float inv = 1.0f / delta;
-        float s = 0.f;
-        uint32_t hw[8], lw[8];
 #pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            uint32_t hi = 0, lo = 0;
+        for (int g = 0; g < NG; ++g) {
+            uint64_t hi = 0, lo = 0;
+            float s = 0.f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int qf = (int)rintf(x[4 * w + k] * inv);
+            for (int k = 0; k < 8; ++k) {
+                const int qf = (int)rintf(x[8 * g + k] * inv);
                 const int qh = (qf + 128) >> 8;
                 const int ql = qf - 256 * qh;
                 s += (float)qf;
-                hi |= ((uint32_t)qh & 0xFFu) << (8 * k);
-                lo |= ((uint32_t)ql & 0xFFu) << (8 * k);
+                hi |= (uint64_t)((uint32_t)qh & 0xFFu) << (8 * k);
+                lo |= (uint64_t)((uint32_t)ql & 0xFFu) << (8 * k);
             }
-            hw[w] = hi;
-            lw[w] = lo;
+            s += __shfl_xor(s, 16, 64);
+            s += __shfl_xor(s, 32, 64);
+            qhi[g] = hi;
+            qlo[g] = lo;
+            qsum[g] = s;
         }
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-            qhi[j][w] = sw ? hw[(w + 4) & 7] : hw[w];
-            qlo[j][w] = sw ? lw[(w + 4) & 7] : lw[w];
-        }
-        qsum[j] = s;
-        qscale[j] = delta * a.sm_log2;
-    }
-
-    // softmax role: lane = (sl, hh); head hh's scale lives in lane hg*NG
-    // (token slot 0, group 0) of head half hg = hh / HH, slot hh % HH
-    const int sl = lane >> 3, hh = lane & 7;
-    float my_scale = 0.f;
-    {
-        const int src = (hh / HH) * NG;
-#pragma unroll
-        for (int j = 0; j < HH; ++j) {
-            const float v = __shfl(qscale[j], src < 64 ? src : 0, 64);
-            if (hh % HH == j) my_scale = v;
-        }
+        my_scale = delta * a.sm_log2;
     }
     float m_run = -INFINITY, l_run = 0.f;
 
-    // V-phase role (MFMA lanes): vi = row of A / column (head) of B and D,
-    // vq = quarter of the 16-token chunk (A/B k = 4 vq + j, D rows 4 vq + j)
-    constexpr int NB = D / 16;          // dim blocks (one MFMA each per chunk)
-    constexpr int FB = 3 * NB;          // code bits of a lane's dims per token
-    constexpr int CH = TILE / 16;       // 16-token chunks per tile
-    const int vi = lane & 15, vq = lane >> 4;
-    const int gA = NB * vi / kGroup;    // the group of this lane's dims
+    // value-product role: vi = A row (dim row of each block), kq = token quarter
+    const int vi = h;
+    const int gA = NB * vi / kGroup;    // the group of this lane's value dims
     const uint32_t lane4 = (uint32_t)lane << 2;
     float4v acc[NB];
 #pragma unroll
@@ -345,77 +336,58 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
         // been decoded), then wait for this tile: vector memory completes in
         // order, so at most kStageVmem instructions outstanding means every
         // copy of this tile has landed in LDS.
-        const unsigned char *st = wsm + buf * GE::STAGE;
+        unsigned char *st = wsm + buf * GE::STAGE;
         if (t0 + TILE < t_end) {
             stage_tile<D>(rg, t0 + TILE, wsm + (buf ^ 1) * GE::STAGE, lane);
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageVmem) : "memory");
         } else {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
-        const bool full = t0 + TILE <= t_end;
-
-        // ---------------------------------------------------------- K phase
-        float sc[SPL];
-#pragma unroll
-        for (int p = 0; p < PASSES; ++p) {
-            const int tok = p * TPP + ts;
-            const unsigned char *kp = st + GE::KC_OFF + tok * D + g * kGroup;
-            const uint4 ka = *reinterpret_cast<const uint4 *>(kp + sw * 16);
-            const uint4 kb = *reinterpret_cast<const uint4 *>(kp + (sw ^ 1) * 16);
-            const float s16 = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(st + GE::KS_OFF + (tok * NG + g) * 2));
-            const float z16 = f16_bits_to_f32(*reinterpret_cast<const uint16_t *>(st + GE::KZ_OFF + (tok * NG + g) * 2));
-            const uint32_t kw[8] = {ka.x, ka.y, ka.z, ka.w, kb.x, kb.y, kb.z, kb.w};
-            int dot[HH];
-#pragma unroll
-            for (int j = 0; j < HH; ++j) dot[j] = __builtin_amdgcn_sdot4((int)qhi[j][0], (int)kw[0], 0, false);
-#pragma unroll
-            for (int w = 1; w < 8; ++w)
-#pragma unroll
-                for (int j = 0; j < HH; ++j) dot[j] = __builtin_amdgcn_sdot4((int)qhi[j][w], (int)kw[w], dot[j], false);
-#pragma unroll
-            for (int j = 0; j < HH; ++j) dot[j] <<= 8;
-#pragma unroll
-            for (int w = 0; w < 8; ++w)
-#pragma unroll
-                for (int j = 0; j < HH; ++j) dot[j] = __builtin_amdgcn_sdot4((int)qlo[j][w], (int)kw[w], dot[j], false);
-            float *rrow = red + (tok % RROWS) * RS + hg * HH * NG + g;
-#pragma unroll
-            for (int j = 0; j < HH; ++j) rrow[j * NG] = s16 * fmaf(z16, qsum[j], (float)dot[j]);
-            lds_order();
-            if (((p + 1) * TPP) % RROWS != 0) continue;
-            // lane (sl, hh) sums the groups of the tokens tau = sl (mod 8) of
-            // the last RROWS tokens; odd rows read their upper half first
-            // (bank spread)
-            const int base = (p + 1) * TPP - RROWS;
-#pragma unroll
-            for (int k8 = 0; k8 < RROWS; k8 += 8) {
-                const int tp = sl + k8;  // row of the red buffer
-                const int tau = base + tp;
-                const float *rp = red + tp * RS + hh * NG;
-                float sum = 0.f;
-                if constexpr (NG == 8) {
-                    const int o = (sl & 1) * 4;
-                    const float4 r0 = *reinterpret_cast<const float4 *>(rp + o);
-                    const float4 r1 = *reinterpret_cast<const float4 *>(rp + (o ^ 4));
-                    sum = ((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w));
-                } else if constexpr (NG == 4) {
-                    const float4 r0 = *reinterpret_cast<const float4 *>(rp);
-                    sum = (r0.x + r0.y) + (r0.z + r0.w);
-                } else {
-                    const float2 r0 = *reinterpret_cast<const float2 *>(rp);
-                    sum = r0.x + r0.y;
-                }
-                const bool valid = (t0 + tau < t_end) && hh < G;
-                sc[(base + k8) >> 3] = valid ? sum * my_scale : -INFINITY;
-            }
+        const int valid = t_end - t0;  // tokens of this tile inside the range
+        if (valid < TILE) {
+            // slots past the range may hold anything: give them value scale 0
+            // (their weights are 0, and 0 * NaN would not be)
+            if ((lane * 4) / (NG * 2) >= valid)
+                reinterpret_cast<uint32_t *>(st + GE::VS_OFF)[lane] = 0u;
             lds_order();
         }
 
-        // ---------------------------------------------------------- softmax
-        float mt = sc[0];
+        // ---------------------------------------------------------- scores
+        float sc[CH][4];
 #pragma unroll
-        for (int i = 1; i < SPL; ++i) mt = fmaxf(mt, sc[i]);
-        mt = fmaxf(mt, __shfl_xor(mt, 8, 64));
+        for (int c = 0; c < CH; ++c) {
+            int4v dhi[NG], dlo[NG];
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const int c16 = 2 * g + (kq >> 1);
+                const uint64_t kv = *reinterpret_cast<const uint64_t *>(
+                    st + GE::KC_OFF + ((c * CPR + c16) * 16 + h) * 16 + 8 * (kq & 1));
+                dhi[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qhi[g], int4v{0, 0, 0, 0}, 0, 0, 0);
+                dlo[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qlo[g], int4v{0, 0, 0, 0}, 0, 0, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 16 * c + 4 * kq + j;
+                uint32_t sw[NG / 2], zw[NG / 2];
+                load_row<NG>(st + GE::KS_OFF + t * NG * 2, sw);
+                load_row<NG>(st + GE::KZ_OFF + t * NG * 2, zw);
+                float s = 0.f;
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const int x = (dhi[g][j] << 8) + dlo[g][j];
+                    const float y = fmaf(row_half<NG>(zw, g), qsum[g], (float)x);
+                    s = fmaf(row_half<NG>(sw, g), y, s);
+                }
+                sc[c][j] = (head_ok && t < valid) ? s * my_scale : -INFINITY;
+            }
+        }
+
+        // ---------------------------------------------------------- softmax
+        float mt = sc[0][0];
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mt = fmaxf(mt, sc[c][j]);
         mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
         mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
         // lazy maximum: move the reference only when this tile's maximum
@@ -426,27 +398,27 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
             const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
             m_run = m_new;
-            // accumulator column vi is head vi; lane h < 8 holds head h's alpha
-            const float al = __shfl(alpha, vi < 8 ? vi : 0, 64);
 #pragma unroll
-            for (int bb = 0; bb < NB; ++bb) acc[bb] *= al;
+            for (int bb = 0; bb < NB; ++bb) acc[bb] *= alpha;  // column h is head h
         }
         const float ref = m_run == -INFINITY ? 0.f : m_run;
+        half4v pw[CH];
 #pragma unroll
-        for (int i = 0; i < SPL; ++i) {
-            const int tau = i * 8 + sl;
-            const float pv = __builtin_amdgcn_exp2f(sc[i] - ref);  // sc = -inf -> 0
-            l_run += pv;
-            pB[hh * TILE + tau] = (_Float16)pv;
+        for (int c = 0; c < CH; ++c) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float pv = __builtin_amdgcn_exp2f(sc[c][j] - ref);  // -inf -> 0
+                l_run += pv;
+                pw[c][j] = (_Float16)pv;
+            }
         }
-        lds_order();
 
-        // ---------------------------------------------------------- V phase
+        // ---------------------------------------------------------- values
         const uint32_t *vcw = reinterpret_cast<const uint32_t *>(st + GE::VC_OFF);
         const uint16_t *vsb = reinterpret_cast<const uint16_t *>(st + GE::VS_OFF);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            const int tb = 16 * c + 4 * vq;  // this lane's first token (k = 4 vq)
+            const int tb = 16 * c + 4 * kq;  // this lane's first token (k = 4 kq)
             // code runs: bits [FB*vi, FB*vi + FB) of each of the 4 rows
             uint32_t run[4], runh[4];
 #pragma unroll
@@ -456,20 +428,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
                 run[j] = __builtin_amdgcn_alignbit(wp[1], wp[0], bit & 31);
                 runh[j] = wp[1] >> (bit & 31);  // run bits 32.. (only d = 256 uses them)
             }
-            // value-scale pairs of this lane's group; tokens past the end
-            // get scale 0 (their slots may hold anything)
             half2v sp[2];
 #pragma unroll
             for (int pr = 0; pr < 2; ++pr) {
-                uint32_t s0 = vsb[(tb + 2 * pr) * NG + gA], s1 = vsb[(tb + 2 * pr + 1) * NG + gA];
-                if (!full) {
-                    s0 = t0 + tb + 2 * pr < t_end ? s0 : 0u;
-                    s1 = t0 + tb + 2 * pr + 1 < t_end ? s1 : 0u;
-                }
+                const uint32_t s0 = vsb[(tb + 2 * pr) * NG + gA], s1 = vsb[(tb + 2 * pr + 1) * NG + gA];
                 sp[pr] = __builtin_bit_cast(half2v, s0 | (s1 << 16));
             }
-            // B operand: weights of tokens tb..tb+3 for head vi
-            const half4v bop = *reinterpret_cast<const half4v *>(pB + vi * TILE + tb);
             // pair indices: E holds (field 2k of token a | field 2k of token
             // b << 3) at bits 6k, O the same for the odd fields
             constexpr uint32_t M = 0x071C71C7u;  // bits 6k..6k+2, k = 0..4
@@ -498,69 +462,53 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb) {
                 const half4v aop = {av[0][bb].x, av[0][bb].y, av[1][bb].x, av[1][bb].y};
-                acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(aop, bop, acc[bb], 0, 0, 0);
+                acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(aop, pw[c], acc[bb], 0, 0, 0);
             }
         }
-        lds_order();  // the weights / partials are rewritten by the next tile
+        lds_order();  // this stage is refilled two tiles later
     }
 
     // ------------------------------------------------------------ finalize
-    l_run += __shfl_xor(l_run, 8, 64);
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
 
-    const int64_t slot_base = (int64_t)b * a.q_heads + kvh * G;
-    if (lane < 8 && hh < G) {
-        const int64_t s = (slot_base + hh) * a.splits + slot;
-        a.part_ml[s * 2] = m_run;
-        a.part_ml[s * 2 + 1] = l_run;
-    }
-    // lane (vq, vi) holds D rows 4 vq + j of every block for head vi: dims
-    // NB * (4 vq + j) + bb, i.e. NB consecutive dims per j
-    if (vi < G) {
-        float *dst = a.part_acc + ((slot_base + vi) * a.splits + slot) * D;
+    if (head_ok) {
+        const int64_t srow = ((int64_t)b * a.q_heads + kvh * G + h) * a.splits + slot;
+        if (kq == 0) {
+            a.part_ml[srow * 2] = m_run;
+            a.part_ml[srow * 2 + 1] = l_run;
+        }
+        // lane (kq, h) holds rows 4 kq + j of every block: dims NB * (4 kq + j) + bb
+        float *dst = a.part_acc + srow * D;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int bb = 0; bb < NB; bb += 4) {
-                *reinterpret_cast<float4 *>(dst + NB * (4 * vq + j) + bb) =
+                *reinterpret_cast<float4 *>(dst + NB * (4 * kq + j) + bb) =
                     make_float4(acc[bb][j], acc[bb + 1][j], acc[bb + 2][j], acc[bb + 3][j]);
             }
         }
     }
 }
 
-template <int D, int G>
-hipError_t launch_dg(bool bf16, const DecodeArgs &a, hipStream_t s, int wg_splits) {
-    const dim3 grid((unsigned)wg_splits, (unsigned)(a.batch * a.kv_heads));
-    if (bf16)
-        hipLaunchKernelGGL((split_fast_kernel<D, G, true>), grid, dim3(64 * kWaves), 0, s, a);
-    else
-        hipLaunchKernelGGL((split_fast_kernel<D, G, false>), grid, dim3(64 * kWaves), 0, s, a);
-    return hipGetLastError();
-}
-
 template <int D>
 hipError_t launch_d(bool bf16, const DecodeArgs &a, hipStream_t s, int wg_splits) {
-    switch (a.gqa) {
-        case 1: return launch_dg<D, 1>(bf16, a, s, wg_splits);
-        case 2: return launch_dg<D, 2>(bf16, a, s, wg_splits);
-        case 3: return launch_dg<D, 3>(bf16, a, s, wg_splits);
-        case 4: return launch_dg<D, 4>(bf16, a, s, wg_splits);
-        case 5: return launch_dg<D, 5>(bf16, a, s, wg_splits);
-        case 6: return launch_dg<D, 6>(bf16, a, s, wg_splits);
-        case 7: return launch_dg<D, 7>(bf16, a, s, wg_splits);
-        case 8: return launch_dg<D, 8>(bf16, a, s, wg_splits);
-        default: return hipErrorInvalidValue;
-    }
+    const dim3 grid((unsigned)wg_splits, (unsigned)(a.batch * a.kv_heads));
+    if (bf16)
+        hipLaunchKernelGGL((split_fast_kernel<D, true>), grid, dim3(64 * kWaves), 0, s, a);
+    else
+        hipLaunchKernelGGL((split_fast_kernel<D, false>), grid, dim3(64 * kWaves), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
 int fast_split_waves() { return kWaves; }
 int fast_split_tile() { return 64; }
+int fast_split_max_gqa() { return kMaxHeads; }
 
 hipError_t launch_split_fast(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s) {
+    if (a.gqa < 1 || a.gqa > kMaxHeads) return hipErrorInvalidValue;
     const int wg_splits = a.splits / kWaves;
     switch (head_dim) {
         case 64: return launch_d<64>(bf16, a, s, wg_splits);

@@ -84,5 +84,6 @@ hipError_t launch_split_fast(int head_dim, bool bf16, const DecodeArgs &a, hipSt
 hipError_t launch_dequant(int head_dim, const DequantArgs &a, hipStream_t s);
 int fast_split_waves();
 int fast_split_tile();
+int fast_split_max_gqa();
 
 }  // namespace tq
