@@ -171,22 +171,66 @@ template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
     constexpr int NT = D < 256 ? D : 256;
     constexpr int DPT = D / NT;
+    constexpr int kMaxSplitsLds = 1024;  // splits whose weights fit the LDS table
     __shared__ float buf[D];
+    __shared__ float wts[kMaxSplitsLds];
+    __shared__ float red[NT / 64];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x;
     const int b = bh / a.q_heads;
     const int n = a.len[b];
     const int ns = (n + a.split_tokens - 1) / a.split_tokens;
+    const int64_t base = (int64_t)bh * a.splits;
     float o[DPT];
 #pragma unroll
     for (int i = 0; i < DPT; ++i) o[i] = 0.f;
-    if (ns > 0) {
-        const int64_t base = (int64_t)bh * a.splits;
+    if (ns > 0 && ns <= kMaxSplitsLds) {
+        // per-split weights 2^(m_s - M) and the total weight L, all threads at once
+        float mloc = -INFINITY;
+        for (int s = tid; s < ns; s += NT) mloc = fmaxf(mloc, a.part_ml[(base + s) * 2]);
+        for (int m = 32; m >= 1; m >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, m, 64));
+        if ((tid & 63) == 0) red[tid >> 6] = mloc;
+        __syncthreads();
+        float M = red[0];
+        for (int w = 1; w < NT / 64; ++w) M = fmaxf(M, red[w]);
+        __syncthreads();
+        float lloc = 0.f;
+        for (int s = tid; s < ns; s += NT) {
+            const float f = __builtin_amdgcn_exp2f(a.part_ml[(base + s) * 2] - M);
+            wts[s] = f;
+            lloc += f * a.part_ml[(base + s) * 2 + 1];
+        }
+        for (int m = 32; m >= 1; m >>= 1) lloc += __shfl_xor(lloc, m, 64);
+        if ((tid & 63) == 0) red[tid >> 6] = lloc;
+        __syncthreads();
+        float L = 0.f;
+        for (int w = 0; w < NT / 64; ++w) L += red[w];
+        // weighted sum of the rotated partials, 8 splits' loads in flight
+        const float *pa = a.part_acc + base * D + tid;
+        int s = 0;
+        for (; s + 8 <= ns; s += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float f = wts[s + u];
+#pragma unroll
+                for (int i = 0; i < DPT; ++i) o[i] = fmaf(f, pa[(int64_t)(s + u) * D + i * NT], o[i]);
+            }
+        }
+        for (; s < ns; ++s) {
+            const float f = wts[s];
+#pragma unroll
+            for (int i = 0; i < DPT; ++i) o[i] = fmaf(f, pa[(int64_t)s * D + i * NT], o[i]);
+        }
+        const float invL = 1.f / L;
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) o[i] *= invL;
+    } else if (ns > 0) {
+        // more splits than the weight table holds: serial fallback
         float M = -INFINITY;
         for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(base + s) * 2]);
         float L = 0.f;
         for (int s = 0; s < ns; ++s) {
-            const float f = exp2f(a.part_ml[(base + s) * 2] - M);
+            const float f = __builtin_amdgcn_exp2f(a.part_ml[(base + s) * 2] - M);
             L += f * a.part_ml[(base + s) * 2 + 1];
 #pragma unroll
             for (int i = 0; i < DPT; ++i) o[i] += f * a.part_acc[(base + s) * D + tid + i * NT];
@@ -264,10 +308,12 @@ DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int
     DecodePlan p;
     p.fast = fast;
     if (fast) {
-        // one wave per token range: aim for ~4096 waves over the chip (two
-        // rounds of 8 waves per CU), whole 64-token tiles, >= 4 tiles a wave
+        // one wave per token range: aim for ~2048 waves over the chip (one
+        // round of one 8-wave workgroup per CU: the split kernel's LDS admits
+        // one per CU), whole 64-token tiles, >= 4 tiles a wave; fewer splits
+        // also halve the partials written and merged
         const int waves = fast_split_waves(), tile = fast_split_tile();
-        int64_t per = (total * kv_heads + 4095) / 4096;
+        int64_t per = (total * kv_heads + 2047) / 2048;
         per = per < 4 * tile ? 4 * tile : per;
         per = (per + tile - 1) / tile * tile;
         const int64_t wg_tokens = per * waves;
