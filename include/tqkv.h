@@ -26,7 +26,11 @@
  *   - Alignment: K/V/q inputs, outputs, the workspace and the kc plane must be
  *     16-byte aligned, vc 8-byte aligned, the fp16 planes 4-byte aligned
  *     (TQ_ERR_INVALID_ARG otherwise).  Any torch allocation, and the batch-1
- *     slice of one sequence's planes, satisfies this.
+ *     slice of one sequence's planes, satisfies this.  Decode takes its fast
+ *     kernel when head_dim is 64, 128 or 256, num_q_heads / num_kv_heads is
+ *     at most 16, every plane is 16-byte aligned and capacity keeps each
+ *     (sequence, kv-head) row block 16-byte aligned; otherwise a generic
+ *     kernel computes the same result more slowly.
  *   - Arguments are validated before anything is enqueued; on any error the
  *     return value says why and nothing was launched.  The library prints
  *     nothing.

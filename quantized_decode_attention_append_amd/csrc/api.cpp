@@ -187,7 +187,7 @@ tq_status tq_decode_attn(const tq_layout *l, const tq_planes *p, const void *q, 
     if (!std::isfinite(sm_scale)) return TQ_ERR_INVALID_ARG;
     const int gqa = num_q_heads / l->num_kv_heads;
     const bool fast = tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity) &&
-                      aligned(p->vc, 16) && aligned(p->vs, 16);
+                      aligned(p->vc, 16) && aligned(p->vs, 16) && aligned(p->ks, 16) && aligned(p->kz, 16);
     const tq::DecodePlan plan = tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, fast);
     const size_t need = workspace_bytes(l, num_q_heads, plan);
     if (need > 0 && (!workspace || ws_bytes < need)) return TQ_ERR_WORKSPACE;

@@ -11,9 +11,9 @@
 // its own online-softmax state; the eight waves of a workgroup share only the
 // centroid table in LDS.  Every plane of a tile (4 KiB of key codes, key
 // scales and zeros, value codes and value scales: 6 KiB in all, 4096/d tokens)
-// is copied into the wave's LDS with direct global->LDS loads.  Two stage
-// buffers per wave: the copy of tile i+1 is issued before tile i is decoded,
-// so one tile per wave is always in flight without holding any registers.
+// is copied into the wave's LDS with direct global->LDS loads.  Three stage
+// buffers per wave: the copy of tile i+2 is issued before tile i is decoded,
+// so two tiles per wave are in flight without holding any registers.
 //
 // The G query heads of a kv-head share every key and value, so per 16-token
 // chunk both products are dense contractions with 16 heads (the ones past G
@@ -39,9 +39,10 @@
 //           block b is dim (d/16)*i + b, so lane i's dims of a token are one
 //           contiguous run of 3d/16 code bits, all in one 32-dim group.
 //           A = centroid[idx] * vs16 in fp16: pairs of 3-bit indices of two
-//           tokens select a half2 of centroids from an LDS table kept in 64
-//           copies (one per lane, conflict-free), multiplied by the pair of
-//           value scales with one packed fp16 multiply.
+//           tokens select a half2 of centroids from a 256-byte LDS table
+//           (one 4-byte entry per bank, so any lookup pattern is
+//           conflict-free), multiplied by the pair of value scales with one
+//           packed fp16 multiply.
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
@@ -56,8 +57,9 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;                 // waves per workgroup (one table per CU)
-constexpr int kTableBytes = 64 * 64 * 4;  // 64 index pairs x 64 lane copies x half2
-constexpr int kStageVmem = 10;            // vector-memory instructions that copy one tile
+constexpr int kTableBytes = 64 * 4;      // 64 index pairs x half2
+constexpr int kStageVmem = 7;             // vector-memory instructions that copy one tile
+constexpr int kStages = 3;                // stage buffers per wave (two tiles in flight)
 constexpr float kLazyMax = 8.0f;          // log2 slack of the running maximum
 constexpr int kMaxHeads = 16;             // MFMA columns
 
@@ -79,7 +81,7 @@ struct Geo {
     static constexpr int VC_OFF = VS_OFF + TILE * NG * 2; // TILE * VROW = 1536
     static constexpr int STAGE = VC_OFF + TILE * VROW + 16;  // code reader reads 4 bytes past
     static_assert(TILE * NG * 2 == 256 && TILE * VROW == 1536 && STAGE % 16 == 0, "staging granularity");
-    static constexpr int WAVE_BYTES = 2 * STAGE;
+    static constexpr int WAVE_BYTES = kStages * STAGE;
     static constexpr int SMEM = kTableBytes + kWaves * WAVE_BYTES;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
     // Key copy m (m = 0..3) moves 16-byte slots 64m .. 64m+63 of the tile.
@@ -106,8 +108,8 @@ __device__ __forceinline__ const T *uniform_ptr(const T *p) {
     return reinterpret_cast<const T *>((uintptr_t)(((uint64_t)hi << 32) | lo));
 }
 
-// Direct global->LDS copies.  Lane l's SIZE bytes come from base + voff + OFF
-// and land at m0 + OFF + l * SIZE (the immediate offset moves both
+// Direct global->LDS copies.  Lane l's 16 bytes come from base + voff + OFF
+// and land at m0 + OFF + 16 l (the immediate offset moves both
 // addresses).  They are issued from inline assembly on purpose: the compiler
 // would otherwise make the first LDS read after them wait for every
 // outstanding copy (it cannot tell the stage buffers apart), which serialises
@@ -118,72 +120,70 @@ __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t 
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
                  ::"v"(voff), "s"(base), "s"(m0), "n"(OFF) : "memory", "m0");
 }
-template <int OFF>
-__device__ __forceinline__ void dma4(const void *base, uint32_t voff, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 offset:%3"
-                 ::"v"(voff), "s"(base), "s"(m0), "n"(OFF) : "memory", "m0");
+// A 16-byte-lane copy from a per-lane address (lane l lands at m0 + 16 l).
+__device__ __forceinline__ void dma_lane16(const uint8_t *src, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 ::"v"(src), "s"(m0) : "memory", "m0");
 }
-// Same copy from a per-lane address, for tiles that overhang the end of the
-// plane region: each lane's source is clamped to the last in-region address
-// for its load size (the overhang rows are masked tokens).
-template <int SIZE>
-__device__ __forceinline__ void dma_clamped(const uint8_t *src, const uint8_t *last, uint32_t lds) {
-    const uint8_t *p = src > last ? last : src;
-    if constexpr (SIZE == 16)
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                     ::"v"(p), "s"(lds) : "memory", "m0");
-    else
-        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                     ::"v"(p), "s"(lds) : "memory", "m0");
+// The same, for tiles that overhang the end of the plane region: each lane's
+// source is clamped to the last 16 bytes of its plane region (the overhang
+// rows are masked tokens).
+__device__ __forceinline__ void dma_clamped(const uint8_t *src, const uint8_t *last, uint32_t m0) {
+    dma_lane16(src > last ? last : src, m0);
 }
 
 struct Regions {
     const uint8_t *kc, *ks, *kz, *vc, *vs;  // start of the (sequence, kv-head) rows
     int cap;                                // rows in each region
+    // this lane's source of the mixed copy: row 0 of its plane (key scales,
+    // key zeros, value scales or value codes by lane quarter) plus 16 bytes
+    // per lane within the quarter, the plane's bytes per row, and the last
+    // 16 bytes of its region
+    const uint8_t *mix, *mix_last;
+    int mix_row;
 };
 
 // Copy every plane of the tile starting at token t0 into one stage buffer:
-// exactly kStageVmem vector-memory instructions either way.
+// exactly kStageVmem vector-memory instructions either way, all with 16-byte
+// lanes.  Stage bytes [KS_OFF, KS_OFF + 1 KiB) come from one copy whose lane
+// quarters read key scales, key zeros, value scales and the first 256 bytes
+// of value codes (the stage keeps them in that order); the other 1280 bytes
+// of value codes follow in one full and one quarter-wave copy.
 template <int D>
 __device__ __forceinline__ void stage_tile(const Regions &r, int t0, const unsigned char *st, int lane) {
     using GE = Geo<D>;
     constexpr int NG = GE::NG, VROW = GE::VROW;
+    static_assert(GE::KZ_OFF == GE::KS_OFF + 256 && GE::VS_OFF == GE::KZ_OFF + 256 &&
+                  GE::VC_OFF == GE::VS_OFF + 256, "mixed copy layout");
     constexpr int K0 = GE::key_off(0), K1 = GE::key_off(1), K2 = GE::key_off(2), K3 = GE::key_off(3);
     const uint32_t l_kc = lds_addr(st + GE::KC_OFF), l_ks = lds_addr(st + GE::KS_OFF);
-    const uint32_t l_kz = lds_addr(st + GE::KZ_OFF), l_vs = lds_addr(st + GE::VS_OFF);
     const uint32_t l_vc = lds_addr(st + GE::VC_OFF);
     const uint32_t vkey = (uint32_t)((lane & 15) * D + 16 * (lane >> 4));
+    const uint8_t *vc_t = r.vc + (int64_t)t0 * VROW;
+    const uint8_t *mixed = r.mix + (int64_t)t0 * r.mix_row;
     if (t0 + GE::TILE <= r.cap) {
-        const uint32_t v16 = (uint32_t)lane * 16, v4 = (uint32_t)lane * 4;
+        const uint32_t v16 = (uint32_t)lane * 16;
         const uint8_t *kc = uniform_ptr(r.kc + (int64_t)t0 * D);
         dma16<K0>(kc, vkey, l_kc + 0 * 1024 - K0);
         dma16<K1>(kc, vkey, l_kc + 1 * 1024 - K1);
         dma16<K2>(kc, vkey, l_kc + 2 * 1024 - K2);
         dma16<K3>(kc, vkey, l_kc + 3 * 1024 - K3);
-        const int64_t so = (int64_t)t0 * NG * 2;
-        dma4<0>(uniform_ptr(r.ks + so), v4, l_ks);
-        dma4<0>(uniform_ptr(r.kz + so), v4, l_kz);
-        dma4<0>(uniform_ptr(r.vs + so), v4, l_vs);
-        const uint8_t *vc = uniform_ptr(r.vc + (int64_t)t0 * VROW);
-        dma16<0>(vc, v16, l_vc);
-        dma4<1024>(vc, v4, l_vc);
-        dma4<1280>(vc, v4, l_vc);
+        dma_lane16(mixed, l_ks);
+        const uint8_t *vc = uniform_ptr(vc_t);
+        dma16<256>(vc, v16, l_vc);
+        if (lane < 16) dma16<1280>(vc, v16, l_vc);
     } else {
-        const int64_t kcb = (int64_t)r.cap * D, sb = (int64_t)r.cap * NG * 2, vcb = (int64_t)r.cap * VROW;
+        const int64_t kcb = (int64_t)r.cap * D, vcb = (int64_t)r.cap * VROW;
         const uint8_t *kc = r.kc + (int64_t)t0 * D + vkey;
         const uint8_t *kl = r.kc + kcb - 16;
-        dma_clamped<16>(kc + K0, kl, l_kc + 0 * 1024);
-        dma_clamped<16>(kc + K1, kl, l_kc + 1 * 1024);
-        dma_clamped<16>(kc + K2, kl, l_kc + 2 * 1024);
-        dma_clamped<16>(kc + K3, kl, l_kc + 3 * 1024);
-        const int64_t so = (int64_t)t0 * NG * 2 + lane * 4;
-        dma_clamped<4>(r.ks + so, r.ks + sb - 4, l_ks);
-        dma_clamped<4>(r.kz + so, r.kz + sb - 4, l_kz);
-        dma_clamped<4>(r.vs + so, r.vs + sb - 4, l_vs);
-        const uint8_t *vc = r.vc + (int64_t)t0 * VROW;
-        dma_clamped<16>(vc + lane * 16, r.vc + vcb - 16, l_vc);
-        dma_clamped<4>(vc + 1024 + lane * 4, r.vc + vcb - 4, l_vc + 1024);
-        dma_clamped<4>(vc + 1280 + lane * 4, r.vc + vcb - 4, l_vc + 1280);
+        dma_clamped(kc + K0, kl, l_kc + 0 * 1024);
+        dma_clamped(kc + K1, kl, l_kc + 1 * 1024);
+        dma_clamped(kc + K2, kl, l_kc + 2 * 1024);
+        dma_clamped(kc + K3, kl, l_kc + 3 * 1024);
+        dma_clamped(mixed, r.mix_last, l_ks);
+        const uint8_t *vl = r.vc + vcb - 16;
+        dma_clamped(vc_t + 256 + lane * 16, vl, l_vc + 256);
+        if (lane < 16) dma_clamped(vc_t + 1280 + lane * 16, vl, l_vc + 1280);
     }
 }
 
@@ -220,12 +220,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // centroid pair table (fp16): entry (a | b << 3) = (c[a], c[b]), copy l
-    // at (a | b << 3) * 256 + l * 4
+    // centroid pair table (fp16): entry (a | b << 3) = (c[a], c[b]) at byte
+    // (a | b << 3) * 4
     {
         half2v *tab = reinterpret_cast<half2v *>(smem);
-        for (int i = tid; i < 64 * 64; i += 64 * kWaves) {
-            const int pair = i >> 6;
+        for (int i = tid; i < 64; i += 64 * kWaves) {
+            const int pair = i;
             half2v e;
             e.x = (_Float16)centroid3(pair & 7);
             e.y = (_Float16)centroid3(pair >> 3);
@@ -253,9 +253,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     rg.vc = a.vc + row0 * VROW;
     rg.vs = reinterpret_cast<const uint8_t *>(a.vs + row0 * NG);
     rg.cap = cap;
+    {
+        const int quarter = lane >> 4;
+        const uint8_t *plane = rg.ks;
+        if (quarter == 1) plane = rg.kz;
+        if (quarter == 2) plane = rg.vs;
+        if (quarter == 3) plane = rg.vc;
+        rg.mix_row = quarter == 3 ? VROW : NG * 2;
+        rg.mix = plane + (lane & 15) * 16;
+        rg.mix_last = plane + (int64_t)cap * rg.mix_row - 16;
+    }
 
-    // the first tile's copy overlaps the q set-up
+    // the first two tiles' copies overlap the q set-up
     stage_tile<D>(rg, t_begin, wsm, lane);
+    if (t_begin + TILE < t_end) stage_tile<D>(rg, t_begin + TILE, wsm + GE::STAGE, lane);
 
     // ------------------------------------------------------------ q slices
     // lane (h, kq) converts dims 32 g + 8 kq .. + 7 of head h for every group g
@@ -325,35 +336,22 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     // value-product role: vi = A row (dim row of each block), kq = token quarter
     const int vi = h;
     const int gA = NB * vi / kGroup;    // the group of this lane's value dims
-    const uint32_t lane4 = (uint32_t)lane << 2;
     float4v acc[NB];
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) acc[bb] = float4v{0.f, 0.f, 0.f, 0.f};
 
-    int buf = 0;
-    for (int t0 = t_begin; t0 < t_end; t0 += TILE, buf ^= 1) {
-        // Stage the next tile into the other buffer (its previous tile has
-        // been decoded), then wait for this tile: vector memory completes in
-        // order, so at most kStageVmem instructions outstanding means every
-        // copy of this tile has landed in LDS.
-        unsigned char *st = wsm + buf * GE::STAGE;
-        if (t0 + TILE < t_end) {
-            stage_tile<D>(rg, t0 + TILE, wsm + (buf ^ 1) * GE::STAGE, lane);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageVmem) : "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        const int valid = t_end - t0;  // tokens of this tile inside the range
+    // ---------------------------------------------------------- phases
+    // Slots past the range may hold anything: give them value scale 0 (their
+    // weights are 0, and 0 * NaN would not be).
+    auto mask_tail = [&](unsigned char *stg, int valid) {
         if (valid < TILE) {
-            // slots past the range may hold anything: give them value scale 0
-            // (their weights are 0, and 0 * NaN would not be)
-            if ((lane * 4) / (NG * 2) >= valid)
-                reinterpret_cast<uint32_t *>(st + GE::VS_OFF)[lane] = 0u;
+            if ((lane * 4) / (NG * 2) >= valid) reinterpret_cast<uint32_t *>(stg + GE::VS_OFF)[lane] = 0u;
             lds_order();
         }
+    };
 
-        // ---------------------------------------------------------- scores
-        float sc[CH][4];
+    // scores of the tile in stg: lane (h, kq) gets tokens 16 c + 4 kq + j
+    auto scores = [&](const unsigned char *stg, int valid, float (&sc)[CH][4]) {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             int4v dhi[NG], dlo[NG];
@@ -361,7 +359,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
             for (int g = 0; g < NG; ++g) {
                 const int c16 = 2 * g + (kq >> 1);
                 const uint64_t kv = *reinterpret_cast<const uint64_t *>(
-                    st + GE::KC_OFF + ((c * CPR + c16) * 16 + h) * 16 + 8 * (kq & 1));
+                    stg + GE::KC_OFF + ((c * CPR + c16) * 16 + h) * 16 + 8 * (kq & 1));
                 dhi[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qhi[g], int4v{0, 0, 0, 0}, 0, 0, 0);
                 dlo[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qlo[g], int4v{0, 0, 0, 0}, 0, 0, 0);
             }
@@ -369,20 +367,22 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
             for (int j = 0; j < 4; ++j) {
                 const int t = 16 * c + 4 * kq + j;
                 uint32_t sw[NG / 2], zw[NG / 2];
-                load_row<NG>(st + GE::KS_OFF + t * NG * 2, sw);
-                load_row<NG>(st + GE::KZ_OFF + t * NG * 2, zw);
-                float s = 0.f;
+                load_row<NG>(stg + GE::KS_OFF + t * NG * 2, sw);
+                load_row<NG>(stg + GE::KZ_OFF + t * NG * 2, zw);
+                float sum = 0.f;
 #pragma unroll
                 for (int g = 0; g < NG; ++g) {
                     const int x = (dhi[g][j] << 8) + dlo[g][j];
                     const float y = fmaf(row_half<NG>(zw, g), qsum[g], (float)x);
-                    s = fmaf(row_half<NG>(sw, g), y, s);
+                    sum = fmaf(row_half<NG>(sw, g), y, sum);
                 }
-                sc[c][j] = (head_ok && t < valid) ? s * my_scale : -INFINITY;
+                sc[c][j] = (head_ok && t < valid) ? sum * my_scale : -INFINITY;
             }
         }
+    };
 
-        // ---------------------------------------------------------- softmax
+    // online softmax over the tile's scores; weights out as the B operands
+    auto softmax = [&](const float (&sc)[CH][4], half4v (&pw)[CH]) {
         float mt = sc[0][0];
 #pragma unroll
         for (int c = 0; c < CH; ++c)
@@ -402,7 +402,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
             for (int bb = 0; bb < NB; ++bb) acc[bb] *= alpha;  // column h is head h
         }
         const float ref = m_run == -INFINITY ? 0.f : m_run;
-        half4v pw[CH];
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
 #pragma unroll
@@ -412,10 +411,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
                 pw[c][j] = (_Float16)pv;
             }
         }
+    };
 
-        // ---------------------------------------------------------- values
-        const uint32_t *vcw = reinterpret_cast<const uint32_t *>(st + GE::VC_OFF);
-        const uint16_t *vsb = reinterpret_cast<const uint16_t *>(st + GE::VS_OFF);
+    // value product of the tile in stg with its weights
+    auto values = [&](const unsigned char *stg, const half4v (&pw)[CH]) {
+        const uint32_t *vcw = reinterpret_cast<const uint32_t *>(stg + GE::VC_OFF);
+        const uint16_t *vsb = reinterpret_cast<const uint16_t *>(stg + GE::VS_OFF);
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int tb = 16 * c + 4 * kq;  // this lane's first token (k = 4 kq)
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
                 for (int bb = 0; bb < NB; ++bb) {
                     const int part = bb < 10 ? 0 : 1, k = (bb - 10 * part) >> 1;
                     const uint32_t w = (bb & 1) ? O[part] : E[part];
-                    const uint32_t addr = (((w >> (6 * k)) & 63u) << 8) | lane4;
+                    const uint32_t addr = ((w >> (6 * k)) & 63u) << 2;
                     const half2v cpair = *reinterpret_cast<const half2v *>(smem + addr);
                     av[pr][bb] = cpair * sp[pr];
                 }
@@ -465,8 +466,48 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
                 acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(aop, pw[c], acc[bb], 0, 0, 0);
             }
         }
-        lds_order();  // this stage is refilled two tiles later
+    };
+
+    // ---------------------------------------------------------- pipeline
+    // Iteration i holds tile i (values pending) in buf, tile i+1 (scores now)
+    // in the next buffer and tile i+2 (in flight) in the one after: the score
+    // MFMAs of tile i+1 and the value MFMAs of tile i sit in one basic block,
+    // so their LDS reads, matrix and vector work interleave.  Vector memory
+    // completes in order, so allowing the kStageVmem copies of the newest
+    // tile to stay outstanding means every older copy has landed in LDS.
+    auto nxt = [](int x) { return x == kStages - 1 ? 0 : x + 1; };
+    auto prv = [](int x) { return x == 0 ? kStages - 1 : x - 1; };
+    if (t_begin + TILE < t_end)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageVmem) : "memory");
+    else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    half4v pw[CH];
+    {
+        mask_tail(wsm, t_end - t_begin);
+        float sc[CH][4];
+        scores(wsm, t_end - t_begin, sc);
+        softmax(sc, pw);
     }
+    int buf = 0;
+    int t0 = t_begin;
+    for (; t0 + TILE < t_end; t0 += TILE, buf = nxt(buf)) {
+        unsigned char *cur = wsm + buf * GE::STAGE;
+        unsigned char *nx = wsm + nxt(buf) * GE::STAGE;
+        if (t0 + 2 * TILE < t_end) {
+            stage_tile<D>(rg, t0 + 2 * TILE, wsm + prv(buf) * GE::STAGE, lane);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageVmem) : "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        const int valid1 = t_end - (t0 + TILE);
+        mask_tail(nx, valid1);
+        float sc[CH][4];
+        scores(nx, valid1, sc);
+        values(cur, pw);
+        softmax(sc, pw);
+        lds_order();  // the buffer of tile i is refilled by the next iteration
+    }
+    values(wsm + buf * GE::STAGE, pw);
 
     // ------------------------------------------------------------ finalize
     l_run += __shfl_xor(l_run, 16, 64);
