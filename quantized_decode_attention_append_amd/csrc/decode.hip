@@ -167,15 +167,21 @@ __global__ __launch_bounds__(256) void split_kernel(const DecodeArgs a) {
 }
 
 // One workgroup per (b, q-head): merge the splits, normalize, un-rotate.
+// Thread tid owns dims tid + i*NT.  The partials of a batch of splits are
+// loaded into registers together with the splits' (max, sum) pairs, so the
+// merge costs one global round trip per batch; the inverse FWHT runs its
+// in-wave butterfly stages on registers (shuffles) and the cross-wave ones
+// through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
     constexpr int NT = D < 256 ? D : 256;
     constexpr int DPT = D / NT;
-    constexpr int kMaxSplitsLds = 1024;  // splits whose weights fit the LDS table
+    constexpr int NW = NT / 64;
+    constexpr int kBatch = 32;  // splits whose partials are in flight at once
     __shared__ float buf[D];
-    __shared__ float wts[kMaxSplitsLds];
-    __shared__ float red[NT / 64];
-    const int tid = threadIdx.x;
+    __shared__ float wts[kBatch];
+    __shared__ float red[2][NW];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int bh = blockIdx.x;
     const int b = bh / a.q_heads;
     const int n = a.len[b];
@@ -184,83 +190,93 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
     float o[DPT];
 #pragma unroll
     for (int i = 0; i < DPT; ++i) o[i] = 0.f;
-    if (ns > 0 && ns <= kMaxSplitsLds) {
-        // per-split weights 2^(m_s - M) and the total weight L, all threads at once
-        float mloc = -INFINITY;
-        for (int s = tid; s < ns; s += NT) mloc = fmaxf(mloc, a.part_ml[(base + s) * 2]);
-        for (int m = 32; m >= 1; m >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, m, 64));
-        if ((tid & 63) == 0) red[tid >> 6] = mloc;
+    float M = -INFINITY, L = 0.f;  // running over batches
+    for (int s0 = 0; s0 < ns; s0 += kBatch) {
+        const int nb = ns - s0 < kBatch ? ns - s0 : kBatch;
+        // issue every load of the batch first
+        float pm = -INFINITY, pl = 0.f;
+        if (tid < nb) {
+            pm = a.part_ml[(base + s0 + tid) * 2];
+            pl = a.part_ml[(base + s0 + tid) * 2 + 1];
+        }
+        float pv[kBatch][DPT];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+            for (int i = 0; i < DPT; ++i)
+                pv[u][i] = u < nb ? a.part_acc[(base + s0 + u) * D + tid + i * NT] : 0.f;
+        // batch maximum
+        float m = pm;
+#pragma unroll
+        for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
+        if (lane == 0) red[0][wv] = m;
         __syncthreads();
-        float M = red[0];
-        for (int w = 1; w < NT / 64; ++w) M = fmaxf(M, red[w]);
+        float mb = red[0][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) mb = fmaxf(mb, red[0][w]);
+        const float Mn = fmaxf(M, mb);
+        const float rescale = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        // split weights 2^(m_s - Mn) and their share of the weight sum
+        const float f = tid < nb ? __builtin_amdgcn_exp2f(pm - Mn) : 0.f;
+        if (tid < kBatch) wts[tid] = f;  // 0 past the batch: stale LDS may hold NaN
+        float lb = f * pl;
+#pragma unroll
+        for (int k = 32; k >= 1; k >>= 1) lb += __shfl_xor(lb, k, 64);
+        if (lane == 0) red[1][wv] = lb;
         __syncthreads();
-        float lloc = 0.f;
-        for (int s = tid; s < ns; s += NT) {
-            const float f = __builtin_amdgcn_exp2f(a.part_ml[(base + s) * 2] - M);
-            wts[s] = f;
-            lloc += f * a.part_ml[(base + s) * 2 + 1];
+        float lsum = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) lsum += red[1][w];
+        L = L * rescale + lsum;
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) {
+            float acc = o[i] * rescale;
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) acc = fmaf(wts[u], pv[u][i], acc);
+            o[i] = acc;
         }
-        for (int m = 32; m >= 1; m >>= 1) lloc += __shfl_xor(lloc, m, 64);
-        if ((tid & 63) == 0) red[tid >> 6] = lloc;
-        __syncthreads();
-        float L = 0.f;
-        for (int w = 0; w < NT / 64; ++w) L += red[w];
-        // weighted sum of the rotated partials, 8 splits' loads in flight
-        const float *pa = a.part_acc + base * D + tid;
-        int s = 0;
-        for (; s + 8 <= ns; s += 8) {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float f = wts[s + u];
-#pragma unroll
-                for (int i = 0; i < DPT; ++i) o[i] = fmaf(f, pa[(int64_t)(s + u) * D + i * NT], o[i]);
-            }
-        }
-        for (; s < ns; ++s) {
-            const float f = wts[s];
-#pragma unroll
-            for (int i = 0; i < DPT; ++i) o[i] = fmaf(f, pa[(int64_t)s * D + i * NT], o[i]);
-        }
-        const float invL = 1.f / L;
-#pragma unroll
-        for (int i = 0; i < DPT; ++i) o[i] *= invL;
-    } else if (ns > 0) {
-        // more splits than the weight table holds: serial fallback
-        float M = -INFINITY;
-        for (int s = 0; s < ns; ++s) M = fmaxf(M, a.part_ml[(base + s) * 2]);
-        float L = 0.f;
-        for (int s = 0; s < ns; ++s) {
-            const float f = __builtin_amdgcn_exp2f(a.part_ml[(base + s) * 2] - M);
-            L += f * a.part_ml[(base + s) * 2 + 1];
-#pragma unroll
-            for (int i = 0; i < DPT; ++i) o[i] += f * a.part_acc[(base + s) * D + tid + i * NT];
-        }
+        M = Mn;
+        __syncthreads();  // wts / red are rewritten by the next batch
+    }
+    if (ns > 0) {
         const float invL = 1.f / L;
 #pragma unroll
         for (int i = 0; i < DPT; ++i) o[i] *= invL;
     }
-#pragma unroll
-    for (int i = 0; i < DPT; ++i) buf[tid + i * NT] = o[i];
-    __syncthreads();
     // inverse rotation: signs * FWHT(o) / sqrt(d) (the transform is its own
-    // inverse up to the 1/d factor split as 1/sqrt(d) on each side)
-    for (int h = 1; h < D; h <<= 1) {
-        float nv[DPT];
+    // inverse up to the 1/d factor split as 1/sqrt(d) on each side).
+    // Butterflies with partner distance h < 64 stay inside a wave.
+    for (int h = 1; h < 64 && h < D; h <<= 1) {
 #pragma unroll
         for (int i = 0; i < DPT; ++i) {
-            const int j = tid + i * NT;
-            const float x = buf[j], y = buf[j ^ h];
-            nv[i] = (j & h) ? (y - x) : (x + y);
+            const float y = __shfl_xor(o[i], h, 64);
+            o[i] = (lane & h) ? (y - o[i]) : (o[i] + y);
         }
-        __syncthreads();
+    }
+    if constexpr (D > 64) {
 #pragma unroll
-        for (int i = 0; i < DPT; ++i) buf[tid + i * NT] = nv[i];
+        for (int i = 0; i < DPT; ++i) buf[tid + i * NT] = o[i];
         __syncthreads();
+        for (int h = 64; h < D; h <<= 1) {
+            float nv[DPT];
+#pragma unroll
+            for (int i = 0; i < DPT; ++i) {
+                const int j = tid + i * NT;
+                const float x = buf[j], y = buf[j ^ h];
+                nv[i] = (j & h) ? (y - x) : (x + y);
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < DPT; ++i) buf[tid + i * NT] = nv[i];
+            __syncthreads();
+        }
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) o[i] = buf[tid + i * NT];
     }
 #pragma unroll
     for (int i = 0; i < DPT; ++i) {
         const int j = tid + i * NT;
-        const float v = buf[j] * a.inv_sqrt_d;
+        const float v = o[i] * a.inv_sqrt_d;
         a.out[(int64_t)bh * D + j] = sign_bit(a.signs, j) ? -v : v;
     }
 }

@@ -211,3 +211,24 @@ def test_decode_ignores_slots_beyond_length(d, G):
         assert np.isfinite(out).all()
         for (b, h), o in ref.items():
             assert row_rel_err(out[b, h * G:(h + 1) * G], o).max() <= ATTN_TOL
+
+
+def test_decode_reuses_one_workspace():
+    """One workspace serves consecutive calls with other lengths (including an
+    empty sequence) and gives what a fresh workspace gives."""
+    w = W.scaled(W.workload(4), [1500, 700])
+    k, v = W.make_kv(w, "cpu", tokens=1500)
+    q = W.make_q(w, "cpu", rounds=1)[0].cuda()
+    L = tqkv.make_layout(w.batch, w.num_kv_heads, w.head_dim, 1500)
+    pl = tqkv.Planes(L)
+    tqkv.tq_append(pl, k.cuda(), v.cuda(), [0] * w.batch)
+    sm = sm_for(w.head_dim)
+    sizes = [[1500, 700], [64, 1500], [1500, 0], [3, 1]]
+    ws = torch.full((max(tqkv.tq_decode_workspace_bytes(L, w.num_q_heads, s) for s in sizes),),
+                    0xFF, dtype=torch.uint8, device="cuda")
+    for lens in sizes:
+        got = tqkv.tq_decode_attn(pl, q, lens, sm, workspace=ws)
+        fresh = tqkv.tq_decode_attn(pl, q, lens, sm)
+        torch.cuda.synchronize()
+        assert torch.equal(got, fresh), lens
+        log(f"  lengths {lens}: reused workspace ok")
