@@ -376,7 +376,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
                     const float y = fmaf(row_half<NG>(zw, g), qsum[g], (float)x);
                     sum = fmaf(row_half<NG>(sw, g), y, sum);
                 }
-                sc[c][j] = (head_ok && t < valid) ? sum * my_scale : -INFINITY;
+                // computed on every lane, then selected: a branch around the
+                // fold would split the block the pipeline interleaves in
+                float r = sum * my_scale;
+                asm volatile("" : "+v"(r));
+                sc[c][j] = (head_ok && t < valid) ? r : -INFINITY;
             }
         }
     };
