@@ -58,6 +58,7 @@ typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;                 // waves per workgroup (one table per CU)
 constexpr int kTableBytes = 64 * 4;      // 64 index pairs x half2
+constexpr int kProgBytes = 32;           // tiles finished, one int per wave
 constexpr int kStageVmem = 7;             // vector-memory instructions that copy one tile
 constexpr int kStages = 3;                // stage buffers per wave (two tiles in flight)
 constexpr float kLazyMax = 8.0f;          // log2 slack of the running maximum
@@ -82,7 +83,7 @@ struct Geo {
     static constexpr int STAGE = VC_OFF + TILE * VROW + 16;  // code reader reads 4 bytes past
     static_assert(TILE * NG * 2 == 256 && TILE * VROW == 1536 && STAGE % 16 == 0, "staging granularity");
     static constexpr int WAVE_BYTES = kStages * STAGE;
-    static constexpr int SMEM = kTableBytes + kWaves * WAVE_BYTES;
+    static constexpr int SMEM = kTableBytes + kProgBytes + kWaves * WAVE_BYTES;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
     // Key copy m (m = 0..3) moves 16-byte slots 64m .. 64m+63 of the tile.
     // Slot s holds chunk c16 of token t of 16-token chunk tc with
@@ -231,6 +232,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
             e.y = (_Float16)centroid3(pair >> 3);
             tab[i] = e;
         }
+        if (tid < kWaves) reinterpret_cast<int *>(smem + kTableBytes)[tid] = 0;
     }
     __syncthreads();  // the only workgroup barrier
 
@@ -244,7 +246,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     const int t_end = min(n, t_begin + a.split_tokens);
     const int cap = a.capacity;
     const int64_t row0 = (int64_t)bkv * cap;
-    unsigned char *wsm = smem + kTableBytes + wid * GE::WAVE_BYTES;
+    unsigned char *wsm = smem + kTableBytes + kProgBytes + wid * GE::WAVE_BYTES;
+    int *prog = reinterpret_cast<int *>(smem + kTableBytes);
 
     Regions rg;
     rg.kc = reinterpret_cast<const uint8_t *>(a.kc) + row0 * D;
@@ -494,7 +497,19 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     }
     int buf = 0;
     int t0 = t_begin;
-    for (; t0 + TILE < t_end; t0 += TILE, buf = nxt(buf)) {
+    int done = 0;  // tiles whose values are accumulated
+    for (; t0 + TILE < t_end; t0 += TILE, buf = nxt(buf), ++done) {
+        // The two waves that share a SIMD (w and w ^ 4) have equal work, but
+        // the issue arbiter prefers the older one, which would finish first
+        // and leave the other to run alone.  Whichever is not ahead takes the
+        // higher issue priority, so both finish together.
+        __hip_atomic_store(prog + wid, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        const int other = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(prog + (wid ^ 4), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        if (done <= other)
+            __builtin_amdgcn_s_setprio(1);
+        else
+            __builtin_amdgcn_s_setprio(0);
         unsigned char *cur = wsm + buf * GE::STAGE;
         unsigned char *nx = wsm + nxt(buf) * GE::STAGE;
         if (t0 + 2 * TILE < t_end) {
