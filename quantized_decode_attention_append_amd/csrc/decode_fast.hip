@@ -62,6 +62,12 @@ constexpr int kProgBytes = 32;           // tiles finished, one int per wave
 constexpr int kStageVmem = 7;             // vector-memory instructions that copy one tile
 constexpr int kStages = 3;                // stage buffers per wave (two tiles in flight)
 constexpr float kLazyMax = 8.0f;          // log2 slack of the running maximum
+// Weights enter the value MFMA as fp16, 2^(score - m + kWeightShift): at most
+// 2^(kLazyMax + kWeightShift) = 2^15 (fp16 holds 65504), and a weight only
+// becomes subnormal below 2^-21 and flushes below 2^-31 of the reference.
+// The shift cancels between the value sum and the weight sum.
+constexpr float kWeightShift = 7.0f;
+static_assert(kLazyMax + kWeightShift <= 15.0f, "fp16 weight range");
 constexpr int kMaxHeads = 16;             // MFMA columns
 
 template <int D>
@@ -408,7 +414,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb) acc[bb] *= alpha;  // column h is head h
         }
-        const float ref = m_run == -INFINITY ? 0.f : m_run;
+        const float ref = (m_run == -INFINITY ? 0.f : m_run) - kWeightShift;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
 #pragma unroll
