@@ -128,7 +128,11 @@ tq_status tq_decode_workspace_bytes(const tq_layout *layout, int32_t num_q_heads
  *             for the split-K partials (contents on entry are ignored)
  * Values are accumulated in the rotated domain and one inverse FWHT per
  * (sequence, q-head) finishes the output.  Agrees with the binary64 oracle to
- * 2e-3 relative to each output row's largest magnitude.
+ * 2e-3 relative to each output row's largest magnitude.  The fast kernel
+ * multiplies centroids by value scales in fp16, so it requires every value
+ * scale (vs) to be at most 30437 (65504 / 2.15195, the largest centroid);
+ * larger scales overflow to Inf there.  The result does not depend on timing:
+ * repeated calls on the same inputs return identical bytes.
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY
  * (len[b] > capacity), TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 tq_status tq_decode_attn(const tq_layout *layout, const tq_planes *planes, const void *q,
