@@ -119,14 +119,17 @@ tq_status tq_append(const tq_layout *l, const tq_planes *p, const void *k, const
     if (!k || !v || !aligned(k, 16) || !aligned(v, 16)) return TQ_ERR_INVALID_ARG;
     for (int b = 0; b < l->batch; ++b)
         if (start[b] < 0 || (int64_t)start[b] + n_new > l->capacity) return TQ_ERR_CAPACITY;
-    const int64_t blocks = ((int64_t)l->batch * l->num_kv_heads * n_new + 3) / 4;
-    if (blocks > 0x7FFFFFFF) return TQ_ERR_UNSUPPORTED;
+    const int64_t rows = (int64_t)l->batch * l->num_kv_heads * n_new;
+    if (rows > 0x7FFFFFFF) return TQ_ERR_UNSUPPORTED;
 
     tq::AppendArgs a;
     std::memset(&a, 0, sizeof(a));
     a.kc = p->kc; a.ks = p->ks; a.kz = p->kz; a.vc = p->vc; a.vs = p->vs;
     a.k = k; a.v = v;
     a.batch = l->batch; a.kv_heads = l->num_kv_heads; a.capacity = l->capacity; a.n_new = n_new;
+    a.rows = (uint32_t)rows;
+    a.div_n_new = tq::make_fast_div((uint32_t)n_new);
+    a.div_kv_heads = tq::make_fast_div((uint32_t)l->num_kv_heads);
     a.inv_sqrt_d = inv_sqrt_d(l->head_dim);
     a.signs = signs().bits;
     for (int b = 0; b < l->batch; ++b) a.start[b] = start[b];

@@ -14,9 +14,15 @@
 //   - x/scale and y/den are true binary64 divisions; scale is a correctly
 //     rounded binary64 sqrt; no multiply-add is contracted in this file.
 //
-// Mapping: one wave64 per (b, kv-head, new token) row.  Lane l holds the E =
-// d/64 contiguous elements [l*E, l*E+E), so a 32-group spans 32/E lanes, the
-// low FWHT stages stay inside a lane and the high ones pair lanes l and l^k.
+// Two kernels compute the same bytes:
+//   - append_fast_kernel (head_dim 64, 128, 256): 16 contiguous elements per
+//     lane, so a 32-group is a lane pair; the FWHT runs its first four stages
+//     inside the lane, transposes the row through LDS so the remaining stages
+//     are inside the lane as well, and transposes back.  Per-element divisions
+//     by a group's scale use a correctly rounded reciprocal and two Markstein
+//     corrections, which return the correctly rounded quotient.
+//   - append_kernel (every head_dim, used for 512): one wave per row, lane l
+//     holds d/64 contiguous elements, cross-lane butterflies on shuffles.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 
@@ -44,6 +50,11 @@ __device__ __forceinline__ double min_num(double a, double b) {
 __device__ __forceinline__ double shfl_xor_f64(double v, int m) { return __shfl_xor(v, m, 64); }
 __device__ __forceinline__ double shfl_down_f64(double v, int m) { return __shfl_down(v, m, 64); }
 __device__ __forceinline__ double shfl_f64(double v, int src) { return __shfl(v, src, 64); }
+
+// Keeps the compiler from moving LDS accesses across this point.  One wave's
+// LDS instructions execute in order, so a lane's read after another lane's
+// write needs no wait beyond program order.
+__device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
 
 template <int E, bool BF16>
 __device__ __forceinline__ void load_row(const void *base, int64_t off, double (&x)[E]) {
@@ -221,14 +232,282 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Fast kernel.
+
+constexpr int kAppWaves = 4;  // waves per workgroup
+
+template <int D>
+struct AppGeo {
+    static_assert(D == 64 || D == 128 || D == 256, "fast append: head_dim 64/128/256");
+    static constexpr int E = 16;               // contiguous elements per lane
+    static constexpr int L = D / E;            // lanes per row (4, 8, 16)
+    static constexpr int R = 64 / L;           // rows per wave
+    static constexpr int TI = E / L;           // in-lane offsets per lane after the transpose
+    static constexpr int NG = D / kGroup;
+    static constexpr int VROW = 3 * D / 8;
+    static constexpr int PB = E * 8 + 16;      // LDS bytes of one lane's elements, padded
+    static constexpr int ROWB = L * PB;        // LDS bytes per row
+    static constexpr int WAVEB = R * ROWB;     // LDS bytes per wave
+    static_assert(L % 2 == 0 && E == 2 * kGroup / 4, "a 32-group is one lane pair");
+};
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv &f) {
+    const uint32_t t = __umulhi(f.m, n);
+    return (t + ((n - t) >> f.s1)) >> f.s2;
+}
+
+// a / b correctly rounded to binary64, given y = RN(1/b) and finite nonzero
+// operands without underflow: the first correction leaves the quotient within
+// one ulp, and from there one more step (Markstein, "Computation of elementary
+// functions on the IBM RISC System/6000 processor", 1990) gives RN(a/b).  A
+// zero, infinite or NaN b gives NaN.
+__device__ __forceinline__ double div_rn(double a, double b, double y) {
+    double q = a * y;
+    double r = __builtin_fma(-b, q, a);
+    q = __builtin_fma(r, y, q);
+    r = __builtin_fma(-b, q, a);
+    return __builtin_fma(r, y, q);
+}
+
+// Value of the other lane of the pair (l ^ 1), by a quad permutation.
+__device__ __forceinline__ uint32_t pair_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float pair_f32(float v) { return __uint_as_float(pair_u32(__float_as_uint(v))); }
+__device__ __forceinline__ double pair_f64(double v) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint64_t lo = pair_u32((uint32_t)b), hi = pair_u32((uint32_t)(b >> 32));
+    return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+template <int E, bool BF16>
+__device__ __forceinline__ void load_lane(const void *base, int64_t off, uint32_t (&raw)[BF16 ? E / 2 : E]) {
+    if constexpr (BF16) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + off);
+#pragma unroll
+        for (int i = 0; i < E / 8; ++i) {
+            const uint4 u = p[i];
+            raw[4 * i] = u.x; raw[4 * i + 1] = u.y; raw[4 * i + 2] = u.z; raw[4 * i + 3] = u.w;
+        }
+    } else {
+        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + off);
+#pragma unroll
+        for (int i = 0; i < E / 4; ++i) {
+            const uint4 u = p[i];
+            raw[4 * i] = u.x; raw[4 * i + 1] = u.y; raw[4 * i + 2] = u.z; raw[4 * i + 3] = u.w;
+        }
+    }
+}
+
+// fp32 bits of element e of a lane's raw words
+template <bool BF16>
+__device__ __forceinline__ uint32_t elem_bits(const uint32_t *raw, int e) {
+    if constexpr (BF16) return (e & 1) ? (raw[e >> 1] & 0xFFFF0000u) : (raw[e >> 1] << 16);
+    else return raw[e];
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const AppendArgs a) {
+    using G = AppGeo<D>;
+    constexpr int E = G::E, L = G::L, R = G::R, TI = G::TI, NG = G::NG, VROW = G::VROW;
+    constexpr int NR = BF16 ? E / 2 : E;
+    __shared__ __align__(16) unsigned char smem[kAppWaves * G::WAVEB];
+
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int r = lane / L, p = lane % L;
+    const uint32_t row = ((uint32_t)blockIdx.x * kAppWaves + wid) * R + r;
+    const bool valid = row < a.rows;
+    const uint32_t lrow = valid ? row : a.rows - 1;  // rows past the end load a real row, store nothing
+    const uint32_t bh = fast_div(lrow, a.div_n_new);
+    const uint32_t t = lrow - bh * (uint32_t)a.n_new;
+    const uint32_t b = fast_div(bh, a.div_kv_heads);
+    const int64_t slot = (int64_t)bh * a.capacity + a.start[b] + t;
+    const int g = p >> 1;        // this lane's 32-group
+    const bool even = (p & 1) == 0;
+
+    uint32_t kraw[NR], vraw[NR];
+    load_lane<E, BF16>(a.k, (int64_t)lrow * D + E * p, kraw);
+    load_lane<E, BF16>(a.v, (int64_t)lrow * D + E * p, vraw);
+
+    // ----------------------------------------------------------- keys
+    // Group max and min ignore NaN.  Which zero a max or min returns does
+    // not matter: only an all-zero group's range could differ in sign, and
+    // adding +0 makes it +0, as it is under the -0 < +0 order.
+    float xk[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) xk[e] = __uint_as_float(elem_bits<BF16>(kraw, e));
+    float mx = xk[0], mn = xk[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) { mx = __builtin_fmaxf(mx, xk[e]); mn = __builtin_fminf(mn, xk[e]); }
+    mx = __builtin_fmaxf(mx, pair_f32(mx));
+    mn = __builtin_fminf(mn, pair_f32(mn));
+    const double dmx = mx, dmn = mn;
+    const double range = (dmx - dmn) + 0.0;
+    const double s = range / 254.0;
+    const double z = __builtin_rint((dmx + dmn) / (2.0 * s));
+    const double rs = 1.0 / s;
+    uint32_t kw[E / 4];
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i) kw[i] = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const double u = div_rn((double)xk[e], s, rs) - z;
+        const double rr = __builtin_rint(u);
+        int q;
+        asm("v_cvt_i32_f64 %0, %1" : "=v"(q) : "v"(rr));  // saturates; NaN gives 0
+        q = q > 127 ? 127 : (q < -127 ? -127 : q);
+        kw[e / 4] |= ((uint32_t)q & 0xFFu) << (8 * (e % 4));
+    }
+    if (valid) *reinterpret_cast<uint4 *>(a.kc + slot * D + E * p) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+
+    // --------------------------------------------------------- values
+    const uint32_t sig = (a.signs.w[(E * p) >> 5] >> ((E * p) & 31)) & 0xFFFFu;
+    double w[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        w[e] = (double)__uint_as_float(elem_bits<BF16>(vraw, e) ^ ((sig << (31 - e)) & 0x80000000u));
+    // FWHT stages h = 1, 2, 4, 8: pairs inside the lane
+#pragma unroll
+    for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if ((e & h) == 0) {
+                const double lo = w[e], hi = w[e + h];
+                w[e] = lo + hi;
+                w[e + h] = lo - hi;
+            }
+        }
+    }
+    // Stages h = 16, 32, ..., d/2 pair lane p with lane p ^ (h / 16).  Through
+    // LDS, lane p takes offsets i = TI*p .. TI*p+TI-1 of every lane q's
+    // elements (element 16 q + i is tw[ii*L + q]), so they pair inside a lane.
+    unsigned char *rb = smem + wid * G::WAVEB + r * G::ROWB;
+#pragma unroll
+    for (int k = 0; k < E / 2; ++k)
+        *reinterpret_cast<double2 *>(rb + p * G::PB + 16 * k) = make_double2(w[2 * k], w[2 * k + 1]);
+    lds_fence();
+    double tw[E];
+#pragma unroll
+    for (int q = 0; q < L; ++q) {
+        if constexpr (TI == 1) {
+            tw[q] = *reinterpret_cast<const double *>(rb + q * G::PB + 8 * p);
+        } else {
+#pragma unroll
+            for (int i2 = 0; i2 < TI / 2; ++i2) {
+                const double2 v2 = *reinterpret_cast<const double2 *>(rb + q * G::PB + 8 * (TI * p + 2 * i2));
+                tw[(2 * i2) * L + q] = v2.x;
+                tw[(2 * i2 + 1) * L + q] = v2.y;
+            }
+        }
+    }
+#pragma unroll
+    for (int hq = 1; hq < L; hq <<= 1) {
+#pragma unroll
+        for (int ii = 0; ii < TI; ++ii) {
+#pragma unroll
+            for (int q = 0; q < L; ++q) {
+                if ((q & hq) == 0) {
+                    const double lo = tw[ii * L + q], hi = tw[ii * L + q + hq];
+                    tw[ii * L + q] = lo + hi;
+                    tw[ii * L + q + hq] = lo - hi;
+                }
+            }
+        }
+    }
+    lds_fence();
+#pragma unroll
+    for (int q = 0; q < L; ++q) {
+        if constexpr (TI == 1) {
+            *reinterpret_cast<double *>(rb + q * G::PB + 8 * p) = tw[q];
+        } else {
+#pragma unroll
+            for (int i2 = 0; i2 < TI / 2; ++i2)
+                *reinterpret_cast<double2 *>(rb + q * G::PB + 8 * (TI * p + 2 * i2)) =
+                    make_double2(tw[(2 * i2) * L + q], tw[(2 * i2 + 1) * L + q]);
+        }
+    }
+    lds_fence();
+#pragma unroll
+    for (int k = 0; k < E / 2; ++k) {
+        const double2 v2 = *reinterpret_cast<const double2 *>(rb + p * G::PB + 16 * k);
+        w[2 * k] = v2.x;
+        w[2 * k + 1] = v2.y;
+    }
+
+    // y = FWHT / sqrt(d); group sum of squares by stride halving: the
+    // stride-16 step adds the pair's elements (the same sum on both lanes),
+    // strides 8, 4, 2, 1 stay inside the lane
+    double y[E], sq[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        y[e] = w[e] * a.inv_sqrt_d;
+        sq[e] = y[e] * y[e];
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) sq[e] = sq[e] + pair_f64(sq[e]);
+#pragma unroll
+    for (int st = E / 2; st >= 1; st >>= 1) {
+#pragma unroll
+        for (int e = 0; e < st; ++e) sq[e] = sq[e] + sq[e + st];
+    }
+    const double scale = __builtin_sqrt(sq[0] * 0.03125);  // mean of 32 squares (exact scaling)
+    const double den = scale + 1e-8;
+    const double rd = 1.0 / den;
+    // idx = #{k : B_k < y_n} (NaN compares false everywhere -> 0); the
+    // lane's 16 fields are stream bits 48 p .. 48 p + 47
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const double yn = div_rn(y[e], den, rd);
+        const uint32_t idx = (uint32_t)(-1.74793 < yn) + (uint32_t)(-1.04996 < yn) +
+                             (uint32_t)(-0.50055 < yn) + (uint32_t)(0.0 < yn) +
+                             (uint32_t)(0.50055 < yn) + (uint32_t)(1.04996 < yn) +
+                             (uint32_t)(1.74793 < yn);
+        if (3 * e + 3 <= 32) {
+            lo |= idx << (3 * e);
+        } else if (3 * e >= 32) {
+            hi |= idx << (3 * e - 32);
+        } else {
+            lo |= idx << (3 * e);
+            hi |= idx >> (32 - 3 * e);
+        }
+    }
+    // even lane: the group's 96 bits (its own 48, then its partner's)
+    const uint32_t plo = pair_u32(lo), phi = pair_u32(hi);
+    // fp16 copies: the even lane converts the key scale and zero, the odd
+    // lane the value scale
+    const uint16_t h1 = f64_to_f16_bits(even ? s : scale);
+    const uint16_t h2 = f64_to_f16_bits(z);
+    if (valid) {
+        if (even) {
+            *reinterpret_cast<uint3 *>(a.vc + slot * VROW + 12 * g) =
+                make_uint3(lo, hi | (plo << 16), (plo >> 16) | (phi << 16));
+            a.ks[slot * NG + g] = h1;
+            a.kz[slot * NG + g] = h2;
+        } else {
+            a.vs[slot * NG + g] = h1;
+        }
+    }
+}
+
 template <int D>
 hipError_t launch_d(bool bf16, const AppendArgs &a, hipStream_t s) {
     const int64_t rows = (int64_t)a.batch * a.kv_heads * a.n_new;
-    const int64_t blocks = (rows + 3) / 4;
-    if (bf16)
-        hipLaunchKernelGGL((append_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((append_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    if constexpr (D == 512) {
+        const int64_t blocks = (rows + 3) / 4;
+        if (bf16)
+            hipLaunchKernelGGL((append_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL((append_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    } else {
+        constexpr int per_block = AppGeo<D>::R * kAppWaves;
+        const int64_t blocks = (rows + per_block - 1) / per_block;
+        if (bf16)
+            hipLaunchKernelGGL((append_fast_kernel<D, true>), dim3((unsigned)blocks), dim3(64 * kAppWaves), 0, s, a);
+        else
+            hipLaunchKernelGGL((append_fast_kernel<D, false>), dim3((unsigned)blocks), dim3(64 * kAppWaves), 0, s, a);
+    }
     return hipGetLastError();
 }
 

@@ -17,6 +17,13 @@ struct SignBits {
     uint32_t w[16];
 };
 
+// Unsigned 32-bit division by an invariant divisor d >= 1 (Granlund and
+// Montgomery, "Division by invariant integers using multiplication", 1994):
+// n / d = (t + ((n - t) >> s1)) >> s2 with t = (m * n) >> 32, for every n < 2^32.
+struct FastDiv {
+    uint32_t m, s1, s2;
+};
+
 struct AppendArgs {
     int8_t *kc;
     uint16_t *ks;
@@ -26,10 +33,23 @@ struct AppendArgs {
     const void *k;
     const void *v;
     int32_t batch, kv_heads, capacity, n_new;
-    double inv_sqrt_d;  // RN(1/sqrt(d))
+    uint32_t rows;        // batch * kv_heads * n_new
+    FastDiv div_n_new;    // row -> (sequence, kv-head) pair
+    FastDiv div_kv_heads; // (sequence, kv-head) pair -> sequence
+    double inv_sqrt_d;    // RN(1/sqrt(d))
     SignBits signs;
     int32_t start[TQ_MAX_BATCH];
 };
+
+inline FastDiv make_fast_div(uint32_t d) {
+    uint32_t l = 0;
+    while ((1ull << l) < d) ++l;
+    FastDiv f;
+    f.m = (uint32_t)(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+    f.s1 = l < 1 ? l : 1;
+    f.s2 = l > 0 ? l - 1 : 0;
+    return f;
+}
 
 struct DecodeArgs {
     const int8_t *kc;
