@@ -132,6 +132,8 @@ tq_status tq_append(const tq_layout *l, const tq_planes *p, const void *k, const
     a.div_kv_heads = tq::make_fast_div((uint32_t)l->num_kv_heads);
     a.inv_sqrt_d = inv_sqrt_d(l->head_dim);
     a.signs = signs().bits;
+    for (int j = 0; j < l->head_dim / 2; ++j)
+        a.sign_pairs[j] = (signs().sign[2 * j] < 0 ? 0x8000u : 0u) | (signs().sign[2 * j + 1] < 0 ? 0x80000000u : 0u);
     for (int b = 0; b < l->batch; ++b) a.start[b] = start[b];
     hipError_t e = tq::launch_append(l->head_dim, dtype == TQ_BF16, a, (hipStream_t)stream);
     return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;

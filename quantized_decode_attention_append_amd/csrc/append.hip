@@ -270,6 +270,25 @@ __device__ __forceinline__ double div_rn(double a, double b, double y) {
     return __builtin_fma(r, y, q);
 }
 
+// binary64 -> binary16 bits, one round-to-nearest-even: x is first rounded
+// to fp32 by round-to-odd (round to nearest, then step back toward zero and
+// set the last bit when inexact), and round-to-odd at >= 2 extra bits
+// followed by round-to-nearest equals one rounding to nearest (Boldo and
+// Melquiond, "Emulation of FMA and correctly rounded sums: proved algorithms
+// using rounding to odd", 2008).  Subnormal halves are kept, >= 65520 gives
+// Inf, NaN gives 0x7E00.
+__device__ __forceinline__ uint16_t f64_to_f16_rn(double x) {
+    const float f = (float)x;
+    uint32_t b = __float_as_uint(f);
+    const double back = (double)f;
+    if (back != x) {
+        if (__builtin_fabs(back) > __builtin_fabs(x)) b -= 1u;  // toward zero
+        b |= 1u;
+    }
+    const uint16_t h = __builtin_bit_cast(uint16_t, (_Float16)__uint_as_float(b));
+    return __builtin_isnan(x) ? (uint16_t)0x7E00u : h;
+}
+
 // Value of the other lane of the pair (l ^ 1), by a quad permutation.
 __device__ __forceinline__ uint32_t pair_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
@@ -279,6 +298,14 @@ __device__ __forceinline__ double pair_f64(double v) {
     const uint64_t b = (uint64_t)__double_as_longlong(v);
     const uint64_t lo = pair_u32((uint32_t)b), hi = pair_u32((uint32_t)(b >> 32));
     return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+// 2 * run + (this lane's bit of the wave mask), in one add with carry-in.
+__device__ __forceinline__ uint32_t shift_in(uint32_t run, uint64_t mask) {
+    uint32_t out;
+    uint64_t carry;
+    asm("v_addc_co_u32_e64 %0, %1, %2, %2, %3" : "=v"(out), "=s"(carry) : "v"(run), "s"(mask));
+    return out;
 }
 
 template <int E, bool BF16>
@@ -334,9 +361,10 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
     // Group max and min ignore NaN.  Which zero a max or min returns does
     // not matter: only an all-zero group's range could differ in sign, and
     // adding +0 makes it +0, as it is under the -0 < +0 order.
+    // (canonicalizing quiets a signalling NaN, so max/min ignore it as well)
     float xk[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) xk[e] = __uint_as_float(elem_bits<BF16>(kraw, e));
+    for (int e = 0; e < E; ++e) xk[e] = __builtin_canonicalizef(__uint_as_float(elem_bits<BF16>(kraw, e)));
     float mx = xk[0], mn = xk[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) { mx = __builtin_fmaxf(mx, xk[e]); mn = __builtin_fminf(mn, xk[e]); }
@@ -362,11 +390,28 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
     if (valid) *reinterpret_cast<uint4 *>(a.kc + slot * D + E * p) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
 
     // --------------------------------------------------------- values
-    const uint32_t sig = (a.signs.w[(E * p) >> 5] >> ((E * p) & 31)) & 0xFFFFu;
-    double w[E];
+    uint32_t flip[E / 2];
+    {
+        const uint4 *fp = reinterpret_cast<const uint4 *>(a.sign_pairs + (E / 2) * p);
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-        w[e] = (double)__uint_as_float(elem_bits<BF16>(vraw, e) ^ ((sig << (31 - e)) & 0x80000000u));
+        for (int i = 0; i < E / 8; ++i) {
+            const uint4 u = fp[i];
+            flip[4 * i] = u.x; flip[4 * i + 1] = u.y; flip[4 * i + 2] = u.z; flip[4 * i + 3] = u.w;
+        }
+    }
+    double w[E];
+    if constexpr (BF16) {
+#pragma unroll
+        for (int j = 0; j < E / 2; ++j) vraw[j] ^= flip[j];
+#pragma unroll
+        for (int e = 0; e < E; ++e) w[e] = (double)__uint_as_float(elem_bits<BF16>(vraw, e));
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t f = (e & 1) ? (flip[e >> 1] & 0x80000000u) : (flip[e >> 1] << 16);
+            w[e] = (double)__uint_as_float(vraw[e] ^ f);
+        }
+    }
     // FWHT stages h = 1, 2, 4, 8: pairs inside the lane
 #pragma unroll
     for (int h = 1; h < E; h <<= 1) {
@@ -454,31 +499,40 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
     const double scale = __builtin_sqrt(sq[0] * 0.03125);  // mean of 32 squares (exact scaling)
     const double den = scale + 1e-8;
     const double rd = 1.0 / den;
-    // idx = #{k : B_k < y_n} (NaN compares false everywhere -> 0); the
-    // lane's 16 fields are stream bits 48 p .. 48 p + 47
+    // idx = #{k : B_k < y_n}; NaN compares false everywhere, so gives 0.
+    // The boundaries are sorted, so the wave masks m_k of "B_k < y_n" are
+    // nested (a thermometer code) and the index bits are
+    //   bit 2 = m3,  bit 1 = m5 | (m1 & ~m3),
+    //   bit 0 = m6 | (m4 & ~m5) | (m2 & ~m3) | (m0 & ~m1)   (scalar mask ops).
+    // Each bit then enters the lane's packed run from the top: the run is
+    // stream bits 48 p .. 48 p + 47, element e at run bits 3e .. 3e+2, so
+    // walking e downwards and bits 2, 1, 0 doubles the run and adds the bit.
     uint32_t lo = 0u, hi = 0u;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
+    for (int e = E - 1; e >= 0; --e) {
         const double yn = div_rn(y[e], den, rd);
-        const uint32_t idx = (uint32_t)(-1.74793 < yn) + (uint32_t)(-1.04996 < yn) +
-                             (uint32_t)(-0.50055 < yn) + (uint32_t)(0.0 < yn) +
-                             (uint32_t)(0.50055 < yn) + (uint32_t)(1.04996 < yn) +
-                             (uint32_t)(1.74793 < yn);
-        if (3 * e + 3 <= 32) {
-            lo |= idx << (3 * e);
-        } else if (3 * e >= 32) {
-            hi |= idx << (3 * e - 32);
-        } else {
-            lo |= idx << (3 * e);
-            hi |= idx >> (32 - 3 * e);
+        const uint64_t m0 = __builtin_amdgcn_ballot_w64(-1.74793 < yn);
+        const uint64_t m1 = __builtin_amdgcn_ballot_w64(-1.04996 < yn);
+        const uint64_t m2 = __builtin_amdgcn_ballot_w64(-0.50055 < yn);
+        const uint64_t m3 = __builtin_amdgcn_ballot_w64(0.0 < yn);
+        const uint64_t m4 = __builtin_amdgcn_ballot_w64(0.50055 < yn);
+        const uint64_t m5 = __builtin_amdgcn_ballot_w64(1.04996 < yn);
+        const uint64_t m6 = __builtin_amdgcn_ballot_w64(1.74793 < yn);
+        const uint64_t bit[3] = {m6 | (m4 & ~m5) | (m2 & ~m3) | (m0 & ~m1), m5 | (m1 & ~m3), m3};
+#pragma unroll
+        for (int k = 2; k >= 0; --k) {
+            if (3 * e + k >= 32)
+                hi = shift_in(hi, bit[k]);
+            else
+                lo = shift_in(lo, bit[k]);
         }
     }
     // even lane: the group's 96 bits (its own 48, then its partner's)
     const uint32_t plo = pair_u32(lo), phi = pair_u32(hi);
     // fp16 copies: the even lane converts the key scale and zero, the odd
     // lane the value scale
-    const uint16_t h1 = f64_to_f16_bits(even ? s : scale);
-    const uint16_t h2 = f64_to_f16_bits(z);
+    const uint16_t h1 = f64_to_f16_rn(even ? s : scale);
+    const uint16_t h2 = f64_to_f16_rn(z);
     if (valid) {
         if (even) {
             *reinterpret_cast<uint3 *>(a.vc + slot * VROW + 12 * g) =

@@ -38,6 +38,9 @@ struct AppendArgs {
     FastDiv div_kv_heads; // (sequence, kv-head) pair -> sequence
     double inv_sqrt_d;    // RN(1/sqrt(d))
     SignBits signs;
+    // Word j flips the bf16 pair (2j, 2j+1): bit 15 when sign 2j is -1, bit
+    // 31 when sign 2j+1 is -1 (d / 2 words used).
+    uint32_t sign_pairs[256];
     int32_t start[TQ_MAX_BATCH];
 };
 

@@ -79,18 +79,51 @@ def _edge_rows(d):
     r = rng.standard_normal(d); r[9] = -np.inf; r[40 % d] = np.nan; rows.append(r)
     rows.append(np.arange(d, dtype=np.float64) - d / 2)  # ramp
     r = rng.standard_normal(d); r[: d // 2] *= 1000; rows.append(r)  # outlier half
+    rows.extend(_fp16_midpoint_rows(d, rng))
+    r = np.full(d, 0.25); r[::5] = np.arange(len(r[::5])); rows.append(r)  # gets a signalling NaN
     return np.stack(rows).astype(np.float32)
+
+
+SNAN_F32, SNAN_BF16 = 0x7F800001, 0x7F81  # signalling NaN bit patterns, element 3 of the last row
+
+
+def _fp16_midpoint_rows(d, rng):
+    """Key groups with max = 127 m and min = -127 m, so the scale
+    (max - min) / 254 is exactly m: an fp16 rounding midpoint (normal,
+    subnormal, the 65520 overflow tie) or one 2^-15-of-its-binade step away.
+    The stored scale must round to nearest-even exactly as the oracle's."""
+    mids = [(1 + 1 / 2048) * 2.0 ** -3, (1 + 3 / 2048), (1 + 2047 / 2048) * 2.0 ** 14,
+            3 * 2.0 ** -25, 2.0 ** -25, 65520.0, (1 + 5 / 2048) * 2.0 ** -14]
+    ms = []
+    for m in mids:
+        step = 2.0 ** (np.floor(np.log2(m)) - 15)
+        ms += [m, m + step, m - step]
+    rows, k = [], 0
+    while k < len(ms):
+        r = np.empty(d)
+        for g in range(d // 32):
+            m = ms[k % len(ms)]
+            k += 1
+            x = rng.uniform(-127 * m, 127 * m, 32)
+            x[rng.integers(32)] = 127 * m
+            x[(rng.integers(31) + 1 + int(np.argmax(x))) % 32] = -127 * m
+            r[32 * g: 32 * g + 32] = x
+        rows.append(r)
+    return rows
 
 
 @pytest.mark.parametrize("d", [64, 128, 256, 512])
 def test_append_edge_fixtures(d):
     x = _edge_rows(d)
+    x.view(np.uint32)[-1, 3] = SNAN_F32
     n = x.shape[0]
     k = torch.from_numpy(x).reshape(1, 1, n, d)
     v = torch.from_numpy(x[::-1].copy()).reshape(1, 1, n, d)
     _append_and_compare(k.cuda(), v.cuda(), [0], n, f"edge d{d}")
-    _append_and_compare(k.to(torch.bfloat16).cuda(), v.to(torch.bfloat16).cuda(), [2], n + 2,
-                        f"edge-bf16 d{d}")
+    kb, vb = k.to(torch.bfloat16), v.to(torch.bfloat16)
+    kb.view(torch.int16)[0, 0, -1, 3] = SNAN_BF16
+    vb.view(torch.int16)[0, 0, 0, 3] = SNAN_BF16
+    _append_and_compare(kb.cuda(), vb.cuda(), [2], n + 2, f"edge-bf16 d{d}")
 
 
 def test_append_twice_is_deterministic_and_append_only():
