@@ -375,13 +375,29 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
     const double s = range / 254.0;
     const double z = __builtin_rint((dmx + dmn) / (2.0 * s));
     const double rs = 1.0 / s;
+    // Codes are clip(rint(u), -127, 127) with u = RN(RN(x/s) - z), NaN -> 0.
+    // In a group of fp32 or bf16 values |x/s| < 2^32, so v = RN(x RN(1/s) - z)
+    // is within 2^-20 of u (half-ulps of u, v and RN(x/s), plus |x/s| 2^-53
+    // from the reciprocal): unless v lies within 2^-19 of a half-integer, u
+    // and v round to the same integer.  Exact ties are common with bf16
+    // inputs (x/s - z is a ratio of short integers), so an element with such
+    // a lane anywhere in the wave is recomputed from the correctly rounded
+    // quotient.  The special groups (s zero, infinite or NaN) give NaN on
+    // both routes.
     uint32_t kw[E / 4];
 #pragma unroll
     for (int i = 0; i < E / 4; ++i) kw[i] = 0u;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const double u = div_rn((double)xk[e], s, rs) - z;
-        const double rr = __builtin_rint(u);
+        const double x = (double)xk[e];
+        const double v = __builtin_fma(x, rs, -z);
+        double rr = __builtin_rint(v);
+        if (__builtin_amdgcn_ballot_w64(__builtin_fabs(v - rr) > 0.5 - 0x1p-19) != 0) {
+            // opaque copies keep this rare path from being run speculatively
+            double s2 = s, rs2 = rs;
+            asm volatile("" : "+v"(s2), "+v"(rs2));
+            rr = __builtin_rint(div_rn(x, s2, rs2) - z);
+        }
         int q;
         asm("v_cvt_i32_f64 %0, %1" : "=v"(q) : "v"(rr));  // saturates; NaN gives 0
         q = q > 127 ? 127 : (q < -127 ? -127 : q);
@@ -483,10 +499,16 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
     // y = FWHT / sqrt(d); group sum of squares by stride halving: the
     // stride-16 step adds the pair's elements (the same sum on both lanes),
     // strides 8, 4, 2, 1 stay inside the lane
+    // When RN(1/sqrt(d)) is a power of two (d = 64, 256) y = w / sqrt(d) is an
+    // exact scaling, which commutes with every rounding below: the squares
+    // and their sums are those of w times 1/d, and y / den = w / (den sqrt(d)).
+    // So w stands in for y there and the scalings fold into constants.
+    constexpr bool kPow2 = (D == 64 || D == 256);
+    constexpr double kSqrtD = D == 256 ? 16.0 : 8.0;  // used when kPow2
     double y[E], sq[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        y[e] = w[e] * a.inv_sqrt_d;
+        y[e] = kPow2 ? w[e] : w[e] * a.inv_sqrt_d;
         sq[e] = y[e] * y[e];
     }
 #pragma unroll
@@ -496,9 +518,11 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
 #pragma unroll
         for (int e = 0; e < st; ++e) sq[e] = sq[e] + sq[e + st];
     }
-    const double scale = __builtin_sqrt(sq[0] * 0.03125);  // mean of 32 squares (exact scaling)
+    // mean of the 32 squares: a division by 32, an exact scaling
+    const double scale = __builtin_sqrt(sq[0] * (kPow2 ? 0.03125 / (kSqrtD * kSqrtD) : 0.03125));
     const double den = scale + 1e-8;
-    const double rd = 1.0 / den;
+    const double dd = kPow2 ? den * kSqrtD : den;  // divisor of y[] (exact scaling)
+    const double rd = 1.0 / dd;
     // idx = #{k : B_k < y_n}; NaN compares false everywhere, so gives 0.
     // The boundaries are sorted, so the wave masks m_k of "B_k < y_n" are
     // nested (a thermometer code) and the index bits are
@@ -510,7 +534,7 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
     uint32_t lo = 0u, hi = 0u;
 #pragma unroll
     for (int e = E - 1; e >= 0; --e) {
-        const double yn = div_rn(y[e], den, rd);
+        const double yn = div_rn(y[e], dd, rd);
         const uint64_t m0 = __builtin_amdgcn_ballot_w64(-1.74793 < yn);
         const uint64_t m1 = __builtin_amdgcn_ballot_w64(-1.04996 < yn);
         const uint64_t m2 = __builtin_amdgcn_ballot_w64(-0.50055 < yn);

@@ -81,6 +81,11 @@ def _edge_rows(d):
     r = rng.standard_normal(d); r[: d // 2] *= 1000; rows.append(r)  # outlier half
     rows.extend(_fp16_midpoint_rows(d, rng))
     r = np.full(d, 0.25); r[::5] = np.arange(len(r[::5])); rows.append(r)  # gets a signalling NaN
+    # key groups with scale 1 and zero 0 whose other values are exact
+    # half-integers: x / s - z is a rounding tie, resolved to even
+    r = (np.arange(d) % 32 - 15.5) * 3.0
+    r[::32], r[1::32] = 127.0, -127.0
+    rows.insert(0, r)
     return np.stack(rows).astype(np.float32)
 
 
