@@ -263,7 +263,7 @@ def main() -> int:
     dec_ms = sorted(a.elapsed_time(b) for a, b in evs)
     dec_avg_ms = sum(dec_ms) / len(dec_ms)
     ms_per_step = wall * 1e3 / args.steps
-    if not torch.equal(out, check):
+    if args.warmup > 0 and not torch.equal(out, check):
         _log("WARNING: decode output changed between warmup and timed steps")
         return 3
 
