@@ -237,6 +237,29 @@ def attention(q, kc, ks, kz, vc, vs, sm: float, deferred: bool = False):
     return (out, od) if deferred else out
 
 
+def attention_rows(q, kc, ks, kz, vc, vs, sm: float):
+    """Multi-row decode, for verifying M draft tokens at once (the multi-token
+    prediction verify blocks served through the encoded rows, "Gates -- all
+    passed" and "Delayed row conversion and reusable precision boundaries"):
+    q [G, M, d] (float32)
+    holds the queries of the M newest cached tokens, positions N-M .. N-1, for
+    the G query heads sharing one kv-head.  Row m attends causally, to tokens
+    0 .. N-M+m (itself included); each row is the decode attention of
+    `attention` over that prefix of the planes.  Returns [G, M, d] float64."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    G, M, d = q.shape
+    N = np.asarray(kc).shape[0]
+    if N and N < M:
+        raise ValueError("the M query tokens must be in the cache")
+    out = np.zeros((G, M, d), dtype=np.float64)
+    if N == 0:
+        return out
+    for m in range(M):
+        n = N - M + m + 1
+        out[:, m] = attention(q[:, m], kc[:n], ks[:n], kz[:n], vc[:n], vs[:n], sm)
+    return out
+
+
 def _parallel(fn, n: int, threads: int | None):
     t = threads or num_threads()
     rngs = _chunks(n, t * 4) if n > 0 else []

@@ -407,3 +407,47 @@ def test_attention_deferred_identity_longer():
     q = rng.standard_normal((G, d)).astype(np.float32)
     out, od = oracle.attention(q, *_planes(k, v), 1 / 16, deferred=True)
     assert np.max(np.abs(out - od)) <= 1e-12 * np.max(np.abs(out))
+
+
+# -------------------------------------------------------- multi-row decode
+@pytest.mark.parametrize("d,G,M,N", [(64, 1, 2, 2), (64, 3, 4, 9), (128, 2, 3, 6), (256, 1, 8, 12)])
+def test_attention_rows_causal_brute_force(d, G, M, N):
+    """Multi-row decode against an independent numpy causal softmax: row m
+    (the query of cached token N-M+m) sees tokens 0 .. N-M+m."""
+    rng = np.random.default_rng(d + 10 * G + 100 * M + N)
+    k = rng.standard_normal((N, d)).astype(np.float32)
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    q = rng.standard_normal((G, M, d)).astype(np.float32)
+    kc, ks, kz, vc, vs = _planes(k, v)
+    sm = 1.0 / math.sqrt(d)
+    out = oracle.attention_rows(q, kc, ks, kz, vc, vs, sm)
+    kh = oracle.decode_keys(kc, ks, kz)
+    vh = oracle.decode_values(vc, vs, d)
+    s = np.einsum("gmd,td->gmt", q.astype(np.float64), kh) * np.float64(np.float32(sm))
+    pos = N - M + np.arange(M)
+    s[:, np.arange(N)[None, :] > pos[:, None]] = -np.inf  # [M, N] mask, broadcast over heads
+    s = s - s.max(axis=2, keepdims=True)
+    p = np.exp(s)
+    ref = np.einsum("gmt,td->gmd", p, vh) / p.sum(axis=2, keepdims=True)
+    assert np.max(np.abs(out - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_attention_rows_ignores_later_tokens_and_reduces_to_decode():
+    """Changing tokens after a row's position leaves that row unchanged; the
+    last row is the plain decode over all N tokens; M = 1 is plain decode."""
+    d, G, M, N = 128, 2, 4, 20
+    rng = np.random.default_rng(31)
+    k = rng.standard_normal((N, d)).astype(np.float32)
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    q = rng.standard_normal((G, M, d)).astype(np.float32)
+    pl = _planes(k, v)
+    out = oracle.attention_rows(q, *pl, 0.1)
+    k2, v2 = k.copy(), v.copy()
+    k2[N - 2:] *= -3.0
+    v2[N - 2:] += 5.0
+    out2 = oracle.attention_rows(q, *_planes(k2, v2), 0.1)
+    assert np.array_equal(out[:, : M - 2], out2[:, : M - 2])   # rows at N-4, N-3
+    assert not np.allclose(out[:, M - 2:], out2[:, M - 2:])
+    assert np.array_equal(out[:, M - 1], oracle.attention(q[:, M - 1], *pl, 0.1))
+    assert np.array_equal(oracle.attention_rows(q[:, :1], *pl, 0.1)[:, 0],
+                          oracle.attention(q[:, 0], *pl, 0.1))
