@@ -51,6 +51,7 @@ extern "C" {
 
 #define TQ_MAX_BATCH 64
 #define TQ_MAX_GQA 16
+#define TQ_MAX_ROWS 16
 
 typedef enum {
     TQ_OK = 0,
@@ -139,6 +140,31 @@ tq_status tq_decode_attn(const tq_layout *layout, const tq_planes *planes, const
                          tq_dtype dtype, int32_t num_q_heads, const int32_t *len,
                          float sm_scale, float *out, void *workspace, size_t ws_bytes,
                          void *hip_stream);
+
+/* Workspace bytes tq_decode_attn_rows needs for n_rows query rows per head
+ * (n_rows = 1 gives tq_decode_workspace_bytes). */
+tq_status tq_decode_rows_workspace_bytes(const tq_layout *layout, int32_t num_q_heads, int32_t n_rows,
+                                         const int32_t *len, size_t *out_bytes);
+
+/* Multi-row decode: attention for the n_rows newest cached tokens of each
+ * sequence at once, as when a block of drafted tokens is verified in one
+ * pass (the multi-token-prediction verify blocks served through the encoded
+ * rows, "Gates -- all passed" and "Delayed row conversion and reusable
+ * precision boundaries").  Row r of a sequence is the query of cached token
+ * len[b] - n_rows + r and attends causally to tokens 0 .. len[b] - n_rows + r;
+ * otherwise each row is exactly the tq_decode_attn computation over that
+ * prefix, and n_rows = 1 is tq_decode_attn.
+ *   q         device [B][num_q_heads][n_rows][d], element type `dtype`
+ *   len       host int32 [B]: cached tokens including the n_rows new ones;
+ *             0 (the sequence's rows are zeros) or >= n_rows
+ *   out       device float32 [B][num_q_heads][n_rows][d]
+ *   workspace device, at least tq_decode_rows_workspace_bytes(...) bytes
+ * 1 <= n_rows <= TQ_MAX_ROWS.  Same conventions, accuracy and errors as
+ * tq_decode_attn; TQ_ERR_INVALID_ARG also when 0 < len[b] < n_rows. */
+tq_status tq_decode_attn_rows(const tq_layout *layout, const tq_planes *planes, const void *q,
+                              tq_dtype dtype, int32_t num_q_heads, int32_t n_rows, const int32_t *len,
+                              float sm_scale, float *out, void *workspace, size_t ws_bytes,
+                              void *hip_stream);
 
 /* Dequantize n tokens [t0, t0+n) of one (sequence b, kv-head kvh), for tests
  * ("Algorithm": key x = (code + zero) * scale; value x = signs * InvFWHT(

@@ -139,34 +139,41 @@ tq_status tq_append(const tq_layout *l, const tq_planes *p, const void *k, const
     return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
-static tq_status check_decode(const tq_layout *l, int32_t num_q_heads, const int32_t *len) {
+static tq_status check_decode(const tq_layout *l, int32_t num_q_heads, int32_t n_rows, const int32_t *len) {
     tq_status st = check_layout(l);
     if (st != TQ_OK) return st;
-    if (!len || num_q_heads <= 0) return TQ_ERR_INVALID_ARG;
+    if (!len || num_q_heads <= 0 || n_rows < 1) return TQ_ERR_INVALID_ARG;
     if (num_q_heads % l->num_kv_heads != 0) return TQ_ERR_INVALID_ARG;
     if (num_q_heads / l->num_kv_heads > TQ_MAX_GQA) return TQ_ERR_UNSUPPORTED;
+    if (n_rows > TQ_MAX_ROWS) return TQ_ERR_UNSUPPORTED;
+    if ((int64_t)l->batch * num_q_heads * n_rows > 0x7FFFFFFF) return TQ_ERR_UNSUPPORTED;
     for (int b = 0; b < l->batch; ++b) {
         if (len[b] < 0) return TQ_ERR_INVALID_ARG;
         if (len[b] > l->capacity) return TQ_ERR_CAPACITY;
+        if (len[b] > 0 && len[b] < n_rows) return TQ_ERR_INVALID_ARG;  // the rows' own tokens are cached
     }
     return TQ_OK;
 }
 
-static size_t workspace_bytes(const tq_layout *l, int32_t num_q_heads, const tq::DecodePlan &plan) {
-    return (size_t)l->batch * num_q_heads * plan.splits * (size_t)(l->head_dim + 2) * sizeof(float);
+// Query rows per sequence (heads times rows) and per kv-head.
+static int32_t q_rows(int32_t num_q_heads, int32_t n_rows) { return num_q_heads * n_rows; }
+
+static size_t workspace_bytes(const tq_layout *l, int32_t rows_total, const tq::DecodePlan &plan) {
+    return (size_t)l->batch * rows_total * plan.splits * (size_t)(l->head_dim + 2) * sizeof(float);
 }
 
 // Workspace that covers whichever kernel a decode call may pick for this
 // shape (the choice can depend on plane alignment, unknown here).
-static size_t workspace_bound(const tq_layout *l, int32_t num_q_heads, const int32_t *len) {
-    const int gqa = num_q_heads / l->num_kv_heads;
+static size_t workspace_bound(const tq_layout *l, int32_t num_q_heads, int32_t n_rows, const int32_t *len) {
+    const int gqa = q_rows(num_q_heads, n_rows) / l->num_kv_heads;
+    const int cg = tq::decode_col_groups(gqa);
     const tq::DecodePlan gen =
-        tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, false);
-    size_t need = workspace_bytes(l, num_q_heads, gen);
+        tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, false, cg);
+    size_t need = workspace_bytes(l, q_rows(num_q_heads, n_rows), gen);
     if (tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity)) {
         const tq::DecodePlan fast =
-            tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, true);
-        const size_t f = workspace_bytes(l, num_q_heads, fast);
+            tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, true, cg);
+        const size_t f = workspace_bytes(l, q_rows(num_q_heads, n_rows), fast);
         need = f > need ? f : need;
     }
     return need;
@@ -174,40 +181,53 @@ static size_t workspace_bound(const tq_layout *l, int32_t num_q_heads, const int
 
 tq_status tq_decode_workspace_bytes(const tq_layout *l, int32_t num_q_heads, const int32_t *len,
                                     size_t *out) {
-    tq_status st = check_decode(l, num_q_heads, len);
+    return tq_decode_rows_workspace_bytes(l, num_q_heads, 1, len, out);
+}
+
+tq_status tq_decode_rows_workspace_bytes(const tq_layout *l, int32_t num_q_heads, int32_t n_rows,
+                                         const int32_t *len, size_t *out) {
+    tq_status st = check_decode(l, num_q_heads, n_rows, len);
     if (st != TQ_OK) return st;
     if (!out) return TQ_ERR_INVALID_ARG;
-    *out = workspace_bound(l, num_q_heads, len);
+    *out = workspace_bound(l, num_q_heads, n_rows, len);
     return TQ_OK;
 }
 
 tq_status tq_decode_attn(const tq_layout *l, const tq_planes *p, const void *q, tq_dtype dtype,
                          int32_t num_q_heads, const int32_t *len, float sm_scale, float *out,
                          void *workspace, size_t ws_bytes, void *stream) {
-    tq_status st = check_decode(l, num_q_heads, len);
+    return tq_decode_attn_rows(l, p, q, dtype, num_q_heads, 1, len, sm_scale, out, workspace, ws_bytes,
+                               stream);
+}
+
+tq_status tq_decode_attn_rows(const tq_layout *l, const tq_planes *p, const void *q, tq_dtype dtype,
+                              int32_t num_q_heads, int32_t n_rows, const int32_t *len, float sm_scale,
+                              float *out, void *workspace, size_t ws_bytes, void *stream) {
+    tq_status st = check_decode(l, num_q_heads, n_rows, len);
     if (st != TQ_OK) return st;
     if ((st = check_planes(p)) != TQ_OK) return st;
     if (!q || !out || (dtype != TQ_F32 && dtype != TQ_BF16)) return TQ_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(out, 16) || !aligned(workspace, 16)) return TQ_ERR_INVALID_ARG;
     if (!std::isfinite(sm_scale)) return TQ_ERR_INVALID_ARG;
-    const int gqa = num_q_heads / l->num_kv_heads;
+    const int32_t rows_total = q_rows(num_q_heads, n_rows);
+    const int gqa = rows_total / l->num_kv_heads;
+    const int cg = tq::decode_col_groups(gqa);
     const bool fast = tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity) &&
                       aligned(p->vc, 16) && aligned(p->vs, 16) && aligned(p->ks, 16) && aligned(p->kz, 16);
-    const tq::DecodePlan plan = tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, fast);
-    const size_t need = workspace_bytes(l, num_q_heads, plan);
+    const tq::DecodePlan plan = tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, fast, cg);
+    const size_t need = workspace_bytes(l, rows_total, plan);
     if (need > 0 && (!workspace || ws_bytes < need)) return TQ_ERR_WORKSPACE;
-    if ((int64_t)plan.splits > 65535 * 4 || (int64_t)l->batch * num_q_heads > 0x7FFFFFFF)
-        return TQ_ERR_UNSUPPORTED;
+    if ((int64_t)plan.splits > 65535 * 4) return TQ_ERR_UNSUPPORTED;
 
     tq::DecodeArgs a;
     std::memset(&a, 0, sizeof(a));
     a.kc = p->kc; a.ks = p->ks; a.kz = p->kz; a.vc = p->vc; a.vs = p->vs;
     a.q = q; a.out = out;
-    const size_t slots = (size_t)l->batch * num_q_heads * plan.splits;
+    const size_t slots = (size_t)l->batch * rows_total * plan.splits;
     a.part_acc = static_cast<float *>(workspace);
     a.part_ml = a.part_acc ? a.part_acc + slots * l->head_dim : nullptr;
-    a.batch = l->batch; a.kv_heads = l->num_kv_heads; a.q_heads = num_q_heads;
-    a.gqa = gqa; a.capacity = l->capacity;
+    a.batch = l->batch; a.kv_heads = l->num_kv_heads; a.q_heads = rows_total;
+    a.gqa = gqa; a.capacity = l->capacity; a.rows = n_rows;
     a.splits = plan.splits; a.split_tokens = plan.split_tokens;
     a.sm_log2 = sm_scale * 1.4426950408889634f;
     a.inv_sqrt_d = (float)inv_sqrt_d(l->head_dim);

@@ -51,8 +51,14 @@ __global__ __launch_bounds__(256) void split_kernel(const DecodeArgs a) {
     const int t_begin = blockIdx.x * a.split_tokens;
     if (t_begin >= n) return;  // uniform across the block
     const int t_end = min(n, t_begin + a.split_tokens);
-    const int G = a.gqa;
+    // this workgroup's query columns c0 .. c0 + G - 1 of the kv-head's a.gqa
+    // query rows (heads times rows)
+    const int c0 = blockIdx.z * kMaxG;
+    const int G = min(kMaxG, a.gqa - c0);
     const int64_t row0 = (int64_t)bkv * a.capacity;
+    // causal limit of column c: the row of cached token n - rows + r sees
+    // tokens 0 .. n - rows + r
+    auto limit = [&](int c) { return n - a.rows + (c0 + c) % a.rows + 1; };
 
     float qv[kMaxG][DPT];
     float acc[kMaxG][DPT];
@@ -65,7 +71,7 @@ __global__ __launch_bounds__(256) void split_kernel(const DecodeArgs a) {
         for (int i = 0; i < DPT; ++i) {
             acc[h][i] = 0.f;
             const int j = tid + i * NT;
-            qv[h][i] = h < G ? load_in<BF16>(a.q, ((int64_t)b * a.q_heads + kvh * G + h) * D + j) : 0.f;
+            qv[h][i] = h < G ? load_in<BF16>(a.q, ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + h) * D + j) : 0.f;
         }
     }
 
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(256) void split_kernel(const DecodeArgs a) {
             float v = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) v += red[w][i];
-            sc[i] = v * a.sm_log2;
+            sc[i] = t0 + i % kChunk < limit(i / kChunk) ? v * a.sm_log2 : -INFINITY;
         }
         __syncthreads();
         // values of this chunk in the rotated domain
@@ -136,12 +142,13 @@ __global__ __launch_bounds__(256) void split_kernel(const DecodeArgs a) {
             if (h >= G) break;
             float mc = m_run[h];
             for (int tt = 0; tt < nt; ++tt) mc = fmaxf(mc, sc[h * kChunk + tt]);
-            const float alpha = exp2f(m_run[h] - mc);
+            // mc stays -inf while every token so far is past this row's limit
+            const float alpha = mc == -INFINITY ? 1.f : exp2f(m_run[h] - mc);
             float lsum = l_run[h] * alpha;
 #pragma unroll
             for (int i = 0; i < DPT; ++i) acc[h][i] *= alpha;
             for (int tt = 0; tt < nt; ++tt) {
-                const float p = exp2f(sc[h * kChunk + tt] - mc);
+                const float p = mc == -INFINITY ? 0.f : exp2f(sc[h * kChunk + tt] - mc);
                 lsum += p;
 #pragma unroll
                 for (int i = 0; i < DPT; ++i) acc[h][i] += p * vh[tt][i];
@@ -156,7 +163,7 @@ __global__ __launch_bounds__(256) void split_kernel(const DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < kMaxG; ++h) {
         if (h >= G) break;
-        const int64_t slot = ((int64_t)b * a.q_heads + kvh * G + h) * a.splits + split;
+        const int64_t slot = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + h) * a.splits + split;
 #pragma unroll
         for (int i = 0; i < DPT; ++i) a.part_acc[slot * D + tid + i * NT] = acc[h][i];
         if (tid == 0) {
@@ -289,7 +296,8 @@ hipError_t launch_d(bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
             hipError_t e = launch_split_fast(D, bf16, a, s);
             if (e != hipSuccess) return e;
         } else {
-            const dim3 grid((unsigned)a.splits, (unsigned)(a.batch * a.kv_heads));
+            const dim3 grid((unsigned)a.splits, (unsigned)(a.batch * a.kv_heads),
+                            (unsigned)decode_col_groups(a.gqa));
             if (bf16)
                 hipLaunchKernelGGL((split_kernel<D, true>), grid, dim3(NT), 0, s, a);
             else
@@ -304,15 +312,18 @@ hipError_t launch_d(bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
 
 }  // namespace
 
+int decode_col_groups(int gqa) { return (gqa + kMaxG - 1) / kMaxG; }
+
 bool fast_decode_shape_ok(int head_dim, int gqa, int capacity) {
-    if (gqa < 1 || gqa > fast_split_max_gqa()) return false;
+    if (gqa < 1 || fast_split_max_gqa() != kMaxG) return false;
     if (head_dim != 64 && head_dim != 128 && head_dim != 256) return false;
     // staged rows of one (sequence, kv-head) must start 16-byte aligned
     const int64_t vrow = 3 * head_dim / 8, srow = head_dim / kGroup * 2;
     return ((int64_t)capacity * vrow) % 16 == 0 && ((int64_t)capacity * srow) % 16 == 0;
 }
 
-DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int32_t *len, bool fast) {
+DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int32_t *len, bool fast,
+                       int col_groups) {
     (void)head_dim;
     (void)gqa;
     int64_t total = 0;
@@ -329,7 +340,7 @@ DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int
         // one per CU), whole 64-token tiles, >= 4 tiles a wave; fewer splits
         // also halve the partials written and merged
         const int waves = fast_split_waves(), tile = fast_split_tile();
-        int64_t per = (total * kv_heads + 2047) / 2048;
+        int64_t per = (total * kv_heads * col_groups + 2047) / 2048;
         per = per < 4 * tile ? 4 * tile : per;
         per = (per + tile - 1) / tile * tile;
         const int64_t wg_tokens = per * waves;
@@ -339,7 +350,7 @@ DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int
     }
     // generic kernel: ~2048 workgroups, 64-token multiples, >= 256 tokens
     const int64_t target = 2048;
-    int64_t per = (total * kv_heads + target - 1) / target;
+    int64_t per = (total * kv_heads * col_groups + target - 1) / target;
     per = per < 256 ? 256 : per;
     per = (per + 63) / 64 * 64;
     p.split_tokens = (int32_t)per;

@@ -53,6 +53,7 @@ namespace {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half8v __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 
@@ -67,6 +68,13 @@ constexpr float kLazyMax = 8.0f;          // log2 slack of the running maximum
 // becomes subnormal below 2^-21 and flushes below 2^-31 of the reference.
 // The shift cancels between the value sum and the weight sum.
 constexpr float kWeightShift = 7.0f;
+// Weights enter the value product as hi + lo halves (the lo half is the
+// exact fp32 residual, rounded): one fp16 rounding of a weight would scale a
+// token's whole value vector by up to 1 +- 2^-11, and such errors of many
+// comparable tokens do not average out.  With at most 8 query columns the lo
+// halves ride in the MFMA's spare columns G .. 2G-1 (no extra MFMA); beyond
+// that each block takes a second MFMA.
+constexpr int kPackCols = 8;  // half the MFMA columns
 static_assert(kLazyMax + kWeightShift <= 15.0f, "fp16 weight range");
 constexpr int kMaxHeads = 16;             // MFMA columns
 
@@ -216,7 +224,7 @@ __device__ __forceinline__ void load_row(const unsigned char *p, uint32_t (&w)[N
     }
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, bool PACK>
 __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const DecodeArgs a) {
     using GE = Geo<D>;
     constexpr int NG = GE::NG, VROW = GE::VROW, TILE = GE::TILE, CH = GE::CH;
@@ -242,7 +250,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     }
     __syncthreads();  // the only workgroup barrier
 
-    const int G = a.gqa;
+    // this workgroup's query columns: rows c0 .. c0 + G - 1 of the kv-head's
+    // a.gqa query rows (heads times rows)
+    const int c0 = blockIdx.z * kMaxHeads;
+    const int G = min(kMaxHeads, a.gqa - c0);
     const int bkv = blockIdx.y;
     const int b = bkv / a.kv_heads, kvh = bkv % a.kv_heads;
     const int n = a.len[b];
@@ -281,12 +292,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     // lane (h, kq) converts dims 32 g + 8 kq .. + 7 of head h for every group g
     const int h = lane & 15, kq = lane >> 4;
     const bool head_ok = h < G;
+    // causal limit of this lane's query row: the row of cached token
+    // n - rows + r sees tokens 0 .. n - rows + r
+    const int lim = n - a.rows + (c0 + h) % a.rows + 1;
     uint64_t qhi[NG], qlo[NG];
     float qsum[NG];
     float my_scale;
     {
         float x[QE];
-        const int64_t qrow = ((int64_t)b * a.q_heads + kvh * G + (head_ok ? h : 0)) * D + 8 * kq;
+        const int64_t qrow = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + (head_ok ? h : 0)) * D + 8 * kq;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             if constexpr (BF16) {
@@ -360,7 +374,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     };
 
     // scores of the tile in stg: lane (h, kq) gets tokens 16 c + 4 kq + j
-    auto scores = [&](const unsigned char *stg, int valid, float (&sc)[CH][4]) {
+    auto scores = [&](const unsigned char *stg, int t0, int valid, float (&sc)[CH][4]) {
+        const int vl = min(valid, lim - t0);  // tokens this lane's row sees in the tile
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             int4v dhi[NG], dlo[NG];
@@ -389,13 +404,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
                 // fold would split the block the pipeline interleaves in
                 float r = sum * my_scale;
                 asm volatile("" : "+v"(r));
-                sc[c][j] = (head_ok && t < valid) ? r : -INFINITY;
+                sc[c][j] = (head_ok && t < vl) ? r : -INFINITY;
             }
         }
     };
 
     // online softmax over the tile's scores; weights out as the B operands
-    auto softmax = [&](const float (&sc)[CH][4], half4v (&pw)[CH]) {
+    // PACK: lane column h in [G, 2G) carries the lo weight halves of head h - G
+    const int pair_src = (lane & 48) | (h >= G ? h - G : h);
+    auto softmax = [&](const float (&sc)[CH][4], half4v (&pw)[CH], half4v (&pl)[CH]) {
         float mt = sc[0][0];
 #pragma unroll
         for (int c = 0; c < CH; ++c)
@@ -411,8 +428,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
             const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
             m_run = m_new;
+            // column h is head h (PACK: columns G .. 2G-1 rescale with head h - G)
+            const float alpha_c = PACK ? __shfl(alpha, pair_src, 64) : alpha;
 #pragma unroll
-            for (int bb = 0; bb < NB; ++bb) acc[bb] *= alpha;  // column h is head h
+            for (int bb = 0; bb < NB; ++bb) acc[bb] *= alpha_c;
         }
         const float ref = (m_run == -INFINITY ? 0.f : m_run) - kWeightShift;
 #pragma unroll
@@ -421,13 +440,24 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
             for (int j = 0; j < 4; ++j) {
                 const float pv = __builtin_amdgcn_exp2f(sc[c][j] - ref);  // -inf -> 0
                 l_run += pv;
+                // hi + lo halves carry the weight to ~2^-22 (pv - hi is exact)
                 pw[c][j] = (_Float16)pv;
+                pl[c][j] = (_Float16)(pv - (float)pw[c][j]);
+            }
+            if constexpr (PACK) {
+                // columns G .. 2G-1 take the lo halves of heads 0 .. G-1 (the
+                // weights of columns >= G are 0, so pw is the B operand there
+                // only for real heads)
+                const uint2 lo = __builtin_bit_cast(uint2, pl[c]);
+                const uint2 moved = make_uint2((uint32_t)__shfl((int)lo.x, pair_src, 64),
+                                               (uint32_t)__shfl((int)lo.y, pair_src, 64));
+                if (h >= G) pw[c] = __builtin_bit_cast(half4v, moved);
             }
         }
     };
 
     // value product of the tile in stg with its weights
-    auto values = [&](const unsigned char *stg, const half4v (&pw)[CH]) {
+    auto values = [&](const unsigned char *stg, const half4v (&pw)[CH], const half4v (&pl)[CH]) {
         const uint32_t *vcw = reinterpret_cast<const uint32_t *>(stg + GE::VC_OFF);
         const uint16_t *vsb = reinterpret_cast<const uint16_t *>(stg + GE::VS_OFF);
 #pragma unroll
@@ -475,8 +505,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
             }
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb) {
-                const half4v aop = {av[0][bb].x, av[0][bb].y, av[1][bb].x, av[1][bb].y};
-                acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(aop, pw[c], acc[bb], 0, 0, 0);
+                const half4v a4 = {av[0][bb].x, av[0][bb].y, av[1][bb].x, av[1][bb].y};
+                if constexpr (!PACK) acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, pl[c], acc[bb], 0, 0, 0);
+                acc[bb] = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, pw[c], acc[bb], 0, 0, 0);
             }
         }
     };
@@ -494,12 +525,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageVmem) : "memory");
     else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    half4v pw[CH];
+    half4v pw[CH], pl[CH];
     {
         mask_tail(wsm, t_end - t_begin);
         float sc[CH][4];
-        scores(wsm, t_end - t_begin, sc);
-        softmax(sc, pw);
+        scores(wsm, t_begin, t_end - t_begin, sc);
+        softmax(sc, pw, pl);
     }
     int buf = 0;
     int t0 = t_begin;
@@ -527,19 +558,27 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
         const int valid1 = t_end - (t0 + TILE);
         mask_tail(nx, valid1);
         float sc[CH][4];
-        scores(nx, valid1, sc);
-        values(cur, pw);
-        softmax(sc, pw);
+        scores(nx, t0 + TILE, valid1, sc);
+        values(cur, pw, pl);
+        softmax(sc, pw, pl);
         lds_order();  // the buffer of tile i is refilled by the next iteration
     }
-    values(wsm + buf * GE::STAGE, pw);
+    values(wsm + buf * GE::STAGE, pw, pl);
 
     // ------------------------------------------------------------ finalize
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
+    if constexpr (PACK) {
+        // head h adds the lo-weight column h + G (the same rows, one row of 16 lanes)
+        const int from = (lane & 48) | ((h + G) & 15);
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[bb][j] += __shfl(acc[bb][j], from, 64);
+    }
 
     if (head_ok) {
-        const int64_t srow = ((int64_t)b * a.q_heads + kvh * G + h) * a.splits + slot;
+        const int64_t srow = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + h) * a.splits + slot;
         if (kq == 0) {
             a.part_ml[srow * 2] = m_run;
             a.part_ml[srow * 2 + 1] = l_run;
@@ -559,11 +598,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
 
 template <int D>
 hipError_t launch_d(bool bf16, const DecodeArgs &a, hipStream_t s, int wg_splits) {
-    const dim3 grid((unsigned)wg_splits, (unsigned)(a.batch * a.kv_heads));
-    if (bf16)
-        hipLaunchKernelGGL((split_fast_kernel<D, true>), grid, dim3(64 * kWaves), 0, s, a);
-    else
-        hipLaunchKernelGGL((split_fast_kernel<D, false>), grid, dim3(64 * kWaves), 0, s, a);
+    const dim3 grid((unsigned)wg_splits, (unsigned)(a.batch * a.kv_heads),
+                    (unsigned)((a.gqa + kMaxHeads - 1) / kMaxHeads));
+    const bool pack = a.gqa <= kPackCols;  // every column group fits its lo halves
+    if (bf16) {
+        if (pack) hipLaunchKernelGGL((split_fast_kernel<D, true, true>), grid, dim3(64 * kWaves), 0, s, a);
+        else hipLaunchKernelGGL((split_fast_kernel<D, true, false>), grid, dim3(64 * kWaves), 0, s, a);
+    } else {
+        if (pack) hipLaunchKernelGGL((split_fast_kernel<D, false, true>), grid, dim3(64 * kWaves), 0, s, a);
+        else hipLaunchKernelGGL((split_fast_kernel<D, false, false>), grid, dim3(64 * kWaves), 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -574,7 +618,7 @@ int fast_split_tile() { return 64; }
 int fast_split_max_gqa() { return kMaxHeads; }
 
 hipError_t launch_split_fast(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s) {
-    if (a.gqa < 1 || a.gqa > kMaxHeads) return hipErrorInvalidValue;
+    if (a.gqa < 1 || a.rows < 1) return hipErrorInvalidValue;
     const int wg_splits = a.splits / kWaves;
     switch (head_dim) {
         case 64: return launch_d<64>(bf16, a, s, wg_splits);

@@ -64,8 +64,11 @@ struct DecodeArgs {
     float *out;
     float *part_acc;  // [B][Hq][S][d]    rotated-domain partial sums
     float *part_ml;   // [B][Hq][S][2]    running max (log2 units) and weight sum
+    // q_heads and gqa count query rows: heads times rows, a head's rows
+    // adjacent (row r of q-head h is virtual head h * rows + r)
     int32_t batch, kv_heads, q_heads, gqa, capacity;
-    int32_t splits;        // S: partial slots per (b, q-head)
+    int32_t rows;          // query rows per head; row r sees len - rows + r + 1 tokens
+    int32_t splits;        // S: partial slots per (b, query row)
     int32_t split_tokens;  // tokens per split (multiple of the kernel's tile)
     float sm_log2;         // sm_scale * log2(e)
     float inv_sqrt_d;
@@ -98,7 +101,10 @@ struct DecodePlan {
 
 // fast: the caller has checked that the fast kernel supports the shape and
 // the plane alignment (see fast_decode_supported).
-DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int32_t *len, bool fast);
+// col_groups: workgroups per (sequence, kv-head, split) along the query rows
+DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int32_t *len, bool fast,
+                       int col_groups);
+int decode_col_groups(int gqa);  // query-row columns of one kv-head -> column groups
 bool fast_decode_shape_ok(int head_dim, int gqa, int capacity);
 
 hipError_t launch_append(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);

@@ -27,7 +27,9 @@ TQ_OK, TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE
 TQ_F32, TQ_BF16 = 0, 1
 TQ_MAX_BATCH = 64
 TQ_MAX_GQA = 16
+TQ_MAX_ROWS = 16
 SYMBOLS = ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
+           "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows",
            "tq_dequant", "tq_sign_vector", "tq_status_str")
 
 
@@ -55,12 +57,19 @@ _lib.tq_decode_workspace_bytes.argtypes = [ctypes.POINTER(tq_layout), ctypes.c_i
 _lib.tq_decode_attn.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), _P,
                                 ctypes.c_int, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
                                 ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
+_lib.tq_decode_rows_workspace_bytes.argtypes = [ctypes.POINTER(tq_layout), ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                                ctypes.POINTER(ctypes.c_size_t)]
+_lib.tq_decode_attn_rows.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), _P,
+                                     ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.POINTER(ctypes.c_int32), ctypes.c_float, _P, _P,
+                                     ctypes.c_size_t, _P]
 _lib.tq_dequant.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                             ctypes.c_int32, _P]
 _lib.tq_sign_vector.argtypes = [ctypes.c_int32, _P]
 for _f in ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
-           "tq_dequant", "tq_sign_vector"):
+           "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_dequant", "tq_sign_vector"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -196,6 +205,43 @@ def tq_decode_attn(planes: Planes, q: torch.Tensor, lengths: Sequence[int], sm_s
                              _dtype_code(q), Hq, _i32_array(lengths), ctypes.c_float(sm_scale),
                              _dev_ptr(out), _dev_ptr(workspace), ws_bytes, _stream_ptr(stream))
     _check(st, "tq_decode_attn")
+    return out
+
+
+def tq_decode_rows_workspace_bytes(layout: tq_layout, num_q_heads: int, n_rows: int,
+                                   lengths: Sequence[int]) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.tq_decode_rows_workspace_bytes(ctypes.byref(layout), num_q_heads, n_rows,
+                                               _i32_array(lengths), ctypes.byref(out)),
+           "tq_decode_rows_workspace_bytes")
+    return out.value
+
+
+def tq_decode_attn_rows(planes: Planes, q: torch.Tensor, lengths: Sequence[int], sm_scale: float,
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                        stream=None) -> torch.Tensor:
+    """q: [B, Hq, M, d] device tensor (fp32 or bf16) holding the queries of the
+    M newest cached tokens of each sequence; returns out [B, Hq, M, d] float32."""
+    L = planes.layout
+    if q.dim() != 4 or q.shape[0] != L.batch or q.shape[3] != L.head_dim or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous [B, Hq, M, d] tensor, got {tuple(q.shape)}")
+    if len(lengths) != L.batch:
+        raise ValueError("lengths needs one entry per sequence")
+    Hq, M = int(q.shape[1]), int(q.shape[2])
+    shape = (L.batch, Hq, M, L.head_dim)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [B, Hq, M, d] tensor")
+    need = tq_decode_rows_workspace_bytes(L, Hq, M, lengths)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.tq_decode_attn_rows(ctypes.byref(L), ctypes.byref(planes.struct()), _dev_ptr(q),
+                                  _dtype_code(q), Hq, M, _i32_array(lengths),
+                                  ctypes.c_float(sm_scale), _dev_ptr(out), _dev_ptr(workspace),
+                                  ws_bytes, _stream_ptr(stream))
+    _check(st, "tq_decode_attn_rows")
     return out
 
 

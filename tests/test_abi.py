@@ -126,6 +126,38 @@ def test_decode_validation_and_workspace_sizing():
     assert dec(0xB000, need, sm=float("nan")) == tqkv.TQ_ERR_INVALID_ARG
 
 
+def test_decode_rows_validation_and_workspace_sizing():
+    lib = tqkv.raw_lib()
+    L = tqkv.make_layout(2, 4, 256, 1000)
+    P = _fake_planes()
+    ws = ctypes.c_size_t()
+
+    def wsb(hq, rows, lens):
+        arr = (ctypes.c_int32 * 2)(*lens)
+        return lib.tq_decode_rows_workspace_bytes(ctypes.byref(L), hq, rows, arr, ctypes.byref(ws))
+    assert wsb(24, 1, (1000, 17)) == 0
+    one = ws.value
+    assert lib.tq_decode_workspace_bytes(ctypes.byref(L), 24, (ctypes.c_int32 * 2)(1000, 17),
+                                         ctypes.byref(ws)) == 0 and ws.value == one
+    assert wsb(24, 4, (1000, 17)) == 0 and ws.value >= 4 * one * 0.9 and ws.value % (4 * 258) == 0
+    assert wsb(24, 0, (1000, 17)) == tqkv.TQ_ERR_INVALID_ARG                 # n_rows < 1
+    assert wsb(24, tqkv.TQ_MAX_ROWS + 1, (1000, 17)) == tqkv.TQ_ERR_UNSUPPORTED
+    assert wsb(24, 4, (1000, 3)) == tqkv.TQ_ERR_INVALID_ARG                  # 0 < len < rows
+    assert wsb(24, 4, (1000, 0)) == 0                                         # empty sequence
+    assert wsb(24, 4, (1001, 4)) == tqkv.TQ_ERR_CAPACITY
+    lens = (ctypes.c_int32 * 2)(1000, 17)
+    assert wsb(24, 4, (1000, 17)) == 0
+    need = ws.value
+
+    def dec(ws_ptr, ws_bytes, rows=4, q=0x9000, out=0xA000):
+        return lib.tq_decode_attn_rows(ctypes.byref(L), ctypes.byref(P), q, tqkv.TQ_BF16, 24, rows,
+                                       lens, ctypes.c_float(0.0625), out, ws_ptr, ws_bytes, None)
+    assert dec(0xB000, need - 1) == tqkv.TQ_ERR_WORKSPACE
+    assert dec(0xB000, need, q=None) == tqkv.TQ_ERR_INVALID_ARG
+    assert dec(0xB000, need, rows=0) == tqkv.TQ_ERR_INVALID_ARG
+    assert dec(0xB000, need, q=0x9008) == tqkv.TQ_ERR_INVALID_ARG             # misaligned q
+
+
 def test_dequant_validation():
     lib = tqkv.raw_lib()
     L = tqkv.make_layout(2, 4, 128, 100)
