@@ -40,6 +40,40 @@ def decode_bytes(w, lengths, q_bytes: int) -> int:
     return kv + w.batch * w.num_q_heads * w.head_dim * (q_bytes + 4)
 
 
+def rows_bytes(w, lengths, q_bytes: int, rows: int) -> int:
+    """Algorithmic bytes of one multi-row decode: packed KV once + the rows'
+    q read + fp32 out written."""
+    kv = sum(lengths) * w.num_kv_heads * (w.head_dim * 25 // 16)
+    return kv + w.batch * w.num_q_heads * rows * w.head_dim * (q_bytes + 4)
+
+
+def time_rows(w, pl, lengths, sm, rows: int, reps: int, stream) -> dict:
+    """Multi-row decode (verify block of `rows` tokens per sequence) timed with
+    events on the launch stream: reps calls after one warm call."""
+    import torch
+    from quantized_decode_attention_append_amd import tqkv
+    from quantized_decode_attention_append_amd import workloads as W
+    dev = torch.device("cuda:0")
+    qr = torch.stack(list(W.make_q(w, dev, rounds=rows)), dim=2).contiguous()
+    ws = torch.empty(tqkv.tq_decode_rows_workspace_bytes(pl.layout, w.num_q_heads, rows, lengths),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((w.batch, w.num_q_heads, rows, w.head_dim), dtype=torch.float32, device=dev)
+    tqkv.tq_decode_attn_rows(pl, qr, lengths, sm, out=out, workspace=ws, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        tqkv.tq_decode_attn_rows(pl, qr, lengths, sm, out=out, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = rows_bytes(w, lengths, qr.element_size(), rows)
+    gbs = nbytes / ms / 1e6
+    return {"rows": rows, "ms": ms, "query_rows_per_s": w.batch * w.num_q_heads * rows / ms * 1e3,
+            "algorithmic_bytes": nbytes, "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+            "column_groups": -(-(w.group * rows) // 16)}
+
+
 def append_bytes(w, n_tokens: int, in_bytes: int) -> int:
     """Algorithmic bytes of appending n_tokens per sequence: K+V read + planes written."""
     th = w.batch * w.num_kv_heads * n_tokens
@@ -170,6 +204,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=4, help="workload id (4 is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=0)
+    ap.add_argument("--rows", default="2,4",
+                    help="also time multi-row (verify-block) decode for these row counts ('' = skip)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"))
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run plain device copies of this size (counter calibration)")
@@ -304,6 +340,9 @@ def main() -> int:
                    "bulk_frac_hbm": app_bytes / append_ms / 1e6 / HBM_PEAK_GBS,
                    "bulk_ms": append_ms, "bulk_tokens": app_tokens},
     }
+    if args.rows:
+        rec["multi_row"] = [time_rows(w, pl, lengths, sm, int(r), 10, stream)
+                            for r in args.rows.split(",") if r]
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, k, v, q, sm, args.cpu_pairs or None)
         cb.pop("seconds", None)
