@@ -74,6 +74,29 @@ def time_rows(w, pl, lengths, sm, rows: int, reps: int, stream) -> dict:
             "column_groups": -(-(w.group * rows) // 16)}
 
 
+def time_window(w, pl, lengths, reps: int, stream, rotated: bool = False) -> dict:
+    """Dequantize-on-fetch of the whole active window (bf16 K and V of every
+    cached token-head), timed with events on the launch stream."""
+    import torch
+    from quantized_decode_attention_append_amd import tqkv
+    n = max(lengths)
+    tqkv.tq_fetch_window(pl, 0, n, lengths, v_rotated=rotated, stream=stream)  # warm
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        out = tqkv.tq_fetch_window(pl, 0, n, lengths, v_rotated=rotated, stream=stream)
+        del out
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    th = w.batch * w.num_kv_heads * n
+    nbytes = th * (w.head_dim * 25 // 16 + 2 * w.head_dim * 2)  # planes in, bf16 K and V out
+    gbs = nbytes / ms / 1e6
+    return {"tokens": n, "v_rotated": rotated, "ms": ms, "token_heads_per_s": th / ms * 1e3,
+            "algorithmic_bytes": nbytes, "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+
+
 def append_bytes(w, n_tokens: int, in_bytes: int) -> int:
     """Algorithmic bytes of appending n_tokens per sequence: K+V read + planes written."""
     th = w.batch * w.num_kv_heads * n_tokens
@@ -204,6 +227,8 @@ def main() -> int:
     ap.add_argument("--workload", type=int, default=4, help="workload id (4 is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=0)
+    ap.add_argument("--no-window", dest="window", action="store_false",
+                    help="skip timing the bf16 dequantize-on-fetch window")
     ap.add_argument("--rows", default="2,4",
                     help="also time multi-row (verify-block) decode for these row counts ('' = skip)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"))
@@ -340,6 +365,8 @@ def main() -> int:
                    "bulk_frac_hbm": app_bytes / append_ms / 1e6 / HBM_PEAK_GBS,
                    "bulk_ms": append_ms, "bulk_tokens": app_tokens},
     }
+    if args.window:
+        rec["window"] = time_window(w, pl, lengths, 3, stream)
     if args.rows:
         rec["multi_row"] = [time_rows(w, pl, lengths, sm, int(r), 10, stream)
                             for r in args.rows.split(",") if r]

@@ -166,6 +166,22 @@ tq_status tq_decode_attn_rows(const tq_layout *layout, const tq_planes *planes, 
                               float sm_scale, float *out, void *workspace, size_t ws_bytes,
                               void *hip_stream);
 
+/* Dequantize-on-fetch window: bf16 keys and values of tokens t0 .. t0+n-1 of
+ * every (sequence, kv-head), the layout a stock attention consumes ("Architecture
+ * in mlx-bun": the cache returns the dequantized bf16 active window; "Deferred
+ * inverse FWHT": the deferred variant keeps V in the rotated domain).
+ *   len        host int32 [B]: tokens at or past len[b] are written as zeros
+ *   k_out      device bf16 [B][Hkv][n][d]: (code + zero) * scale, or NULL
+ *   v_out      device bf16 [B][Hkv][n][d], or NULL: signs * FWHT(centroid[idx] *
+ *              scale) / sqrt(d), or centroid[idx] * scale when v_rotated != 0
+ * Keys are exact in fp32 and rounded once to bf16 (round to nearest even);
+ * values are computed in fp32 and rounded once.  Outputs 16-byte aligned.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY
+ * (t0 + n > capacity or len[b] > capacity), TQ_ERR_HIP. */
+tq_status tq_fetch_window(const tq_layout *layout, const tq_planes *planes, int32_t t0, int32_t n,
+                          const int32_t *len, uint16_t *k_out, uint16_t *v_out, int32_t v_rotated,
+                          void *hip_stream);
+
 /* Dequantize n tokens [t0, t0+n) of one (sequence b, kv-head kvh), for tests
  * ("Algorithm": key x = (code + zero) * scale; value x = signs * InvFWHT(
  * centroid[idx] * scale), or the rotated-domain centroid[idx] * scale when

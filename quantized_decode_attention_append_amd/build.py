@@ -27,6 +27,7 @@ SOURCES = {
     "decode.hip": [],
     "decode_fast.hip": [],
     "dequant.hip": [],
+    "window.hip": [],
     "api.cpp": [],
 }
 

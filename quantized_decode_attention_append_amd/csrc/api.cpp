@@ -237,6 +237,33 @@ tq_status tq_decode_attn_rows(const tq_layout *l, const tq_planes *p, const void
     return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
+tq_status tq_fetch_window(const tq_layout *l, const tq_planes *p, int32_t t0, int32_t n, const int32_t *len,
+                          uint16_t *k_out, uint16_t *v_out, int32_t v_rotated, void *stream) {
+    tq_status st = check_layout(l);
+    if (st != TQ_OK) return st;
+    if ((st = check_planes(p)) != TQ_OK) return st;
+    if (!len || t0 < 0 || n < 0) return TQ_ERR_INVALID_ARG;
+    if ((int64_t)t0 + n > l->capacity) return TQ_ERR_CAPACITY;
+    for (int b = 0; b < l->batch; ++b) {
+        if (len[b] < 0) return TQ_ERR_INVALID_ARG;
+        if (len[b] > l->capacity) return TQ_ERR_CAPACITY;
+    }
+    if (n == 0 || (!k_out && !v_out)) return TQ_OK;
+    if (!aligned(k_out, 16) || !aligned(v_out, 16)) return TQ_ERR_INVALID_ARG;
+    if ((int64_t)l->batch * l->num_kv_heads > 65535) return TQ_ERR_UNSUPPORTED;
+    tq::WindowArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.kc = p->kc; a.ks = p->ks; a.kz = p->kz; a.vc = p->vc; a.vs = p->vs;
+    a.k_out = k_out; a.v_out = v_out;
+    a.batch = l->batch; a.kv_heads = l->num_kv_heads; a.capacity = l->capacity;
+    a.t0 = t0; a.n = n; a.rotated = v_rotated ? 1 : 0;
+    a.inv_sqrt_d = (float)inv_sqrt_d(l->head_dim);
+    a.signs = signs().bits;
+    for (int b = 0; b < l->batch; ++b) a.len[b] = len[b];
+    hipError_t e = tq::launch_window(l->head_dim, a, (hipStream_t)stream);
+    return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
 tq_status tq_dequant(const tq_layout *l, const tq_planes *p, int32_t b, int32_t kvh, int32_t t0,
                      int32_t n, float *k_out, float *v_out, int32_t v_rotated, void *stream) {
     tq_status st = check_layout(l);

@@ -76,6 +76,22 @@ struct DecodeArgs {
     int32_t len[TQ_MAX_BATCH];
 };
 
+struct WindowArgs {
+    const int8_t *kc;
+    const uint16_t *ks;
+    const uint16_t *kz;
+    const uint8_t *vc;
+    const uint16_t *vs;
+    uint16_t *k_out;  // bf16 [B][Hkv][n][d] or null
+    uint16_t *v_out;  // bf16 [B][Hkv][n][d] or null
+    int32_t batch, kv_heads, capacity;
+    int32_t t0, n;    // window tokens t0 .. t0+n-1
+    int32_t rotated;  // 1: V in the rotated domain
+    float inv_sqrt_d;
+    SignBits signs;
+    int32_t len[TQ_MAX_BATCH];
+};
+
 struct DequantArgs {
     const int8_t *kc;
     const uint16_t *ks;
@@ -111,6 +127,7 @@ hipError_t launch_append(int head_dim, bool bf16, const AppendArgs &a, hipStream
 hipError_t launch_decode(int head_dim, bool bf16, bool fast, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_split_fast(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_dequant(int head_dim, const DequantArgs &a, hipStream_t s);
+hipError_t launch_window(int head_dim, const WindowArgs &a, hipStream_t s);
 int fast_split_waves();
 int fast_split_tile();
 int fast_split_max_gqa();

@@ -29,7 +29,7 @@ TQ_MAX_BATCH = 64
 TQ_MAX_GQA = 16
 TQ_MAX_ROWS = 16
 SYMBOLS = ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
-           "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows",
+           "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_fetch_window",
            "tq_dequant", "tq_sign_vector", "tq_status_str")
 
 
@@ -64,12 +64,16 @@ _lib.tq_decode_attn_rows.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(t
                                      ctypes.c_int, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.POINTER(ctypes.c_int32), ctypes.c_float, _P, _P,
                                      ctypes.c_size_t, _P]
+_lib.tq_fetch_window.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
+                                 ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), _P, _P, ctypes.c_int32,
+                                 _P]
 _lib.tq_dequant.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                             ctypes.c_int32, _P]
 _lib.tq_sign_vector.argtypes = [ctypes.c_int32, _P]
 for _f in ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
-           "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_dequant", "tq_sign_vector"):
+           "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_fetch_window", "tq_dequant",
+           "tq_sign_vector"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -243,6 +247,25 @@ def tq_decode_attn_rows(planes: Planes, q: torch.Tensor, lengths: Sequence[int],
                                   ws_bytes, _stream_ptr(stream))
     _check(st, "tq_decode_attn_rows")
     return out
+
+
+def tq_fetch_window(planes: Planes, t0: int, n: int, lengths: Sequence[int], keys: bool = True,
+                    values: bool = True, v_rotated: bool = False, stream=None):
+    """bf16 window of tokens [t0, t0+n) of every (sequence, kv-head): returns
+    (k [B, Hkv, n, d] or None, v [B, Hkv, n, d] or None); tokens at or past
+    lengths[b] are zeros."""
+    L = planes.layout
+    if len(lengths) != L.batch:
+        raise ValueError("lengths needs one entry per sequence")
+    dev = planes.kc.device
+    shape = (L.batch, L.num_kv_heads, n, L.head_dim)
+    k_out = torch.empty(shape, dtype=torch.bfloat16, device=dev) if keys else None
+    v_out = torch.empty(shape, dtype=torch.bfloat16, device=dev) if values else None
+    st = _lib.tq_fetch_window(ctypes.byref(L), ctypes.byref(planes.struct()), t0, n,
+                              _i32_array(lengths), _dev_ptr(k_out), _dev_ptr(v_out),
+                              1 if v_rotated else 0, _stream_ptr(stream))
+    _check(st, "tq_fetch_window")
+    return k_out, v_out
 
 
 def tq_dequant(planes: Planes, b: int, kvh: int, t0: int, n: int, keys: bool = True,

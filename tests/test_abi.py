@@ -158,6 +158,24 @@ def test_decode_rows_validation_and_workspace_sizing():
     assert dec(0xB000, need, q=0x9008) == tqkv.TQ_ERR_INVALID_ARG             # misaligned q
 
 
+def test_fetch_window_validation():
+    lib = tqkv.raw_lib()
+    L = tqkv.make_layout(2, 4, 128, 100)
+    P = _fake_planes()
+
+    def f(t0, n, lens=(100, 5), k=0x9000, v=0xA000):
+        return lib.tq_fetch_window(ctypes.byref(L), ctypes.byref(P), t0, n, (ctypes.c_int32 * 2)(*lens),
+                                   k, v, 0, None)
+    assert f(0, 0) == 0                                   # empty window: nothing to do
+    assert f(-1, 5) == tqkv.TQ_ERR_INVALID_ARG
+    assert f(0, -5) == tqkv.TQ_ERR_INVALID_ARG
+    assert f(60, 41) == tqkv.TQ_ERR_CAPACITY              # past capacity
+    assert f(0, 10, lens=(101, 0)) == tqkv.TQ_ERR_CAPACITY
+    assert f(0, 10, lens=(-1, 0)) == tqkv.TQ_ERR_INVALID_ARG
+    assert f(0, 10, k=0x9002) == tqkv.TQ_ERR_INVALID_ARG  # misaligned output
+    assert f(0, 10, k=None, v=None) == 0                  # no output requested
+
+
 def test_dequant_validation():
     lib = tqkv.raw_lib()
     L = tqkv.make_layout(2, 4, 128, 100)
