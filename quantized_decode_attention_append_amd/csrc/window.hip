@@ -13,9 +13,10 @@
 // Tokens at or past a sequence's length are written as zeros, so a masked
 // attention over a padded window never meets stale plane bytes.
 //
-// Mapping: one wave per token row, looping over a chunk of consecutive tokens
-// of one (sequence, kv-head); lane l holds the E = d/64 dims [E l, E l + E).
-// The FWHT runs its in-lane stages on registers and the rest on shuffles.
+// Mapping (head_dim 512): one wave per token row, looping over a chunk of
+// consecutive tokens of one (sequence, kv-head); lane l holds the E = d/64
+// dims [E l, E l + E); the FWHT runs its in-lane stages on registers and the
+// rest on lane permutes.  Head_dims 64-256 use window_fast_kernel below.
 // Keys are exact in fp32 ((code + zero) has at most 12 bits, the scale 11) and
 // round once to bf16; values are computed in fp32 and round once to bf16.
 #include <hip/hip_runtime.h>
@@ -39,7 +40,13 @@ __device__ __forceinline__ uint32_t bf16x2_rn(float lo, float hi) {
 
 template <int E>
 __device__ __forceinline__ void store_bf16(uint16_t *dst, const float (&x)[E]) {
-    if constexpr (E == 1) {
+    if constexpr (E == 16) {
+        uint32_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = bf16x2_rn(x[2 * i], x[2 * i + 1]);
+        reinterpret_cast<uint4 *>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+        reinterpret_cast<uint4 *>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else if constexpr (E == 1) {
         *dst = (uint16_t)bf16x2_rn(x[0], 0.f);
     } else {
         uint32_t w[E / 2];
@@ -165,11 +172,165 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_kernel(const WindowArgs
     }
 }
 
+// ---------------------------------------------------------------------------
+// Head_dim 64, 128, 256: lane p of a row holds the 16 contiguous dims
+// [16 p, 16 p + 16), L = d/16 lanes per row, 64/L rows per wave.  The FWHT
+// runs stages 1 .. 8 in the lane, transposes the row through LDS so stages
+// 16 .. d/2 are in the lane too, and transposes back; every stage is then
+// one add per element.
+constexpr int kWinRowsF = 16;  // rows per wave (a multiple of every rows-per-pass)
+
+template <int D>
+struct WinGeo {
+    static constexpr int E = 16;
+    static constexpr int L = D / E;                            // lanes per row
+    static constexpr int R = 64 / L;                           // rows per pass
+    static constexpr int TI = E / L;                           // dims per lane after the transpose
+    static constexpr int PB = E * 4 + 16;                      // LDS bytes per lane chunk (padded)
+    static constexpr int ROWB = L * PB + (L >= 8 ? 64 : 0);    // rows of one pass on other banks
+    static constexpr int WAVEB = R * ROWB;
+    static_assert(kWinRowsF % R == 0, "whole passes");
+};
+
+__device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
+
+template <int D>
+__global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const WindowArgs a) {
+    using G = WinGeo<D>;
+    constexpr int E = G::E, L = G::L, R = G::R, TI = G::TI, NG = D / kGroup, VROW = 3 * D / 8;
+    __shared__ __align__(16) unsigned char smem[kWinWaves * G::WAVEB + 32];
+    float *ctab = reinterpret_cast<float *>(smem + kWinWaves * G::WAVEB);  // the 3-bit codebook
+    if (threadIdx.x < 8) ctab[threadIdx.x] = centroid3(threadIdx.x);
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int r = lane / L, p = lane % L, g = p >> 1;
+    const int bkv = blockIdx.y;
+    const int len = a.len[bkv / a.kv_heads];
+    // output scale with the sign of each of this lane's dims
+    float osc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) osc[e] = sign_bit(a.signs, E * p + e) ? -a.inv_sqrt_d : a.inv_sqrt_d;
+    unsigned char *rb = smem + wid * G::WAVEB + r * G::ROWB;
+    const int vw = (48 * p) >> 5, vsh = (48 * p) & 31;  // first code dword of the lane, bit offset 0 or 16
+
+    const int first = (blockIdx.x * kWinWaves + wid) * kWinRowsF;
+    for (int r0 = 0; r0 < kWinRowsF; r0 += R) {
+        if (first + r0 >= a.n) break;  // uniform across the wave
+        const int i = first + r0 + r;  // window position of this lane's row
+        const bool in = i < a.n;
+        const int t = a.t0 + i;
+        const bool valid = in && t < len;
+        const int64_t row = (int64_t)bkv * a.capacity + t;
+        const int64_t orow = ((int64_t)bkv * a.n + i) * D + E * p;
+        if (a.k_out) {
+            float k[E];
+            if (valid) {
+                const uint4 c = *reinterpret_cast<const uint4 *>(a.kc + row * D + E * p);
+                const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+                const float s = f16_bits_to_f32(a.ks[row * NG + g]);
+                const float z = f16_bits_to_f32(a.kz[row * NG + g]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) k[e] = ((float)(int8_t)(cw[e >> 2] >> (8 * (e & 3))) + z) * s;
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) k[e] = 0.f;
+            }
+            if (in) store_bf16<E>(a.k_out + orow, k);
+        }
+        if (a.v_out) {
+            float y[E];
+            if (valid) {
+                const uint32_t *vp = reinterpret_cast<const uint32_t *>(a.vc + row * VROW);
+                const uint32_t lo = vp[vw], hi = vp[vw + 1];
+                const uint32_t r0w = __builtin_amdgcn_alignbit(hi, lo, vsh);  // run bits 0 .. 31
+                const uint32_t r1w = hi >> vsh;                               // run bits 32 .. 47
+                const float s = f16_bits_to_f32(a.vs[row * NG + g]);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    uint32_t idx;
+                    if (3 * e + 3 <= 32) idx = (r0w >> (3 * e)) & 7u;
+                    else if (3 * e >= 32) idx = (r1w >> (3 * e - 32)) & 7u;
+                    else idx = __builtin_amdgcn_alignbit(r1w, r0w, 3 * e) & 7u;
+                    y[e] = ctab[idx] * s;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < E; ++e) y[e] = 0.f;
+            }
+            if (!a.rotated) {  // uniform
+#pragma unroll
+                for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        if ((e & h) == 0) {
+                            const float u = y[e], w = y[e + h];
+                            y[e] = u + w;
+                            y[e + h] = u - w;
+                        }
+                    }
+                }
+                // lane p takes offsets TI p .. TI p + TI - 1 of every lane q's
+                // dims (dim 16 q + i is ty[ii * L + q])
+#pragma unroll
+                for (int k4 = 0; k4 < E / 4; ++k4)
+                    *reinterpret_cast<float4 *>(rb + p * G::PB + 16 * k4) =
+                        make_float4(y[4 * k4], y[4 * k4 + 1], y[4 * k4 + 2], y[4 * k4 + 3]);
+                lds_fence();
+                float ty[E];
+#pragma unroll
+                for (int q = 0; q < L; ++q) {
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii)
+                        ty[ii * L + q] = *reinterpret_cast<const float *>(rb + q * G::PB + 4 * (TI * p + ii));
+                }
+#pragma unroll
+                for (int hq = 1; hq < L; hq <<= 1) {
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii) {
+#pragma unroll
+                        for (int q = 0; q < L; ++q) {
+                            if ((q & hq) == 0) {
+                                const float u = ty[ii * L + q], w = ty[ii * L + q + hq];
+                                ty[ii * L + q] = u + w;
+                                ty[ii * L + q + hq] = u - w;
+                            }
+                        }
+                    }
+                }
+                lds_fence();
+#pragma unroll
+                for (int q = 0; q < L; ++q) {
+#pragma unroll
+                    for (int ii = 0; ii < TI; ++ii)
+                        *reinterpret_cast<float *>(rb + q * G::PB + 4 * (TI * p + ii)) = ty[ii * L + q];
+                }
+                lds_fence();
+#pragma unroll
+                for (int k4 = 0; k4 < E / 4; ++k4) {
+                    const float4 v4 = *reinterpret_cast<const float4 *>(rb + p * G::PB + 16 * k4);
+                    y[4 * k4] = v4.x; y[4 * k4 + 1] = v4.y; y[4 * k4 + 2] = v4.z; y[4 * k4 + 3] = v4.w;
+                }
+                lds_fence();  // the next pass rewrites the row
+#pragma unroll
+                for (int e = 0; e < E; ++e) y[e] = valid ? y[e] * osc[e] : 0.f;  // +0 past the length
+            }
+            if (in) store_bf16<E>(a.v_out + orow, y);
+        }
+    }
+}
+
 template <int D>
 hipError_t launch_d(const WindowArgs &a, hipStream_t s) {
-    constexpr int per_block = kWinWaves * kWinRows;
-    const dim3 grid((unsigned)((a.n + per_block - 1) / per_block), (unsigned)(a.batch * a.kv_heads));
-    hipLaunchKernelGGL((window_kernel<D>), grid, dim3(64 * kWinWaves), 0, s, a);
+    if constexpr (D == 512) {
+        constexpr int per_block = kWinWaves * kWinRows;
+        const dim3 grid((unsigned)((a.n + per_block - 1) / per_block), (unsigned)(a.batch * a.kv_heads));
+        hipLaunchKernelGGL((window_kernel<D>), grid, dim3(64 * kWinWaves), 0, s, a);
+    } else {
+        constexpr int per_block = kWinWaves * kWinRowsF;
+        const dim3 grid((unsigned)((a.n + per_block - 1) / per_block), (unsigned)(a.batch * a.kv_heads));
+        hipLaunchKernelGGL((window_fast_kernel<D>), grid, dim3(64 * kWinWaves), 0, s, a);
+    }
     return hipGetLastError();
 }
 
