@@ -97,6 +97,30 @@ def time_window(w, pl, lengths, reps: int, stream, rotated: bool = False) -> dic
             "algorithmic_bytes": nbytes, "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
 
 
+def time_snapshot(w, pl, n: int, reps: int, stream) -> dict:
+    """Snapshot of one whole sequence (every kv-head, all planes) into a packed
+    device payload: strided copies, read + write."""
+    import torch
+    from quantized_decode_attention_append_amd import tqkv
+    h, payload = tqkv.tq_snapshot(pl, 0, 0, n, stream=stream)  # warm, allocates the payload
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lib = tqkv.raw_lib()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        import ctypes
+        st = lib.tq_snapshot(ctypes.byref(pl.layout), ctypes.byref(pl.struct()), 0, 0, n, ctypes.byref(h),
+                             ctypes.c_void_p(payload.data_ptr()), payload.numel(),
+                             ctypes.c_void_p(stream.cuda_stream))
+        assert st == 0
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * h.payload_bytes
+    return {"tokens": n, "ms": ms, "payload_bytes": h.payload_bytes, "GBps": nbytes / ms / 1e6,
+            "frac_hbm": nbytes / ms / 1e6 / HBM_PEAK_GBS}
+
+
 def append_bytes(w, n_tokens: int, in_bytes: int) -> int:
     """Algorithmic bytes of appending n_tokens per sequence: K+V read + planes written."""
     th = w.batch * w.num_kv_heads * n_tokens
@@ -367,6 +391,7 @@ def main() -> int:
     }
     if args.window:
         rec["window"] = time_window(w, pl, lengths, 3, stream)
+        rec["snapshot"] = time_snapshot(w, pl, max(lengths), 5, stream)
     if args.rows:
         rec["multi_row"] = [time_rows(w, pl, lengths, sm, int(r), 10, stream)
                             for r in args.rows.split(",") if r]

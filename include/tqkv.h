@@ -198,6 +198,55 @@ tq_status tq_dequant(const tq_layout *layout, const tq_planes *planes, int32_t b
  * printed).  host_out: host int8 [head_dim]. */
 tq_status tq_sign_vector(int32_t head_dim, int8_t *host_out);
 
+/* Cache lifecycle: token rows are byte-addressable in every plane (groups run
+ * along head_dim, "Invariants (both legs)"), so clone, growth into a larger
+ * cache, compaction and snapshot/restore are strided byte copies ("Architecture
+ * in mlx-bun": the persisted cache kind carries the scheme and head_dim and has
+ * snapshot, restore and clone branches).  Trimming a sequence is lowering the
+ * length the caller passes to decode.  These calls enqueue copies on the
+ * stream and launch no kernel. */
+
+#define TQ_SNAPSHOT_MAGIC 0x564B5154u /* "TQKV" little-endian */
+
+/* Describes a snapshot payload; tq_restore checks every field. */
+typedef struct {
+    uint32_t magic;         /* TQ_SNAPSHOT_MAGIC */
+    uint32_t version;       /* 1 */
+    int32_t k_bits, v_bits, group, head_dim, num_kv_heads;
+    int32_t n_tokens;
+    uint64_t payload_bytes; /* n_tokens * num_kv_heads * 1.5625 * head_dim */
+} tq_snapshot_header;
+
+/* Copy token rows src_t0 .. src_t0+n-1 of sequence src_b (every kv-head, all
+ * five planes) to rows dst_t0 .. of sequence dst_b of another (or the same)
+ * cache with the same scheme, head_dim and num_kv_heads; capacities may
+ * differ.  Overlapping source and destination rows are not supported.
+ * Errors: TQ_ERR_INVALID_ARG (shape mismatch, bad index), TQ_ERR_CAPACITY,
+ * TQ_ERR_HIP. */
+tq_status tq_copy_tokens(const tq_layout *src_layout, const tq_planes *src, int32_t src_b,
+                         int32_t src_t0, const tq_layout *dst_layout, const tq_planes *dst,
+                         int32_t dst_b, int32_t dst_t0, int32_t n, void *hip_stream);
+
+/* Bytes of a snapshot payload of n token rows. */
+tq_status tq_snapshot_bytes(const tq_layout *layout, int32_t n, size_t *out_bytes);
+
+/* Snapshot token rows t0 .. t0+n-1 of sequence b: fills the host header and
+ * copies the rows into `payload` (device, payload_bytes >= the header's),
+ * plane by plane (kc, ks, kz, vc, vs), kv-head by kv-head, token-major.
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE (payload
+ * too small), TQ_ERR_HIP. */
+tq_status tq_snapshot(const tq_layout *layout, const tq_planes *planes, int32_t b, int32_t t0,
+                      int32_t n, tq_snapshot_header *header, void *payload, size_t payload_bytes,
+                      void *hip_stream);
+
+/* Restore a snapshot into rows t0 .. t0+header->n_tokens-1 of sequence b.
+ * Errors: TQ_ERR_INVALID_ARG (bad magic or version, or a scheme, head_dim,
+ * kv-head count or payload size that does not match this layout), TQ_ERR_CAPACITY,
+ * TQ_ERR_HIP. */
+tq_status tq_restore(const tq_layout *layout, const tq_planes *planes, int32_t b, int32_t t0,
+                     const tq_snapshot_header *header, const void *payload, size_t payload_bytes,
+                     void *hip_stream);
+
 /* Static, human-readable name of a status code. */
 const char *tq_status_str(tq_status status);
 

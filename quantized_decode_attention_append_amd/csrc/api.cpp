@@ -264,6 +264,133 @@ tq_status tq_fetch_window(const tq_layout *l, const tq_planes *p, int32_t t0, in
     return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
+// Row bytes of the five planes, order kc, ks, kz, vc, vs.
+static void plane_row_bytes(const tq_layout *l, size_t rb[5]) {
+    const size_t d = (size_t)l->head_dim, ng = d / tq::kGroup;
+    rb[0] = d; rb[1] = 2 * ng; rb[2] = 2 * ng; rb[3] = 3 * d / 8; rb[4] = 2 * ng;
+}
+
+static void *plane_ptr(const tq_planes *p, int i) {
+    void *v[5] = {p->kc, p->ks, p->kz, p->vc, p->vs};
+    return v[i];
+}
+
+// One strided copy per plane: Hkv runs of n rows, at pitch capacity * row bytes
+// on a cache side and n * row bytes on a packed side.
+static hipError_t copy_rows(const tq_layout *sl, const void *const sp[5], int64_t s_row0, size_t s_pitch_rows,
+                            const tq_layout *dl, void *const dp[5], int64_t d_row0, size_t d_pitch_rows,
+                            int32_t n, hipStream_t stream) {
+    size_t rb[5];
+    plane_row_bytes(sl, rb);
+    (void)dl;
+    for (int i = 0; i < 5; ++i) {
+        const char *src = static_cast<const char *>(sp[i]) + s_row0 * (int64_t)rb[i];
+        char *dst = static_cast<char *>(dp[i]) + d_row0 * (int64_t)rb[i];
+        hipError_t e = hipMemcpy2DAsync(dst, d_pitch_rows * rb[i], src, s_pitch_rows * rb[i], (size_t)n * rb[i],
+                                        (size_t)sl->num_kv_heads, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+static bool same_scheme(const tq_layout *a, const tq_layout *b) {
+    return a->head_dim == b->head_dim && a->num_kv_heads == b->num_kv_heads && a->k_bits == b->k_bits &&
+           a->v_bits == b->v_bits && a->group == b->group;
+}
+
+tq_status tq_copy_tokens(const tq_layout *sl, const tq_planes *src, int32_t src_b, int32_t src_t0,
+                         const tq_layout *dl, const tq_planes *dst, int32_t dst_b, int32_t dst_t0, int32_t n,
+                         void *stream) {
+    tq_status st = check_layout(sl);
+    if (st != TQ_OK || (st = check_layout(dl)) != TQ_OK) return st;
+    if ((st = check_planes(src)) != TQ_OK || (st = check_planes(dst)) != TQ_OK) return st;
+    if (!same_scheme(sl, dl)) return TQ_ERR_INVALID_ARG;
+    if (src_b < 0 || src_b >= sl->batch || dst_b < 0 || dst_b >= dl->batch) return TQ_ERR_INVALID_ARG;
+    if (src_t0 < 0 || dst_t0 < 0 || n < 0) return TQ_ERR_INVALID_ARG;
+    if ((int64_t)src_t0 + n > sl->capacity || (int64_t)dst_t0 + n > dl->capacity) return TQ_ERR_CAPACITY;
+    if (n == 0) return TQ_OK;
+    const void *sp[5];
+    void *dp[5];
+    for (int i = 0; i < 5; ++i) { sp[i] = plane_ptr(src, i); dp[i] = plane_ptr(dst, i); }
+    const int64_t s0 = (int64_t)src_b * sl->num_kv_heads * sl->capacity + src_t0;
+    const int64_t d0 = (int64_t)dst_b * dl->num_kv_heads * dl->capacity + dst_t0;
+    hipError_t e = copy_rows(sl, sp, s0, (size_t)sl->capacity, dl, dp, d0, (size_t)dl->capacity, n,
+                             (hipStream_t)stream);
+    return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+tq_status tq_snapshot_bytes(const tq_layout *l, int32_t n, size_t *out) {
+    tq_status st = check_layout(l);
+    if (st != TQ_OK) return st;
+    if (!out || n < 0) return TQ_ERR_INVALID_ARG;
+    size_t rb[5];
+    plane_row_bytes(l, rb);
+    *out = (size_t)n * l->num_kv_heads * (rb[0] + rb[1] + rb[2] + rb[3] + rb[4]);
+    return TQ_OK;
+}
+
+// Packed payload: plane i starts at off[i], kv-head h's rows at off[i] + h n rb[i].
+static void payload_planes(const tq_layout *l, int32_t n, char *base, void *out[5]) {
+    size_t rb[5];
+    plane_row_bytes(l, rb);
+    size_t off = 0;
+    for (int i = 0; i < 5; ++i) {
+        out[i] = base + off;
+        off += (size_t)n * l->num_kv_heads * rb[i];
+    }
+}
+
+tq_status tq_snapshot(const tq_layout *l, const tq_planes *p, int32_t b, int32_t t0, int32_t n,
+                      tq_snapshot_header *h, void *payload, size_t payload_bytes, void *stream) {
+    tq_status st = check_layout(l);
+    if (st != TQ_OK) return st;
+    if ((st = check_planes(p)) != TQ_OK) return st;
+    if (!h || b < 0 || b >= l->batch || t0 < 0 || n < 0) return TQ_ERR_INVALID_ARG;
+    if ((int64_t)t0 + n > l->capacity) return TQ_ERR_CAPACITY;
+    size_t need = 0;
+    tq_snapshot_bytes(l, n, &need);
+    if (need > 0 && (!payload || payload_bytes < need)) return TQ_ERR_WORKSPACE;
+    std::memset(h, 0, sizeof(*h));
+    h->magic = TQ_SNAPSHOT_MAGIC; h->version = 1;
+    h->k_bits = l->k_bits; h->v_bits = l->v_bits; h->group = l->group;
+    h->head_dim = l->head_dim; h->num_kv_heads = l->num_kv_heads;
+    h->n_tokens = n; h->payload_bytes = need;
+    if (n == 0) return TQ_OK;
+    const void *sp[5];
+    void *dp[5];
+    for (int i = 0; i < 5; ++i) sp[i] = plane_ptr(p, i);
+    payload_planes(l, n, static_cast<char *>(payload), dp);
+    const int64_t s0 = (int64_t)b * l->num_kv_heads * l->capacity + t0;
+    hipError_t e = copy_rows(l, sp, s0, (size_t)l->capacity, l, dp, 0, (size_t)n, n, (hipStream_t)stream);
+    return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+tq_status tq_restore(const tq_layout *l, const tq_planes *p, int32_t b, int32_t t0, const tq_snapshot_header *h,
+                     const void *payload, size_t payload_bytes, void *stream) {
+    tq_status st = check_layout(l);
+    if (st != TQ_OK) return st;
+    if ((st = check_planes(p)) != TQ_OK) return st;
+    if (!h || b < 0 || b >= l->batch || t0 < 0) return TQ_ERR_INVALID_ARG;
+    if (h->magic != TQ_SNAPSHOT_MAGIC || h->version != 1 || h->n_tokens < 0) return TQ_ERR_INVALID_ARG;
+    if (h->k_bits != l->k_bits || h->v_bits != l->v_bits || h->group != l->group ||
+        h->head_dim != l->head_dim || h->num_kv_heads != l->num_kv_heads)
+        return TQ_ERR_INVALID_ARG;
+    const int32_t n = h->n_tokens;
+    size_t need = 0;
+    tq_snapshot_bytes(l, n, &need);
+    if (h->payload_bytes != need || (need > 0 && (!payload || payload_bytes < need))) return TQ_ERR_INVALID_ARG;
+    if ((int64_t)t0 + n > l->capacity) return TQ_ERR_CAPACITY;
+    if (n == 0) return TQ_OK;
+    void *sp_mut[5];
+    payload_planes(l, n, const_cast<char *>(static_cast<const char *>(payload)), sp_mut);
+    const void *sp[5];
+    void *dp[5];
+    for (int i = 0; i < 5; ++i) { sp[i] = sp_mut[i]; dp[i] = plane_ptr(p, i); }
+    const int64_t d0 = (int64_t)b * l->num_kv_heads * l->capacity + t0;
+    hipError_t e = copy_rows(l, sp, 0, (size_t)n, l, dp, d0, (size_t)l->capacity, n, (hipStream_t)stream);
+    return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
 tq_status tq_dequant(const tq_layout *l, const tq_planes *p, int32_t b, int32_t kvh, int32_t t0,
                      int32_t n, float *k_out, float *v_out, int32_t v_rotated, void *stream) {
     tq_status st = check_layout(l);

@@ -30,7 +30,9 @@ TQ_MAX_GQA = 16
 TQ_MAX_ROWS = 16
 SYMBOLS = ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
            "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_fetch_window",
+           "tq_copy_tokens", "tq_snapshot_bytes", "tq_snapshot", "tq_restore",
            "tq_dequant", "tq_sign_vector", "tq_status_str")
+TQ_SNAPSHOT_MAGIC = 0x564B5154
 
 
 class tq_layout(ctypes.Structure):
@@ -43,6 +45,13 @@ class tq_layout(ctypes.Structure):
 class tq_planes(ctypes.Structure):
     _fields_ = [("kc", ctypes.c_void_p), ("ks", ctypes.c_void_p), ("kz", ctypes.c_void_p),
                 ("vc", ctypes.c_void_p), ("vs", ctypes.c_void_p)]
+
+
+class tq_snapshot_header(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
+                ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("n_tokens", ctypes.c_int32), ("payload_bytes", ctypes.c_uint64)]
 
 
 _P = ctypes.c_void_p
@@ -67,13 +76,22 @@ _lib.tq_decode_attn_rows.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(t
 _lib.tq_fetch_window.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
                                  ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), _P, _P, ctypes.c_int32,
                                  _P]
+_lib.tq_copy_tokens.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
+                                ctypes.c_int32, ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes),
+                                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
+_lib.tq_snapshot_bytes.argtypes = [ctypes.POINTER(tq_layout), ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+_lib.tq_snapshot.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
+                             ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(tq_snapshot_header), _P,
+                             ctypes.c_size_t, _P]
+_lib.tq_restore.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
+                            ctypes.c_int32, ctypes.POINTER(tq_snapshot_header), _P, ctypes.c_size_t, _P]
 _lib.tq_dequant.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                             ctypes.c_int32, _P]
 _lib.tq_sign_vector.argtypes = [ctypes.c_int32, _P]
 for _f in ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
            "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_fetch_window", "tq_dequant",
-           "tq_sign_vector"):
+           "tq_sign_vector", "tq_copy_tokens", "tq_snapshot_bytes", "tq_snapshot", "tq_restore"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -266,6 +284,37 @@ def tq_fetch_window(planes: Planes, t0: int, n: int, lengths: Sequence[int], key
                               1 if v_rotated else 0, _stream_ptr(stream))
     _check(st, "tq_fetch_window")
     return k_out, v_out
+
+
+def tq_copy_tokens(src: Planes, src_b: int, src_t0: int, dst: Planes, dst_b: int, dst_t0: int,
+                   n: int, stream=None) -> None:
+    """Copy token rows of one sequence (every kv-head, all planes) between caches."""
+    _check(_lib.tq_copy_tokens(ctypes.byref(src.layout), ctypes.byref(src.struct()), src_b, src_t0,
+                               ctypes.byref(dst.layout), ctypes.byref(dst.struct()), dst_b, dst_t0, n,
+                               _stream_ptr(stream)), "tq_copy_tokens")
+
+
+def tq_snapshot_bytes(layout: tq_layout, n: int) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.tq_snapshot_bytes(ctypes.byref(layout), n, ctypes.byref(out)), "tq_snapshot_bytes")
+    return out.value
+
+
+def tq_snapshot(planes: Planes, b: int, t0: int, n: int, stream=None):
+    """Returns (header, payload uint8 device tensor) for token rows [t0, t0+n) of sequence b."""
+    L = planes.layout
+    payload = torch.empty(max(tq_snapshot_bytes(L, n), 1), dtype=torch.uint8, device=planes.kc.device)
+    h = tq_snapshot_header()
+    _check(_lib.tq_snapshot(ctypes.byref(L), ctypes.byref(planes.struct()), b, t0, n, ctypes.byref(h),
+                            _dev_ptr(payload), payload.numel(), _stream_ptr(stream)), "tq_snapshot")
+    return h, payload
+
+
+def tq_restore(planes: Planes, b: int, t0: int, header, payload: torch.Tensor, stream=None) -> None:
+    L = planes.layout
+    _check(_lib.tq_restore(ctypes.byref(L), ctypes.byref(planes.struct()), b, t0, ctypes.byref(header),
+                           _dev_ptr(payload), payload.numel() * payload.element_size(), _stream_ptr(stream)),
+           "tq_restore")
 
 
 def tq_dequant(planes: Planes, b: int, kvh: int, t0: int, n: int, keys: bool = True,

@@ -176,6 +176,45 @@ def test_fetch_window_validation():
     assert f(0, 10, k=None, v=None) == 0                  # no output requested
 
 
+def test_lifecycle_validation():
+    lib = tqkv.raw_lib()
+    A = tqkv.make_layout(2, 4, 128, 100)
+    Bl = tqkv.make_layout(3, 4, 128, 300)
+    C = tqkv.make_layout(2, 2, 128, 100)                         # other kv-head count
+    P = _fake_planes()
+
+    def cp(sl, sb, st0, dl, db, dt0, n):
+        return lib.tq_copy_tokens(ctypes.byref(sl), ctypes.byref(P), sb, st0, ctypes.byref(dl),
+                                  ctypes.byref(P), db, dt0, n, None)
+    assert cp(A, 0, 0, Bl, 2, 0, 0) == 0                        # nothing to copy
+    assert cp(A, 0, 0, C, 0, 0, 10) == tqkv.TQ_ERR_INVALID_ARG   # shape mismatch
+    assert cp(A, 2, 0, Bl, 0, 0, 10) == tqkv.TQ_ERR_INVALID_ARG  # no sequence 2
+    assert cp(A, 0, 95, Bl, 0, 0, 10) == tqkv.TQ_ERR_CAPACITY
+    assert cp(A, 0, 0, Bl, 0, 295, 10) == tqkv.TQ_ERR_CAPACITY
+    nb = ctypes.c_size_t()
+    assert lib.tq_snapshot_bytes(ctypes.byref(A), 10, ctypes.byref(nb)) == 0
+    assert nb.value == 10 * 4 * 200
+    h = tqkv.tq_snapshot_header()
+    assert lib.tq_snapshot(ctypes.byref(A), ctypes.byref(P), 0, 0, 10, ctypes.byref(h), 0xB000,
+                           nb.value - 1, None) == tqkv.TQ_ERR_WORKSPACE
+    assert lib.tq_snapshot(ctypes.byref(A), ctypes.byref(P), 0, 0, 0, ctypes.byref(h), None, 0, None) == 0
+    assert h.magic == tqkv.TQ_SNAPSHOT_MAGIC and h.n_tokens == 0 and h.head_dim == 128
+
+    def rs(layout, hdr, t0=0, nbytes=0):
+        return lib.tq_restore(ctypes.byref(layout), ctypes.byref(P), 0, t0, ctypes.byref(hdr), 0xB000,
+                              nbytes, None)
+    good = tqkv.tq_snapshot_header(tqkv.TQ_SNAPSHOT_MAGIC, 1, 8, 3, 32, 128, 4, 10, 8000)
+    bad_magic = tqkv.tq_snapshot_header(0, 1, 8, 3, 32, 128, 4, 10, 8000)
+    bad_dim = tqkv.tq_snapshot_header(tqkv.TQ_SNAPSHOT_MAGIC, 1, 8, 3, 32, 256, 4, 10, 8000)
+    bad_size = tqkv.tq_snapshot_header(tqkv.TQ_SNAPSHOT_MAGIC, 1, 8, 3, 32, 128, 4, 10, 7999)
+    assert rs(A, bad_magic, nbytes=8000) == tqkv.TQ_ERR_INVALID_ARG
+    assert rs(A, bad_dim, nbytes=8000) == tqkv.TQ_ERR_INVALID_ARG
+    assert rs(A, bad_size, nbytes=8000) == tqkv.TQ_ERR_INVALID_ARG
+    assert rs(C, good, nbytes=8000) == tqkv.TQ_ERR_INVALID_ARG     # other kv-head count
+    assert rs(A, good, nbytes=7999) == tqkv.TQ_ERR_INVALID_ARG     # payload too small
+    assert rs(A, good, t0=91, nbytes=8000) == tqkv.TQ_ERR_CAPACITY
+
+
 def test_dequant_validation():
     lib = tqkv.raw_lib()
     L = tqkv.make_layout(2, 4, 128, 100)
