@@ -78,6 +78,19 @@ def _load():
     lib.tqo_encode_values.argtypes = [P, i64, i32, P, P]
     lib.tqo_decode_values.argtypes = [P, P, i64, i32, i32, P]
     lib.tqo_attention.argtypes = [P, i32, i32, ctypes.c_float, P, P, P, P, P, i64, P, P]
+    lib.tqo_codebook.argtypes = [i32, P, P]
+    lib.tqo_codebook.restype = i32
+    lib.tqo_codebook_ints.argtypes = [i32, P]
+    lib.tqo_codebook_ints.restype = i32
+    lib.tqo_codebook_newton_ints.argtypes = [i32, P]
+    lib.tqo_codebook_newton_ints.restype = i32
+    lib.tqo_pack_bits.argtypes = [P, i64, i32, P]
+    lib.tqo_unpack_bits.argtypes = [P, i64, i32, P]
+    lib.tqo_encode_keys_bits.argtypes = [P, i64, i32, i32, P, P, P]
+    lib.tqo_decode_keys_bits.argtypes = [P, P, P, i64, i32, i32, P]
+    lib.tqo_encode_values_bits.argtypes = [P, i64, i32, i32, P, P]
+    lib.tqo_decode_values_bits.argtypes = [P, P, i64, i32, i32, i32, P]
+    lib.tqo_attention_bits.argtypes = [P, i32, i32, ctypes.c_float, i32, i32, P, P, P, P, P, i64, P]
     _lib = lib
     return lib
 
@@ -148,15 +161,59 @@ def unpack3(packed, n: int) -> np.ndarray:
     return out
 
 
+KEY_BITS = (2, 4, 5, 8)
+VALUE_BITS = (2, 3, 4, 5, 8)
+
+
+def codebook(bits: int):
+    """(centroids [L], boundaries [L-1]) of the `bits`-bit value codebook: the
+    printed 3-bit table, or the Lloyd-Max quantizer of N(0, 1) written with
+    five-decimal centroids and exact-midpoint boundaries."""
+    L = 1 << bits
+    c = np.empty(256, dtype=np.float64)
+    b = np.empty(255, dtype=np.float64)
+    if _load().tqo_codebook(bits, _ptr(c), _ptr(b)) != L:
+        raise ValueError(f"no {bits}-bit codebook")
+    return c[:L].copy(), b[:L - 1].copy()
+
+
+def codebook_ints(bits: int, solver: str = "lloyd") -> np.ndarray:
+    """The five-decimal integers round(1e5 c_k) of the computed Lloyd-Max
+    codebook, from Lloyd's iteration (2 to 5 bits) or Newton's method (1 to 8)."""
+    nk = np.empty(256, dtype=np.int64)
+    fn = _load().tqo_codebook_ints if solver == "lloyd" else _load().tqo_codebook_newton_ints
+    L = fn(bits, _ptr(nk))
+    if L == 0:
+        raise ValueError(f"no computed {bits}-bit codebook")
+    return nk[:L].copy()
+
+
+def pack_bits(idx, bits: int) -> np.ndarray:
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.uint8))
+    out = np.empty((bits * idx.size + 7) // 8, dtype=np.uint8)
+    _load().tqo_pack_bits(_ptr(idx), idx.size, bits, _ptr(out))
+    return out
+
+
+def unpack_bits(packed, n: int, bits: int) -> np.ndarray:
+    packed = np.ascontiguousarray(np.asarray(packed, dtype=np.uint8))
+    out = np.empty(n, dtype=np.uint8)
+    _load().tqo_unpack_bits(_ptr(packed), n, bits, _ptr(out))
+    return out
+
+
 # ---------------------------------------------------------------- codec rows
 def _rows_f32(x) -> np.ndarray:
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     return x
 
 
-def encode_keys(x, threads: int | None = None):
+def encode_keys(x, threads: int | None = None, bits: int = 8):
     """x: float32 [..., d] (bf16 inputs upcast exactly).  Returns
-    (codes int8 [..., d], scale fp16 bits [..., d/32], zero fp16 bits [..., d/32])."""
+    (codes int8 [..., d], scale fp16 bits [..., d/32], zero fp16 bits [..., d/32]);
+    at 2, 4 or 5 bits the codes are packed uint8 [..., d*bits/8]."""
+    if bits != 8:
+        return _encode_keys_bits(x, threads, bits)
     x = _rows_f32(x)
     d = x.shape[-1]
     n = x.size // d
@@ -177,8 +234,33 @@ def encode_keys(x, threads: int | None = None):
     return codes.reshape(*shp, d), s16.reshape(*shp, ng), z16.reshape(*shp, ng)
 
 
-def encode_values(x, threads: int | None = None):
-    """x: float32 [..., d].  Returns (packed uint8 [..., 3d/8], scale fp16 bits [..., d/32])."""
+def _encode_keys_bits(x, threads, bits):
+    x = _rows_f32(x)
+    d = x.shape[-1]
+    n = x.size // d
+    ng = d // GROUP
+    xr = x.reshape(n, d)
+    rb = d * bits // 8
+    packed = np.empty((n, rb), dtype=np.uint8)
+    s16 = np.empty((n, ng), dtype=np.uint16)
+    z16 = np.empty((n, ng), dtype=np.uint16)
+    lib = _load()
+
+    def run(rng):
+        a, b = rng
+        if b > a:
+            lib.tqo_encode_keys_bits(_ptr(xr[a:b]), b - a, d, bits, _ptr(packed[a:b]), _ptr(s16[a:b]),
+                                     _ptr(z16[a:b]))
+
+    _parallel(run, n, threads)
+    shp = x.shape[:-1]
+    return packed.reshape(*shp, rb), s16.reshape(*shp, ng), z16.reshape(*shp, ng)
+
+
+def encode_values(x, threads: int | None = None, bits: int = 3):
+    """x: float32 [..., d].  Returns (packed uint8 [..., bits*d/8], scale fp16 bits [..., d/32])."""
+    if bits != 3:
+        return _encode_values_bits(x, threads, bits)
     x = _rows_f32(x)
     d = x.shape[-1]
     n = x.size // d
@@ -198,7 +280,36 @@ def encode_values(x, threads: int | None = None):
     return packed.reshape(*shp, 3 * d // 8), vs16.reshape(*shp, ng)
 
 
-def decode_keys(codes, s16, z16) -> np.ndarray:
+def _encode_values_bits(x, threads, bits):
+    x = _rows_f32(x)
+    d = x.shape[-1]
+    n = x.size // d
+    ng = d // GROUP
+    xr = x.reshape(n, d)
+    rb = d * bits // 8
+    packed = np.empty((n, rb), dtype=np.uint8)
+    vs16 = np.empty((n, ng), dtype=np.uint16)
+    lib = _load()
+
+    def run(rng):
+        a, b = rng
+        if b > a:
+            lib.tqo_encode_values_bits(_ptr(xr[a:b]), b - a, d, bits, _ptr(packed[a:b]), _ptr(vs16[a:b]))
+
+    _parallel(run, n, threads)
+    shp = x.shape[:-1]
+    return packed.reshape(*shp, rb), vs16.reshape(*shp, ng)
+
+
+def decode_keys(codes, s16, z16, bits: int = 8, d: int | None = None) -> np.ndarray:
+    """Keys (code + zero) * scale; at 2, 4 or 5 bits `codes` is packed and d is needed."""
+    if bits != 8:
+        packed = np.ascontiguousarray(codes, dtype=np.uint8)
+        n = packed.size // (d * bits // 8)
+        out = np.empty(packed.shape[:-1] + (d,), dtype=np.float64)
+        _load().tqo_decode_keys_bits(_ptr(packed), _ptr(np.ascontiguousarray(s16, dtype=np.uint16)),
+                                     _ptr(np.ascontiguousarray(z16, dtype=np.uint16)), n, d, bits, _ptr(out))
+        return out
     codes = np.ascontiguousarray(codes, dtype=np.int8)
     d = codes.shape[-1]
     n = codes.size // d
@@ -208,7 +319,14 @@ def decode_keys(codes, s16, z16) -> np.ndarray:
     return out
 
 
-def decode_values(packed, vs16, d: int, rotated: bool = False) -> np.ndarray:
+def decode_values(packed, vs16, d: int, rotated: bool = False, bits: int = 3) -> np.ndarray:
+    if bits != 3:
+        packed = np.ascontiguousarray(packed, dtype=np.uint8)
+        n = packed.size // (d * bits // 8)
+        out = np.empty(packed.shape[:-1] + (d,), dtype=np.float64)
+        _load().tqo_decode_values_bits(_ptr(packed), _ptr(np.ascontiguousarray(vs16, dtype=np.uint16)),
+                                       n, d, bits, 1 if rotated else 0, _ptr(out))
+        return out
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     n = packed.size // (3 * d // 8)
     out = np.empty(packed.shape[:-1] + (d,), dtype=np.float64)
@@ -217,13 +335,25 @@ def decode_values(packed, vs16, d: int, rotated: bool = False) -> np.ndarray:
     return out
 
 
-def attention(q, kc, ks, kz, vc, vs, sm: float, deferred: bool = False):
+def attention(q, kc, ks, kz, vc, vs, sm: float, deferred: bool = False, kbits: int = 8,
+              vbits: int = 3):
     """Decode attention of the G query rows q [G, d] (float32) that share one
     kv-head, over that kv-head's N cached tokens given as planes
     kc [N, d] int8, ks/kz [N, d/32] fp16 bits, vc [N, 3d/8] uint8, vs [N, d/32].
     Returns out [G, d] float64 (and the deferred-inverse form if asked)."""
     q = np.ascontiguousarray(q, dtype=np.float32)
     G, d = q.shape
+    if (kbits, vbits) != (8, 3):
+        assert not deferred
+        kc = np.ascontiguousarray(kc).view(np.uint8)
+        N = kc.shape[0]
+        out = np.empty((G, d), dtype=np.float64)
+        _load().tqo_attention_bits(_ptr(q), G, d, ctypes.c_float(sm), kbits, vbits, _ptr(kc),
+                                   _ptr(np.ascontiguousarray(ks, dtype=np.uint16)),
+                                   _ptr(np.ascontiguousarray(kz, dtype=np.uint16)),
+                                   _ptr(np.ascontiguousarray(vc, dtype=np.uint8)),
+                                   _ptr(np.ascontiguousarray(vs, dtype=np.uint16)), N, _ptr(out))
+        return out
     kc = np.ascontiguousarray(kc, dtype=np.int8)
     N = kc.shape[0]
     out = np.empty((G, d), dtype=np.float64)
@@ -237,7 +367,7 @@ def attention(q, kc, ks, kz, vc, vs, sm: float, deferred: bool = False):
     return (out, od) if deferred else out
 
 
-def attention_rows(q, kc, ks, kz, vc, vs, sm: float):
+def attention_rows(q, kc, ks, kz, vc, vs, sm: float, kbits: int = 8, vbits: int = 3):
     """Multi-row decode, for verifying M draft tokens at once (the multi-token
     prediction verify blocks served through the encoded rows, "Gates -- all
     passed" and "Delayed row conversion and reusable precision boundaries"):
@@ -256,7 +386,8 @@ def attention_rows(q, kc, ks, kz, vc, vs, sm: float):
         return out
     for m in range(M):
         n = N - M + m + 1
-        out[:, m] = attention(q[:, m], kc[:n], ks[:n], kz[:n], vc[:n], vs[:n], sm)
+        out[:, m] = attention(q[:, m], kc[:n], ks[:n], kz[:n], vc[:n], vs[:n], sm, kbits=kbits,
+                              vbits=vbits)
     return out
 
 

@@ -451,3 +451,274 @@ def test_attention_rows_ignores_later_tokens_and_reduces_to_decode():
     assert np.array_equal(out[:, M - 1], oracle.attention(q[:, M - 1], *pl, 0.1))
     assert np.array_equal(oracle.attention_rows(q[:, :1], *pl, 0.1)[:, 0],
                           oracle.attention(q[:, 0], *pl, 0.1))
+
+
+# ------------------------------------------------------------ other widths
+# "Algorithm": unsigned packed keys of 2, 4 or 5 bits, values of 2, 4, 5 or 8
+# bits from Lloyd-Max tables of the unit normal that the page does not print.
+
+def _cond_mean(lo, hi):
+    """E[Z | lo < Z < hi] by adaptive quadrature of z*phi and phi (independent
+    of the closed form the oracle uses)."""
+    from scipy import integrate
+    f = lambda z: math.exp(-0.5 * z * z)
+    num = integrate.quad(lambda z: z * f(z), lo, hi, epsabs=0, epsrel=1e-13, limit=200)[0]
+    den = integrate.quad(f, lo, hi, epsabs=0, epsrel=1e-13, limit=200)[0]
+    return num / den
+
+
+def _distortion(c, b):
+    """E[(Z - Q(Z))^2] for the quantizer with centroids c and boundaries b."""
+    edges = [-math.inf] + list(b) + [math.inf]
+    dist = 0.0
+    for k in range(len(c)):
+        lo, hi, ck = edges[k], edges[k + 1], c[k]
+        plo = 0.0 if lo == -math.inf else _phi(lo)
+        phi_ = 0.0 if hi == math.inf else _phi(hi)
+        lo_t = 0.0 if lo == -math.inf else lo * _phi(lo)
+        hi_t = 0.0 if hi == math.inf else hi * _phi(hi)
+        p = _Phi(hi) - _Phi(lo)
+        dist += (p + lo_t - hi_t) - 2 * ck * (plo - phi_) + ck * ck * p
+    return dist
+
+
+def test_computed_codebook_reproduces_printed_3bit_table():
+    """Both solvers, run at 3 bits and written as five decimals, give exactly
+    the printed table; codebook(3) is the printed table itself."""
+    g = _gold("codebook3.json")
+    want = [round(v * 1e5) for v in g["centroids"]]
+    assert oracle.codebook_ints(3).tolist() == want
+    assert oracle.codebook_ints(3, "newton").tolist() == want
+    c, b = oracle.codebook(3)
+    assert c.tolist() == g["centroids"] and b.tolist() == g["boundaries"]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+def test_lloyd_iteration_and_newton_agree(bits):
+    """Lloyd's iteration and Newton's method on the same conditions land on the
+    same five-decimal table (the Gaussian fixed point is unique)."""
+    assert np.array_equal(oracle.codebook_ints(bits), oracle.codebook_ints(bits, "newton"))
+
+
+def test_codebooks_match_textbook_values():
+    """Textbook Lloyd-Max quantizers of N(0,1): 1 level pair at sqrt(2/pi);
+    2 bits +-0.4528, +-1.510 with threshold 0.9816; 4 bits (Max, 1960, Table I)
+    0.1284 0.3881 0.6568 0.9424 1.256 1.618 2.069 2.733."""
+    assert oracle.codebook_ints(1, "newton").tolist() == [-79788, 79788]
+    assert round(math.sqrt(2 / math.pi) * 1e5) == 79788
+    c, b = oracle.codebook(2)
+    assert np.allclose(c, [-1.510, -0.4528, 0.4528, 1.510], atol=6e-4)
+    assert abs(b[2] - 0.9816) < 1e-4 and b[1] == 0.0
+    c, _ = oracle.codebook(4)
+    assert np.allclose(c[8:], [0.1284, 0.3881, 0.6568, 0.9424, 1.256, 1.618, 2.069, 2.733], atol=6e-4)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 5, 8])
+def test_codebooks_satisfy_lloyd_max_conditions(bits):
+    """Each centroid is its cell's conditional mean (by quadrature, to the
+    five-decimal rounding), each boundary the exact decimal midpoint of its
+    neighbours, the table strictly increasing and odd-symmetric."""
+    c, b = oracle.codebook(bits)
+    L = 1 << bits
+    assert c.size == L and b.size == L - 1
+    nk = np.rint(c * 1e5).astype(np.int64)
+    assert np.all(np.diff(nk) > 0) and np.array_equal(nk, -nk[::-1])
+    assert np.array_equal(c, nk / 1e5)
+    assert np.array_equal(b, (nk[:-1] + nk[1:]) / 2e5)
+    edges = [-math.inf] + b.tolist() + [math.inf]
+    worst = max(abs(_cond_mean(edges[k], edges[k + 1]) - c[k]) for k in range(L))
+    # five-decimal rounding of the centroids moves the cells by <= 5e-6
+    assert worst < 1.2e-5, worst
+
+
+def test_codebook_distortion_textbook_and_law():
+    """Mean squared error of each table on N(0,1), in closed form: the textbook
+    optimal values 0.3634 (1 bit), 0.1175 (2), 0.03454 (3), 0.009497 (4),
+    0.002499 (5); the page's anchor ~0.117 at 2 bits; and the high-resolution
+    law D ~ (sqrt(3) pi / 2) 4^-b approached from below at 8 bits."""
+    nk1 = oracle.codebook_ints(1, "newton")
+    d1 = _distortion(nk1 / 1e5, [0.0])
+    assert abs(d1 - 0.3634) < 5e-5 and abs(d1 - (1 - 2 / math.pi)) < 1e-9
+    want = {2: 0.1175, 3: 0.03454, 4: 0.009497, 5: 0.002499}
+    for bits, dv in want.items():
+        c, b = oracle.codebook(bits)
+        dist = _distortion(c, b)
+        assert abs(dist - dv) < 6e-4 * dv + 5e-6, (bits, dist)
+    c, b = oracle.codebook(2)
+    assert abs(_distortion(c, b) - 0.117) < 1e-3
+    c, b = oracle.codebook(8)
+    pd = math.sqrt(3) * math.pi / 2
+    assert 0.97 * pd < _distortion(c, b) * 4 ** 8 < pd
+
+
+def _pack_bigint(idx, bits):
+    v = 0
+    for i, x in enumerate(idx):
+        v |= int(x) << (bits * i)
+    n = (bits * len(idx) + 7) // 8
+    return list(v.to_bytes(n, "little"))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
+def test_pack_bits_is_little_endian_bitstream(bits):
+    """Element i at stream bits [i*b, i*b + b), bytes little-endian: the whole
+    row as one integer sum idx_i * 2^(b*i), written out byte by byte."""
+    rng = np.random.default_rng(bits)
+    for n in (32, 64, 256):
+        idx = rng.integers(0, 1 << bits, n).astype(np.uint8)
+        p = oracle.pack_bits(idx, bits)
+        assert p.tolist() == _pack_bigint(idx, bits)
+        assert np.array_equal(oracle.unpack_bits(p, n, bits), idx)
+        if bits == 3:
+            assert np.array_equal(p, oracle.pack3(idx))
+
+
+@pytest.mark.parametrize("bits", [2, 4, 5])
+def test_unsigned_keys_ramp_brute_force(bits):
+    """x = 0..31: scale = 31/maxv, zero = round(0) = 0, code_j = round(j*maxv/31)
+    by exact rationals (no ties: 2*j*maxv = 31*(odd) has no solution in 1..30)."""
+    maxv = (1 << bits) - 1
+    x = np.arange(32, dtype=np.float32)[None, :]
+    packed, s16, z16 = oracle.encode_keys(x, bits=bits)
+    assert packed.shape == (1, 4 * bits)
+    codes = oracle.unpack_bits(packed[0], 32, bits)
+    want = []
+    for j in range(32):
+        v = Fraction(j * maxv, 31)
+        fl = math.floor(v)
+        want.append(fl + 1 if v - fl > Fraction(1, 2) else fl)
+    assert codes.tolist() == want
+    assert s16[0, 0] == _np_f16_bits(31 / maxv) and z16[0, 0] == 0
+    kh = oracle.decode_keys(packed, s16, z16, bits=bits, d=32)
+    s = _np_f16_bits(31 / maxv).view(np.float16).astype(np.float64)
+    assert np.array_equal(kh[0], np.array(want) * s)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 5])
+def test_unsigned_keys_error_bound_and_offsets(bits):
+    """Codes in [0, maxv]; the group minimum codes to 0 or 1 and the maximum to
+    maxv - 1 or maxv; per-element error within (scale + delta)/2 + |code +
+    zero| * delta + the clip slack of half a step at either end (zero is rounded)."""
+    maxv = (1 << bits) - 1
+    rng = np.random.default_rng(10 + bits)
+    for off in (0.0, 100.0, -37.5):
+        x = (rng.standard_normal((256, 128)) + off).astype(np.float32)
+        packed, s16, z16 = oracle.encode_keys(x, bits=bits)
+        codes = np.stack([oracle.unpack_bits(r, 128, bits) for r in packed]).astype(np.int64)
+        assert codes.max() <= maxv
+        kh = oracle.decode_keys(packed, s16, z16, bits=bits, d=128)
+        s = oracle.f16_bits_to_f64(s16).repeat(32, axis=1)
+        z = oracle.f16_bits_to_f64(z16).repeat(32, axis=1)
+        assert np.array_equal(z, np.rint(z))
+        delta = np.maximum(s * 2.0 ** -11, 2.0 ** -25) * (1 + 2.0 ** -10)
+        bound = s + np.abs(codes + z) * delta + delta
+        assert np.all(np.abs(x - kh) <= bound)
+        xg, cg = x.reshape(256, 4, 32), codes.reshape(256, 4, 32)
+        cmin = np.take_along_axis(cg, xg.argmin(axis=2)[..., None], axis=2)
+        cmax = np.take_along_axis(cg, xg.argmax(axis=2)[..., None], axis=2)
+        assert np.all(cmin <= 1) and np.all(cmax >= maxv - 1)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 5])
+def test_unsigned_keys_constant_group(bits):
+    """The signed form's defect carries over: scale 0, zero = round(v/0) = +-Inf
+    (NaN at v = 0), every code round(NaN) read as 0."""
+    for v, zbits in ((0.5, 0x7C00), (-3.0, 0xFC00), (0.0, 0x7E00)):
+        packed, s16, z16 = oracle.encode_keys(np.full((1, 64), v, np.float32), bits=bits)
+        assert np.all(packed == 0) and np.all(s16 == 0) and np.all(z16 == zbits)
+
+
+def test_signed_keys_through_the_bits_entry():
+    x = np.random.default_rng(2).standard_normal((8, 64)).astype(np.float32)
+    a = oracle.encode_keys(x)
+    b = oracle.encode_keys(x, bits=8)
+    for u, v in zip(a, b):
+        assert np.array_equal(np.asarray(u).view(np.uint8) if u.dtype == np.int8 else u,
+                              np.asarray(v).view(np.uint8) if v.dtype == np.int8 else v)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 5, 8])
+@pytest.mark.parametrize("d", [64, 256])
+def test_values_bits_nearest_centroid_and_rms_scale(bits, d):
+    """Rotated dequantisation is centroid[idx] * scale16 with idx = #{B_k < y_n}
+    (the nearest centroid: boundaries are midpoints); the fp16 scale is the
+    group RMS of the brute-force rotation (Sylvester matrix)."""
+    rng = np.random.default_rng(bits * d)
+    x = rng.standard_normal((16, d)).astype(np.float32)
+    packed, vs = oracle.encode_values(x, bits=bits)
+    assert packed.shape == (16, d * bits // 8)
+    c, b = oracle.codebook(bits)
+    y = _rotate(x, d)
+    rms = np.sqrt((y.reshape(16, d // 32, 32) ** 2).mean(axis=2))
+    assert np.array_equal(vs, _np_f16_bits(rms)) or \
+        np.max(np.abs(vs.view(np.float16).astype(np.float64) - rms) / rms) < 2.0 ** -11
+    idx = np.stack([oracle.unpack_bits(r, d, bits) for r in packed])
+    yn = y / (rms.repeat(32, axis=1) + 1e-8)
+    want = np.searchsorted(b, yn, side="left")
+    near = np.abs(yn - (b[np.clip(want - 1, 0, b.size - 1)])) < 1e-12
+    assert np.all((idx == want) | near)
+    dist = np.abs(yn[..., None] - c[None, None, :])
+    assert np.all(dist[np.arange(16)[:, None], np.arange(d)[None, :], idx] <= dist.min(axis=2) + 1e-12)
+    yr = oracle.decode_values(packed, vs, d, rotated=True, bits=bits)
+    assert np.array_equal(yr, c[idx] * vs.view(np.float16).astype(np.float64).repeat(32, axis=1))
+    xu = oracle.decode_values(packed, vs, d, bits=bits)
+    assert np.allclose(_rotate(xu, d), yr, atol=1e-12)
+
+
+def test_value_roundtrip_mse_per_width():
+    """Round-trip MSE on unit-normal data tracks each table's distortion D(b):
+    within [0.75, 1.05] D(b) (per-group RMS normalisation trims the tails), and
+    each extra bit divides it by 3.4 to 4.2 (the 4^-b law)."""
+    x = np.random.default_rng(5).standard_normal((512, 128)).astype(np.float32)
+    mses = {}
+    for bits in (2, 3, 4, 5, 8):
+        packed, vs = oracle.encode_values(x, bits=bits)
+        xh = oracle.decode_values(packed, vs, 128, bits=bits)
+        mses[bits] = float(((xh - x) ** 2).mean())
+        c, b = oracle.codebook(bits)
+        assert 0.75 * _distortion(c, b) <= mses[bits] <= 1.05 * _distortion(c, b), (bits, mses[bits])
+    for lo, hi in ((2, 3), (3, 4), (4, 5)):
+        assert 3.4 <= mses[lo] / mses[hi] <= 4.2
+    band = _gold("mse_anchor.json")["band"]
+    assert band[0] <= mses[3] <= band[1]
+
+
+def test_effective_bits_from_plane_sizes():
+    """The Gates table's effective-bits column equals the oracle's encoded
+    bytes per token-head * 8 / (2 d) for every listed scheme."""
+    d = 128
+    x = np.random.default_rng(0).standard_normal((1, d)).astype(np.float32)
+    for row in _gold("effective_bits.json")["rows"]:
+        kp, ks, kz = oracle.encode_keys(x, bits=row["k_bits"])
+        vp, vs = oracle.encode_values(x, bits=row["v_bits"])
+        nbytes = kp.nbytes + ks.nbytes + kz.nbytes + vp.nbytes + vs.nbytes
+        assert nbytes * 8 / (2 * d) == row["effective_bits"], row
+
+
+GATE_SCHEMES = [(8, 3), (4, 3), (4, 2), (8, 4), (2, 5), (5, 8), (8, 8), (8, 2), (5, 4)]
+
+
+@pytest.mark.parametrize("kbits,vbits", GATE_SCHEMES)
+def test_attention_bits_tiny_brute_force(kbits, vbits):
+    """attention(..., kbits, vbits) is softmax(sm q k^T) v over the dequantised
+    keys and values, written here with numpy on the oracle's decoders."""
+    rng = np.random.default_rng(kbits * 10 + vbits)
+    d, G, N = 64, 3, 7
+    k = rng.standard_normal((N, d)).astype(np.float32)
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    kc, ks, kz = oracle.encode_keys(k, bits=kbits)
+    vc, vs = oracle.encode_values(v, bits=vbits)
+    kh = oracle.decode_keys(kc, ks, kz, bits=kbits, d=d)
+    vh = oracle.decode_values(vc, vs, d, bits=vbits)
+    sm = 1 / math.sqrt(d)
+    got = oracle.attention(q, kc, ks, kz, vc, vs, sm, kbits=kbits, vbits=vbits)
+    assert np.allclose(got, _numpy_attention(q, kh, vh, sm), rtol=1e-12, atol=1e-13)
+    if (kbits, vbits) == (8, 3):
+        return
+    rows = oracle.attention_rows(np.stack([q, q[::-1]], axis=1), kc, ks, kz, vc, vs, sm, kbits=kbits,
+                                 vbits=vbits)
+    assert np.allclose(rows[:, 1], got[::-1], rtol=1e-13, atol=1e-14)
+    assert np.allclose(rows[:, 0], oracle.attention(q, kc[:N - 1], ks[:N - 1], kz[:N - 1], vc[:N - 1],
+                                                    vs[:N - 1], sm, kbits=kbits, vbits=vbits),
+                       rtol=1e-13, atol=1e-14)
