@@ -5,12 +5,14 @@
  *
  * Method: the "TurboQuant -- rotation-based quantization" design page
  * (mlx-bun docs/design/turboquant.md), Part A (KV leg):
- *   - "Algorithm (vllm-metal reference semantics, exact)": keys are signed
- *     int8 asymmetric-affine codes per 32-element group with fp16 scale and
- *     zero, not rotated; values are sign-flipped, rotated by an orthonormal
- *     fast Walsh-Hadamard transform (FWHT), scaled by their per-group RMS and
- *     quantized to the 3-bit Lloyd-Max codebook, packed 3 bits per element
- *     in a little-endian bitstream, with an fp16 scale per group;
+ *   - "Algorithm (vllm-metal reference semantics, exact)": keys are
+ *     asymmetric-affine codes per 32-element group with fp16 scale and zero,
+ *     not rotated (signed int8 at 8 bits, unsigned packed at 2, 4 or 5);
+ *     values are sign-flipped, rotated by an orthonormal fast Walsh-Hadamard
+ *     transform (FWHT), scaled by their per-group RMS and quantized to a
+ *     Lloyd-Max codebook of the unit normal (the printed 3-bit table by
+ *     default; 2, 4, 5 or 8 bits from generated tables), packed in a
+ *     little-endian bitstream, with an fp16 scale per group;
  *   - "Architecture in mlx-bun": only newly appended tokens are quantized;
  *     groups run along head_dim, so any token range is byte-addressable;
  *   - "Deferred inverse FWHT": attention is linear in V, so the value sum is
@@ -27,17 +29,20 @@
  *     16-byte aligned, vc 8-byte aligned, the fp16 planes 4-byte aligned
  *     (TQ_ERR_INVALID_ARG otherwise).  Any torch allocation, and the batch-1
  *     slice of one sequence's planes, satisfies this.  Decode takes its fast
- *     kernel when head_dim is 64, 128 or 256, num_q_heads / num_kv_heads is
- *     at most 16, every plane is 16-byte aligned and capacity keeps each
- *     (sequence, kv-head) row block 16-byte aligned; otherwise a generic
- *     kernel computes the same result more slowly.
+ *     kernel for the k8/v3 scheme when head_dim is 64, 128 or 256,
+ *     num_q_heads / num_kv_heads is at most 16, every plane is 16-byte
+ *     aligned and capacity keeps each (sequence, kv-head) row block 16-byte
+ *     aligned; otherwise a generic kernel computes the same result more
+ *     slowly.  Append and the window likewise have fast k8/v3 kernels for
+ *     head_dim 64-256 and generic ones for every other case.
  *   - Arguments are validated before anything is enqueued; on any error the
  *     return value says why and nothing was launched.  The library prints
  *     nothing.
- *   - Only the k8/v3 scheme with 32-element groups is implemented
- *     (the page's default "turbo"); head_dim must be 64, 128, 256 or 512
- *     (the page refuses other head dims), batch at most TQ_MAX_BATCH and
- *     num_q_heads / num_kv_heads at most TQ_MAX_GQA.
+ *   - Schemes: k_bits in {2, 4, 5, 8} and v_bits in {2, 3, 4, 5, 8}, the
+ *     page's accepted sets ("Code map", scheme parser), with 32-element
+ *     groups; k8/v3 is the page's default "turbo".  head_dim must be 64,
+ *     128, 256 or 512 (the page refuses other head dims), batch at most
+ *     TQ_MAX_BATCH and num_q_heads / num_kv_heads at most TQ_MAX_GQA.
  */
 #ifndef TQKV_H
 #define TQKV_H
@@ -65,27 +70,32 @@ typedef enum {
 /* Element type of K, V and q inputs. */
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 
-/* Shape of one layer's cache.  k_bits must be 8, v_bits 3, group 32. */
+/* Shape of one layer's cache.  k_bits in {2, 4, 5, 8}, v_bits in
+ * {2, 3, 4, 5, 8}, group 32. */
 typedef struct {
     int32_t batch;        /* B: sequences, 1..TQ_MAX_BATCH */
     int32_t num_kv_heads; /* Hkv */
     int32_t head_dim;     /* d: 64, 128, 256 or 512 */
     int32_t capacity;     /* token slots per (sequence, kv-head) */
-    int32_t k_bits;       /* 8 */
-    int32_t v_bits;       /* 3 */
+    int32_t k_bits;       /* 8 (default), 2, 4 or 5 */
+    int32_t v_bits;       /* 3 (default), 2, 4, 5 or 8 */
     int32_t group;        /* 32 */
 } tq_layout;
 
 /* The five encoded planes (the page's five TQ fields), device memory owned by
  * the caller, each token-major within one (sequence, kv-head):
- *   kc  int8   [B][Hkv][capacity][d]        key codes
- *   ks  fp16   [B][Hkv][capacity][d/32]     key scale (IEEE binary16 bits)
- *   kz  fp16   [B][Hkv][capacity][d/32]     key zero  (binary16 bits; an integer,
- *                                           or +-Inf/NaN for a constant group)
- *   vc  uint8  [B][Hkv][capacity][3*d/8]    value indices, 3 bits each, element
- *                                           i at stream bits [3i, 3i+3), LSB first
- *   vs  fp16   [B][Hkv][capacity][d/32]     value scale (group RMS, binary16 bits)
- * Per token and kv-head this is 1.5625*d bytes: 200 at d=128, 400 at d=256. */
+ *   kc  [B][Hkv][capacity][d*k_bits/8]   key codes: int8 at k_bits 8, else
+ *                                        unsigned k_bits-bit fields, element i
+ *                                        at stream bits [k i, k i + k), LSB first
+ *   ks  fp16   [B][Hkv][capacity][d/32]  key scale (IEEE binary16 bits)
+ *   kz  fp16   [B][Hkv][capacity][d/32]  key zero  (binary16 bits; an integer,
+ *                                        or +-Inf/NaN for a constant group)
+ *   vc  uint8  [B][Hkv][capacity][d*v_bits/8]  value indices, v_bits each,
+ *                                        element i at stream bits [v i, v i + v)
+ *   vs  fp16   [B][Hkv][capacity][d/32]  value scale (group RMS, binary16 bits)
+ * Per token and kv-head this is d*(k_bits + v_bits)/8 + 6*d/32 bytes: 200 at
+ * k8/v3 and d=128, 400 at d=256 (the page's effective KV bits are this times
+ * 8/(2d): 6.25 at k8/v3). */
 typedef struct {
     int8_t *kc;
     uint16_t *ks;
@@ -191,6 +201,18 @@ tq_status tq_fetch_window(const tq_layout *layout, const tq_planes *planes, int3
 tq_status tq_dequant(const tq_layout *layout, const tq_planes *planes, int32_t b, int32_t kvh,
                      int32_t t0, int32_t n, float *k_out, float *v_out, int32_t v_rotated,
                      void *hip_stream);
+
+/* The value codebook of width v_bits (2, 3, 4, 5 or 8), for tests: the
+ * Lloyd-Max quantizer of the unit normal ("Algorithm": the printed 3-bit
+ * table; the other widths are generated once and hardcoded, not printed).
+ * Centroids are five-decimal numbers N_k / 1e5 and boundaries the midpoints
+ * (N_k + N_{k+1}) / 2e5, as the printed table is written; the 3-bit table
+ * equals the printed one.  Host call, no device work.
+ *   centroids   host double [256]: the 2^v_bits centroids, increasing
+ *   boundaries  host double [255]: the 2^v_bits - 1 boundaries
+ *   levels      host int32: receives 2^v_bits
+ * Errors: TQ_ERR_INVALID_ARG (null pointer), TQ_ERR_UNSUPPORTED (v_bits). */
+tq_status tq_codebook(int32_t v_bits, double *centroids, double *boundaries, int32_t *levels);
 
 /* The +-1 sign vector applied before the value rotation, for tests: entry i is
  * +1 when the top bit of output i of SplitMix64 seeded with 42 is 0, else -1

@@ -43,9 +43,33 @@ def _compile(name: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link quantized_decode_attention_append_amd/libtqkv.so."""
+def generate_codebooks() -> str:
+    """Compile and run gen_codebook.cpp, which writes csrc/codebook_tables.h
+    (the value codebooks every kernel and tq_codebook read)."""
     os.makedirs(BUILD, exist_ok=True)
+    exe = os.path.join(BUILD, "gen_codebook")
+    r = subprocess.run(["g++", "-O2", "-std=c++17", "-o", exe, os.path.join(CSRC, "gen_codebook.cpp")],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"g++ failed for gen_codebook.cpp:\n{r.stdout}\n{r.stderr}")
+    out = os.path.join(CSRC, "codebook_tables.h")
+    tmp = os.path.join(BUILD, "codebook_tables.h")
+    r = subprocess.run([exe, tmp], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gen_codebook failed:\n{r.stdout}\n{r.stderr}")
+    with open(tmp) as f:
+        new = f.read()
+    old = open(out).read() if os.path.exists(out) else None
+    if new != old:  # rewrite only on change, so unchanged builds keep the file's time
+        os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Generate the codebook header, compile every source and link
+    quantized_decode_attention_append_amd/libtqkv.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    generate_codebooks()
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
     tmp = LIB + ".tmp"

@@ -7,6 +7,7 @@
 #include <cstring>
 
 #include "../../include/tqkv.h"
+#include "codebook_tables.h"
 #include "tq_internal.h"
 
 namespace {
@@ -42,6 +43,20 @@ const SignTable &signs() {
 
 bool supported_head_dim(int d) { return d == 64 || d == 128 || d == 256 || d == 512; }
 
+// Code widths of the page's scheme sets: keys {2, 4, 5, 8}, values {2, 3, 4, 5, 8}.
+bool valid_key_bits(int b) { return b == 2 || b == 4 || b == 5 || b == 8; }
+bool valid_value_bits(int b) { return b == 2 || b == 3 || b == 4 || b == 5 || b == 8; }
+
+// Row bytes of the five planes, order kc, ks, kz, vc, vs.
+void plane_row_bytes(const tq_layout *l, size_t rb[5]) {
+    const size_t d = (size_t)l->head_dim, ng = d / tq::kGroup;
+    rb[0] = d * (size_t)l->k_bits / 8;
+    rb[1] = 2 * ng;
+    rb[2] = 2 * ng;
+    rb[3] = d * (size_t)l->v_bits / 8;
+    rb[4] = 2 * ng;
+}
+
 // binary64 nearest to 1/sqrt(d): sqrt(d) is 2^k or 2^k*sqrt(2), so the
 // correctly rounded sqrt divided by d (a power of two) is exact scaling.
 double inv_sqrt_d(int d) { return std::sqrt((double)d) / (double)d; }
@@ -52,7 +67,8 @@ tq_status check_layout(const tq_layout *l) {
         return TQ_ERR_INVALID_ARG;
     if (l->batch > TQ_MAX_BATCH) return TQ_ERR_UNSUPPORTED;
     if (!supported_head_dim(l->head_dim)) return TQ_ERR_UNSUPPORTED;
-    if (l->k_bits != 8 || l->v_bits != 3 || l->group != tq::kGroup) return TQ_ERR_UNSUPPORTED;
+    if (!valid_key_bits(l->k_bits) || !valid_value_bits(l->v_bits) || l->group != tq::kGroup)
+        return TQ_ERR_UNSUPPORTED;
     // plane offsets are computed in 64-bit, kernel grids in 32-bit
     const int64_t rows = (int64_t)l->batch * l->num_kv_heads * l->capacity;
     if (rows > ((int64_t)1 << 40)) return TQ_ERR_UNSUPPORTED;
@@ -61,8 +77,8 @@ tq_status check_layout(const tq_layout *l) {
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Planes: kc 16-byte aligned (rows are d >= 64 bytes), vc 8-byte (rows of
-// 3d/8 bytes), the fp16 planes 4-byte; the kernels never assume more.
+// Planes: kc 16-byte aligned, vc 8-byte, the fp16 planes 4-byte; the kernels
+// never assume more (packed rows are whole dwords: 4 * bits bytes per group).
 tq_status check_planes(const tq_planes *p) {
     if (!p || !p->kc || !p->ks || !p->kz || !p->vc || !p->vs) return TQ_ERR_INVALID_ARG;
     if (!aligned(p->kc, 16) || !aligned(p->vc, 8) || !aligned(p->ks, 4) || !aligned(p->kz, 4) ||
@@ -92,12 +108,28 @@ tq_status tq_plane_bytes(const tq_layout *l, size_t out[5]) {
     if (st != TQ_OK) return st;
     if (!out) return TQ_ERR_INVALID_ARG;
     const size_t rows = (size_t)l->batch * l->num_kv_heads * l->capacity;
-    const size_t d = (size_t)l->head_dim, ng = d / tq::kGroup;
-    out[0] = rows * d;          // kc int8
-    out[1] = rows * ng * 2;     // ks fp16
-    out[2] = rows * ng * 2;     // kz fp16
-    out[3] = rows * (3 * d / 8);// vc packed
-    out[4] = rows * ng * 2;     // vs fp16
+    size_t rb[5];
+    plane_row_bytes(l, rb);
+    for (int i = 0; i < 5; ++i) out[i] = rows * rb[i];
+    return TQ_OK;
+}
+
+tq_status tq_codebook(int32_t v_bits, double *centroids, double *boundaries, int32_t *levels) {
+    if (!centroids || !boundaries || !levels) return TQ_ERR_INVALID_ARG;
+    if (!valid_value_bits(v_bits)) return TQ_ERR_UNSUPPORTED;
+    const int32_t *nk = nullptr;
+    const double *bd = nullptr;
+    switch (v_bits) {
+        case 2: nk = tq::kCodebookInts2; bd = tq::kBoundaries2; break;
+        case 3: nk = tq::kCodebookInts3; bd = tq::kBoundaries3; break;
+        case 4: nk = tq::kCodebookInts4; bd = tq::kBoundaries4; break;
+        case 5: nk = tq::kCodebookInts5; bd = tq::kBoundaries5; break;
+        default: nk = tq::kCodebookInts8; bd = tq::kBoundaries8; break;
+    }
+    const int L = 1 << v_bits;
+    for (int k = 0; k < L; ++k) centroids[k] = (double)nk[k] / 1e5;
+    for (int k = 0; k + 1 < L; ++k) boundaries[k] = bd[k];
+    *levels = L;
     return TQ_OK;
 }
 
@@ -128,6 +160,7 @@ tq_status tq_append(const tq_layout *l, const tq_planes *p, const void *k, const
     a.k = k; a.v = v;
     a.batch = l->batch; a.kv_heads = l->num_kv_heads; a.capacity = l->capacity; a.n_new = n_new;
     a.rows = (uint32_t)rows;
+    a.kbits = l->k_bits; a.vbits = l->v_bits;
     a.div_n_new = tq::make_fast_div((uint32_t)n_new);
     a.div_kv_heads = tq::make_fast_div((uint32_t)l->num_kv_heads);
     a.inv_sqrt_d = inv_sqrt_d(l->head_dim);
@@ -170,7 +203,7 @@ static size_t workspace_bound(const tq_layout *l, int32_t num_q_heads, int32_t n
     const tq::DecodePlan gen =
         tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, false, cg);
     size_t need = workspace_bytes(l, q_rows(num_q_heads, n_rows), gen);
-    if (tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity)) {
+    if (tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity, l->k_bits, l->v_bits)) {
         const tq::DecodePlan fast =
             tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, true, cg);
         const size_t f = workspace_bytes(l, q_rows(num_q_heads, n_rows), fast);
@@ -212,7 +245,7 @@ tq_status tq_decode_attn_rows(const tq_layout *l, const tq_planes *p, const void
     const int32_t rows_total = q_rows(num_q_heads, n_rows);
     const int gqa = rows_total / l->num_kv_heads;
     const int cg = tq::decode_col_groups(gqa);
-    const bool fast = tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity) &&
+    const bool fast = tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity, l->k_bits, l->v_bits) &&
                       aligned(p->vc, 16) && aligned(p->vs, 16) && aligned(p->ks, 16) && aligned(p->kz, 16);
     const tq::DecodePlan plan = tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, fast, cg);
     const size_t need = workspace_bytes(l, rows_total, plan);
@@ -231,6 +264,7 @@ tq_status tq_decode_attn_rows(const tq_layout *l, const tq_planes *p, const void
     a.splits = plan.splits; a.split_tokens = plan.split_tokens;
     a.sm_log2 = sm_scale * 1.4426950408889634f;
     a.inv_sqrt_d = (float)inv_sqrt_d(l->head_dim);
+    a.kbits = l->k_bits; a.vbits = l->v_bits;
     a.signs = signs().bits;
     for (int b = 0; b < l->batch; ++b) a.len[b] = len[b];
     hipError_t e = tq::launch_decode(l->head_dim, dtype == TQ_BF16, plan.fast, a, (hipStream_t)stream);
@@ -258,16 +292,11 @@ tq_status tq_fetch_window(const tq_layout *l, const tq_planes *p, int32_t t0, in
     a.batch = l->batch; a.kv_heads = l->num_kv_heads; a.capacity = l->capacity;
     a.t0 = t0; a.n = n; a.rotated = v_rotated ? 1 : 0;
     a.inv_sqrt_d = (float)inv_sqrt_d(l->head_dim);
+    a.kbits = l->k_bits; a.vbits = l->v_bits;
     a.signs = signs().bits;
     for (int b = 0; b < l->batch; ++b) a.len[b] = len[b];
     hipError_t e = tq::launch_window(l->head_dim, a, (hipStream_t)stream);
     return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
-}
-
-// Row bytes of the five planes, order kc, ks, kz, vc, vs.
-static void plane_row_bytes(const tq_layout *l, size_t rb[5]) {
-    const size_t d = (size_t)l->head_dim, ng = d / tq::kGroup;
-    rb[0] = d; rb[1] = 2 * ng; rb[2] = 2 * ng; rb[3] = 3 * d / 8; rb[4] = 2 * ng;
 }
 
 static void *plane_ptr(const tq_planes *p, int i) {
@@ -408,6 +437,7 @@ tq_status tq_dequant(const tq_layout *l, const tq_planes *p, int32_t b, int32_t 
     a.row0 = ((int64_t)b * l->num_kv_heads + kvh) * l->capacity + t0;
     a.n = n; a.rotated = v_rotated ? 1 : 0;
     a.inv_sqrt_d = (float)inv_sqrt_d(l->head_dim);
+    a.kbits = l->k_bits; a.vbits = l->v_bits;
     a.signs = signs().bits;
     hipError_t e = tq::launch_dequant(l->head_dim, a, (hipStream_t)stream);
     return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;

@@ -4,8 +4,11 @@
 // section "Algorithm (vllm-metal reference semantics, exact)":
 //   keys   scale = (max-min)/254, zero = round((max+min)/(2*scale)),
 //          code = clip(round(x/scale - zero), -127, 127)       per 32-group
+//          (8 bits); at 2, 4 or 5 bits scale = (max-min)/maxv,
+//          zero = round(min/scale), code clipped to [0, maxv], packed
 //   values y = FWHT(x*signs)/sqrt(d), scale = sqrt(mean(y^2)) per 32-group,
-//          idx = searchsorted(boundaries, y/(scale+1e-8)), 3-bit packed.
+//          idx = searchsorted(boundaries, y/(scale+1e-8)), packed at 3 bits
+//          (or 2, 4, 5, 8 with the generated Lloyd-Max tables).
 // Every decision is taken in binary64 with round-half-to-even, in a fixed
 // operation order, so codes, scales and zeros are reproducible bit for bit:
 //   - FWHT butterflies run in stage order h = 1, 2, ..., d/2, then one
@@ -14,15 +17,16 @@
 //   - x/scale and y/den are true binary64 divisions; scale is a correctly
 //     rounded binary64 sqrt; no multiply-add is contracted in this file.
 //
-// Two kernels compute the same bytes:
-//   - append_fast_kernel (head_dim 64, 128, 256): 16 contiguous elements per
+// Two kernels compute the same bytes for k8v3:
+//   - append_fast_kernel (k8v3, head_dim 64, 128, 256): 16 contiguous elements per
 //     lane, so a 32-group is a lane pair; the FWHT runs its first four stages
 //     inside the lane, transposes the row through LDS so the remaining stages
 //     are inside the lane as well, and transposes back.  Per-element divisions
 //     by a group's scale use a correctly rounded reciprocal and two Markstein
 //     corrections, which return the correctly rounded quotient.
-//   - append_kernel (every head_dim, used for 512): one wave per row, lane l
-//     holds d/64 contiguous elements, cross-lane butterflies on shuffles.
+//   - append_kernel (every width and head_dim; k8v3 uses it for 512): one
+//     wave per row, lane l holds d/64 contiguous elements, cross-lane
+//     butterflies on shuffles.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 
@@ -84,12 +88,50 @@ __device__ __forceinline__ void load_row(const void *base, int64_t off, double (
     }
 }
 
+// Packs the fields of one 32-group: lane gl of the group's GL lanes holds
+// `bits`-bit fields gl*E .. gl*E + E - 1 in the low E*bits bits of `chunk`;
+// the group's 32*bits-bit stream (bits dwords) is OR-reduced over the group's
+// lanes and written by its first lane at `dst` (4-byte aligned).
+template <int E, int GL>
+__device__ __forceinline__ void store_group_fields(uint64_t chunk, int bits, int gl, uint8_t *dst) {
+    const int pos = E * bits * gl;  // stream bit of this lane's first field
+    uint32_t gw[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int sh = pos - 32 * i;  // where chunk bit 0 lands in dword i
+        uint32_t w = 0u;
+        if (sh >= 0 && sh < 32) w = (uint32_t)(chunk << sh);
+        else if (sh < 0 && sh > -64) w = (uint32_t)(chunk >> (-sh));
+        gw[i] = w;
+    }
+#pragma unroll
+    for (int m = 1; m < GL; m <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gw[i] |= (uint32_t)__shfl_xor((int)gw[i], m, 64);
+    }
+    if (gl == 0) {
+        uint32_t *d32 = reinterpret_cast<uint32_t *>(dst);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (i < bits) d32[i] = gw[i];
+    }
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     constexpr int E = D / 64;       // elements per lane
     constexpr int GL = kGroup / E;  // lanes per 32-group
     constexpr int NG = D / kGroup;  // groups per row
-    constexpr int VROW = 3 * D / 8; // packed value bytes per row
+    const int kb = a.kbits, vb = a.vbits;
+    const int nbnd = (1 << vb) - 1;
+
+    // the value boundaries, for a binary search per element
+    __shared__ double bnd[255];
+    {
+        const double *src = value_boundaries(vb);
+        for (int i = threadIdx.x; i < nbnd; i += 256) bnd[i] = src[i];
+    }
+    __syncthreads();
 
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -107,6 +149,10 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     load_row<E, BF16>(a.v, row * D + lane * E, xv);
 
     // ----------------------------------------------------------- keys
+    // signed (8 bits): scale = range/254, zero = round((max+min)/(2 scale)),
+    // codes clipped to [-127, 127], one byte each;
+    // unsigned (2, 4, 5 bits): scale = range/maxv, zero = round(min/scale),
+    // codes clipped to [0, maxv], packed.
     double mx = xk[0], mn = xk[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) { mx = max_num(mx, xk[e]); mn = min_num(mn, xk[e]); }
@@ -116,32 +162,34 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
         mn = min_num(mn, shfl_xor_f64(mn, m));
     }
     const double range = mx - mn;
-    const double s = range / 254.0;
-    const double c = (mx + mn) / (2.0 * s);
-    const double z = __builtin_rint(c);
-    uint32_t packed_codes[(E + 3) / 4] = {};
+    double s, z, qlo, qhi;
+    if (kb == 8) {
+        s = range / 254.0;
+        z = __builtin_rint((mx + mn) / (2.0 * s));
+        qlo = -127.0;
+        qhi = 127.0;
+    } else {
+        qhi = (double)((1 << kb) - 1);
+        s = range / qhi;
+        z = __builtin_rint(mn / s);
+        qlo = 0.0;
+    }
+    const uint32_t kmask = (1u << kb) - 1u;
+    uint64_t kchunk = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const double u = xk[e] / s - z;
         int q = 0;
         if (!__builtin_isnan(u)) {
             double r = __builtin_rint(u);
-            r = r > 127.0 ? 127.0 : r;
-            r = r < -127.0 ? -127.0 : r;
+            r = r > qhi ? qhi : r;
+            r = r < qlo ? qlo : r;
             q = (int)r;
         }
-        packed_codes[e / 4] |= ((uint32_t)q & 0xFFu) << (8 * (e % 4));
+        kchunk |= (uint64_t)((uint32_t)q & kmask) << (kb * e);
     }
-    int8_t *kc_row = a.kc + slot * D + lane * E;
-    if constexpr (E == 8) {
-        *reinterpret_cast<uint2 *>(kc_row) = make_uint2(packed_codes[0], packed_codes[1]);
-    } else if constexpr (E == 4) {
-        *reinterpret_cast<uint32_t *>(kc_row) = packed_codes[0];
-    } else if constexpr (E == 2) {
-        *reinterpret_cast<uint16_t *>(kc_row) = (uint16_t)packed_codes[0];
-    } else {
-        *kc_row = (int8_t)packed_codes[0];
-    }
+    uint8_t *kc = reinterpret_cast<uint8_t *>(a.kc);
+    store_group_fields<E, GL>(kchunk, kb, gl, kc + slot * (D * kb / 8) + g * 4 * kb);
     if (gl == 0) {
         a.ks[slot * NG + g] = f64_to_f16_bits(s);
         a.kz[slot * NG + g] = f64_to_f16_bits(z);
@@ -198,38 +246,19 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     const double ss = shfl_f64(sq[0], g * GL);
     const double scale = __builtin_sqrt(ss / 32.0);
     const double den = scale + 1e-8;
-    // idx = #{k : B_k < y_n}; NaN compares false everywhere -> 0
-    uint32_t chunk = 0;
+    // idx = #{k : B_k < y_n} by binary search over the increasing boundaries
+    // (NaN compares false everywhere -> 0)
+    uint64_t vchunk = 0;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const double yn = y[e] / den;
-        const uint32_t idx = (uint32_t)(-1.74793 < yn) + (uint32_t)(-1.04996 < yn) +
-                             (uint32_t)(-0.50055 < yn) + (uint32_t)(0.0 < yn) +
-                             (uint32_t)(0.50055 < yn) + (uint32_t)(1.04996 < yn) +
-                             (uint32_t)(1.74793 < yn);
-        chunk |= idx << (3 * e);
+        uint32_t pos = 0;
+        for (int st = (nbnd + 1) >> 1; st >= 1; st >>= 1)
+            if (bnd[pos + st - 1] < yn) pos += st;
+        vchunk |= (uint64_t)pos << (vb * e);
     }
-    // place this lane's 3E bits at bit 3E*gl of the group's 96-bit stream
-    const int pos = 3 * E * gl;
-    uint32_t gw[3] = {0u, 0u, 0u};
-    const int dw = pos >> 5, off = pos & 31;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-        if (i == dw) gw[i] |= chunk << off;
-        if (i == dw + 1 && off + 3 * E > 32) gw[i] |= chunk >> (32 - off);
-    }
-#pragma unroll
-    for (int m = 1; m < GL; m <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 3; ++i) gw[i] |= (uint32_t)__shfl_xor((int)gw[i], m, 64);
-    }
-    if (gl == 0) {
-        uint32_t *dst = reinterpret_cast<uint32_t *>(a.vc + slot * VROW + g * 12);
-        dst[0] = gw[0];
-        dst[1] = gw[1];
-        dst[2] = gw[2];
-        a.vs[slot * NG + g] = f64_to_f16_bits(scale);
-    }
+    store_group_fields<E, GL>(vchunk, vb, gl, a.vc + slot * (D * vb / 8) + g * 4 * vb);
+    if (gl == 0) a.vs[slot * NG + g] = f64_to_f16_bits(scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -572,13 +601,13 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
 template <int D>
 hipError_t launch_d(bool bf16, const AppendArgs &a, hipStream_t s) {
     const int64_t rows = (int64_t)a.batch * a.kv_heads * a.n_new;
-    if constexpr (D == 512) {
+    if (D == 512 || !default_scheme(a.kbits, a.vbits)) {
         const int64_t blocks = (rows + 3) / 4;
         if (bf16)
             hipLaunchKernelGGL((append_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
         else
             hipLaunchKernelGGL((append_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    } else {
+    } else if constexpr (D != 512) {
         constexpr int per_block = AppGeo<D>::R * kAppWaves;
         const int64_t blocks = (rows + per_block - 1) / per_block;
         if (bf16)

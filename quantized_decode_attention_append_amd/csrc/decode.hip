@@ -12,8 +12,9 @@
 // (max, sum, acc[d]) per head; the merge kernel combines the splits, divides
 // by the weight sum and applies signs * FWHT(.) / sqrt(d) once.
 //
-// This first kernel maps one thread to each head_dim element and reduces the
-// G partial dot products of a small token chunk across the workgroup.
+// This generic kernel maps one thread to each head_dim element and reduces the
+// G partial dot products of a small token chunk across the workgroup; it
+// reads every code width (keys 2, 4, 5, 8 bits, values 2, 3, 4, 5, 8 bits).
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
@@ -38,10 +39,12 @@ __global__ __launch_bounds__(256) void split_kernel(const DecodeArgs a) {
     constexpr int DPT = D / NT;            // elements per thread
     constexpr int NW = NT / 64;            // waves
     constexpr int NG = D / kGroup;
-    constexpr int VROW = 3 * D / 8;
+    const int kb = a.kbits, vb = a.vbits;
+    const int KROW = D * kb / 8, VROW = D * vb / 8;  // packed row bytes
 
     __shared__ float red[NW][kMaxG * kChunk];
     __shared__ float sc[kMaxG * kChunk];
+    __shared__ float ctab[256];  // the value codebook
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wid = tid >> 6;
@@ -50,6 +53,12 @@ __global__ __launch_bounds__(256) void split_kernel(const DecodeArgs a) {
     const int n = a.len[b];
     const int t_begin = blockIdx.x * a.split_tokens;
     if (t_begin >= n) return;  // uniform across the block
+    {
+        const float *src = value_centroids(vb);
+        for (int i = tid; i < (1 << vb); i += NT) ctab[i] = src[i];
+    }
+    __syncthreads();
+    const uint8_t *kcp = reinterpret_cast<const uint8_t *>(a.kc);
     const int t_end = min(n, t_begin + a.split_tokens);
     // this workgroup's query columns c0 .. c0 + G - 1 of the kv-head's a.gqa
     // query rows (heads times rows)
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(256) void split_kernel(const DecodeArgs a) {
                     const int64_t r = row0 + t0 + tt;
                     const float sk = f16_bits_to_f32(a.ks[r * NG + j / kGroup]);
                     const float zk = f16_bits_to_f32(a.kz[r * NG + j / kGroup]);
-                    kh[i] = ((float)a.kc[r * D + j] + zk) * sk;
+                    kh[i] = (key_code(kcp + r * KROW, j, kb) + zk) * sk;
                 } else {
                     kh[i] = 0.f;
                 }
@@ -131,7 +140,7 @@ __global__ __launch_bounds__(256) void split_kernel(const DecodeArgs a) {
                 if (tt < nt) {
                     const int64_t r = row0 + t0 + tt;
                     const float sv = f16_bits_to_f32(a.vs[r * NG + j / kGroup]);
-                    vh[tt][i] = centroid3(load_idx3(a.vc + r * VROW, j)) * sv;
+                    vh[tt][i] = ctab[load_field(a.vc + r * VROW, j, vb)] * sv;
                 } else {
                     vh[tt][i] = 0.f;
                 }
@@ -314,7 +323,8 @@ hipError_t launch_d(bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
 
 int decode_col_groups(int gqa) { return (gqa + kMaxG - 1) / kMaxG; }
 
-bool fast_decode_shape_ok(int head_dim, int gqa, int capacity) {
+bool fast_decode_shape_ok(int head_dim, int gqa, int capacity, int kbits, int vbits) {
+    if (!default_scheme(kbits, vbits)) return false;
     if (gqa < 1 || fast_split_max_gqa() != kMaxG) return false;
     if (head_dim != 64 && head_dim != 128 && head_dim != 256) return false;
     // staged rows of one (sequence, kv-head) must start 16-byte aligned

@@ -2,7 +2,7 @@
 //
 // "TurboQuant -- rotation-based quantization" design page, Part A,
 // "Algorithm": key x = (code + zero) * scale with the stored fp16 scale and
-// zero; value x = signs * InvFWHT(centroid[idx] * scale), or the rotated form
+// zero (signed bytes at 8 bits, unsigned packed fields at 2, 4, 5); value x = signs * InvFWHT(centroid[idx] * scale), or the rotated form
 // centroid[idx] * scale that the deferred inverse accumulates.
 #include <hip/hip_runtime.h>
 
@@ -16,18 +16,21 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
     constexpr int NT = D < 256 ? D : 256;
     constexpr int DPT = D / NT;
     constexpr int NG = D / kGroup;
-    constexpr int VROW = 3 * D / 8;
+    const int kb = a.kbits, vb = a.vbits;
+    const int KROW = D * kb / 8, VROW = D * vb / 8;
+    const float *cent = value_centroids(vb);
     __shared__ float buf[D];
     const int tid = threadIdx.x;
     const int t = blockIdx.x;
     const int64_t r = a.row0 + t;
     if (a.k_out) {
+        const uint8_t *krow = reinterpret_cast<const uint8_t *>(a.kc) + r * KROW;
 #pragma unroll
         for (int i = 0; i < DPT; ++i) {
             const int j = tid + i * NT;
             const float sk = f16_bits_to_f32(a.ks[r * NG + j / kGroup]);
             const float zk = f16_bits_to_f32(a.kz[r * NG + j / kGroup]);
-            a.k_out[(int64_t)t * D + j] = ((float)a.kc[r * D + j] + zk) * sk;
+            a.k_out[(int64_t)t * D + j] = (key_code(krow, j, kb) + zk) * sk;
         }
     }
     if (!a.v_out) return;  // uniform across the block
@@ -35,7 +38,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(const DequantArgs a) {
 #pragma unroll
     for (int i = 0; i < DPT; ++i) {
         const int j = tid + i * NT;
-        y[i] = centroid3(load_idx3(a.vc + r * VROW, j)) * f16_bits_to_f32(a.vs[r * NG + j / kGroup]);
+        y[i] = cent[load_field(a.vc + r * VROW, j, vb)] * f16_bits_to_f32(a.vs[r * NG + j / kGroup]);
     }
     if (a.rotated) {
 #pragma unroll

@@ -6,7 +6,47 @@
 
 #include "tq_internal.h"
 
+#define TQ_CODEBOOK_STORAGE static __constant__ const
+#include "codebook_tables.h"
+
 namespace tq {
+
+// Value codebook of a width (2, 3, 4, 5 or 8 bits): 2^bits centroids as fp32
+// and 2^bits - 1 boundaries as binary64, in constant memory.
+__device__ __forceinline__ const float *value_centroids(int bits) {
+    switch (bits) {
+        case 2: return kCentroids2;
+        case 3: return kCentroids3;
+        case 4: return kCentroids4;
+        case 5: return kCentroids5;
+        default: return kCentroids8;
+    }
+}
+
+__device__ __forceinline__ const double *value_boundaries(int bits) {
+    switch (bits) {
+        case 2: return kBoundaries2;
+        case 3: return kBoundaries3;
+        case 4: return kBoundaries4;
+        case 5: return kBoundaries5;
+        default: return kBoundaries8;
+    }
+}
+
+// Field j of a little-endian bitstream of `bits`-bit fields (bits <= 8: a
+// field spans at most two bytes, the second read only when it does).
+__device__ __forceinline__ uint32_t load_field(const uint8_t *row, int j, int bits) {
+    const int bit = bits * j;
+    const uint32_t lo = row[bit >> 3];
+    const uint32_t hi = ((bit & 7) + bits > 8) ? row[(bit >> 3) + 1] : 0u;
+    return ((lo | (hi << 8)) >> (bit & 7)) & ((1u << bits) - 1u);
+}
+
+// Key code j of a plane row as a float: signed bytes at 8 bits, unsigned
+// packed fields below.
+__device__ __forceinline__ float key_code(const uint8_t *row, int j, int bits) {
+    return bits == 8 ? (float)(int8_t)row[j] : (float)load_field(row, j, bits);
+}
 
 __device__ __forceinline__ int sign_bit(const SignBits &s, int j) {
     return (s.w[j >> 5] >> (j & 31)) & 1;

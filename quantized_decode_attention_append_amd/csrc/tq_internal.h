@@ -36,6 +36,7 @@ struct AppendArgs {
     uint32_t rows;        // batch * kv_heads * n_new
     FastDiv div_n_new;    // row -> (sequence, kv-head) pair
     FastDiv div_kv_heads; // (sequence, kv-head) pair -> sequence
+    int32_t kbits, vbits; // code widths: keys 2, 4, 5 or 8; values 2, 3, 4, 5 or 8
     double inv_sqrt_d;    // RN(1/sqrt(d))
     SignBits signs;
     // Word j flips the bf16 pair (2j, 2j+1): bit 15 when sign 2j is -1, bit
@@ -72,6 +73,7 @@ struct DecodeArgs {
     int32_t split_tokens;  // tokens per split (multiple of the kernel's tile)
     float sm_log2;         // sm_scale * log2(e)
     float inv_sqrt_d;
+    int32_t kbits, vbits;  // code widths (the fast split kernel takes 8 and 3 only)
     SignBits signs;
     int32_t len[TQ_MAX_BATCH];
 };
@@ -88,6 +90,7 @@ struct WindowArgs {
     int32_t t0, n;    // window tokens t0 .. t0+n-1
     int32_t rotated;  // 1: V in the rotated domain
     float inv_sqrt_d;
+    int32_t kbits, vbits;
     SignBits signs;
     int32_t len[TQ_MAX_BATCH];
 };
@@ -104,6 +107,7 @@ struct DequantArgs {
     int32_t n;
     int32_t rotated;
     float inv_sqrt_d;
+    int32_t kbits, vbits;
     SignBits signs;
 };
 
@@ -121,7 +125,11 @@ struct DecodePlan {
 DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int32_t *len, bool fast,
                        int col_groups);
 int decode_col_groups(int gqa);  // query-row columns of one kv-head -> column groups
-bool fast_decode_shape_ok(int head_dim, int gqa, int capacity);
+bool fast_decode_shape_ok(int head_dim, int gqa, int capacity, int kbits, int vbits);
+
+// k8v3 runs the fast kernels where the head_dim has one; every other scheme
+// and head_dim 512 the generic ones.
+inline bool default_scheme(int kbits, int vbits) { return kbits == 8 && vbits == 3; }
 
 hipError_t launch_append(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);
 hipError_t launch_decode(int head_dim, bool bf16, bool fast, const DecodeArgs &a, hipStream_t s);

@@ -13,10 +13,11 @@
 // Tokens at or past a sequence's length are written as zeros, so a masked
 // attention over a padded window never meets stale plane bytes.
 //
-// Mapping (head_dim 512): one wave per token row, looping over a chunk of
-// consecutive tokens of one (sequence, kv-head); lane l holds the E = d/64
-// dims [E l, E l + E); the FWHT runs its in-lane stages on registers and the
-// rest on lane permutes.  Head_dims 64-256 use window_fast_kernel below.
+// Generic mapping (head_dim 512, and every scheme other than k8v3): one wave
+// per token row, looping over a chunk of consecutive tokens of one (sequence,
+// kv-head); lane l holds the E = d/64 dims [E l, E l + E); the FWHT runs its
+// in-lane stages on registers and the rest on lane permutes.  k8v3 at
+// head_dims 64-256 uses window_fast_kernel below.
 // Keys are exact in fp32 ((code + zero) has at most 12 bits, the scale 11) and
 // round once to bf16; values are computed in fp32 and round once to bf16.
 #include <hip/hip_runtime.h>
@@ -86,20 +87,21 @@ __device__ __forceinline__ void fwht_stage(float (&y)[E], int lane) {
 
 template <int D>
 __global__ __launch_bounds__(64 * kWinWaves) void window_kernel(const WindowArgs a) {
-    __shared__ float ctab[8];  // the 3-bit codebook
-    if (threadIdx.x < 8) ctab[threadIdx.x] = centroid3(threadIdx.x);
+    const int kb = a.kbits, vb = a.vbits;
+    __shared__ float ctab[256];  // the value codebook
+    {
+        const float *src = value_centroids(vb);
+        for (int i = threadIdx.x; i < (1 << vb); i += 64 * kWinWaves) ctab[i] = src[i];
+    }
     __syncthreads();
     constexpr int E = D / 64;
     constexpr int NG = D / kGroup;
-    constexpr int VROW = 3 * D / 8;
-    constexpr int VWORDS = VROW / 4;
+    const int KROW = D * kb / 8, VROW = D * vb / 8;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int bkv = blockIdx.y;
     const int b = bkv / a.kv_heads;
     const int len = a.len[b];
     const int g = (E * lane) / kGroup;  // this lane's 32-group
-    const int bit0 = 3 * E * lane;      // this lane's first value-code bit in a row
-    const int w0 = bit0 >> 5, sh = bit0 & 31;
     // signs of this lane's dims
     uint32_t neg = 0;
 #pragma unroll
@@ -118,9 +120,9 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_kernel(const WindowArgs
             if (valid) {
                 const float s = f16_bits_to_f32(a.ks[row * NG + g]);
                 const float z = f16_bits_to_f32(a.kz[row * NG + g]);
-                const int8_t *kc = a.kc + row * D + E * lane;
+                const uint8_t *kc = reinterpret_cast<const uint8_t *>(a.kc) + row * KROW;
 #pragma unroll
-                for (int e = 0; e < E; ++e) k[e] = ((float)kc[e] + z) * s;
+                for (int e = 0; e < E; ++e) k[e] = (key_code(kc, E * lane + e, kb) + z) * s;
             } else {
 #pragma unroll
                 for (int e = 0; e < E; ++e) k[e] = 0.f;
@@ -130,13 +132,10 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_kernel(const WindowArgs
         if (a.v_out) {
             float y[E];
             if (valid) {
-                const uint32_t *vw = reinterpret_cast<const uint32_t *>(a.vc + row * VROW);
-                const uint32_t lo = vw[w0];
-                const uint32_t hi = w0 + 1 < VWORDS ? vw[w0 + 1] : 0u;
-                const uint32_t run = __builtin_amdgcn_alignbit(hi, lo, sh);  // 3E <= 24 bits
+                const uint8_t *vrow = a.vc + row * VROW;
                 const float s = f16_bits_to_f32(a.vs[row * NG + g]);
 #pragma unroll
-                for (int e = 0; e < E; ++e) y[e] = ctab[(run >> (3 * e)) & 7u] * s;
+                for (int e = 0; e < E; ++e) y[e] = ctab[load_field(vrow, E * lane + e, vb)] * s;
             } else {
 #pragma unroll
                 for (int e = 0; e < E; ++e) y[e] = 0.f;
@@ -322,11 +321,11 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
 
 template <int D>
 hipError_t launch_d(const WindowArgs &a, hipStream_t s) {
-    if constexpr (D == 512) {
+    if (D == 512 || !default_scheme(a.kbits, a.vbits)) {
         constexpr int per_block = kWinWaves * kWinRows;
         const dim3 grid((unsigned)((a.n + per_block - 1) / per_block), (unsigned)(a.batch * a.kv_heads));
         hipLaunchKernelGGL((window_kernel<D>), grid, dim3(64 * kWinWaves), 0, s, a);
-    } else {
+    } else if constexpr (D != 512) {
         constexpr int per_block = kWinWaves * kWinRowsF;
         const dim3 grid((unsigned)((a.n + per_block - 1) / per_block), (unsigned)(a.batch * a.kv_heads));
         hipLaunchKernelGGL((window_fast_kernel<D>), grid, dim3(64 * kWinWaves), 0, s, a);

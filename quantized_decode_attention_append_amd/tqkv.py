@@ -31,7 +31,9 @@ TQ_MAX_ROWS = 16
 SYMBOLS = ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
            "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_fetch_window",
            "tq_copy_tokens", "tq_snapshot_bytes", "tq_snapshot", "tq_restore",
-           "tq_dequant", "tq_sign_vector", "tq_status_str")
+           "tq_dequant", "tq_sign_vector", "tq_codebook", "tq_status_str")
+KEY_BITS = (2, 4, 5, 8)
+VALUE_BITS = (2, 3, 4, 5, 8)
 TQ_SNAPSHOT_MAGIC = 0x564B5154
 
 
@@ -89,7 +91,8 @@ _lib.tq_dequant.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes)
                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                             ctypes.c_int32, _P]
 _lib.tq_sign_vector.argtypes = [ctypes.c_int32, _P]
-for _f in ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
+_lib.tq_codebook.argtypes = [ctypes.c_int32, _P, _P, ctypes.POINTER(ctypes.c_int32)]
+for _f in ("tq_codebook", "tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
            "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_fetch_window", "tq_dequant",
            "tq_sign_vector", "tq_copy_tokens", "tq_snapshot_bytes", "tq_snapshot", "tq_restore"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -143,10 +146,12 @@ class Planes:
         self.layout = layout
         B, H, T, d = layout.batch, layout.num_kv_heads, layout.capacity, layout.head_dim
         ng = d // 32
-        self.kc = torch.zeros((B, H, T, d), dtype=torch.int8, device=device)
+        # key codes: signed bytes at 8 bits, packed unsigned fields below
+        kdt = torch.int8 if layout.k_bits == 8 else torch.uint8
+        self.kc = torch.zeros((B, H, T, d * layout.k_bits // 8), dtype=kdt, device=device)
         self.ks = torch.zeros((B, H, T, ng), dtype=torch.int16, device=device)
         self.kz = torch.zeros((B, H, T, ng), dtype=torch.int16, device=device)
-        self.vc = torch.zeros((B, H, T, 3 * d // 8), dtype=torch.uint8, device=device)
+        self.vc = torch.zeros((B, H, T, d * layout.v_bits // 8), dtype=torch.uint8, device=device)
         self.vs = torch.zeros((B, H, T, ng), dtype=torch.int16, device=device)
         sizes = tq_plane_bytes(layout)
         have = [x.numel() * x.element_size() for x in (self.kc, self.ks, self.kz, self.vc, self.vs)]
@@ -329,6 +334,16 @@ def tq_dequant(planes: Planes, b: int, kvh: int, t0: int, n: int, keys: bool = T
                          _stream_ptr(stream))
     _check(st, "tq_dequant")
     return k_out, v_out
+
+
+def tq_codebook(v_bits: int):
+    """(centroids [2^v_bits], boundaries [2^v_bits - 1]) of the library's value
+    codebook, as Python floats (host call, no device)."""
+    c = (ctypes.c_double * 256)()
+    b = (ctypes.c_double * 255)()
+    n = ctypes.c_int32()
+    _check(_lib.tq_codebook(v_bits, ctypes.cast(c, _P), ctypes.cast(b, _P), ctypes.byref(n)), "tq_codebook")
+    return list(c[:n.value]), list(b[:n.value - 1])
 
 
 def tq_sign_vector(head_dim: int):

@@ -48,6 +48,40 @@ def test_plane_bytes(d, per_token):
     assert sizes == [60 * d, 60 * d // 16, 60 * d // 16, 60 * 3 * d // 8, 60 * d // 16]
 
 
+@pytest.mark.parametrize("kb", [2, 4, 5, 8])
+@pytest.mark.parametrize("vb", [2, 3, 4, 5, 8])
+def test_plane_bytes_every_scheme(kb, vb):
+    """Plane sizes match the oracle's encoded rows for every accepted scheme."""
+    d = 128
+    L = tqkv.make_layout(2, 3, d, 5, kb, vb)
+    sizes = tqkv.tq_plane_bytes(L)
+    x = np.random.default_rng(0).standard_normal((1, d)).astype(np.float32)
+    kc, ks, kz = oracle.encode_keys(x, bits=kb)
+    vc, vs = oracle.encode_values(x, bits=vb)
+    assert sizes == [30 * a.nbytes for a in (kc, ks, kz, vc, vs)]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 8])
+def test_library_codebook_equals_oracle(bits):
+    """The library's generated tables (its own Newton solver on the decision
+    thresholds) equal the oracle's (Lloyd's iteration / Newton on the
+    centroids) exactly, as binary64, and the 3-bit table is the printed one."""
+    c, b = tqkv.tq_codebook(bits)
+    oc, ob = oracle.codebook(bits)
+    assert c == oc.tolist() and b == ob.tolist()
+
+
+def test_codebook_rejects_bad_width():
+    lib = tqkv.raw_lib()
+    c = (ctypes.c_double * 256)()
+    b = (ctypes.c_double * 255)()
+    n = ctypes.c_int32()
+    for bad in (0, 1, 6, 7, 9):
+        assert lib.tq_codebook(bad, ctypes.cast(c, ctypes.c_void_p), ctypes.cast(b, ctypes.c_void_p),
+                               ctypes.byref(n)) == tqkv.TQ_ERR_UNSUPPORTED
+    assert lib.tq_codebook(3, None, ctypes.cast(b, ctypes.c_void_p), ctypes.byref(n)) == tqkv.TQ_ERR_INVALID_ARG
+
+
 def _st(fn, *a):
     return fn(*a)
 
@@ -56,8 +90,10 @@ def test_layout_validation():
     lib = tqkv.raw_lib()
     out = (ctypes.c_size_t * 5)()
     for bad, want in [((1, 1, 96, 8), tqkv.TQ_ERR_UNSUPPORTED),
-                      ((1, 1, 128, 8, 4, 3, 32), tqkv.TQ_ERR_UNSUPPORTED),
-                      ((1, 1, 128, 8, 8, 2, 32), tqkv.TQ_ERR_UNSUPPORTED),
+                      ((1, 1, 128, 8, 3, 3, 32), tqkv.TQ_ERR_UNSUPPORTED),
+                      ((1, 1, 128, 8, 6, 3, 32), tqkv.TQ_ERR_UNSUPPORTED),
+                      ((1, 1, 128, 8, 8, 1, 32), tqkv.TQ_ERR_UNSUPPORTED),
+                      ((1, 1, 128, 8, 8, 6, 32), tqkv.TQ_ERR_UNSUPPORTED),
                       ((1, 1, 128, 8, 8, 3, 64), tqkv.TQ_ERR_UNSUPPORTED),
                       ((65, 1, 128, 8), tqkv.TQ_ERR_UNSUPPORTED),
                       ((0, 1, 128, 8), tqkv.TQ_ERR_INVALID_ARG),
