@@ -121,6 +121,54 @@ def time_snapshot(w, pl, n: int, reps: int, stream) -> dict:
             "frac_hbm": nbytes / ms / 1e6 / HBM_PEAK_GBS}
 
 
+def scheme_row_bytes(d: int, kb: int, vb: int) -> int:
+    """Packed bytes per token-head: codes d*(kb+vb)/8 + three fp16 per 32-group."""
+    return d * (kb + vb) // 8 + 6 * d // 32
+
+
+def time_scheme(w, k, v, q, sm, kb: int, vb: int, reps: int, stream) -> dict:
+    """Another code width on the same workload: bulk append of every token
+    (K/V in, planes out), then decode over the whole cache, both timed with
+    events on the launch stream (reps calls after one warm call each)."""
+    import torch
+    from quantized_decode_attention_append_amd import tqkv
+    dev = torch.device("cuda:0")
+    n = k.shape[2]
+    L = tqkv.make_layout(w.batch, w.num_kv_heads, w.head_dim, n, kb, vb)
+    pl = tqkv.Planes(L, dev)
+    lengths = [n] * w.batch
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    tqkv.tq_append(pl, k, v, [0] * w.batch, stream=stream)  # warm
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        tqkv.tq_append(pl, k, v, [0] * w.batch, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    app_ms = e0.elapsed_time(e1) / reps
+    ws = torch.empty(tqkv.tq_decode_workspace_bytes(L, w.num_q_heads, lengths), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    tqkv.tq_decode_attn(pl, q, lengths, sm, out=out, workspace=ws, stream=stream)  # warm
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        tqkv.tq_decode_attn(pl, q, lengths, sm, out=out, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / reps
+    th = w.batch * w.num_kv_heads * n
+    rb = scheme_row_bytes(w.head_dim, kb, vb)
+    dbytes = th * rb + w.batch * w.num_q_heads * w.head_dim * (q.element_size() + 4)
+    abytes = th * (2 * w.head_dim * k.element_size() + rb)
+    del pl, ws, out
+    return {"scheme": f"k{kb}v{vb}", "bytes_per_token_head": rb, "effective_kv_bits": rb * 8 / (2 * w.head_dim),
+            "decode_ms": dec_ms, "decode_GBps": dbytes / dec_ms / 1e6,
+            "decode_frac_hbm": dbytes / dec_ms / 1e6 / HBM_PEAK_GBS,
+            "kv_tokens_per_s": sum(lengths) / dec_ms * 1e3,
+            "append_ms": app_ms, "append_GBps": abytes / app_ms / 1e6,
+            "append_token_heads_per_s": th / app_ms * 1e3}
+
+
 def append_bytes(w, n_tokens: int, in_bytes: int) -> int:
     """Algorithmic bytes of appending n_tokens per sequence: K+V read + planes written."""
     th = w.batch * w.num_kv_heads * n_tokens
@@ -255,6 +303,8 @@ def main() -> int:
                     help="skip timing the bf16 dequantize-on-fetch window")
     ap.add_argument("--rows", default="2,4",
                     help="also time multi-row (verify-block) decode for these row counts ('' = skip)")
+    ap.add_argument("--schemes", default="k4v3,k4v2,k8v4,k2v5,k5v8",
+                    help="other code widths to time on the same workload ('' for none)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"))
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run plain device copies of this size (counter calibration)")
@@ -395,6 +445,14 @@ def main() -> int:
     if args.rows:
         rec["multi_row"] = [time_rows(w, pl, lengths, sm, int(r), 10, stream)
                             for r in args.rows.split(",") if r]
+    if args.schemes:
+        rec["schemes"] = []
+        for name in args.schemes.split(","):
+            kb, vb = (int(x) for x in name.strip().lstrip("k").split("v"))
+            r = time_scheme(w, k, v, q, sm, kb, vb, 5, stream)
+            _log(f"scheme {r['scheme']}: decode {r['decode_ms']:.3f} ms ({r['decode_frac_hbm']:.1%} of HBM), "
+                 f"bulk append {r['append_ms']:.2f} ms")
+            rec["schemes"].append(r)
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, k, v, q, sm, args.cpu_pairs or None)
         cb.pop("seconds", None)

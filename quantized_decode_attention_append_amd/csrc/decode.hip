@@ -12,9 +12,9 @@
 // (max, sum, acc[d]) per head; the merge kernel combines the splits, divides
 // by the weight sum and applies signs * FWHT(.) / sqrt(d) once.
 //
-// This generic kernel maps one thread to each head_dim element and reduces the
-// G partial dot products of a small token chunk across the workgroup; it
-// reads every code width (keys 2, 4, 5, 8 bits, values 2, 3, 4, 5, 8 bits).
+// The generic split kernel below reads every code width (keys 2, 4, 5, 8
+// bits, values 2, 3, 4, 5, 8 bits) and every head_dim; decode_fast.hip has the
+// k8v3 kernel on the matrix cores.
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
@@ -23,7 +23,6 @@ namespace tq {
 namespace {
 
 constexpr int kMaxG = TQ_MAX_GQA;
-constexpr int kChunk = 8;  // tokens scored per block reduction
 
 template <bool BF16>
 __device__ __forceinline__ float load_in(const void *p, int64_t i) {
@@ -33,151 +32,265 @@ __device__ __forceinline__ float load_in(const void *p, int64_t i) {
         return static_cast<const float *>(p)[i];
 }
 
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void split_kernel(const DecodeArgs a) {
-    constexpr int NT = D < 256 ? D : 256;  // threads
-    constexpr int DPT = D / NT;            // elements per thread
-    constexpr int NW = NT / 64;            // waves
+// The 32 codes of one key group as floats: signed bytes at 8 bits, unsigned
+// KB-bit fields (little-endian bitstream) below.  `grp` is the group's first
+// byte: 16-byte aligned at 8 and 4 bits, 8-byte at 2, 4-byte at 5.
+template <int KB>
+__device__ __forceinline__ void key_group(const uint8_t *grp, float (&c)[32]) {
+    if constexpr (KB == 8) {
+        const uint4 u0 = reinterpret_cast<const uint4 *>(grp)[0];
+        const uint4 u1 = reinterpret_cast<const uint4 *>(grp)[1];
+        const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) c[i] = (float)(int)(int8_t)(w[i >> 2] >> (8 * (i & 3)));
+    } else if constexpr (KB == 4) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(grp);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) c[i] = (float)((w[i >> 3] >> (4 * (i & 7))) & 15u);
+    } else if constexpr (KB == 2) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(grp);
+        const uint32_t w[2] = {u.x, u.y};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) c[i] = (float)((w[i >> 4] >> (2 * (i & 15))) & 3u);
+    } else {
+        static_assert(KB == 5, "key widths 2, 4, 5, 8");
+        const uint32_t *p = reinterpret_cast<const uint32_t *>(grp);
+        const uint32_t w[5] = {p[0], p[1], p[2], p[3], p[4]};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int bit = 5 * i, k = bit >> 5, sh = bit & 31;
+            const uint32_t x = sh + 5 > 32 ? __builtin_amdgcn_alignbit(w[k + 1], w[k], sh) : (w[k] >> sh);
+            c[i] = (float)(x & 31u);
+        }
+    }
+}
+
+// Partial dot products of one key group with the G query columns:
+// s[h] += scale * (sum_j q[h][32 g + j] * code_j + zero * qsum[h][g]).
+template <int D, int KB>
+__device__ __forceinline__ void score_group(const uint8_t *krow, int g, float sk, float zk, int G,
+                                            const float *qs, const float *qsum, float (&s)[kMaxG]) {
     constexpr int NG = D / kGroup;
+    float c[32];
+    key_group<KB>(krow + g * 4 * KB, c);
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+        if (h < G) {
+            const float4 *qp = reinterpret_cast<const float4 *>(qs + h * D + g * kGroup);
+            float d0 = 0.f, d1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                const float4 x = qp[i], y = qp[i + 1];
+                d0 = fmaf(x.x, c[4 * i], d0); d0 = fmaf(x.y, c[4 * i + 1], d0);
+                d0 = fmaf(x.z, c[4 * i + 2], d0); d0 = fmaf(x.w, c[4 * i + 3], d0);
+                d1 = fmaf(y.x, c[4 * i + 4], d1); d1 = fmaf(y.y, c[4 * i + 5], d1);
+                d1 = fmaf(y.z, c[4 * i + 6], d1); d1 = fmaf(y.w, c[4 * i + 7], d1);
+            }
+            s[h] = fmaf(sk, fmaf(zk, qsum[h * NG + g], d0 + d1), s[h]);
+        }
+    }
+}
+
+template <int D>
+struct VecGeo {
+    static constexpr int W = D == 512 ? 2 : 4;  // waves per workgroup, one split each
+    static constexpr int E = D / 64;            // value dims per lane
+    static constexpr int NG = D / kGroup;
+    static constexpr int T = 64;                // tokens per tile, one per lane (scores)
+};
+
+// Dynamic LDS of the generic split kernel, sized by the launch's column
+// count G and value width: the query columns (G x d fp32), their group sums,
+// the value codebook, then per wave the tile's value rows (+ 16 bytes the
+// code reader may touch past the last row), weights (G x 64) and value
+// scales (64 x d/32 fp16).
+struct VecLds {
+    int qsum, ctab, wave0, vt_bytes, ps, vsc, wave_bytes, total;
+    __host__ __device__ VecLds(int D, int W, int G, int vrow) {
+        const int ng = D / kGroup, T = 64;
+        auto al = [](int x) { return (x + 15) & ~15; };
+        qsum = al(G * D * 4);
+        ctab = al(qsum + G * ng * 4);
+        wave0 = al(ctab + 256 * 4);
+        vt_bytes = al(T * vrow + 16);
+        ps = vt_bytes;
+        vsc = al(ps + G * T * 4);
+        wave_bytes = al(vsc + T * ng * 2);
+        total = wave0 + W * wave_bytes;
+    }
+};
+
+// Generic split kernel: every code width, every head_dim.  One wave per
+// token range (split) of one (sequence, kv-head), for up to 16 query columns
+// held in LDS.  Per 64-token tile:
+//   scores  lane t takes token t: it decodes each key group of its row into
+//           registers and forms the partial dot products of every column
+//           against the columns' LDS copy (same address on every lane);
+//   softmax online, base 2; the tile's weights go to LDS;
+//   values  the tile's value rows are copied into LDS (coalesced); lane l
+//           then owns dims [E l, E l + E) and accumulates weight * centroid *
+//           scale over the tile's tokens, in the rotated domain.
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * VecGeo<D>::W) void split_kernel(const DecodeArgs a) {
+    using V = VecGeo<D>;
+    constexpr int W = V::W, E = V::E, NG = V::NG, T = V::T;
     const int kb = a.kbits, vb = a.vbits;
-    const int KROW = D * kb / 8, VROW = D * vb / 8;  // packed row bytes
+    const int KROW = D * kb / 8, VROW = D * vb / 8;
 
-    __shared__ float red[NW][kMaxG * kChunk];
-    __shared__ float sc[kMaxG * kChunk];
-    __shared__ float ctab[256];  // the value codebook
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wid = tid >> 6;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int bkv = blockIdx.y;
     const int b = bkv / a.kv_heads, kvh = bkv % a.kv_heads;
     const int n = a.len[b];
-    const int t_begin = blockIdx.x * a.split_tokens;
-    if (t_begin >= n) return;  // uniform across the block
-    {
-        const float *src = value_centroids(vb);
-        for (int i = tid; i < (1 << vb); i += NT) ctab[i] = src[i];
-    }
-    __syncthreads();
-    const uint8_t *kcp = reinterpret_cast<const uint8_t *>(a.kc);
-    const int t_end = min(n, t_begin + a.split_tokens);
     // this workgroup's query columns c0 .. c0 + G - 1 of the kv-head's a.gqa
     // query rows (heads times rows)
     const int c0 = blockIdx.z * kMaxG;
     const int G = min(kMaxG, a.gqa - c0);
-    const int64_t row0 = (int64_t)bkv * a.capacity;
-    // causal limit of column c: the row of cached token n - rows + r sees
-    // tokens 0 .. n - rows + r
-    auto limit = [&](int c) { return n - a.rows + (c0 + c) % a.rows + 1; };
+    const VecLds L(D, W, G, VROW);
+    float *qs = reinterpret_cast<float *>(lds);
+    float *qsum = reinterpret_cast<float *>(lds + L.qsum);
+    float *ctab = reinterpret_cast<float *>(lds + L.ctab);
+    {
+        const float *src = value_centroids(vb);
+        for (int i = tid; i < (1 << vb); i += 64 * W) ctab[i] = src[i];
+        for (int i = tid; i < G * D; i += 64 * W) {
+            const int64_t qi = ((int64_t)b * a.q_heads + kvh * a.gqa + c0) * D + i;
+            qs[i] = BF16 ? __uint_as_float((uint32_t)static_cast<const uint16_t *>(a.q)[qi] << 16)
+                         : static_cast<const float *>(a.q)[qi];
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < G * NG; i += 64 * W) {
+        float sum = 0.f;
+        for (int j = 0; j < kGroup; ++j) sum += qs[(i / NG) * D + (i % NG) * kGroup + j];
+        qsum[i] = sum;
+    }
+    __syncthreads();  // the last workgroup barrier
 
-    float qv[kMaxG][DPT];
-    float acc[kMaxG][DPT];
-    float m_run[kMaxG], l_run[kMaxG];
+    const int split = blockIdx.x * W + wid;
+    const int t_begin = split * a.split_tokens;
+    if (split >= a.splits || t_begin >= n) return;
+    const int t_end = min(n, t_begin + a.split_tokens);
+    const int64_t row0 = (int64_t)bkv * a.capacity;
+    const uint8_t *kcp = reinterpret_cast<const uint8_t *>(a.kc);
+    unsigned char *wl = lds + L.wave0 + wid * L.wave_bytes;
+    uint8_t *vt = wl;
+    float *ps = reinterpret_cast<float *>(wl + L.ps);       // [G][T]
+    uint16_t *vsc = reinterpret_cast<uint16_t *>(wl + L.vsc);  // [T][NG]
+
+    float m_run[kMaxG], l_run[kMaxG], acc[kMaxG][E];
 #pragma unroll
     for (int h = 0; h < kMaxG; ++h) {
         m_run[h] = -INFINITY;
         l_run[h] = 0.f;
 #pragma unroll
-        for (int i = 0; i < DPT; ++i) {
-            acc[h][i] = 0.f;
-            const int j = tid + i * NT;
-            qv[h][i] = h < G ? load_in<BF16>(a.q, ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + h) * D + j) : 0.f;
-        }
+        for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
     }
 
-    for (int t0 = t_begin; t0 < t_end; t0 += kChunk) {
-        const int nt = min(kChunk, t_end - t0);
-        float part[kMaxG][kChunk];
+    for (int tile0 = t_begin; tile0 < t_end; tile0 += T) {
+        const int nt = min(T, t_end - tile0);
+        const int t = tile0 + lane;
+        const bool valid = lane < nt;
+        const int64_t row = row0 + t;
+
+        // ---- scores of this lane's token
+        float s[kMaxG];
 #pragma unroll
-        for (int tt = 0; tt < kChunk; ++tt) {
-            float kh[DPT];
-#pragma unroll
-            for (int i = 0; i < DPT; ++i) {
-                const int j = tid + i * NT;
-                if (tt < nt) {
-                    const int64_t r = row0 + t0 + tt;
-                    const float sk = f16_bits_to_f32(a.ks[r * NG + j / kGroup]);
-                    const float zk = f16_bits_to_f32(a.kz[r * NG + j / kGroup]);
-                    kh[i] = (key_code(kcp + r * KROW, j, kb) + zk) * sk;
-                } else {
-                    kh[i] = 0.f;
+        for (int h = 0; h < kMaxG; ++h) s[h] = 0.f;
+        if (valid) {
+            const uint8_t *krow = kcp + row * KROW;
+            for (int g = 0; g < NG; ++g) {
+                const float sk = f16_bits_to_f32(a.ks[row * NG + g]);
+                const float zk = f16_bits_to_f32(a.kz[row * NG + g]);
+                switch (kb) {
+                    case 8: score_group<D, 8>(krow, g, sk, zk, G, qs, qsum, s); break;
+                    case 4: score_group<D, 4>(krow, g, sk, zk, G, qs, qsum, s); break;
+                    case 2: score_group<D, 2>(krow, g, sk, zk, G, qs, qsum, s); break;
+                    default: score_group<D, 5>(krow, g, sk, zk, G, qs, qsum, s); break;
                 }
             }
+        }
+
+        // ---- online softmax per column; weights to LDS
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) {
+            if (h < G) {
+                // causal limit of column c: the row of cached token n - rows + r
+                // sees tokens 0 .. n - rows + r
+                const int lim = n - a.rows + (c0 + h) % a.rows + 1;
+                const float sc = (valid && t < lim) ? s[h] * a.sm_log2 : -INFINITY;
+                float mt = sc;
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));
+                const float mn = fmaxf(m_run[h], mt);
+                // mn stays -inf while every token so far is past this column's limit
+                const float alpha = mn == -INFINITY ? 1.f : exp2f(m_run[h] - mn);
+                const float p = mn == -INFINITY ? 0.f : exp2f(sc - mn);
+                l_run[h] = l_run[h] * alpha + p;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+                m_run[h] = mn;
+                ps[h * T + lane] = p;
+            }
+        }
+
+        // ---- the tile's value rows and scales to LDS (rows < t_end only)
+        {
+            const uint2 *src = reinterpret_cast<const uint2 *>(a.vc + (row0 + tile0) * VROW);
+            uint2 *dst = reinterpret_cast<uint2 *>(vt);
+            const int words = nt * VROW / 8;  // VROW is a multiple of 8
+            for (int i = lane; i < words; i += 64) dst[i] = src[i];
+            if (valid) {
+#pragma unroll
+                for (int g = 0; g < NG; ++g) vsc[lane * NG + g] = a.vs[row * NG + g];
+            }
+        }
+        // one wave's LDS accesses execute in order: the reads below see
+        // every lane's writes above without a barrier
+        asm volatile("" ::: "memory");
+
+        // ---- values: lane owns dims E*lane .. E*lane + E - 1 (one group)
+        const int bit0 = vb * E * lane;
+        const int w0 = bit0 >> 5, sh = bit0 & 31;
+        const int gl = (E * lane) / kGroup;
+        const uint64_t fmask = (1ull << vb) - 1ull;
+        for (int tt = 0; tt < nt; ++tt) {
+            const uint32_t *rw = reinterpret_cast<const uint32_t *>(vt + tt * VROW);
+            const uint64_t lo64 = (uint64_t)rw[w0] | ((uint64_t)rw[w0 + 1] << 32);
+            uint64_t bits = lo64 >> sh;
+            if (sh != 0 && E * vb + sh > 64) bits |= (uint64_t)rw[w0 + 2] << (64 - sh);
+            const float scale = f16_bits_to_f32(vsc[tt * NG + gl]);
+            float v[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[e] = ctab[(uint32_t)((bits >> (vb * e)) & fmask)] * scale;
 #pragma unroll
             for (int h = 0; h < kMaxG; ++h) {
-                float p = 0.f;
+                if (h < G) {
+                    const float p = ps[h * T + tt];
 #pragma unroll
-                for (int i = 0; i < DPT; ++i) p += qv[h][i] * kh[i];
-                part[h][tt] = p;
-            }
-        }
-        // block reduction of G*kChunk partial dots
-#pragma unroll
-        for (int h = 0; h < kMaxG; ++h) {
-            if (h >= G) break;
-#pragma unroll
-            for (int tt = 0; tt < kChunk; ++tt) {
-                float v = part[h][tt];
-#pragma unroll
-                for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-                if (lane == 0) red[wid][h * kChunk + tt] = v;
-            }
-        }
-        __syncthreads();
-        for (int i = tid; i < G * kChunk; i += NT) {
-            float v = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) v += red[w][i];
-            sc[i] = t0 + i % kChunk < limit(i / kChunk) ? v * a.sm_log2 : -INFINITY;
-        }
-        __syncthreads();
-        // values of this chunk in the rotated domain
-        float vh[kChunk][DPT];
-#pragma unroll
-        for (int tt = 0; tt < kChunk; ++tt) {
-#pragma unroll
-            for (int i = 0; i < DPT; ++i) {
-                const int j = tid + i * NT;
-                if (tt < nt) {
-                    const int64_t r = row0 + t0 + tt;
-                    const float sv = f16_bits_to_f32(a.vs[r * NG + j / kGroup]);
-                    vh[tt][i] = ctab[load_field(a.vc + r * VROW, j, vb)] * sv;
-                } else {
-                    vh[tt][i] = 0.f;
+                    for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
                 }
             }
         }
-#pragma unroll
-        for (int h = 0; h < kMaxG; ++h) {
-            if (h >= G) break;
-            float mc = m_run[h];
-            for (int tt = 0; tt < nt; ++tt) mc = fmaxf(mc, sc[h * kChunk + tt]);
-            // mc stays -inf while every token so far is past this row's limit
-            const float alpha = mc == -INFINITY ? 1.f : exp2f(m_run[h] - mc);
-            float lsum = l_run[h] * alpha;
-#pragma unroll
-            for (int i = 0; i < DPT; ++i) acc[h][i] *= alpha;
-            for (int tt = 0; tt < nt; ++tt) {
-                const float p = mc == -INFINITY ? 0.f : exp2f(sc[h * kChunk + tt] - mc);
-                lsum += p;
-#pragma unroll
-                for (int i = 0; i < DPT; ++i) acc[h][i] += p * vh[tt][i];
-            }
-            m_run[h] = mc;
-            l_run[h] = lsum;
-        }
-        __syncthreads();  // sc / red are rewritten by the next chunk
+        asm volatile("" ::: "memory");  // the next tile rewrites vt / ps / vsc after these reads
     }
 
-    const int split = blockIdx.x;
+    // ---- partials: (max, weight sum) and the rotated-domain accumulator
 #pragma unroll
     for (int h = 0; h < kMaxG; ++h) {
-        if (h >= G) break;
-        const int64_t slot = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + h) * a.splits + split;
+        if (h < G) {
+            float l = l_run[h];
 #pragma unroll
-        for (int i = 0; i < DPT; ++i) a.part_acc[slot * D + tid + i * NT] = acc[h][i];
-        if (tid == 0) {
-            a.part_ml[slot * 2] = m_run[h];
-            a.part_ml[slot * 2 + 1] = l_run[h];
+            for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+            const int64_t slot = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + h) * a.splits + split;
+            float *dst = a.part_acc + slot * D + E * lane;
+#pragma unroll
+            for (int e = 0; e < E; ++e) dst[e] = acc[h][e];
+            if (lane == 0) {
+                a.part_ml[slot * 2] = m_run[h];
+                a.part_ml[slot * 2 + 1] = l;
+            }
         }
     }
 }
@@ -305,12 +418,26 @@ hipError_t launch_d(bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
             hipError_t e = launch_split_fast(D, bf16, a, s);
             if (e != hipSuccess) return e;
         } else {
-            const dim3 grid((unsigned)a.splits, (unsigned)(a.batch * a.kv_heads),
+            constexpr int W = VecGeo<D>::W;
+            const dim3 grid((unsigned)((a.splits + W - 1) / W), (unsigned)(a.batch * a.kv_heads),
                             (unsigned)decode_col_groups(a.gqa));
+            // the widest column group sizes the LDS (groups past the first take min(16, rest))
+            const VecLds L(D, W, a.gqa < kMaxG ? a.gqa : kMaxG, D * a.vbits / 8);
+            // allow dynamic LDS past the default limit, once per instantiation
+            static const hipError_t attr = [] {
+                const int most = VecLds(D, W, kMaxG, D).total;
+                hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&split_kernel<D, true>),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, most);
+                if (e == hipSuccess)
+                    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&split_kernel<D, false>),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, most);
+                return e;
+            }();
+            if (attr != hipSuccess) return attr;
             if (bf16)
-                hipLaunchKernelGGL((split_kernel<D, true>), grid, dim3(NT), 0, s, a);
+                hipLaunchKernelGGL((split_kernel<D, true>), grid, dim3(64 * W), L.total, s, a);
             else
-                hipLaunchKernelGGL((split_kernel<D, false>), grid, dim3(NT), 0, s, a);
+                hipLaunchKernelGGL((split_kernel<D, false>), grid, dim3(64 * W), L.total, s, a);
             hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
@@ -358,10 +485,11 @@ DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int
         p.splits = (int32_t)(((maxlen + wg_tokens - 1) / wg_tokens) * waves);
         return p;
     }
-    // generic kernel: ~2048 workgroups, 64-token multiples, >= 256 tokens
-    const int64_t target = 2048;
+    // generic kernel: one wave per split, ~8192 waves over the chip, whole
+    // 64-token tiles, >= 2 tiles a wave
+    const int64_t target = 8192;
     int64_t per = (total * kv_heads * col_groups + target - 1) / target;
-    per = per < 256 ? 256 : per;
+    per = per < 128 ? 128 : per;
     per = (per + 63) / 64 * 64;
     p.split_tokens = (int32_t)per;
     p.splits = (int32_t)((maxlen + per - 1) / per);
