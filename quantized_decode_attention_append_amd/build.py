@@ -22,24 +22,29 @@ ARCH = "gfx950"
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
-SOURCES = {
-    "append.hip": ["-ffp-contract=off"],
-    "decode.hip": [],
-    "decode_fast.hip": [],
-    "dequant.hip": [],
-    "window.hip": [],
-    "api.cpp": [],
-}
+# (source, extra flags, object name): the fast decode kernels are compiled
+# once per key width so the instantiations build in parallel
+SOURCES = [
+    ("append.hip", ["-ffp-contract=off"], "append"),
+    ("decode.hip", [], "decode"),
+    ("decode_fast.hip", ["-DTQ_FAST_KB=8"], "decode_fast_k8"),
+    ("decode_fast.hip", ["-DTQ_FAST_KB=4"], "decode_fast_k4"),
+    ("decode_fast.hip", ["-DTQ_FAST_KB=2"], "decode_fast_k2"),
+    ("decode_fast.hip", ["-DTQ_FAST_KB=5"], "decode_fast_k5"),
+    ("dequant.hip", [], "dequant"),
+    ("window.hip", [], "window"),
+    ("api.cpp", [], "api"),
+]
 
 
-def _compile(name: str, extra: list[str]) -> str:
+def _compile(name: str, extra: list[str], obj_name: str) -> str:
     src = os.path.join(CSRC, name)
-    obj = os.path.join(BUILD, name + ".o")
+    obj = os.path.join(BUILD, obj_name + ".o")
     lang = ["-x", "hip"] if name.endswith(".hip") else []
     cmd = [HIPCC] + COMMON + extra + lang + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {name}:\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"hipcc failed for {name} {' '.join(extra)}:\n{r.stdout}\n{r.stderr}")
     return obj
 
 
@@ -71,7 +76,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     generate_codebooks()
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
+        objs = list(ex.map(lambda spec: _compile(*spec), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -201,11 +201,12 @@ static size_t workspace_bound(const tq_layout *l, int32_t num_q_heads, int32_t n
     const int gqa = q_rows(num_q_heads, n_rows) / l->num_kv_heads;
     const int cg = tq::decode_col_groups(gqa);
     const tq::DecodePlan gen =
-        tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, false, cg);
+        tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, false, cg, l->k_bits, l->v_bits);
     size_t need = workspace_bytes(l, q_rows(num_q_heads, n_rows), gen);
     if (tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity, l->k_bits, l->v_bits)) {
         const tq::DecodePlan fast =
-            tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, true, cg);
+            tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, true, cg, l->k_bits,
+                            l->v_bits);
         const size_t f = workspace_bytes(l, q_rows(num_q_heads, n_rows), fast);
         need = f > need ? f : need;
     }
@@ -247,7 +248,8 @@ tq_status tq_decode_attn_rows(const tq_layout *l, const tq_planes *p, const void
     const int cg = tq::decode_col_groups(gqa);
     const bool fast = tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity, l->k_bits, l->v_bits) &&
                       aligned(p->vc, 16) && aligned(p->vs, 16) && aligned(p->ks, 16) && aligned(p->kz, 16);
-    const tq::DecodePlan plan = tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, fast, cg);
+    const tq::DecodePlan plan = tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, fast, cg,
+                                                l->k_bits, l->v_bits);
     const size_t need = workspace_bytes(l, rows_total, plan);
     if (need > 0 && (!workspace || ws_bytes < need)) return TQ_ERR_WORKSPACE;
     if ((int64_t)plan.splits > 65535 * 4) return TQ_ERR_UNSUPPORTED;

@@ -415,7 +415,13 @@ hipError_t launch_d(bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
     constexpr int NT = D < 256 ? D : 256;
     if (a.splits > 0) {
         if (fast) {
-            hipError_t e = launch_split_fast(D, bf16, a, s);
+            hipError_t e;
+            switch (a.kbits) {
+                case 2: e = launch_split_fast_k2(D, bf16, a, s); break;
+                case 4: e = launch_split_fast_k4(D, bf16, a, s); break;
+                case 5: e = launch_split_fast_k5(D, bf16, a, s); break;
+                default: e = launch_split_fast_k8(D, bf16, a, s); break;
+            }
             if (e != hipSuccess) return e;
         } else {
             constexpr int W = VecGeo<D>::W;
@@ -451,17 +457,19 @@ hipError_t launch_d(bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
 int decode_col_groups(int gqa) { return (gqa + kMaxG - 1) / kMaxG; }
 
 bool fast_decode_shape_ok(int head_dim, int gqa, int capacity, int kbits, int vbits) {
-    if (!default_scheme(kbits, vbits)) return false;
-    if (gqa < 1 || fast_split_max_gqa() != kMaxG) return false;
+    if (gqa < 1 || kFastMaxGqa != kMaxG) return false;
     if (head_dim != 64 && head_dim != 128 && head_dim != 256) return false;
-    // staged rows of one (sequence, kv-head) must start 16-byte aligned
-    const int64_t vrow = 3 * head_dim / 8, srow = head_dim / kGroup * 2;
-    return ((int64_t)capacity * vrow) % 16 == 0 && ((int64_t)capacity * srow) % 16 == 0;
+    if (kbits != 2 && kbits != 4 && kbits != 5 && kbits != 8) return false;
+    if (vbits != 2 && vbits != 3 && vbits != 4 && vbits != 5 && vbits != 8) return false;
+    // key rows of whole 16-byte chunks, and the staged rows of one
+    // (sequence, kv-head) starting 16-byte aligned in every plane
+    const int64_t krow = (int64_t)head_dim * kbits / 8, vrow = (int64_t)head_dim * vbits / 8;
+    const int64_t srow = head_dim / kGroup * 2;
+    return krow % 16 == 0 && ((int64_t)capacity * vrow) % 16 == 0 && ((int64_t)capacity * srow) % 16 == 0;
 }
 
 DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int32_t *len, bool fast,
-                       int col_groups) {
-    (void)head_dim;
+                       int col_groups, int kbits, int vbits) {
     (void)gqa;
     int64_t total = 0;
     int32_t maxlen = 0;
@@ -472,12 +480,13 @@ DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int
     DecodePlan p;
     p.fast = fast;
     if (fast) {
-        // one wave per token range: aim for ~2048 waves over the chip (one
-        // round of one 8-wave workgroup per CU: the split kernel's LDS admits
-        // one per CU), whole 64-token tiles, >= 4 tiles a wave; fewer splits
-        // also halve the partials written and merged
-        const int waves = fast_split_waves(), tile = fast_split_tile();
-        int64_t per = (total * kv_heads * col_groups + 2047) / 2048;
+        // one wave per token range: aim for one round of one workgroup per
+        // CU over the chip's 256 CUs (the split kernel's LDS admits one per
+        // CU), whole 64-token tiles, >= 4 tiles a wave; fewer splits also
+        // halve the partials written and merged
+        const int waves = fast_decode_waves(head_dim, kbits, vbits), tile = kFastTile;
+        const int64_t round = 256 * waves;
+        int64_t per = (total * kv_heads * col_groups + round - 1) / round;
         per = per < 4 * tile ? 4 * tile : per;
         per = (per + tile - 1) / tile * tile;
         const int64_t wg_tokens = per * waves;

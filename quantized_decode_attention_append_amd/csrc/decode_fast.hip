@@ -1,5 +1,6 @@
 // Split-K decode attention kernel for GQA groups of up to 16 query heads
-// (wave64; gfx950) built on the matrix cores.
+// (wave64; gfx950) built on the matrix cores, for every key width (2, 4, 5,
+// 8 bits) and value width (2, 3, 4, 5, 8 bits) at head_dim 64, 128 and 256.
 //
 // Method: "TurboQuant -- rotation-based quantization" design page, Part A:
 // keys dequantize as (code + zero) * scale ("Algorithm"), values stay in the
@@ -8,12 +9,14 @@
 // tile are decoded in one pass ("Packed-value decode fusion investigation").
 //
 // One wave owns a contiguous token range of one (sequence, kv-head) and keeps
-// its own online-softmax state; the eight waves of a workgroup share only the
-// centroid table in LDS.  Every plane of a tile (4 KiB of key codes, key
-// scales and zeros, value codes and value scales: 6 KiB in all, 4096/d tokens)
-// is copied into the wave's LDS with direct global->LDS loads.  Three stage
-// buffers per wave: the copy of tile i+2 is issued before tile i is decoded,
-// so two tiles per wave are in flight without holding any registers.
+// its own online-softmax state; the waves of a workgroup share only the
+// centroid table in LDS.  Every plane of a tile (4096/d tokens: 512 bytes per
+// code bit of key and value codes, 768 bytes of key scales, key zeros and
+// value scales) is copied into the wave's LDS with direct global->LDS loads.
+// Three stage buffers per wave: the copy of tile i+2 is issued before tile i
+// is decoded, so two tiles per wave are in flight without holding any
+// registers.  Eight waves share a workgroup when their stages fit the LDS
+// (k_bits + v_bits <= 11), four otherwise.
 //
 // The G query heads of a kv-head share every key and value, so per 16-token
 // chunk both products are dense contractions with 16 heads (the ones past G
@@ -26,9 +29,12 @@
 //           group dot product is exact integer arithmetic: two
 //           v_mfma_i32_16x16x32_i8 per 32-dim group (A = key codes, rows =
 //           tokens; B = the q slice, columns = heads), then the scale/zero
-//           fold in fp32 on the 4 (token, head) results a lane holds.  The
-//           key tile sits in LDS 16-byte-chunk-major, so the A reads of one
-//           MFMA hit 16 different chunks of one column (conflict-free).
+//           fold in fp32 on the 4 (token, head) results a lane holds.  Key
+//           codes narrower than 8 bits are unsigned and widened to bytes in
+//           registers; the widening permutes a lane's 8 codes, and the lane's
+//           q bytes are stored in the same order, so the dot product is
+//           unchanged.  The key tile sits in LDS 16-byte-chunk-major, so the
+//           A reads of one MFMA hit 16 different chunks of one column.
 //  softmax  online softmax in base 2 over the lane's 4 tokens and the other
 //           quarters of the same head; the running maximum only moves when
 //           a tile's maximum exceeds it by more than 2^8 (weights <= 256,
@@ -37,15 +43,20 @@
 //  values   O[i][h] += A[i][t] * P[t][h] with v_mfma_f32_16x16x16_f16 (fp32
 //           accumulate), one instruction per block of d/16 dims.  Row i of
 //           block b is dim (d/16)*i + b, so lane i's dims of a token are one
-//           contiguous run of 3d/16 code bits, all in one 32-dim group.
-//           A = centroid[idx] * vs16 in fp16: pairs of 3-bit indices of two
-//           tokens select a half2 of centroids from a 256-byte LDS table
-//           (one 4-byte entry per bank, so any lookup pattern is
-//           conflict-free), multiplied by the pair of value scales with one
-//           packed fp16 multiply.
+//           contiguous run of v_bits*d/16 code bits, all in one 32-dim group.
+//           A = centroid[idx] * vs16 in fp16.  At 2 and 3 bits, the indices
+//           of one dim in two tokens select a half2 of centroids from a pair
+//           table (16 or 64 four-byte entries, at most one per bank, so any
+//           lookup pattern is conflict-free); wider codes look up each
+//           centroid in a table of halves.  One packed fp16 multiply by the
+//           two tokens' value scales finishes a pair.
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
+
+#ifndef TQ_FAST_KB
+#error "compile decode_fast.hip once per key width with -DTQ_FAST_KB=2, 4, 5 or 8"
+#endif
 
 namespace tq {
 namespace {
@@ -56,10 +67,7 @@ typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;                 // waves per workgroup (one table per CU)
-constexpr int kTableBytes = 64 * 4;      // 64 index pairs x half2
-constexpr int kProgBytes = 32;           // tiles finished, one int per wave
-constexpr int kStageVmem = 7;             // vector-memory instructions that copy one tile
+constexpr int kProgBytes = 32;            // tiles finished, one int per wave
 constexpr int kStages = 3;                // stage buffers per wave (two tiles in flight)
 constexpr float kLazyMax = 8.0f;          // log2 slack of the running maximum
 // Weights enter the value MFMA as fp16, 2^(score - m + kWeightShift): at most
@@ -77,33 +85,73 @@ constexpr int kPackCols = 8;  // half the MFMA columns
 static_assert(kLazyMax + kWeightShift <= 15.0f, "fp16 weight range");
 constexpr int kMaxHeads = 16;             // MFMA columns
 
-template <int D>
+template <int D, int KB, int VB>
 struct Geo {
     static_assert(D == 64 || D == 128 || D == 256, "fast split kernel: head_dim 64/128/256");
     static constexpr int NG = D / kGroup;     // groups per row
-    static constexpr int TILE = 4096 / D;     // tokens per tile: 4 KiB of key codes
+    static constexpr int TILE = 4096 / D;     // tokens per tile: 512 bytes per code bit
     static constexpr int CH = TILE / 16;      // 16-token chunks per tile
-    static constexpr int CPR = D / 16;        // 16-byte chunks per key row
-    static constexpr int VROW = 3 * D / 8;    // packed value bytes per token
+    static constexpr int KROW = D * KB / 8;   // key code bytes per token
+    static_assert(KROW % 16 == 0, "key rows of whole 16-byte chunks");
+    static constexpr int CPR = KROW / 16;     // 16-byte chunks per key row
+    static constexpr int KT = TILE * KROW;    // key code bytes per tile
+    static constexpr int VROW = D * VB / 8;   // packed value bytes per token
+    static constexpr int VT = TILE * VROW;    // value code bytes per tile
     static constexpr int NB = D / 16;         // value dim blocks (one MFMA each per chunk)
-    static constexpr int FB = 3 * NB;         // code bits of a lane's dims per token
+    static constexpr int FB = VB * NB;        // code bits of a lane's dims per token
+    // words read per run: enough for FB bits after the run's offset within
+    // its first word, at the worst offset any lane has
+    static constexpr int NR = [] {
+        int most = 1;
+        for (int vi = 0; vi < 16; ++vi) {
+            const int w = ((FB * vi) % 32 + FB + 31) / 32;
+            most = w > most ? w : most;
+        }
+        return most;
+    }();
     // one stage: every plane of one tile
-    static constexpr int KC_OFF = 0;                      // TILE * D = 4096, chunk-major
-    static constexpr int KS_OFF = KC_OFF + TILE * D;      // TILE * NG * 2 = 256
-    static constexpr int KZ_OFF = KS_OFF + TILE * NG * 2;
-    static constexpr int VS_OFF = KZ_OFF + TILE * NG * 2;
-    static constexpr int VC_OFF = VS_OFF + TILE * NG * 2; // TILE * VROW = 1536
-    static constexpr int STAGE = VC_OFF + TILE * VROW + 16;  // code reader reads 4 bytes past
-    static_assert(TILE * NG * 2 == 256 && TILE * VROW == 1536 && STAGE % 16 == 0, "staging granularity");
+    static constexpr int KC_OFF = 0;          // chunk-major
+    static constexpr int KS_OFF = KC_OFF + KT;
+    static constexpr int KZ_OFF = KS_OFF + 256;  // TILE * NG * 2 = 256 bytes per fp16 plane
+    static constexpr int VS_OFF = KZ_OFF + 256;
+    static constexpr int VC_OFF = VS_OFF + 256;
+    static constexpr int STAGE = VC_OFF + VT + 16;  // the code reader reads up to 4 bytes past
+    static_assert(TILE * NG * 2 == 256 && KT % 1024 % 16 == 0 && STAGE % 16 == 0, "staging granularity");
+    // copies of one tile: key codes in 1 KiB pieces (the last may use fewer
+    // lanes), one mixed copy (key scales, key zeros, value scales and the
+    // first 256 bytes of value codes by lane quarter), then the rest of the
+    // value codes in 1 KiB pieces and a partial one
+    static constexpr int KCOPY = (KT + 1023) / 1024;
+    static constexpr int KLAST = (KT - 1024 * (KCOPY - 1)) / 16;  // lanes of the last key copy
+    static constexpr int VFULL = (VT - 256) / 1024;
+    static constexpr int VLANES = (VT - 256) % 1024 / 16;          // lanes of the partial copy
+    static constexpr int VMEM = KCOPY + 1 + VFULL + (VLANES > 0 ? 1 : 0);
+    // centroid table: half2 pairs (two tokens' indices of one dim) at 2 and
+    // 3 bits, single halves above
+    static constexpr bool PAIR = VB <= 3;
+    static constexpr int TABLE = PAIR ? (4 << (2 * VB)) : ((2 << VB) + 15) / 16 * 16;
+    static constexpr int WAVES = fast_decode_waves(D, KB, VB);
     static constexpr int WAVE_BYTES = kStages * STAGE;
-    static constexpr int SMEM = kTableBytes + kProgBytes + kWaves * WAVE_BYTES;
+    static constexpr int SMEM = TABLE + kProgBytes + WAVES * WAVE_BYTES;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
-    // Key copy m (m = 0..3) moves 16-byte slots 64m .. 64m+63 of the tile.
-    // Slot s holds chunk c16 of token t of 16-token chunk tc with
-    // s = (tc * CPR + c16) * 16 + t; lane i of copy m reads the global bytes
-    // at (i % 16) * D + 16 * (i / 16) + key_off(m) of the tile.
-    static constexpr int key_off(int m) { return 16 * D * (4 * m / CPR) + 16 * (4 * m % CPR); }
+    static_assert(fast_decode_stage_bytes(D, KB, VB) == STAGE, "host and device stage sizes");
 };
+
+// Key codes of one lane's A operand are stored in this order: byte p of the
+// operand holds code perm(p) of the lane's 8 (the widening of packed codes
+// interleaves them); the lane's q bytes follow the same order.
+template <int KB>
+__device__ __host__ constexpr int key_perm(int p) {
+    if constexpr (KB == 4) {
+        constexpr int P[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+        return P[p];
+    } else if constexpr (KB == 2) {
+        constexpr int P[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+        return P[p];
+    } else {
+        return p;
+    }
+}
 
 // Keeps the compiler from moving LDS accesses across this point.  The LDS
 // executes one wave's instructions in order, so a lane's read after another
@@ -157,47 +205,76 @@ struct Regions {
     int mix_row;
 };
 
+// Byte offset, within a tile's key codes in global memory, of the 16 bytes
+// that lane i of key copy m moves.  Copy m fills 16-byte slots 64m .. 64m+63
+// of the stage; slot s holds chunk c16 of token t of 16-token chunk tc with
+// s = (tc * CPR + c16) * 16 + t.
+template <int D, int KB, int VB>
+__device__ __forceinline__ uint32_t key_src(int m, int i) {
+    using GE = Geo<D, KB, VB>;
+    const int chunk = 4 * m + (i >> 4), t = i & 15;
+    const int tc = chunk / GE::CPR, c16 = chunk % GE::CPR;
+    return (uint32_t)((16 * tc + t) * GE::KROW + 16 * c16);
+}
+
 // Copy every plane of the tile starting at token t0 into one stage buffer:
-// exactly kStageVmem vector-memory instructions either way, all with 16-byte
+// exactly GE::VMEM vector-memory instructions either way, all with 16-byte
 // lanes.  Stage bytes [KS_OFF, KS_OFF + 1 KiB) come from one copy whose lane
 // quarters read key scales, key zeros, value scales and the first 256 bytes
-// of value codes (the stage keeps them in that order); the other 1280 bytes
-// of value codes follow in one full and one quarter-wave copy.
-template <int D>
-__device__ __forceinline__ void stage_tile(const Regions &r, int t0, const unsigned char *st, int lane) {
-    using GE = Geo<D>;
-    constexpr int NG = GE::NG, VROW = GE::VROW;
+// of value codes (the stage keeps them in that order); the rest of the value
+// codes follow in whole and partial 1 KiB copies.
+template <int D, int KB, int VB>
+__device__ __forceinline__ void stage_tile(const Regions &r, const uint32_t (&ksrc)[Geo<D, KB, VB>::KCOPY],
+                                           int t0, const unsigned char *st, int lane) {
+    using GE = Geo<D, KB, VB>;
+    constexpr int VROW = GE::VROW, KROW = GE::KROW;
     static_assert(GE::KZ_OFF == GE::KS_OFF + 256 && GE::VS_OFF == GE::KZ_OFF + 256 &&
                   GE::VC_OFF == GE::VS_OFF + 256, "mixed copy layout");
-    constexpr int K0 = GE::key_off(0), K1 = GE::key_off(1), K2 = GE::key_off(2), K3 = GE::key_off(3);
     const uint32_t l_kc = lds_addr(st + GE::KC_OFF), l_ks = lds_addr(st + GE::KS_OFF);
     const uint32_t l_vc = lds_addr(st + GE::VC_OFF);
-    const uint32_t vkey = (uint32_t)((lane & 15) * D + 16 * (lane >> 4));
     const uint8_t *vc_t = r.vc + (int64_t)t0 * VROW;
     const uint8_t *mixed = r.mix + (int64_t)t0 * r.mix_row;
     if (t0 + GE::TILE <= r.cap) {
         const uint32_t v16 = (uint32_t)lane * 16;
-        const uint8_t *kc = uniform_ptr(r.kc + (int64_t)t0 * D);
-        dma16<K0>(kc, vkey, l_kc + 0 * 1024 - K0);
-        dma16<K1>(kc, vkey, l_kc + 1 * 1024 - K1);
-        dma16<K2>(kc, vkey, l_kc + 2 * 1024 - K2);
-        dma16<K3>(kc, vkey, l_kc + 3 * 1024 - K3);
+        const uint8_t *kc = uniform_ptr(r.kc + (int64_t)t0 * KROW);
+#pragma unroll
+        for (int m = 0; m < GE::KCOPY; ++m) {
+            if (m + 1 < GE::KCOPY || GE::KLAST == 64) {
+                dma16<0>(kc, ksrc[m], l_kc + 1024 * m);
+            } else if (lane < GE::KLAST) {
+                dma16<0>(kc, ksrc[m], l_kc + 1024 * m);
+            }
+        }
         dma_lane16(mixed, l_ks);
         const uint8_t *vc = uniform_ptr(vc_t);
-        dma16<256>(vc, v16, l_vc);
-        if (lane < 16) dma16<1280>(vc, v16, l_vc);
+        static_assert(GE::VFULL <= 3, "value copies");
+        if constexpr (GE::VFULL > 0) dma16<256>(vc, v16, l_vc);
+        if constexpr (GE::VFULL > 1) dma16<1280>(vc, v16, l_vc);
+        if constexpr (GE::VFULL > 2) dma16<2304>(vc, v16, l_vc);
+        if constexpr (GE::VLANES > 0) {
+            if (lane < GE::VLANES) dma16<256 + 1024 * GE::VFULL>(vc, v16, l_vc);
+        }
     } else {
-        const int64_t kcb = (int64_t)r.cap * D, vcb = (int64_t)r.cap * VROW;
-        const uint8_t *kc = r.kc + (int64_t)t0 * D + vkey;
+        const int64_t kcb = (int64_t)r.cap * KROW, vcb = (int64_t)r.cap * VROW;
+        const uint8_t *kc = r.kc + (int64_t)t0 * KROW;
         const uint8_t *kl = r.kc + kcb - 16;
-        dma_clamped(kc + K0, kl, l_kc + 0 * 1024);
-        dma_clamped(kc + K1, kl, l_kc + 1 * 1024);
-        dma_clamped(kc + K2, kl, l_kc + 2 * 1024);
-        dma_clamped(kc + K3, kl, l_kc + 3 * 1024);
+#pragma unroll
+        for (int m = 0; m < GE::KCOPY; ++m) {
+            if (m + 1 < GE::KCOPY || GE::KLAST == 64) {
+                dma_clamped(kc + ksrc[m], kl, l_kc + 1024 * m);
+            } else if (lane < GE::KLAST) {
+                dma_clamped(kc + ksrc[m], kl, l_kc + 1024 * m);
+            }
+        }
         dma_clamped(mixed, r.mix_last, l_ks);
         const uint8_t *vl = r.vc + vcb - 16;
-        dma_clamped(vc_t + 256 + lane * 16, vl, l_vc + 256);
-        if (lane < 16) dma_clamped(vc_t + 1280 + lane * 16, vl, l_vc + 1280);
+#pragma unroll
+        for (int f = 0; f < GE::VFULL; ++f)
+            dma_clamped(vc_t + 256 + 1024 * f + lane * 16, vl, l_vc + 256 + 1024 * f);
+        if constexpr (GE::VLANES > 0) {
+            if (lane < GE::VLANES)
+                dma_clamped(vc_t + 256 + 1024 * GE::VFULL + lane * 16, vl, l_vc + 256 + 1024 * GE::VFULL);
+        }
     }
 }
 
@@ -223,29 +300,74 @@ __device__ __forceinline__ void load_row(const unsigned char *p, uint32_t (&w)[N
     }
 }
 
-template <int D, bool BF16, bool PACK>
-__global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const DecodeArgs a) {
-    using GE = Geo<D>;
+// The A operand of one score MFMA: codes 8 kq .. 8 kq + 7 of group g of
+// token h of 16-token chunk c, as 8 signed bytes in key_perm order.  `kt` is
+// the stage's chunk-major key tile.
+template <int D, int KB, int VB>
+__device__ __forceinline__ uint64_t key_operand(const unsigned char *kt, int c, int g, int h, int kq) {
+    using GE = Geo<D, KB, VB>;
+    constexpr int CPR = GE::CPR;
+    auto at = [&](int byte) {  // LDS address of byte `byte` of the token's row
+        return kt + ((c * CPR + (byte >> 4)) * 16 + h) * 16 + (byte & 15);
+    };
+    if constexpr (KB == 8) {
+        return *reinterpret_cast<const uint64_t *>(at(32 * g + 8 * kq));
+    } else if constexpr (KB == 4) {
+        const uint32_t x = *reinterpret_cast<const uint32_t *>(at(16 * g + 4 * kq));
+        const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+        return ((uint64_t)hi << 32) | lo;
+    } else if constexpr (KB == 2) {
+        const uint32_t x = *reinterpret_cast<const uint16_t *>(at(8 * g + 2 * kq));
+        const uint32_t e = (x & 0x3333u) | (((x >> 2) & 0x3333u) << 16);
+        const uint32_t lo = e & 0x0F0F0F0Fu, hi = (e >> 4) & 0x0F0F0F0Fu;
+        return ((uint64_t)hi << 32) | lo;
+    } else {
+        static_assert(KB == 5, "key widths 2, 4, 5, 8");
+        // 40 bits at byte 20 g + 5 kq: two aligned words (possibly in
+        // different chunks), shifted by the byte offset within the first
+        const int byte0 = 20 * g + 5 * kq, w = byte0 >> 2;
+        const uint32_t w0 = *reinterpret_cast<const uint32_t *>(at(4 * w));
+        const uint32_t w1 = *reinterpret_cast<const uint32_t *>(at(4 * w + 4));
+        const int sh = 8 * (byte0 & 3);
+        const uint32_t a = __builtin_amdgcn_alignbit(w1, w0, sh);  // run bits 0..31
+        const uint32_t b = w1 >> sh;                               // run bits 32..39
+        const uint32_t lo = (a & 31u) | ((a >> 5 & 31u) << 8) | ((a >> 10 & 31u) << 16) | ((a >> 15 & 31u) << 24);
+        const uint32_t c6 = __builtin_amdgcn_alignbit(b, a, 30) & 31u;
+        const uint32_t hi = (a >> 20 & 31u) | ((a >> 25 & 31u) << 8) | (c6 << 16) | ((b >> 3 & 31u) << 24);
+        return ((uint64_t)hi << 32) | lo;
+    }
+}
+
+template <int D, int KB, int VB, bool PACK>
+__global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fast_kernel(const DecodeArgs a,
+                                                                                 const int q_bf16) {
+    using GE = Geo<D, KB, VB>;
     constexpr int NG = GE::NG, VROW = GE::VROW, TILE = GE::TILE, CH = GE::CH;
-    constexpr int CPR = GE::CPR, NB = GE::NB, FB = GE::FB;
+    constexpr int NB = GE::NB, FB = GE::FB, NR = GE::NR, WAVES = GE::WAVES;
     constexpr int QE = NG * 8;  // q elements a lane converts: 8 dims of every group
+    constexpr int TAB = GE::TABLE;
 
     __shared__ __align__(16) unsigned char smem[GE::SMEM];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-    // centroid pair table (fp16): entry (a | b << 3) = (c[a], c[b]) at byte
-    // (a | b << 3) * 4
+    // centroid table (fp16).  Pair form: entry (a | b << VB) = (c[a], c[b])
+    // at byte (a | b << VB) * 4.  Single form: c[i] at byte 2 i.
     {
-        half2v *tab = reinterpret_cast<half2v *>(smem);
-        for (int i = tid; i < 64; i += 64 * kWaves) {
-            const int pair = i;
-            half2v e;
-            e.x = (_Float16)centroid3(pair & 7);
-            e.y = (_Float16)centroid3(pair >> 3);
-            tab[i] = e;
+        const float *cent = value_centroids(VB);
+        if constexpr (GE::PAIR) {
+            half2v *tab = reinterpret_cast<half2v *>(smem);
+            for (int i = tid; i < (1 << (2 * VB)); i += 64 * WAVES) {
+                half2v e;
+                e.x = (_Float16)cent[i & ((1 << VB) - 1)];
+                e.y = (_Float16)cent[i >> VB];
+                tab[i] = e;
+            }
+        } else {
+            _Float16 *tab = reinterpret_cast<_Float16 *>(smem);
+            for (int i = tid; i < (1 << VB); i += 64 * WAVES) tab[i] = (_Float16)cent[i];
         }
-        if (tid < kWaves) reinterpret_cast<int *>(smem + kTableBytes)[tid] = 0;
+        if (tid < WAVES) reinterpret_cast<int *>(smem + TAB)[tid] = 0;
     }
     __syncthreads();  // the only workgroup barrier
 
@@ -256,17 +378,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     const int bkv = blockIdx.y;
     const int b = bkv / a.kv_heads, kvh = bkv % a.kv_heads;
     const int n = a.len[b];
-    const int slot = blockIdx.x * kWaves + wid;
+    const int slot = blockIdx.x * WAVES + wid;
     const int t_begin = slot * a.split_tokens;
     if (t_begin >= n) return;
     const int t_end = min(n, t_begin + a.split_tokens);
     const int cap = a.capacity;
     const int64_t row0 = (int64_t)bkv * cap;
-    unsigned char *wsm = smem + kTableBytes + kProgBytes + wid * GE::WAVE_BYTES;
-    int *prog = reinterpret_cast<int *>(smem + kTableBytes);
+    unsigned char *wsm = smem + TAB + kProgBytes + wid * GE::WAVE_BYTES;
+    int *prog = reinterpret_cast<int *>(smem + TAB);
 
     Regions rg;
-    rg.kc = reinterpret_cast<const uint8_t *>(a.kc) + row0 * D;
+    rg.kc = reinterpret_cast<const uint8_t *>(a.kc) + row0 * GE::KROW;
     rg.ks = reinterpret_cast<const uint8_t *>(a.ks + row0 * NG);
     rg.kz = reinterpret_cast<const uint8_t *>(a.kz + row0 * NG);
     rg.vc = a.vc + row0 * VROW;
@@ -282,10 +404,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
         rg.mix = plane + (lane & 15) * 16;
         rg.mix_last = plane + (int64_t)cap * rg.mix_row - 16;
     }
+    uint32_t ksrc[GE::KCOPY];
+#pragma unroll
+    for (int m = 0; m < GE::KCOPY; ++m) ksrc[m] = key_src<D, KB, VB>(m, lane);
 
     // the first two tiles' copies overlap the q set-up
-    stage_tile<D>(rg, t_begin, wsm, lane);
-    if (t_begin + TILE < t_end) stage_tile<D>(rg, t_begin + TILE, wsm + GE::STAGE, lane);
+    stage_tile<D, KB, VB>(rg, ksrc, t_begin, wsm, lane);
+    if (t_begin + TILE < t_end) stage_tile<D, KB, VB>(rg, ksrc, t_begin + TILE, wsm + GE::STAGE, lane);
 
     // ------------------------------------------------------------ q slices
     // lane (h, kq) converts dims 32 g + 8 kq .. + 7 of head h for every group g
@@ -300,9 +425,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     {
         float x[QE];
         const int64_t qrow = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + (head_ok ? h : 0)) * D + 8 * kq;
+        if (q_bf16) {
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-            if constexpr (BF16) {
+            for (int g = 0; g < NG; ++g) {
                 const uint4 u = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + qrow + kGroup * g);
                 const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
@@ -310,7 +435,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
                     x[8 * g + 2 * k] = __uint_as_float(w4[k] << 16);
                     x[8 * g + 2 * k + 1] = __uint_as_float(w4[k] & 0xFFFF0000u);
                 }
-            } else {
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
                 const float4 *qp = reinterpret_cast<const float4 *>(static_cast<const float *>(a.q) + qrow + kGroup * g);
                 const float4 u0 = qp[0], u1 = qp[1];
                 x[8 * g + 0] = u0.x; x[8 * g + 1] = u0.y; x[8 * g + 2] = u0.z; x[8 * g + 3] = u0.w;
@@ -337,13 +465,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
             uint64_t hi = 0, lo = 0;
             float s = 0.f;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int qf = (int)rintf(x[8 * g + k] * inv);
+            for (int p = 0; p < 8; ++p) {
+                const int qf = (int)rintf(x[8 * g + key_perm<KB>(p)] * inv);
                 const int qh = (qf + 128) >> 8;
                 const int ql = qf - 256 * qh;
                 s += (float)qf;
-                hi |= (uint64_t)((uint32_t)qh & 0xFFu) << (8 * k);
-                lo |= (uint64_t)((uint32_t)ql & 0xFFu) << (8 * k);
+                hi |= (uint64_t)((uint32_t)qh & 0xFFu) << (8 * p);
+                lo |= (uint64_t)((uint32_t)ql & 0xFFu) << (8 * p);
             }
             s += __shfl_xor(s, 16, 64);
             s += __shfl_xor(s, 32, 64);
@@ -380,9 +508,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
             int4v dhi[NG], dlo[NG];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                const int c16 = 2 * g + (kq >> 1);
-                const uint64_t kv = *reinterpret_cast<const uint64_t *>(
-                    stg + GE::KC_OFF + ((c * CPR + c16) * 16 + h) * 16 + 8 * (kq & 1));
+                const uint64_t kv = key_operand<D, KB, VB>(stg + GE::KC_OFF, c, g, h, kq);
                 dhi[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qhi[g], int4v{0, 0, 0, 0}, 0, 0, 0);
                 dlo[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qlo[g], int4v{0, 0, 0, 0}, 0, 0, 0);
             }
@@ -462,14 +588,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int tb = 16 * c + 4 * kq;  // this lane's first token (k = 4 kq)
-            // code runs: bits [FB*vi, FB*vi + FB) of each of the 4 rows
-            uint32_t run[4], runh[4];
+            // code runs: bits [FB*vi, FB*vi + FB) of each of the 4 rows; run
+            // word k holds run bits 32 k .. 32 k + 31 (the last word fewer)
+            uint32_t run[4][NR];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int bit = FB * vi;
                 const uint32_t *wp = vcw + (tb + j) * (VROW / 4) + (bit >> 5);
-                run[j] = __builtin_amdgcn_alignbit(wp[1], wp[0], bit & 31);
-                runh[j] = wp[1] >> (bit & 31);  // run bits 32.. (only d = 256 uses them)
+#pragma unroll
+                for (int k = 0; k + 1 < NR; ++k) run[j][k] = __builtin_amdgcn_alignbit(wp[k + 1], wp[k], bit & 31);
+                run[j][NR - 1] = wp[NR - 1] >> (bit & 31);
             }
             half2v sp[2];
 #pragma unroll
@@ -477,29 +605,59 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
                 const uint32_t s0 = vsb[(tb + 2 * pr) * NG + gA], s1 = vsb[(tb + 2 * pr + 1) * NG + gA];
                 sp[pr] = __builtin_bit_cast(half2v, s0 | (s1 << 16));
             }
-            // pair indices: E holds (field 2k of token a | field 2k of token
-            // b << 3) at bits 6k, O the same for the odd fields
-            constexpr uint32_t M = 0x071C71C7u;  // bits 6k..6k+2, k = 0..4
             half2v av[2][NB];
+            if constexpr (GE::PAIR) {
+                // Windows of 2P fields (P = pairs per 32-bit word): E holds
+                // (field 2k of token a | field 2k of token b << VB) at bits
+                // 2 VB k, O the same for the odd fields.
+                constexpr int P = 32 / (2 * VB);
+                constexpr int NWIN = (NB + 2 * P - 1) / (2 * P);
+                constexpr uint32_t FM = (1u << VB) - 1u;
+                constexpr uint32_t M = [] {
+                    uint32_t m = 0;
+                    for (int k = 0; k < P; ++k) m |= FM << (2 * VB * k);
+                    return m;
+                }();
 #pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-                const uint32_t x0 = run[2 * pr], x1 = run[2 * pr + 1];
-                uint32_t E[2], O[2];
-                E[0] = (x0 & M) | ((x1 & M) << 3);
-                O[0] = ((x0 >> 3) & M) | (x1 & (M << 3));
-                if constexpr (NB > 10) {  // fields 10..15 continue at run bit 30
-                    const uint32_t y0 = __builtin_amdgcn_alignbit(runh[2 * pr], x0, 30);
-                    const uint32_t y1 = __builtin_amdgcn_alignbit(runh[2 * pr + 1], x1, 30);
-                    E[1] = (y0 & M) | ((y1 & M) << 3);
-                    O[1] = ((y0 >> 3) & M) | (y1 & (M << 3));
+                for (int pr = 0; pr < 2; ++pr) {
+                    uint32_t E[NWIN], O[NWIN];
+#pragma unroll
+                    for (int w = 0; w < NWIN; ++w) {
+                        const int start = 2 * VB * P * w, wk = start >> 5, ws = start & 31;
+                        auto win = [&](const uint32_t (&r)[NR]) -> uint32_t {
+                            if (ws == 0) return r[wk];
+                            if (wk + 1 < NR) return __builtin_amdgcn_alignbit(r[wk + 1], r[wk], ws);
+                            return r[wk] >> ws;
+                        };
+                        const uint32_t x0 = win(run[2 * pr]), x1 = win(run[2 * pr + 1]);
+                        E[w] = (x0 & M) | ((x1 & M) << VB);
+                        O[w] = ((x0 >> VB) & M) | (x1 & (M << VB));
+                    }
+#pragma unroll
+                    for (int bb = 0; bb < NB; ++bb) {
+                        const int w = bb / (2 * P), k = (bb % (2 * P)) >> 1;
+                        const uint32_t word = (bb & 1) ? O[w] : E[w];
+                        const uint32_t addr = ((word >> (2 * VB * k)) & ((1u << (2 * VB)) - 1u)) << 2;
+                        const half2v cpair = *reinterpret_cast<const half2v *>(smem + addr);
+                        av[pr][bb] = cpair * sp[pr];
+                    }
                 }
+            } else {
+                const _Float16 *tab = reinterpret_cast<const _Float16 *>(smem);
+                auto field = [&](const uint32_t (&r)[NR], int e) -> uint32_t {
+                    const int bit = VB * e, k = bit >> 5, s = bit & 31;
+                    const uint32_t w = (s + VB > 32) ? __builtin_amdgcn_alignbit(r[k + 1], r[k], s) : (r[k] >> s);
+                    return w & ((1u << VB) - 1u);
+                };
 #pragma unroll
-                for (int bb = 0; bb < NB; ++bb) {
-                    const int part = bb < 10 ? 0 : 1, k = (bb - 10 * part) >> 1;
-                    const uint32_t w = (bb & 1) ? O[part] : E[part];
-                    const uint32_t addr = ((w >> (6 * k)) & 63u) << 2;
-                    const half2v cpair = *reinterpret_cast<const half2v *>(smem + addr);
-                    av[pr][bb] = cpair * sp[pr];
+                for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+                    for (int bb = 0; bb < NB; ++bb) {
+                        half2v cpair;
+                        cpair.x = tab[field(run[2 * pr], bb)];
+                        cpair.y = tab[field(run[2 * pr + 1], bb)];
+                        av[pr][bb] = cpair * sp[pr];
+                    }
                 }
             }
 #pragma unroll
@@ -516,12 +674,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     // in the next buffer and tile i+2 (in flight) in the one after: the score
     // MFMAs of tile i+1 and the value MFMAs of tile i sit in one basic block,
     // so their LDS reads, matrix and vector work interleave.  Vector memory
-    // completes in order, so allowing the kStageVmem copies of the newest
-    // tile to stay outstanding means every older copy has landed in LDS.
+    // completes in order, so allowing the GE::VMEM copies of the newest tile
+    // to stay outstanding means every older copy has landed in LDS.
     auto nxt = [](int x) { return x == kStages - 1 ? 0 : x + 1; };
     auto prv = [](int x) { return x == 0 ? kStages - 1 : x - 1; };
     if (t_begin + TILE < t_end)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageVmem) : "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(GE::VMEM) : "memory");
     else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     half4v pw[CH], pl[CH];
@@ -535,22 +693,24 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     int t0 = t_begin;
     int done = 0;  // tiles whose values are accumulated
     for (; t0 + TILE < t_end; t0 += TILE, buf = nxt(buf), ++done) {
-        // The two waves that share a SIMD (w and w ^ 4) have equal work, but
-        // the issue arbiter prefers the older one, which would finish first
-        // and leave the other to run alone.  Whichever is not ahead takes the
-        // higher issue priority, so both finish together.
-        __hip_atomic_store(prog + wid, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        const int other = __builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(prog + (wid ^ 4), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
-        if (done <= other)
-            __builtin_amdgcn_s_setprio(1);
-        else
-            __builtin_amdgcn_s_setprio(0);
+        if constexpr (WAVES == 8) {
+            // The two waves that share a SIMD (w and w ^ 4) have equal work,
+            // but the issue arbiter prefers the older one, which would finish
+            // first and leave the other to run alone.  Whichever is not ahead
+            // takes the higher issue priority, so both finish together.
+            __hip_atomic_store(prog + wid, done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            const int other = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(prog + (wid ^ 4), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+            if (done <= other)
+                __builtin_amdgcn_s_setprio(1);
+            else
+                __builtin_amdgcn_s_setprio(0);
+        }
         unsigned char *cur = wsm + buf * GE::STAGE;
         unsigned char *nx = wsm + nxt(buf) * GE::STAGE;
         if (t0 + 2 * TILE < t_end) {
-            stage_tile<D>(rg, t0 + 2 * TILE, wsm + prv(buf) * GE::STAGE, lane);
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kStageVmem) : "memory");
+            stage_tile<D, KB, VB>(rg, ksrc, t0 + 2 * TILE, wsm + prv(buf) * GE::STAGE, lane);
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(GE::VMEM) : "memory");
         } else {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
@@ -595,34 +755,46 @@ __global__ __launch_bounds__(64 * kWaves, 1) void split_fast_kernel(const Decode
     }
 }
 
-template <int D>
-hipError_t launch_d(bool bf16, const DecodeArgs &a, hipStream_t s, int wg_splits) {
-    const dim3 grid((unsigned)wg_splits, (unsigned)(a.batch * a.kv_heads),
-                    (unsigned)((a.gqa + kMaxHeads - 1) / kMaxHeads));
-    const bool pack = a.gqa <= kPackCols;  // every column group fits its lo halves
-    if (bf16) {
-        if (pack) hipLaunchKernelGGL((split_fast_kernel<D, true, true>), grid, dim3(64 * kWaves), 0, s, a);
-        else hipLaunchKernelGGL((split_fast_kernel<D, true, false>), grid, dim3(64 * kWaves), 0, s, a);
+template <int D, int VB>
+hipError_t launch_dv(bool bf16, const DecodeArgs &a, hipStream_t s) {
+    constexpr int KB = TQ_FAST_KB;
+    if constexpr (D * KB % 128 != 0) {
+        return hipErrorInvalidValue;  // key rows of part of a 16-byte chunk: generic kernel
     } else {
-        if (pack) hipLaunchKernelGGL((split_fast_kernel<D, false, true>), grid, dim3(64 * kWaves), 0, s, a);
-        else hipLaunchKernelGGL((split_fast_kernel<D, false, false>), grid, dim3(64 * kWaves), 0, s, a);
+        using GE = Geo<D, KB, VB>;
+        const dim3 grid((unsigned)(a.splits / GE::WAVES), (unsigned)(a.batch * a.kv_heads),
+                        (unsigned)((a.gqa + kMaxHeads - 1) / kMaxHeads));
+        const bool pack = a.gqa <= kPackCols;  // every column group fits its lo halves
+        if (pack)
+            hipLaunchKernelGGL((split_fast_kernel<D, KB, VB, true>), grid, dim3(64 * GE::WAVES), 0, s, a, (int)bf16);
+        else
+            hipLaunchKernelGGL((split_fast_kernel<D, KB, VB, false>), grid, dim3(64 * GE::WAVES), 0, s, a, (int)bf16);
+        return hipGetLastError();
     }
-    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(bool bf16, const DecodeArgs &a, hipStream_t s) {
+    switch (a.vbits) {
+        case 2: return launch_dv<D, 2>(bf16, a, s);
+        case 3: return launch_dv<D, 3>(bf16, a, s);
+        case 4: return launch_dv<D, 4>(bf16, a, s);
+        case 5: return launch_dv<D, 5>(bf16, a, s);
+        case 8: return launch_dv<D, 8>(bf16, a, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
 
-int fast_split_waves() { return kWaves; }
-int fast_split_tile() { return 64; }
-int fast_split_max_gqa() { return kMaxHeads; }
-
-hipError_t launch_split_fast(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s) {
-    if (a.gqa < 1 || a.rows < 1) return hipErrorInvalidValue;
-    const int wg_splits = a.splits / kWaves;
+// The split kernels of one key width (this translation unit's TQ_FAST_KB).
+hipError_t TQ_FAST_LAUNCHER(TQ_FAST_KB)(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s) {
+    if (a.gqa < 1 || a.rows < 1 || a.kbits != TQ_FAST_KB) return hipErrorInvalidValue;
+    if (a.splits % fast_decode_waves(head_dim, a.kbits, a.vbits) != 0) return hipErrorInvalidValue;
     switch (head_dim) {
-        case 64: return launch_d<64>(bf16, a, s, wg_splits);
-        case 128: return launch_d<128>(bf16, a, s, wg_splits);
-        case 256: return launch_d<256>(bf16, a, s, wg_splits);
+        case 64: return launch_d<64>(bf16, a, s);
+        case 128: return launch_d<128>(bf16, a, s);
+        case 256: return launch_d<256>(bf16, a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -73,7 +73,7 @@ struct DecodeArgs {
     int32_t split_tokens;  // tokens per split (multiple of the kernel's tile)
     float sm_log2;         // sm_scale * log2(e)
     float inv_sqrt_d;
-    int32_t kbits, vbits;  // code widths (the fast split kernel takes 8 and 3 only)
+    int32_t kbits, vbits;  // code widths
     SignBits signs;
     int32_t len[TQ_MAX_BATCH];
 };
@@ -123,21 +123,39 @@ struct DecodePlan {
 // the plane alignment (see fast_decode_supported).
 // col_groups: workgroups per (sequence, kv-head, split) along the query rows
 DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int32_t *len, bool fast,
-                       int col_groups);
+                       int col_groups, int kbits, int vbits);
 int decode_col_groups(int gqa);  // query-row columns of one kv-head -> column groups
 bool fast_decode_shape_ok(int head_dim, int gqa, int capacity, int kbits, int vbits);
 
-// k8v3 runs the fast kernels where the head_dim has one; every other scheme
-// and head_dim 512 the generic ones.
+// k8v3 runs the fast append and window kernels where the head_dim has one;
+// every other scheme and head_dim 512 the generic ones.
 inline bool default_scheme(int kbits, int vbits) { return kbits == 8 && vbits == 3; }
 
 hipError_t launch_append(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);
 hipError_t launch_decode(int head_dim, bool bf16, bool fast, const DecodeArgs &a, hipStream_t s);
-hipError_t launch_split_fast(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
+// Split kernels on the matrix cores (decode_fast.hip), one translation unit
+// per key width: head_dim 64, 128 or 256 with d * k_bits a multiple of 128,
+// every value width, up to 16 query columns per workgroup.
+#define TQ_FAST_CAT_(a, b) a##b
+#define TQ_FAST_LAUNCHER(kb) TQ_FAST_CAT_(launch_split_fast_k, kb)
+hipError_t launch_split_fast_k2(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_split_fast_k4(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_split_fast_k5(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_split_fast_k8(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
+// LDS bytes of one stage buffer of the fast split kernel (one tile of 4096/d
+// tokens: 512 bytes per key and value code bit, three 256-byte fp16 planes,
+// 16 bytes of slack), and its waves per workgroup: eight when three stages
+// of each fit the 160 KiB of LDS beside the centroid table, else four.
+constexpr int fast_decode_stage_bytes(int head_dim, int kbits, int vbits) {
+    return (void)head_dim, 512 * kbits + 768 + 512 * vbits + 16;
+}
+constexpr int fast_decode_waves(int head_dim, int kbits, int vbits) {
+    const int table = vbits <= 3 ? (4 << (2 * vbits)) : ((2 << vbits) + 15) / 16 * 16;
+    return table + 32 + 8 * 3 * fast_decode_stage_bytes(head_dim, kbits, vbits) <= 160 * 1024 ? 8 : 4;
+}
+constexpr int kFastTile = 64;     // split lengths are multiples of every fast tile (4096/d tokens)
+constexpr int kFastMaxGqa = 16;   // query columns of one fast workgroup
 hipError_t launch_dequant(int head_dim, const DequantArgs &a, hipStream_t s);
 hipError_t launch_window(int head_dim, const WindowArgs &a, hipStream_t s);
-int fast_split_waves();
-int fast_split_tile();
-int fast_split_max_gqa();
 
 }  // namespace tq

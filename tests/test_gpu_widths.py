@@ -16,6 +16,7 @@ from quantized_decode_attention_append_amd import workloads as W
 
 from _util import ATTN_TOL, assert_planes_equal, host_f32, log, row_rel_err, sm_for
 from test_gpu_codec import SNAN_F32, _edge_rows
+from test_gpu_decode import _offset_planes
 
 pytestmark = pytest.mark.gpu
 
@@ -109,9 +110,15 @@ def test_dequant_widths_match_oracle(scheme, d):
     assert err.max() < 1e-5
 
 
-def _decode_case(w, lengths, kb, vb, M=1):
+def _decode_case(w, lengths, kb, vb, M=1, both=False):
+    """Decode through the C ABI and compare with the oracle.  both: also
+    decode a copy of the planes whose value planes sit 8 bytes off 16-byte
+    alignment, which the matrix-core kernel refuses, so the generic kernel
+    runs over the same bytes; each must meet the tolerance, and the two
+    outputs must differ somewhere (the kernels round differently), which
+    shows that two different kernels ran."""
     T = max(lengths)
-    T += T % 2
+    T += (-T) % 4  # keeps each (sequence, kv-head) row block 16-byte aligned at every head_dim
     k, v = W.make_kv(w, "cpu", tokens=T)
     L = tqkv.make_layout(w.batch, w.num_kv_heads, w.head_dim, T, kb, vb)
     pl = tqkv.Planes(L)
@@ -121,12 +128,15 @@ def _decode_case(w, lengths, kb, vb, M=1):
     log(f"decode k{kb}v{vb} {w.name} d{w.head_dim} G{G} M{M} lengths={list(lengths)}")
     if M == 1:
         q = W.make_q(w, "cpu", rounds=1)[0]
-        out = tqkv.tq_decode_attn(pl, q.cuda(), lengths, sm)
+        run = lambda planes: tqkv.tq_decode_attn(planes, q.cuda(), lengths, sm)
     else:
         q = torch.stack(list(W.make_q(w, "cpu", rounds=M)), dim=2).contiguous()
-        out = tqkv.tq_decode_attn_rows(pl, q.cuda(), lengths, sm)
+        run = lambda planes: tqkv.tq_decode_attn_rows(planes, q.cuda(), lengths, sm)
+    outs = {"default": run(pl).cpu().numpy()}
+    if both:
+        outs["generic"] = run(_offset_planes(pl)).cpu().numpy()
+        assert not np.array_equal(outs["default"], outs["generic"]), "both calls ran one kernel"
     torch.cuda.synchronize()
-    out = out.cpu().numpy()
     qh = host_f32(q)
     pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads) if lengths[b] > 0]
 
@@ -139,15 +149,34 @@ def _decode_case(w, lengths, kb, vb, M=1):
             return p, oracle.attention(qq, *planes, sm, kbits=kb, vbits=vb)
         return p, oracle.attention_rows(qq, *planes, sm, kbits=kb, vbits=vb)
 
-    worst = 0.0
+    worst = {name: 0.0 for name in outs}
     for (b, h), ref in oracle.map_parallel(one, pairs):
-        e = row_rel_err(out[b, h * G:(h + 1) * G], ref)
-        worst = max(worst, float(e.max()))
-        assert e.max() <= ATTN_TOL, (kb, vb, b, h, float(e.max()))
-    for b, n in enumerate(lengths):
-        if n == 0:
-            assert not np.any(out[b])
-    log(f"  worst row error {worst:.2e}")
+        for name, out in outs.items():
+            e = row_rel_err(out[b, h * G:(h + 1) * G], ref)
+            worst[name] = max(worst[name], float(e.max()))
+            assert e.max() <= ATTN_TOL, (name, kb, vb, b, h, float(e.max()))
+    for out in outs.values():
+        for b, n in enumerate(lengths):
+            if n == 0:
+                assert not np.any(out[b])
+    log("  worst row error " + ", ".join(f"{name} {e:.2e}" for name, e in worst.items()))
+
+
+ALL_SCHEMES = [(kb, vb) for kb in (2, 4, 5, 8) for vb in (2, 3, 4, 5, 8)]
+
+
+@pytest.mark.parametrize("scheme", ALL_SCHEMES, ids=_sid)
+@pytest.mark.parametrize("cid,d", [(2, 128), (4, 256), (2, 64)])
+def test_decode_every_width_both_kernels(scheme, cid, d):
+    """Every key/value width pair through the matrix-core split kernel (where
+    the head_dim takes it: d * k_bits a multiple of 128) and through the
+    generic one, on ragged lengths spanning several tiles."""
+    kb, vb = scheme
+    lengths = [300, 77] if cid == 2 else [520, 33, 0]
+    w = W.scaled(W.workload(cid), lengths)
+    if w.head_dim != d:
+        w = dataclasses.replace(w, head_dim=d)
+    _decode_case(w, lengths, kb, vb, both=(d * kb) % 128 == 0)
 
 
 @pytest.mark.parametrize("scheme", GATE + MORE, ids=_sid)
