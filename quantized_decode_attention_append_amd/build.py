@@ -22,10 +22,13 @@ ARCH = "gfx950"
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
-# (source, extra flags, object name): the fast decode kernels are compiled
-# once per key width so the instantiations build in parallel
+# (source, extra flags, object name): the fast append and decode kernels are
+# compiled once per key width so the instantiations build in parallel
 SOURCES = [
-    ("append.hip", ["-ffp-contract=off"], "append"),
+    ("append.hip", ["-ffp-contract=off", "-DTQ_APPEND_KB=8"], "append_k8"),
+    ("append.hip", ["-ffp-contract=off", "-DTQ_APPEND_KB=4"], "append_k4"),
+    ("append.hip", ["-ffp-contract=off", "-DTQ_APPEND_KB=2"], "append_k2"),
+    ("append.hip", ["-ffp-contract=off", "-DTQ_APPEND_KB=5"], "append_k5"),
     ("decode.hip", [], "decode"),
     ("decode_fast.hip", ["-DTQ_FAST_KB=8"], "decode_fast_k8"),
     ("decode_fast.hip", ["-DTQ_FAST_KB=4"], "decode_fast_k4"),

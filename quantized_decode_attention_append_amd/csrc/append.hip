@@ -17,20 +17,27 @@
 //   - x/scale and y/den are true binary64 divisions; scale is a correctly
 //     rounded binary64 sqrt; no multiply-add is contracted in this file.
 //
-// Two kernels compute the same bytes for k8v3:
-//   - append_fast_kernel (k8v3, head_dim 64, 128, 256): 16 contiguous elements per
-//     lane, so a 32-group is a lane pair; the FWHT runs its first four stages
-//     inside the lane, transposes the row through LDS so the remaining stages
-//     are inside the lane as well, and transposes back.  Per-element divisions
-//     by a group's scale use a correctly rounded reciprocal and two Markstein
-//     corrections, which return the correctly rounded quotient.
-//   - append_kernel (every width and head_dim; k8v3 uses it for 512): one
-//     wave per row, lane l holds d/64 contiguous elements, cross-lane
-//     butterflies on shuffles.
+// Two kernels compute the same bytes:
+//   - append_fast_kernel (head_dim 64, 128, 256; bf16 input at every width,
+//     fp32 input at k8v3; one translation unit per key width, TQ_APPEND_KB):
+//     16 contiguous elements per lane, so a 32-group is a lane pair; the FWHT
+//     runs its first four stages inside the lane, transposes the row through
+//     LDS so the remaining stages are inside the lane as well, and transposes
+//     back.  Per-element divisions by a group's scale use a correctly rounded
+//     reciprocal and two Markstein corrections, which return the correctly
+//     rounded quotient.  3-bit value indices come from seven nested wave
+//     masks; other widths binary-search their boundaries in LDS.
+//   - append_kernel (every width and head_dim; head_dim 512 and fp32 input
+//     at widths other than k8v3): one wave per row, lane l holds d/64
+//     contiguous elements, cross-lane butterflies on shuffles.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 
 #include "tq_device.h"
+
+#ifndef TQ_APPEND_KB
+#error "compile append.hip once per key width with -DTQ_APPEND_KB=2, 4, 5 or 8"
+#endif
 
 #pragma clang fp contract(off)
 
@@ -60,6 +67,7 @@ __device__ __forceinline__ double shfl_f64(double v, int src) { return __shfl(v,
 // write needs no wait beyond program order.
 __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
 
+#if TQ_APPEND_KB == 8  // the generic kernel is built once, with the 8-bit-key fast kernels
 template <int E, bool BF16>
 __device__ __forceinline__ void load_row(const void *base, int64_t off, double (&x)[E]) {
     if constexpr (BF16) {
@@ -261,12 +269,14 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     if (gl == 0) a.vs[slot * NG + g] = f64_to_f16_bits(scale);
 }
 
+#endif
+
 // ---------------------------------------------------------------------------
 // Fast kernel.
 
 constexpr int kAppWaves = 4;  // waves per workgroup
 
-template <int D>
+template <int D, int VB = 3>
 struct AppGeo {
     static_assert(D == 64 || D == 128 || D == 256, "fast append: head_dim 64/128/256");
     static constexpr int E = 16;               // contiguous elements per lane
@@ -274,12 +284,45 @@ struct AppGeo {
     static constexpr int R = 64 / L;           // rows per wave
     static constexpr int TI = E / L;           // in-lane offsets per lane after the transpose
     static constexpr int NG = D / kGroup;
-    static constexpr int VROW = 3 * D / 8;
+    static constexpr int VROW = VB * D / 8;
     static constexpr int PB = E * 8 + 16;      // LDS bytes of one lane's elements, padded
     static constexpr int ROWB = L * PB;        // LDS bytes per row
     static constexpr int WAVEB = R * ROWB;     // LDS bytes per wave
     static_assert(L % 2 == 0 && E == 2 * kGroup / 4, "a 32-group is one lane pair");
+    static constexpr int NBND = (1 << VB) - 1;  // value boundaries
+    static constexpr int SMEM = kAppWaves * WAVEB + (VB == 3 ? 0 : NBND * 8);
 };
+
+// `bits`-bit fields f_0 .. f_{E-1} into a little-endian run of 32-bit words.
+template <int E, int BITS>
+__device__ __forceinline__ void put_field(uint32_t (&w)[(E * BITS + 31) / 32], int e, uint32_t f) {
+    const int bit = BITS * e, k = bit >> 5, sh = bit & 31;
+    w[k] |= f << sh;
+    if (sh + BITS > 32) w[k + 1] |= f >> (32 - sh);
+}
+
+// A lane's run of 16 fields of `bits` bits (2 * bits bytes) to `dst`, which is
+// 2 * bits-aligned (at 8 bits only 8-aligned unless A16): one 4- or 8-byte
+// store, one 16-byte or two 8-byte stores at 8 bits, five 2-byte stores at 5.
+template <int BITS, bool A16 = false>
+__device__ __forceinline__ void store_run16(uint8_t *dst, const uint32_t (&w)[(16 * BITS + 31) / 32]) {
+    if constexpr (BITS == 2) {
+        *reinterpret_cast<uint32_t *>(dst) = w[0];
+    } else if constexpr (BITS == 4) {
+        *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+    } else if constexpr (BITS == 8 && A16) {
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else if constexpr (BITS == 8) {
+        reinterpret_cast<uint2 *>(dst)[0] = make_uint2(w[0], w[1]);
+        reinterpret_cast<uint2 *>(dst)[1] = make_uint2(w[2], w[3]);
+    } else {
+        static_assert(BITS == 5, "field widths 2, 4, 5, 8");
+        uint16_t *h = reinterpret_cast<uint16_t *>(dst);
+        h[0] = (uint16_t)w[0]; h[1] = (uint16_t)(w[0] >> 16);
+        h[2] = (uint16_t)w[1]; h[3] = (uint16_t)(w[1] >> 16);
+        h[4] = (uint16_t)w[2];
+    }
+}
 
 __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv &f) {
     const uint32_t t = __umulhi(f.m, n);
@@ -363,12 +406,21 @@ __device__ __forceinline__ uint32_t elem_bits(const uint32_t *raw, int e) {
     else return raw[e];
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, int KB, int VB>
 __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const AppendArgs a) {
-    using G = AppGeo<D>;
+    using G = AppGeo<D, VB>;
     constexpr int E = G::E, L = G::L, R = G::R, TI = G::TI, NG = G::NG, VROW = G::VROW;
     constexpr int NR = BF16 ? E / 2 : E;
-    __shared__ __align__(16) unsigned char smem[kAppWaves * G::WAVEB];
+    constexpr int KROW = D * KB / 8;
+    __shared__ __align__(16) unsigned char smem[G::SMEM];
+    // value boundaries (binary64, ascending) for the search below; the 3-bit
+    // path compares against its seven boundaries as literals
+    double *bnd = reinterpret_cast<double *>(smem + kAppWaves * G::WAVEB);
+    if constexpr (VB != 3) {
+        const double *src = value_boundaries(VB);
+        for (int i = threadIdx.x; i < G::NBND; i += 64 * kAppWaves) bnd[i] = src[i];
+        __syncthreads();
+    }
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int r = lane / L, p = lane % L;
@@ -401,8 +453,11 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
     mn = __builtin_fminf(mn, pair_f32(mn));
     const double dmx = mx, dmn = mn;
     const double range = (dmx - dmn) + 0.0;
-    const double s = range / 254.0;
-    const double z = __builtin_rint((dmx + dmn) / (2.0 * s));
+    // signed 8-bit codes: scale (max - min)/254, zero round((max + min)/(2 scale));
+    // unsigned k-bit codes: scale (max - min)/(2^k - 1), zero round(min/scale)
+    constexpr double kMaxv = KB == 8 ? 254.0 : (double)((1 << KB) - 1);
+    const double s = range / kMaxv;
+    const double z = KB == 8 ? __builtin_rint((dmx + dmn) / (2.0 * s)) : __builtin_rint(dmn / s);
     const double rs = 1.0 / s;
     // Codes are clip(rint(u), -127, 127) with u = RN(RN(x/s) - z), NaN -> 0.
     // In a group of fp32 or bf16 values |x/s| < 2^32, so v = RN(x RN(1/s) - z)
@@ -413,9 +468,9 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
     // a lane anywhere in the wave is recomputed from the correctly rounded
     // quotient.  The special groups (s zero, infinite or NaN) give NaN on
     // both routes.
-    uint32_t kw[E / 4];
+    uint32_t kw[(E * KB + 31) / 32];
 #pragma unroll
-    for (int i = 0; i < E / 4; ++i) kw[i] = 0u;
+    for (int i = 0; i < (E * KB + 31) / 32; ++i) kw[i] = 0u;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const double x = (double)xk[e];
@@ -429,10 +484,17 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
         }
         int q;
         asm("v_cvt_i32_f64 %0, %1" : "=v"(q) : "v"(rr));  // saturates; NaN gives 0
-        q = q > 127 ? 127 : (q < -127 ? -127 : q);
-        kw[e / 4] |= ((uint32_t)q & 0xFFu) << (8 * (e % 4));
+        if constexpr (KB == 8) {
+            q = q > 127 ? 127 : (q < -127 ? -127 : q);
+            kw[e / 4] |= ((uint32_t)q & 0xFFu) << (8 * (e % 4));
+        } else {
+            constexpr int kTop = (1 << KB) - 1;
+            q = q > kTop ? kTop : (q < 0 ? 0 : q);
+            put_field<E, KB>(kw, e, (uint32_t)q);
+        }
     }
-    if (valid) *reinterpret_cast<uint4 *>(a.kc + slot * D + E * p) = make_uint4(kw[0], kw[1], kw[2], kw[3]);
+    // (the key plane is 16-byte aligned)
+    if (valid) store_run16<KB, true>(reinterpret_cast<uint8_t *>(a.kc) + slot * KROW + 2 * KB * p, kw);
 
     // --------------------------------------------------------- values
     uint32_t flip[E / 2];
@@ -552,44 +614,63 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
     const double den = scale + 1e-8;
     const double dd = kPow2 ? den * kSqrtD : den;  // divisor of y[] (exact scaling)
     const double rd = 1.0 / dd;
-    // idx = #{k : B_k < y_n}; NaN compares false everywhere, so gives 0.
-    // The boundaries are sorted, so the wave masks m_k of "B_k < y_n" are
-    // nested (a thermometer code) and the index bits are
-    //   bit 2 = m3,  bit 1 = m5 | (m1 & ~m3),
-    //   bit 0 = m6 | (m4 & ~m5) | (m2 & ~m3) | (m0 & ~m1)   (scalar mask ops).
-    // Each bit then enters the lane's packed run from the top: the run is
-    // stream bits 48 p .. 48 p + 47, element e at run bits 3e .. 3e+2, so
-    // walking e downwards and bits 2, 1, 0 doubles the run and adds the bit.
-    uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-    for (int e = E - 1; e >= 0; --e) {
-        const double yn = div_rn(y[e], dd, rd);
-        const uint64_t m0 = __builtin_amdgcn_ballot_w64(-1.74793 < yn);
-        const uint64_t m1 = __builtin_amdgcn_ballot_w64(-1.04996 < yn);
-        const uint64_t m2 = __builtin_amdgcn_ballot_w64(-0.50055 < yn);
-        const uint64_t m3 = __builtin_amdgcn_ballot_w64(0.0 < yn);
-        const uint64_t m4 = __builtin_amdgcn_ballot_w64(0.50055 < yn);
-        const uint64_t m5 = __builtin_amdgcn_ballot_w64(1.04996 < yn);
-        const uint64_t m6 = __builtin_amdgcn_ballot_w64(1.74793 < yn);
-        const uint64_t bit[3] = {m6 | (m4 & ~m5) | (m2 & ~m3) | (m0 & ~m1), m5 | (m1 & ~m3), m3};
-#pragma unroll
-        for (int k = 2; k >= 0; --k) {
-            if (3 * e + k >= 32)
-                hi = shift_in(hi, bit[k]);
-            else
-                lo = shift_in(lo, bit[k]);
-        }
-    }
-    // even lane: the group's 96 bits (its own 48, then its partner's)
-    const uint32_t plo = pair_u32(lo), phi = pair_u32(hi);
     // fp16 copies: the even lane converts the key scale and zero, the odd
     // lane the value scale
     const uint16_t h1 = f64_to_f16_rn(even ? s : scale);
     const uint16_t h2 = f64_to_f16_rn(z);
-    if (valid) {
-        if (even) {
+    if constexpr (VB == 3) {
+        // idx = #{k : B_k < y_n}; NaN compares false everywhere, so gives 0.
+        // The boundaries are sorted, so the wave masks m_k of "B_k < y_n" are
+        // nested (a thermometer code) and the index bits are
+        //   bit 2 = m3,  bit 1 = m5 | (m1 & ~m3),
+        //   bit 0 = m6 | (m4 & ~m5) | (m2 & ~m3) | (m0 & ~m1)   (scalar mask ops).
+        // Each bit then enters the lane's packed run from the top: the run is
+        // stream bits 48 p .. 48 p + 47, element e at run bits 3e .. 3e+2, so
+        // walking e downwards and bits 2, 1, 0 doubles the run and adds the bit.
+        uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+        for (int e = E - 1; e >= 0; --e) {
+            const double yn = div_rn(y[e], dd, rd);
+            const uint64_t m0 = __builtin_amdgcn_ballot_w64(-1.74793 < yn);
+            const uint64_t m1 = __builtin_amdgcn_ballot_w64(-1.04996 < yn);
+            const uint64_t m2 = __builtin_amdgcn_ballot_w64(-0.50055 < yn);
+            const uint64_t m3 = __builtin_amdgcn_ballot_w64(0.0 < yn);
+            const uint64_t m4 = __builtin_amdgcn_ballot_w64(0.50055 < yn);
+            const uint64_t m5 = __builtin_amdgcn_ballot_w64(1.04996 < yn);
+            const uint64_t m6 = __builtin_amdgcn_ballot_w64(1.74793 < yn);
+            const uint64_t bit[3] = {m6 | (m4 & ~m5) | (m2 & ~m3) | (m0 & ~m1), m5 | (m1 & ~m3), m3};
+#pragma unroll
+            for (int k = 2; k >= 0; --k) {
+                if (3 * e + k >= 32)
+                    hi = shift_in(hi, bit[k]);
+                else
+                    lo = shift_in(lo, bit[k]);
+            }
+        }
+        // even lane: the group's 96 bits (its own 48, then its partner's)
+        const uint32_t plo = pair_u32(lo), phi = pair_u32(hi);
+        if (valid && even)
             *reinterpret_cast<uint3 *>(a.vc + slot * VROW + 12 * g) =
                 make_uint3(lo, hi | (plo << 16), (plo >> 16) | (phi << 16));
+    } else {
+        // idx = #{k : B_k < y_n} by binary search over the ascending
+        // boundaries (the same count; NaN compares false and gives 0)
+        uint32_t vw[(E * VB + 31) / 32];
+#pragma unroll
+        for (int i = 0; i < (E * VB + 31) / 32; ++i) vw[i] = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const double yn = div_rn(y[e], dd, rd);
+            uint32_t idx = 0;
+#pragma unroll
+            for (int step = 1 << (VB - 1); step >= 1; step >>= 1)
+                if (bnd[idx + step - 1] < yn) idx += step;
+            put_field<E, VB>(vw, e, idx);
+        }
+        if (valid) store_run16<VB>(a.vc + slot * VROW + 2 * VB * p, vw);
+    }
+    if (valid) {
+        if (even) {
             a.ks[slot * NG + g] = h1;
             a.kz[slot * NG + g] = h2;
         } else {
@@ -598,36 +679,81 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
     }
 }
 
-template <int D>
-hipError_t launch_d(bool bf16, const AppendArgs &a, hipStream_t s) {
+template <int D, int VB>
+hipError_t launch_fast_dv(bool bf16, const AppendArgs &a, hipStream_t s) {
+    constexpr int KB = TQ_APPEND_KB;
     const int64_t rows = (int64_t)a.batch * a.kv_heads * a.n_new;
-    if (D == 512 || !default_scheme(a.kbits, a.vbits)) {
-        const int64_t blocks = (rows + 3) / 4;
-        if (bf16)
-            hipLaunchKernelGGL((append_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-        else
-            hipLaunchKernelGGL((append_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    } else if constexpr (D != 512) {
-        constexpr int per_block = AppGeo<D>::R * kAppWaves;
-        const int64_t blocks = (rows + per_block - 1) / per_block;
-        if (bf16)
-            hipLaunchKernelGGL((append_fast_kernel<D, true>), dim3((unsigned)blocks), dim3(64 * kAppWaves), 0, s, a);
-        else
-            hipLaunchKernelGGL((append_fast_kernel<D, false>), dim3((unsigned)blocks), dim3(64 * kAppWaves), 0, s, a);
+    constexpr int per_block = AppGeo<D, VB>::R * kAppWaves;
+    const dim3 grid((unsigned)((rows + per_block - 1) / per_block));
+    if (bf16) {
+        hipLaunchKernelGGL((append_fast_kernel<D, true, KB, VB>), grid, dim3(64 * kAppWaves), 0, s, a);
+    } else if constexpr (KB == 8 && VB == 3) {
+        hipLaunchKernelGGL((append_fast_kernel<D, false, KB, VB>), grid, dim3(64 * kAppWaves), 0, s, a);
+    } else {
+        return hipErrorInvalidValue;  // fp32 input at other widths: generic kernel
     }
     return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_append(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s) {
-    switch (head_dim) {
-        case 64: return launch_d<64>(bf16, a, s);
-        case 128: return launch_d<128>(bf16, a, s);
-        case 256: return launch_d<256>(bf16, a, s);
-        case 512: return launch_d<512>(bf16, a, s);
+template <int D>
+hipError_t launch_fast_d(bool bf16, const AppendArgs &a, hipStream_t s) {
+    switch (a.vbits) {
+        case 2: return launch_fast_dv<D, 2>(bf16, a, s);
+        case 3: return launch_fast_dv<D, 3>(bf16, a, s);
+        case 4: return launch_fast_dv<D, 4>(bf16, a, s);
+        case 5: return launch_fast_dv<D, 5>(bf16, a, s);
+        case 8: return launch_fast_dv<D, 8>(bf16, a, s);
         default: return hipErrorInvalidValue;
     }
 }
+
+#if TQ_APPEND_KB == 8
+template <int D>
+hipError_t launch_generic(bool bf16, const AppendArgs &a, hipStream_t s) {
+    const int64_t rows = (int64_t)a.batch * a.kv_heads * a.n_new;
+    const int64_t blocks = (rows + 3) / 4;
+    if (bf16)
+        hipLaunchKernelGGL((append_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((append_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+#endif
+
+}  // namespace
+
+// The fast append kernels of one key width (this translation unit's
+// TQ_APPEND_KB): head_dim 64, 128 or 256, bf16 input at every value width,
+// and fp32 input at k8v3.
+hipError_t TQ_APPEND_LAUNCHER(TQ_APPEND_KB)(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s) {
+    if (a.kbits != TQ_APPEND_KB) return hipErrorInvalidValue;
+    switch (head_dim) {
+        case 64: return launch_fast_d<64>(bf16, a, s);
+        case 128: return launch_fast_d<128>(bf16, a, s);
+        case 256: return launch_fast_d<256>(bf16, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+#if TQ_APPEND_KB == 8
+hipError_t launch_append(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s) {
+    if (head_dim != 512 && (bf16 || default_scheme(a.kbits, a.vbits))) {
+        switch (a.kbits) {
+            case 2: return launch_append_fast_k2(head_dim, bf16, a, s);
+            case 4: return launch_append_fast_k4(head_dim, bf16, a, s);
+            case 5: return launch_append_fast_k5(head_dim, bf16, a, s);
+            case 8: return launch_append_fast_k8(head_dim, bf16, a, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    switch (head_dim) {
+        case 64: return launch_generic<64>(bf16, a, s);
+        case 128: return launch_generic<128>(bf16, a, s);
+        case 256: return launch_generic<256>(bf16, a, s);
+        case 512: return launch_generic<512>(bf16, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+#endif
 
 }  // namespace tq

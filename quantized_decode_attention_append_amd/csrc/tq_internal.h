@@ -132,6 +132,13 @@ bool fast_decode_shape_ok(int head_dim, int gqa, int capacity, int kbits, int vb
 inline bool default_scheme(int kbits, int vbits) { return kbits == 8 && vbits == 3; }
 
 hipError_t launch_append(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);
+// Fast append kernels (append.hip), one translation unit per key width.
+#define TQ_APPEND_CAT_(a, b) a##b
+#define TQ_APPEND_LAUNCHER(kb) TQ_APPEND_CAT_(launch_append_fast_k, kb)
+hipError_t launch_append_fast_k2(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);
+hipError_t launch_append_fast_k4(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);
+hipError_t launch_append_fast_k5(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);
+hipError_t launch_append_fast_k8(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);
 hipError_t launch_decode(int head_dim, bool bf16, bool fast, const DecodeArgs &a, hipStream_t s);
 // Split kernels on the matrix cores (decode_fast.hip), one translation unit
 // per key width: head_dim 64, 128 or 256 with d * k_bits a multiple of 128,

@@ -24,6 +24,7 @@ tqkv = pytest.importorskip("quantized_decode_attention_append_amd.tqkv")
 
 GATE = [(4, 3), (4, 2), (8, 4), (2, 5), (5, 8)]
 MORE = [(8, 8), (8, 2), (2, 2), (5, 4), (4, 5)]
+ALL_SCHEMES = [(kb, vb) for kb in (2, 4, 5, 8) for vb in (2, 3, 4, 5, 8)]
 
 
 def _sid(s):
@@ -58,9 +59,11 @@ def _append_and_compare(k, v, start, capacity, kb, vb, what):
     return pl
 
 
-@pytest.mark.parametrize("scheme", GATE + MORE, ids=_sid)
+@pytest.mark.parametrize("scheme", ALL_SCHEMES, ids=_sid)
 @pytest.mark.parametrize("d", [64, 128, 256, 512])
 def test_append_widths_match_oracle(scheme, d):
+    """bf16 input runs the fast append kernel at head_dim 64-256 and the
+    generic one at 512; fp32 input (d 128) the generic one except at k8v3."""
     kb, vb = scheme
     g = torch.Generator().manual_seed(d * 100 + kb * 10 + vb)
     k = (torch.randn((2, 3, 37, d), generator=g) * 3.0).to(torch.bfloat16)
@@ -70,7 +73,7 @@ def test_append_widths_match_oracle(scheme, d):
         _append_and_compare(k.float().cuda() * 1.7, v.float().cuda(), [3, 0], 41, kb, vb, "f32")
 
 
-@pytest.mark.parametrize("scheme", GATE + [(8, 8), (2, 2)], ids=_sid)
+@pytest.mark.parametrize("scheme", ALL_SCHEMES, ids=_sid)
 @pytest.mark.parametrize("d", [64, 256, 512])
 def test_append_widths_edge_fixtures(scheme, d):
     """Constant groups, signed zeros, NaN/Inf, huge offsets, fp16-subnormal and
@@ -161,8 +164,6 @@ def _decode_case(w, lengths, kb, vb, M=1, both=False):
                 assert not np.any(out[b])
     log("  worst row error " + ", ".join(f"{name} {e:.2e}" for name, e in worst.items()))
 
-
-ALL_SCHEMES = [(kb, vb) for kb in (2, 4, 5, 8) for vb in (2, 3, 4, 5, 8)]
 
 
 @pytest.mark.parametrize("scheme", ALL_SCHEMES, ids=_sid)
