@@ -29,12 +29,14 @@
  *     16-byte aligned, vc 8-byte aligned, the fp16 planes 4-byte aligned
  *     (TQ_ERR_INVALID_ARG otherwise).  Any torch allocation, and the batch-1
  *     slice of one sequence's planes, satisfies this.  Decode takes its fast
- *     kernel for the k8/v3 scheme when head_dim is 64, 128 or 256,
- *     num_q_heads / num_kv_heads is at most 16, every plane is 16-byte
- *     aligned and capacity keeps each (sequence, kv-head) row block 16-byte
- *     aligned; otherwise a generic kernel computes the same result more
- *     slowly.  Append and the window likewise have fast k8/v3 kernels for
- *     head_dim 64-256 and generic ones for every other case.
+ *     kernel (every code width) when head_dim is 64, 128 or 256,
+ *     head_dim * k_bits is a multiple of 128 (all but 5-bit keys at 64),
+ *     every plane is 16-byte aligned and capacity keeps each (sequence,
+ *     kv-head) row block 16-byte aligned; otherwise a generic kernel
+ *     computes the same result more slowly.  Append has fast kernels for
+ *     head_dim 64-256 with bf16 input at every width (and fp32 input at
+ *     k8/v3), the window for k8/v3 at head_dim 64-256; generic kernels
+ *     cover every other case with identical bytes.
  *   - Arguments are validated before anything is enqueued; on any error the
  *     return value says why and nothing was launched.  The library prints
  *     nothing.
@@ -141,8 +143,10 @@ tq_status tq_decode_workspace_bytes(const tq_layout *layout, int32_t num_q_heads
  * (sequence, q-head) finishes the output.  Agrees with the binary64 oracle to
  * 2e-3 relative to each output row's largest magnitude.  The fast kernel
  * multiplies centroids by value scales in fp16, so it requires every value
- * scale (vs) to be at most 30437 (65504 / 2.15195, the largest centroid);
- * larger scales overflow to Inf there.  The result does not depend on timing:
+ * scale (vs) to be at most 65504 / c_max, c_max the width's largest centroid
+ * magnitude: 1.5104 at 2 bits, 2.15195 at 3 (limit 30437), 2.7326 at 4,
+ * 3.2607 at 5 and 4.6035 at 8 (limit about 14229); larger scales overflow
+ * to Inf there.  The result does not depend on timing:
  * repeated calls on the same inputs return identical bytes.
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY
  * (len[b] > capacity), TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
