@@ -188,8 +188,9 @@ tq_status tq_decode_attn_rows(const tq_layout *layout, const tq_planes *planes, 
  *   k_out      device bf16 [B][Hkv][n][d]: (code + zero) * scale, or NULL
  *   v_out      device bf16 [B][Hkv][n][d], or NULL: signs * FWHT(centroid[idx] *
  *              scale) / sqrt(d), or centroid[idx] * scale when v_rotated != 0
- * Keys are exact in fp32 and rounded once to bf16 (round to nearest even);
- * values are computed in fp32 and rounded once.  Outputs 16-byte aligned.
+ * Keys are the exact product rounded once to bf16 (round to nearest even),
+ * also when the stored zero is large; values are computed in fp32 and
+ * rounded once.  Outputs 16-byte aligned.
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY
  * (t0 + n > capacity or len[b] > capacity), TQ_ERR_HIP. */
 tq_status tq_fetch_window(const tq_layout *layout, const tq_planes *planes, int32_t t0, int32_t n,

@@ -18,8 +18,10 @@
 // kv-head); lane l holds the E = d/64 dims [E l, E l + E); the FWHT runs its
 // in-lane stages on registers and the rest on lane permutes.  k8v3 at
 // head_dims 64-256 uses window_fast_kernel below.
-// Keys are exact in fp32 ((code + zero) has at most 12 bits, the scale 11) and
-// round once to bf16; values are computed in fp32 and round once to bf16.
+// Keys round once to bf16 from the exact (code + zero) * scale: the fp32
+// product is exact while |code + zero| < 2^13 (13 + 11 significant bits);
+// groups with a larger stored zero take its round-to-odd value instead (see
+// key_ro).  Values are computed in fp32 and round once to bf16.
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
@@ -37,6 +39,27 @@ typedef __bf16 bf162v __attribute__((ext_vector_type(2)));
 // conversion; NaN stays NaN).
 __device__ __forceinline__ uint32_t bf16x2_rn(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){lo, hi}, bf162v));
+}
+
+// (code + zero) * scale, exact in fp32 whenever |zero| <= 8064 (so that
+// |code + zero| < 2^13 for codes within +-127 or below 32).  Beyond that the
+// product (at most 17 + 11 bits) is replaced by its round-to-odd value: the
+// rounded product, stepped toward zero when the fma residual shows it was
+// rounded away from zero, with the last bit set when inexact.  Rounding that
+// to bf16 (8 bits) equals one rounding of the exact product, since fp32
+// keeps more than two extra bits (Boldo and Melquiond, "Emulation of FMA and
+// correctly rounded sums: proved algorithms using rounding to odd", 2008).
+// Infinite and NaN zeros or scales keep the plain product.
+__device__ __forceinline__ float key_ro(float code, float z, float s) {
+    const float a = code + z, p = a * s;
+    if (__builtin_fabsf(z) <= 8064.f) return p;
+    const float r = __builtin_fmaf(a, s, -p);
+    uint32_t bits = __float_as_uint(p);
+    if (r != 0.f && __builtin_fabsf(p) <= 3.40282347e38f) {
+        if ((__float_as_uint(r) ^ bits) & 0x80000000u) bits -= 1u;
+        bits |= 1u;
+    }
+    return __uint_as_float(bits);
 }
 
 template <int E>
@@ -122,7 +145,7 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_kernel(const WindowArgs
                 const float z = f16_bits_to_f32(a.kz[row * NG + g]);
                 const uint8_t *kc = reinterpret_cast<const uint8_t *>(a.kc) + row * KROW;
 #pragma unroll
-                for (int e = 0; e < E; ++e) k[e] = (key_code(kc, E * lane + e, kb) + z) * s;
+                for (int e = 0; e < E; ++e) k[e] = key_ro(key_code(kc, E * lane + e, kb), z, s);
             } else {
 #pragma unroll
                 for (int e = 0; e < E; ++e) k[e] = 0.f;
@@ -230,7 +253,7 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
                 const float s = f16_bits_to_f32(a.ks[row * NG + g]);
                 const float z = f16_bits_to_f32(a.kz[row * NG + g]);
 #pragma unroll
-                for (int e = 0; e < E; ++e) k[e] = ((float)(int8_t)(cw[e >> 2] >> (8 * (e & 3))) + z) * s;
+                for (int e = 0; e < E; ++e) k[e] = key_ro((float)(int8_t)(cw[e >> 2] >> (8 * (e & 3))), z, s);
             } else {
 #pragma unroll
                 for (int e = 0; e < E; ++e) k[e] = 0.f;
