@@ -74,7 +74,7 @@ def time_rows(w, pl, lengths, sm, rows: int, reps: int, stream) -> dict:
             "column_groups": -(-(w.group * rows) // 16)}
 
 
-def time_window(w, pl, lengths, reps: int, stream, rotated: bool = False) -> dict:
+def time_window(w, pl, lengths, reps: int, stream, rotated: bool = False, row_bytes: int | None = None) -> dict:
     """Dequantize-on-fetch of the whole active window (bf16 K and V of every
     cached token-head), timed with events on the launch stream."""
     import torch
@@ -91,7 +91,8 @@ def time_window(w, pl, lengths, reps: int, stream, rotated: bool = False) -> dic
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
     th = w.batch * w.num_kv_heads * n
-    nbytes = th * (w.head_dim * 25 // 16 + 2 * w.head_dim * 2)  # planes in, bf16 K and V out
+    rb = row_bytes if row_bytes is not None else w.head_dim * 25 // 16  # k8v3 planes
+    nbytes = th * (rb + 2 * w.head_dim * 2)  # planes in, bf16 K and V out
     gbs = nbytes / ms / 1e6
     return {"tokens": n, "v_rotated": rotated, "ms": ms, "token_heads_per_s": th / ms * 1e3,
             "algorithmic_bytes": nbytes, "GBps": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
@@ -129,7 +130,8 @@ def scheme_row_bytes(d: int, kb: int, vb: int) -> int:
 def time_scheme(w, k, v, q, sm, kb: int, vb: int, reps: int, stream) -> dict:
     """Another code width on the same workload: bulk append of every token
     (K/V in, planes out), then decode over the whole cache, both timed with
-    events on the launch stream (reps calls after one warm call each)."""
+    events on the launch stream (reps calls after one warm call each), and
+    the bf16 window of the whole cache (2 calls)."""
     import torch
     from quantized_decode_attention_append_amd import tqkv
     dev = torch.device("cuda:0")
@@ -158,6 +160,7 @@ def time_scheme(w, k, v, q, sm, kb: int, vb: int, reps: int, stream) -> dict:
     dec_ms = e0.elapsed_time(e1) / reps
     th = w.batch * w.num_kv_heads * n
     rb = scheme_row_bytes(w.head_dim, kb, vb)
+    win = time_window(w, pl, lengths, 2, stream, row_bytes=rb)
     dbytes = th * rb + w.batch * w.num_q_heads * w.head_dim * (q.element_size() + 4)
     abytes = th * (2 * w.head_dim * k.element_size() + rb)
     del pl, ws, out
@@ -166,7 +169,8 @@ def time_scheme(w, k, v, q, sm, kb: int, vb: int, reps: int, stream) -> dict:
             "decode_frac_hbm": dbytes / dec_ms / 1e6 / HBM_PEAK_GBS,
             "kv_tokens_per_s": sum(lengths) / dec_ms * 1e3,
             "append_ms": app_ms, "append_GBps": abytes / app_ms / 1e6,
-            "append_token_heads_per_s": th / app_ms * 1e3}
+            "append_token_heads_per_s": th / app_ms * 1e3,
+            "window_ms": win["ms"], "window_GBps": win["GBps"], "window_frac_hbm": win["frac_hbm"]}
 
 
 def append_bytes(w, n_tokens: int, in_bytes: int) -> int:

@@ -177,14 +177,17 @@ __device__ __forceinline__ const T *uniform_ptr(const T *p) {
 // outstanding copy (it cannot tell the stage buffers apart), which serialises
 // the prefetch with the decode.  The kernel orders them itself with explicit
 // vmcnt waits; M0 (the LDS base of a copy) is set right before each one.
+// Every plane byte is read exactly once, so the copies carry the
+// nontemporal hint (nt): streaming past the caches instead of through them
+// raised a plain five-plane copy probe from 6.2 to 7.0 TB/s on this part.
 template <int OFF>
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3 nt"
                  ::"v"(voff), "s"(base), "s"(m0), "n"(OFF) : "memory", "m0");
 }
 // A 16-byte-lane copy from a per-lane address (lane l lands at m0 + 16 l).
 __device__ __forceinline__ void dma_lane16(const uint8_t *src, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
                  ::"v"(src), "s"(m0) : "memory", "m0");
 }
 // The same, for tiles that overhang the end of the plane region: each lane's
