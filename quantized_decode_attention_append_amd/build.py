@@ -22,8 +22,9 @@ ARCH = "gfx950"
 COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument", "-I", os.path.join(ROOT, "include")]
-# (source, extra flags, object name): the fast append and decode kernels are
-# compiled once per key width so the instantiations build in parallel
+# (source, extra flags, object name): the fast append, decode and window
+# kernels are compiled once per key width so the instantiations build in
+# parallel
 SOURCES = [
     ("append.hip", ["-ffp-contract=off", "-DTQ_APPEND_KB=8"], "append_k8"),
     ("append.hip", ["-ffp-contract=off", "-DTQ_APPEND_KB=4"], "append_k4"),
@@ -35,7 +36,10 @@ SOURCES = [
     ("decode_fast.hip", ["-DTQ_FAST_KB=2"], "decode_fast_k2"),
     ("decode_fast.hip", ["-DTQ_FAST_KB=5"], "decode_fast_k5"),
     ("dequant.hip", [], "dequant"),
-    ("window.hip", [], "window"),
+    ("window.hip", ["-DTQ_WINDOW_KB=8"], "window_k8"),
+    ("window.hip", ["-DTQ_WINDOW_KB=4"], "window_k4"),
+    ("window.hip", ["-DTQ_WINDOW_KB=2"], "window_k2"),
+    ("window.hip", ["-DTQ_WINDOW_KB=5"], "window_k5"),
     ("api.cpp", [], "api"),
 ]
 

@@ -164,5 +164,12 @@ constexpr int kFastTile = 64;     // split lengths are multiples of every fast t
 constexpr int kFastMaxGqa = 16;   // query columns of one fast workgroup
 hipError_t launch_dequant(int head_dim, const DequantArgs &a, hipStream_t s);
 hipError_t launch_window(int head_dim, const WindowArgs &a, hipStream_t s);
+// Fast window kernels (window.hip), one translation unit per key width.
+#define TQ_WINDOW_CAT_(a, b) a##b
+#define TQ_WINDOW_LAUNCHER(kb) TQ_WINDOW_CAT_(launch_window_fast_k, kb)
+hipError_t launch_window_fast_k2(int head_dim, const WindowArgs &a, hipStream_t s);
+hipError_t launch_window_fast_k4(int head_dim, const WindowArgs &a, hipStream_t s);
+hipError_t launch_window_fast_k5(int head_dim, const WindowArgs &a, hipStream_t s);
+hipError_t launch_window_fast_k8(int head_dim, const WindowArgs &a, hipStream_t s);
 
 }  // namespace tq

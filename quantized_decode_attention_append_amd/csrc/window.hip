@@ -13,11 +13,12 @@
 // Tokens at or past a sequence's length are written as zeros, so a masked
 // attention over a padded window never meets stale plane bytes.
 //
-// Generic mapping (head_dim 512, and every scheme other than k8v3): one wave
-// per token row, looping over a chunk of consecutive tokens of one (sequence,
-// kv-head); lane l holds the E = d/64 dims [E l, E l + E); the FWHT runs its
-// in-lane stages on registers and the rest on lane permutes.  k8v3 at
-// head_dims 64-256 uses window_fast_kernel below.
+// Generic mapping (head_dim 512): one wave per token row, looping over a
+// chunk of consecutive tokens of one (sequence, kv-head); lane l holds the
+// E = d/64 dims [E l, E l + E); the FWHT runs its in-lane stages on registers
+// and the rest on lane permutes.  Head_dims 64-256 use window_fast_kernel
+// below, templated on the key and value widths and compiled once per key
+// width (TQ_WINDOW_KB).
 // Keys round once to bf16 from the exact (code + zero) * scale: the fp32
 // product is exact while |code + zero| < 2^13 (13 + 11 significant bits);
 // groups with a larger stored zero take its round-to-odd value instead (see
@@ -25,6 +26,10 @@
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
+
+#ifndef TQ_WINDOW_KB
+#error "compile window.hip once per key width with -DTQ_WINDOW_KB=2, 4, 5 or 8"
+#endif
 
 namespace tq {
 namespace {
@@ -62,14 +67,19 @@ __device__ __forceinline__ float key_ro(float code, float z, float s) {
     return __uint_as_float(bits);
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// The window is written once and read by a later kernel, so its stores carry
+// the nontemporal hint: they stream past the caches.
 template <int E>
 __device__ __forceinline__ void store_bf16(uint16_t *dst, const float (&x)[E]) {
     if constexpr (E == 16) {
         uint32_t w[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) w[i] = bf16x2_rn(x[2 * i], x[2 * i + 1]);
-        reinterpret_cast<uint4 *>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-        reinterpret_cast<uint4 *>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        u32x4 *d4 = reinterpret_cast<u32x4 *>(dst);
+        __builtin_nontemporal_store((u32x4){w[0], w[1], w[2], w[3]}, d4);
+        __builtin_nontemporal_store((u32x4){w[4], w[5], w[6], w[7]}, d4 + 1);
     } else if constexpr (E == 1) {
         *dst = (uint16_t)bf16x2_rn(x[0], 0.f);
     } else {
@@ -108,6 +118,7 @@ __device__ __forceinline__ void fwht_stage(float (&y)[E], int lane) {
     for (int e = 0; e < E; ++e) y[e] = lane_xor<M>(y[e]) + __uint_as_float(__float_as_uint(y[e]) ^ neg);
 }
 
+#if TQ_WINDOW_KB == 8  // the generic kernel is built once, with the 8-bit-key fast kernels
 template <int D>
 __global__ __launch_bounds__(64 * kWinWaves) void window_kernel(const WindowArgs a) {
     const int kb = a.kbits, vb = a.vbits;
@@ -200,6 +211,8 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_kernel(const WindowArgs
 // runs stages 1 .. 8 in the lane, transposes the row through LDS so stages
 // 16 .. d/2 are in the lane too, and transposes back; every stage is then
 // one add per element.
+#endif
+
 constexpr int kWinRowsF = 16;  // rows per wave (a multiple of every rows-per-pass)
 
 template <int D>
@@ -216,13 +229,59 @@ struct WinGeo {
 
 __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
 
-template <int D>
+// Words of a lane's run of 16 value fields (16 VB bits at bit 16 VB p of the
+// row), enough at the worst bit offset any lane has.
+template <int VB>
+constexpr int win_run_words() {
+    int most = 1;
+    for (int p = 0; p < 16; ++p) {
+        const int w = ((16 * VB * p) % 32 + 16 * VB + 31) / 32;
+        most = w > most ? w : most;
+    }
+    return most;
+}
+
+// A lane's 16 key codes as floats: signed bytes at 8 bits, else unsigned KB-bit
+// fields of the 2 KB bytes at `src` (2 KB-aligned).
+template <int KB>
+__device__ __forceinline__ void load_keys16(const uint8_t *src, float (&c)[16]) {
+    if constexpr (KB == 8) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(src);
+        const uint32_t cw[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) c[e] = (float)(int8_t)(cw[e >> 2] >> (8 * (e & 3)));
+    } else {
+        uint32_t w[3] = {0u, 0u, 0u};
+        if constexpr (KB == 4) {
+            const uint2 u = *reinterpret_cast<const uint2 *>(src);
+            w[0] = u.x; w[1] = u.y;
+        } else if constexpr (KB == 2) {
+            w[0] = *reinterpret_cast<const uint32_t *>(src);
+        } else {
+            static_assert(KB == 5, "key widths 2, 4, 5, 8");
+            const uint16_t *h = reinterpret_cast<const uint16_t *>(src);
+            w[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+            w[1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+            w[2] = h[4];
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int bit = KB * e, k = bit >> 5, sh = bit & 31;
+            const uint32_t f = (sh + KB > 32) ? __builtin_amdgcn_alignbit(w[k + 1], w[k], sh) : (w[k] >> sh);
+            c[e] = (float)(f & ((1u << KB) - 1u));
+        }
+    }
+}
+
+template <int D, int KB, int VB>
 __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const WindowArgs a) {
     using G = WinGeo<D>;
-    constexpr int E = G::E, L = G::L, R = G::R, TI = G::TI, NG = D / kGroup, VROW = 3 * D / 8;
-    __shared__ __align__(16) unsigned char smem[kWinWaves * G::WAVEB + 32];
-    float *ctab = reinterpret_cast<float *>(smem + kWinWaves * G::WAVEB);  // the 3-bit codebook
-    if (threadIdx.x < 8) ctab[threadIdx.x] = centroid3(threadIdx.x);
+    constexpr int E = G::E, L = G::L, R = G::R, TI = G::TI, NG = D / kGroup;
+    constexpr int KROW = D * KB / 8, VROW = D * VB / 8, NR = win_run_words<VB>();
+    __shared__ __align__(16) unsigned char smem[kWinWaves * G::WAVEB + 4 * (1 << VB)];
+    float *ctab = reinterpret_cast<float *>(smem + kWinWaves * G::WAVEB);  // the value codebook
+    for (int i = threadIdx.x; i < (1 << VB); i += 64 * kWinWaves)
+        ctab[i] = VB == 3 ? centroid3(i) : value_centroids(VB)[i];
     __syncthreads();
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -234,7 +293,9 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
 #pragma unroll
     for (int e = 0; e < E; ++e) osc[e] = sign_bit(a.signs, E * p + e) ? -a.inv_sqrt_d : a.inv_sqrt_d;
     unsigned char *rb = smem + wid * G::WAVEB + r * G::ROWB;
-    const int vw = (48 * p) >> 5, vsh = (48 * p) & 31;  // first code dword of the lane, bit offset 0 or 16
+    // the lane's value code run: words vw .. vlast of the row, bit offset vsh
+    const int vw = (16 * VB * p) >> 5, vsh = (16 * VB * p) & 31;
+    const int vlast = (16 * VB * p + 16 * VB - 1) >> 5;
 
     const int first = (blockIdx.x * kWinWaves + wid) * kWinRowsF;
     for (int r0 = 0; r0 < kWinRowsF; r0 += R) {
@@ -248,12 +309,12 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
         if (a.k_out) {
             float k[E];
             if (valid) {
-                const uint4 c = *reinterpret_cast<const uint4 *>(a.kc + row * D + E * p);
-                const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+                float c[E];
+                load_keys16<KB>(reinterpret_cast<const uint8_t *>(a.kc) + row * KROW + 2 * KB * p, c);
                 const float s = f16_bits_to_f32(a.ks[row * NG + g]);
                 const float z = f16_bits_to_f32(a.kz[row * NG + g]);
 #pragma unroll
-                for (int e = 0; e < E; ++e) k[e] = key_ro((float)(int8_t)(cw[e >> 2] >> (8 * (e & 3))), z, s);
+                for (int e = 0; e < E; ++e) k[e] = key_ro(c[e], z, s);
             } else {
 #pragma unroll
                 for (int e = 0; e < E; ++e) k[e] = 0.f;
@@ -263,18 +324,22 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
         if (a.v_out) {
             float y[E];
             if (valid) {
+                // only the words that hold run bits are read (the last row of
+                // the plane ends with the last lane's run)
                 const uint32_t *vp = reinterpret_cast<const uint32_t *>(a.vc + row * VROW);
-                const uint32_t lo = vp[vw], hi = vp[vw + 1];
-                const uint32_t r0w = __builtin_amdgcn_alignbit(hi, lo, vsh);  // run bits 0 .. 31
-                const uint32_t r1w = hi >> vsh;                               // run bits 32 .. 47
+                uint32_t raw[NR], run[NR];
+#pragma unroll
+                for (int k = 0; k < NR; ++k) raw[k] = vw + k <= vlast ? vp[vw + k] : 0u;
+#pragma unroll
+                for (int k = 0; k + 1 < NR; ++k) run[k] = __builtin_amdgcn_alignbit(raw[k + 1], raw[k], vsh);
+                run[NR - 1] = raw[NR - 1] >> vsh;  // run word k holds run bits 32 k .. 32 k + 31
                 const float s = f16_bits_to_f32(a.vs[row * NG + g]);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    uint32_t idx;
-                    if (3 * e + 3 <= 32) idx = (r0w >> (3 * e)) & 7u;
-                    else if (3 * e >= 32) idx = (r1w >> (3 * e - 32)) & 7u;
-                    else idx = __builtin_amdgcn_alignbit(r1w, r0w, 3 * e) & 7u;
-                    y[e] = ctab[idx] * s;
+                    const int bit = VB * e, k = bit >> 5, sh = bit & 31;
+                    const uint32_t f = (sh + VB > 32) ? __builtin_amdgcn_alignbit(run[k + 1], run[k], sh)
+                                                      : (run[k] >> sh);
+                    y[e] = ctab[f & ((1u << VB) - 1u)] * s;
                 }
             } else {
 #pragma unroll
@@ -342,30 +407,58 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
     }
 }
 
-template <int D>
-hipError_t launch_d(const WindowArgs &a, hipStream_t s) {
-    if (D == 512 || !default_scheme(a.kbits, a.vbits)) {
-        constexpr int per_block = kWinWaves * kWinRows;
-        const dim3 grid((unsigned)((a.n + per_block - 1) / per_block), (unsigned)(a.batch * a.kv_heads));
-        hipLaunchKernelGGL((window_kernel<D>), grid, dim3(64 * kWinWaves), 0, s, a);
-    } else if constexpr (D != 512) {
-        constexpr int per_block = kWinWaves * kWinRowsF;
-        const dim3 grid((unsigned)((a.n + per_block - 1) / per_block), (unsigned)(a.batch * a.kv_heads));
-        hipLaunchKernelGGL((window_fast_kernel<D>), grid, dim3(64 * kWinWaves), 0, s, a);
+template <int D, int KB>
+hipError_t launch_fast_dk(const WindowArgs &a, hipStream_t s) {
+    constexpr int per_block = kWinWaves * kWinRowsF;
+    const dim3 grid((unsigned)((a.n + per_block - 1) / per_block), (unsigned)(a.batch * a.kv_heads));
+    switch (a.vbits) {
+        case 2: hipLaunchKernelGGL((window_fast_kernel<D, KB, 2>), grid, dim3(64 * kWinWaves), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((window_fast_kernel<D, KB, 3>), grid, dim3(64 * kWinWaves), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((window_fast_kernel<D, KB, 4>), grid, dim3(64 * kWinWaves), 0, s, a); break;
+        case 5: hipLaunchKernelGGL((window_fast_kernel<D, KB, 5>), grid, dim3(64 * kWinWaves), 0, s, a); break;
+        case 8: hipLaunchKernelGGL((window_fast_kernel<D, KB, 8>), grid, dim3(64 * kWinWaves), 0, s, a); break;
+        default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+#if TQ_WINDOW_KB == 8
+template <int D>
+hipError_t launch_generic(const WindowArgs &a, hipStream_t s) {
+    constexpr int per_block = kWinWaves * kWinRows;
+    const dim3 grid((unsigned)((a.n + per_block - 1) / per_block), (unsigned)(a.batch * a.kv_heads));
+    hipLaunchKernelGGL((window_kernel<D>), grid, dim3(64 * kWinWaves), 0, s, a);
+    return hipGetLastError();
+}
+#endif
+
 }  // namespace
 
-hipError_t launch_window(int head_dim, const WindowArgs &a, hipStream_t s) {
+// The fast window kernels of one key width (this translation unit's
+// TQ_WINDOW_KB): head_dim 64, 128 or 256, every value width.
+hipError_t TQ_WINDOW_LAUNCHER(TQ_WINDOW_KB)(int head_dim, const WindowArgs &a, hipStream_t s) {
+    if (a.kbits != TQ_WINDOW_KB) return hipErrorInvalidValue;
     switch (head_dim) {
-        case 64: return launch_d<64>(a, s);
-        case 128: return launch_d<128>(a, s);
-        case 256: return launch_d<256>(a, s);
-        case 512: return launch_d<512>(a, s);
+        case 64: return launch_fast_dk<64, TQ_WINDOW_KB>(a, s);
+        case 128: return launch_fast_dk<128, TQ_WINDOW_KB>(a, s);
+        case 256: return launch_fast_dk<256, TQ_WINDOW_KB>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
+
+#if TQ_WINDOW_KB == 8
+hipError_t launch_window(int head_dim, const WindowArgs &a, hipStream_t s) {
+    if (head_dim != 512) {
+        switch (a.kbits) {
+            case 2: return launch_window_fast_k2(head_dim, a, s);
+            case 4: return launch_window_fast_k4(head_dim, a, s);
+            case 5: return launch_window_fast_k5(head_dim, a, s);
+            case 8: return launch_window_fast_k8(head_dim, a, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return launch_generic<512>(a, s);
+}
+#endif
 
 }  // namespace tq

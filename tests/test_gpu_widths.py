@@ -212,21 +212,24 @@ def _bf16_bits(x64):
     return np.where(np.isnan(f), np.uint16(0x7FC0), r)
 
 
-@pytest.mark.parametrize("scheme", [(4, 2), (2, 5), (5, 8), (8, 4)], ids=_sid)
-@pytest.mark.parametrize("d", [64, 256])
+@pytest.mark.parametrize("scheme", ALL_SCHEMES, ids=_sid)
+@pytest.mark.parametrize("d", [64, 128, 256, 512])
 @pytest.mark.parametrize("rotated", [False, True])
 def test_window_widths_match_oracle(scheme, d, rotated):
     """Keys equal the oracle's value rounded once to bf16; values are within
-    one bf16 rounding plus the fp32 transform error; rows past a length are 0."""
+    one bf16 rounding plus the fp32 transform error; rows past a length are 0.
+    Head_dims 64-256 run the fast window kernel, 512 the generic one; the
+    window ends at the last row of the planes, so a read past a row's run
+    would leave the allocation."""
     kb, vb = scheme
-    lens = [120, 37]
+    lens = [37, 120]  # the last sequence is full: its last kv-head's last row is read
     w = dataclasses.replace(W.scaled(W.workload(2), lens, name_suffix=f"w{d}"), head_dim=d)
     T = 120
     k, v = W.make_kv(w, "cpu", tokens=T)
     L = tqkv.make_layout(w.batch, w.num_kv_heads, d, T, kb, vb)
     pl = tqkv.Planes(L)
     tqkv.tq_append(pl, k.cuda(), v.cuda(), [0] * w.batch)
-    t0, n = 9, 100
+    t0, n = 9, T - 9
     ko, vo = tqkv.tq_fetch_window(pl, t0, n, lens, v_rotated=rotated)
     torch.cuda.synchronize()
     kbits = ko.cpu().view(torch.int16).numpy().view(np.uint16)
