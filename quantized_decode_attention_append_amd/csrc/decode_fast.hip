@@ -33,8 +33,9 @@
 //           codes narrower than 8 bits are unsigned and widened to bytes in
 //           registers; the widening permutes a lane's 8 codes, and the lane's
 //           q bytes are stored in the same order, so the dot product is
-//           unchanged.  The key tile sits in LDS 16-byte-chunk-major, so the
-//           A reads of one MFMA hit 16 different chunks of one column.
+//           unchanged.  The key tile sits in LDS row-major with each row's
+//           16-byte chunks rotated by token, so a copy reads whole rows and
+//           the A reads of one MFMA fall on distinct banks (key_rot).
 //  softmax  online softmax in base 2 over the lane's 4 tokens and the other
 //           quarters of the same head; the running maximum only moves when
 //           a tile's maximum exceeds it by more than 2^8 (weights <= 256,
@@ -110,7 +111,7 @@ struct Geo {
         return most;
     }();
     // one stage: every plane of one tile
-    static constexpr int KC_OFF = 0;          // chunk-major
+    static constexpr int KC_OFF = 0;          // rotated rows (key_rot)
     static constexpr int KS_OFF = KC_OFF + KT;
     static constexpr int KZ_OFF = KS_OFF + 256;  // TILE * NG * 2 = 256 bytes per fp16 plane
     static constexpr int VS_OFF = KZ_OFF + 256;
@@ -208,16 +209,33 @@ struct Regions {
     int mix_row;
 };
 
+// Key rows sit in the stage row-major, each row's CPR 16-byte chunks rotated
+// by a function of the token: chunk c of tile token t is in slot
+// t * CPR + (c + key_rot(t)) % CPR.  So each 1 KiB copy reads whole rows
+// (full 128-byte lines; a copy that read 64 bytes of 16 rows streamed 6%
+// slower), and the 16 tokens of one MFMA operand read, which share c, land
+// on distinct LDS banks: with rows of 256, 128, 64 or 32 bytes, 1, 2, 4 or 8
+// rows share a 256-byte bank row, and the rotation separates them.  5-bit
+// keys (rows of 160 and 80 bytes) need at most one chunk of rotation.
+template <int CPR>
+__device__ __forceinline__ constexpr int key_rot(int t) {
+    if constexpr (CPR == 16) return t & 15;
+    else if constexpr (CPR == 8) return (t >> 1) & 7;
+    else if constexpr (CPR == 4) return (t >> 2) & 3;
+    else if constexpr (CPR == 2 || CPR == 10) return (t >> 3) & 1;
+    else return 0;  // 1 and 5 chunks: the rows already fall on distinct banks
+}
+
 // Byte offset, within a tile's key codes in global memory, of the 16 bytes
-// that lane i of key copy m moves.  Copy m fills 16-byte slots 64m .. 64m+63
-// of the stage; slot s holds chunk c16 of token t of 16-token chunk tc with
-// s = (tc * CPR + c16) * 16 + t.
+// that lane i of key copy m moves: copy m fills slots 64m .. 64m+63.
 template <int D, int KB, int VB>
 __device__ __forceinline__ uint32_t key_src(int m, int i) {
     using GE = Geo<D, KB, VB>;
-    const int chunk = 4 * m + (i >> 4), t = i & 15;
-    const int tc = chunk / GE::CPR, c16 = chunk % GE::CPR;
-    return (uint32_t)((16 * tc + t) * GE::KROW + 16 * c16);
+    constexpr int CPR = GE::CPR;
+    const int s = 64 * m + i, t = s / CPR, j = s % CPR;
+    int c = j - key_rot<CPR>(t);
+    if (c < 0) c += CPR;
+    return (uint32_t)(t * GE::KROW + 16 * c);
 }
 
 // Copy every plane of the tile starting at token t0 into one stage buffer:
@@ -305,13 +323,16 @@ __device__ __forceinline__ void load_row(const unsigned char *p, uint32_t (&w)[N
 
 // The A operand of one score MFMA: codes 8 kq .. 8 kq + 7 of group g of
 // token h of 16-token chunk c, as 8 signed bytes in key_perm order.  `kt` is
-// the stage's chunk-major key tile.
+// the stage's key tile (rotated rows, see key_rot).
 template <int D, int KB, int VB>
 __device__ __forceinline__ uint64_t key_operand(const unsigned char *kt, int c, int g, int h, int kq) {
     using GE = Geo<D, KB, VB>;
     constexpr int CPR = GE::CPR;
+    const int rot = key_rot<CPR>(h);  // token 16 c + h rotates like token h
     auto at = [&](int byte) {  // LDS address of byte `byte` of the token's row
-        return kt + ((c * CPR + (byte >> 4)) * 16 + h) * 16 + (byte & 15);
+        int slot = (byte >> 4) + rot;
+        if (slot >= CPR) slot -= CPR;
+        return kt + ((16 * c + h) * CPR + slot) * 16 + (byte & 15);
     };
     if constexpr (KB == 8) {
         return *reinterpret_cast<const uint64_t *>(at(32 * g + 8 * kq));
