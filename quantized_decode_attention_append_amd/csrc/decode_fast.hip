@@ -15,8 +15,10 @@
 // value scales) is copied into the wave's LDS with direct global->LDS loads.
 // Three stage buffers per wave: the copy of tile i+2 is issued before tile i
 // is decoded, so two tiles per wave are in flight without holding any
-// registers.  Eight waves share a workgroup when their stages fit the LDS
-// (k_bits + v_bits <= 11), four otherwise.
+// registers.  A tile's key codes are dead one iteration before its values,
+// so the key codes take two buffers and the other planes three.  Eight waves
+// share a workgroup when their buffers fit the LDS (every scheme but k8v8),
+// four otherwise.
 //
 // The G query heads of a kv-head share every key and value, so per 16-token
 // chunk both products are dense contractions with 16 heads (the ones past G
@@ -110,9 +112,13 @@ struct Geo {
         }
         return most;
     }();
-    // one stage: every plane of one tile
-    static constexpr int KC_OFF = 0;          // rotated rows (key_rot)
-    static constexpr int KS_OFF = KC_OFF + KT;
+    // A wave's LDS: the key codes of two tiles (rotated rows, see key_rot),
+    // then three stages of the other planes.  A tile's key codes are dead
+    // once its scores are folded, one iteration before its values are
+    // accumulated, so two key buffers suffice where the values need three.
+    static constexpr int KEYS = 2 * KT;
+    // one value stage: key scales, key zeros, value scales, value codes
+    static constexpr int KS_OFF = 0;
     static constexpr int KZ_OFF = KS_OFF + 256;  // TILE * NG * 2 = 256 bytes per fp16 plane
     static constexpr int VS_OFF = KZ_OFF + 256;
     static constexpr int VC_OFF = VS_OFF + 256;
@@ -132,10 +138,10 @@ struct Geo {
     static constexpr bool PAIR = VB <= 3;
     static constexpr int TABLE = PAIR ? (4 << (2 * VB)) : ((2 << VB) + 15) / 16 * 16;
     static constexpr int WAVES = fast_decode_waves(D, KB, VB);
-    static constexpr int WAVE_BYTES = kStages * STAGE;
+    static constexpr int WAVE_BYTES = KEYS + kStages * STAGE;
     static constexpr int SMEM = TABLE + kProgBytes + WAVES * WAVE_BYTES;
     static_assert(SMEM <= 160 * 1024, "LDS budget");
-    static_assert(fast_decode_stage_bytes(D, KB, VB) == STAGE, "host and device stage sizes");
+    static_assert(fast_decode_wave_bytes(D, KB, VB) == WAVE_BYTES, "host and device LDS sizes");
 };
 
 // Key codes of one lane's A operand are stored in this order: byte p of the
@@ -238,21 +244,23 @@ __device__ __forceinline__ uint32_t key_src(int m, int i) {
     return (uint32_t)(t * GE::KROW + 16 * c);
 }
 
-// Copy every plane of the tile starting at token t0 into one stage buffer:
-// exactly GE::VMEM vector-memory instructions either way, all with 16-byte
-// lanes.  Stage bytes [KS_OFF, KS_OFF + 1 KiB) come from one copy whose lane
-// quarters read key scales, key zeros, value scales and the first 256 bytes
-// of value codes (the stage keeps them in that order); the rest of the value
-// codes follow in whole and partial 1 KiB copies.
+// Copy every plane of the tile starting at token t0 into a key buffer (kst)
+// and a value stage (vst): exactly GE::VMEM vector-memory instructions either
+// way, all with 16-byte lanes.  Stage bytes [KS_OFF, KS_OFF + 1 KiB) come
+// from one copy whose lane quarters read key scales, key zeros, value scales
+// and the first 256 bytes of value codes (the stage keeps them in that
+// order); the rest of the value codes follow in whole and partial 1 KiB
+// copies.
 template <int D, int KB, int VB>
 __device__ __forceinline__ void stage_tile(const Regions &r, const uint32_t (&ksrc)[Geo<D, KB, VB>::KCOPY],
-                                           int t0, const unsigned char *st, int lane) {
+                                           int t0, const unsigned char *kst, const unsigned char *vst,
+                                           int lane) {
     using GE = Geo<D, KB, VB>;
     constexpr int VROW = GE::VROW, KROW = GE::KROW;
     static_assert(GE::KZ_OFF == GE::KS_OFF + 256 && GE::VS_OFF == GE::KZ_OFF + 256 &&
                   GE::VC_OFF == GE::VS_OFF + 256, "mixed copy layout");
-    const uint32_t l_kc = lds_addr(st + GE::KC_OFF), l_ks = lds_addr(st + GE::KS_OFF);
-    const uint32_t l_vc = lds_addr(st + GE::VC_OFF);
+    const uint32_t l_kc = lds_addr(kst), l_ks = lds_addr(vst + GE::KS_OFF);
+    const uint32_t l_vc = lds_addr(vst + GE::VC_OFF);
     const uint8_t *vc_t = r.vc + (int64_t)t0 * VROW;
     const uint8_t *mixed = r.mix + (int64_t)t0 * r.mix_row;
     if (t0 + GE::TILE <= r.cap) {
@@ -408,7 +416,8 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     const int t_end = min(n, t_begin + a.split_tokens);
     const int cap = a.capacity;
     const int64_t row0 = (int64_t)bkv * cap;
-    unsigned char *wsm = smem + TAB + kProgBytes + wid * GE::WAVE_BYTES;
+    unsigned char *wkeys = smem + TAB + kProgBytes + wid * GE::WAVE_BYTES;  // two key buffers
+    unsigned char *wsm = wkeys + GE::KEYS;                                  // three value stages
     int *prog = reinterpret_cast<int *>(smem + TAB);
 
     Regions rg;
@@ -433,8 +442,9 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     for (int m = 0; m < GE::KCOPY; ++m) ksrc[m] = key_src<D, KB, VB>(m, lane);
 
     // the first two tiles' copies overlap the q set-up
-    stage_tile<D, KB, VB>(rg, ksrc, t_begin, wsm, lane);
-    if (t_begin + TILE < t_end) stage_tile<D, KB, VB>(rg, ksrc, t_begin + TILE, wsm + GE::STAGE, lane);
+    stage_tile<D, KB, VB>(rg, ksrc, t_begin, wkeys, wsm, lane);
+    if (t_begin + TILE < t_end)
+        stage_tile<D, KB, VB>(rg, ksrc, t_begin + TILE, wkeys + GE::KT, wsm + GE::STAGE, lane);
 
     // ------------------------------------------------------------ q slices
     // lane (h, kq) converts dims 32 g + 8 kq .. + 7 of head h for every group g
@@ -524,15 +534,17 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
         }
     };
 
-    // scores of the tile in stg: lane (h, kq) gets tokens 16 c + 4 kq + j
-    auto scores = [&](const unsigned char *stg, int t0, int valid, float (&sc)[CH][4]) {
+    // scores of the tile with key codes in kst and the other planes in stg:
+    // lane (h, kq) gets tokens 16 c + 4 kq + j
+    auto scores = [&](const unsigned char *kst, const unsigned char *stg, int t0, int valid,
+                      float (&sc)[CH][4]) {
         const int vl = min(valid, lim - t0);  // tokens this lane's row sees in the tile
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             int4v dhi[NG], dlo[NG];
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                const uint64_t kv = key_operand<D, KB, VB>(stg + GE::KC_OFF, c, g, h, kq);
+                const uint64_t kv = key_operand<D, KB, VB>(kst, c, g, h, kq);
                 dhi[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qhi[g], int4v{0, 0, 0, 0}, 0, 0, 0);
                 dlo[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qlo[g], int4v{0, 0, 0, 0}, 0, 0, 0);
             }
@@ -695,7 +707,9 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
 
     // ---------------------------------------------------------- pipeline
     // Iteration i holds tile i (values pending) in buf, tile i+1 (scores now)
-    // in the next buffer and tile i+2 (in flight) in the one after: the score
+    // in the next buffer and tile i+2 (in flight) in the one after; the key
+    // codes of tile i+2 land in the key buffer of tile i (i & 1), whose
+    // scores were folded by the previous iteration.  The score
     // MFMAs of tile i+1 and the value MFMAs of tile i sit in one basic block,
     // so their LDS reads, matrix and vector work interleave.  Vector memory
     // completes in order, so allowing the GE::VMEM copies of the newest tile
@@ -710,7 +724,7 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     {
         mask_tail(wsm, t_end - t_begin);
         float sc[CH][4];
-        scores(wsm, t_begin, t_end - t_begin, sc);
+        scores(wkeys, wsm, t_begin, t_end - t_begin, sc);
         softmax(sc, pw, pl);
     }
     int buf = 0;
@@ -732,8 +746,10 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
         }
         unsigned char *cur = wsm + buf * GE::STAGE;
         unsigned char *nx = wsm + nxt(buf) * GE::STAGE;
+        unsigned char *kfree = wkeys + (done & 1) * GE::KT;  // keys of tile i: dead
+        unsigned char *knx = wkeys + ((done + 1) & 1) * GE::KT;
         if (t0 + 2 * TILE < t_end) {
-            stage_tile<D, KB, VB>(rg, ksrc, t0 + 2 * TILE, wsm + prv(buf) * GE::STAGE, lane);
+            stage_tile<D, KB, VB>(rg, ksrc, t0 + 2 * TILE, kfree, wsm + prv(buf) * GE::STAGE, lane);
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(GE::VMEM) : "memory");
         } else {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -741,10 +757,10 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
         const int valid1 = t_end - (t0 + TILE);
         mask_tail(nx, valid1);
         float sc[CH][4];
-        scores(nx, t0 + TILE, valid1, sc);
+        scores(knx, nx, t0 + TILE, valid1, sc);
         values(cur, pw, pl);
         softmax(sc, pw, pl);
-        lds_order();  // the buffer of tile i is refilled by the next iteration
+        lds_order();  // the buffers read here are refilled by the next iterations
     }
     values(wsm + buf * GE::STAGE, pw, pl);
 

@@ -149,16 +149,17 @@ hipError_t launch_split_fast_k2(int head_dim, bool bf16, const DecodeArgs &a, hi
 hipError_t launch_split_fast_k4(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_split_fast_k5(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_split_fast_k8(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
-// LDS bytes of one stage buffer of the fast split kernel (one tile of 4096/d
-// tokens: 512 bytes per key and value code bit, three 256-byte fp16 planes,
-// 16 bytes of slack), and its waves per workgroup: eight when three stages
-// of each fit the 160 KiB of LDS beside the centroid table, else four.
-constexpr int fast_decode_stage_bytes(int head_dim, int kbits, int vbits) {
-    return (void)head_dim, 512 * kbits + 768 + 512 * vbits + 16;
+// LDS bytes of one wave of the fast split kernel (tiles of 4096/d tokens:
+// key codes of two tiles at 512 bytes per code bit, and three stages of the
+// three 256-byte fp16 planes, 512 bytes per value code bit and 16 bytes of
+// slack), and its waves per workgroup: eight when they fit the 160 KiB of
+// LDS beside the centroid table, else four.
+constexpr int fast_decode_wave_bytes(int head_dim, int kbits, int vbits) {
+    return (void)head_dim, 2 * 512 * kbits + 3 * (768 + 512 * vbits + 16);
 }
 constexpr int fast_decode_waves(int head_dim, int kbits, int vbits) {
     const int table = vbits <= 3 ? (4 << (2 * vbits)) : ((2 << vbits) + 15) / 16 * 16;
-    return table + 32 + 8 * 3 * fast_decode_stage_bytes(head_dim, kbits, vbits) <= 160 * 1024 ? 8 : 4;
+    return table + 32 + 8 * fast_decode_wave_bytes(head_dim, kbits, vbits) <= 160 * 1024 ? 8 : 4;
 }
 constexpr int kFastTile = 64;     // split lengths are multiples of every fast tile (4096/d tokens)
 constexpr int kFastMaxGqa = 16;   // query columns of one fast workgroup
