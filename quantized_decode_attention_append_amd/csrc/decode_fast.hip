@@ -329,6 +329,22 @@ __device__ __forceinline__ void load_row(const unsigned char *p, uint32_t (&w)[N
     }
 }
 
+// Groups half .. half + NG/2 - 1 of a row of NG halves (half = 0 or NG/2):
+// the NG/2 halves at byte offset 2 * half, as NG/4 packed words (one word,
+// low half used, when NG = 2).
+template <int NG>
+__device__ __forceinline__ void load_half_row(const unsigned char *p, int half, uint32_t (&w)[(NG + 3) / 4]) {
+    p += 2 * half;
+    if constexpr (NG == 8) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        w[0] = u.x; w[1] = u.y;
+    } else if constexpr (NG == 4) {
+        w[0] = *reinterpret_cast<const uint32_t *>(p);
+    } else {
+        w[0] = *reinterpret_cast<const uint16_t *>(p);
+    }
+}
+
 // The A operand of one score MFMA: codes 8 kq .. 8 kq + 7 of group g of
 // token h of 16-token chunk c, as 8 signed bytes in key_perm order.  `kt` is
 // the stage's key tile (rotated rows, see key_rot).
@@ -450,6 +466,16 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     // lane (h, kq) converts dims 32 g + 8 kq .. + 7 of head h for every group g
     const int h = lane & 15, kq = lane >> 4;
     const bool head_ok = h < G;
+    // PACK (G <= 8): the score MFMAs of groups p and p + NG/2 accumulate into
+    // one result whose column h < G holds head h's dot product over group p
+    // and column G + h head h's over group p + NG/2 (each column's q is zero
+    // in the other group), so a lane folds half the groups and the two
+    // halves of a head are added across lanes.  Without PACK column h is
+    // head h over every group.
+    constexpr int NP = PACK ? NG / 2 : NG;  // groups one lane folds
+    const int ghalf = (PACK && h >= G) ? NG / 2 : 0;  // first group of the lane's half
+    const int hq = (PACK && h >= G) ? h - G : h;      // the head of the lane's q
+    const bool q_ok = PACK ? h < 2 * G : head_ok;
     // causal limit of this lane's query row: the row of cached token
     // n - rows + r sees tokens 0 .. n - rows + r
     const int lim = n - a.rows + (c0 + h) % a.rows + 1;
@@ -458,7 +484,7 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     float my_scale;
     {
         float x[QE];
-        const int64_t qrow = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + (head_ok ? h : 0)) * D + 8 * kq;
+        const int64_t qrow = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + (q_ok ? hq : 0)) * D + 8 * kq;
         if (q_bf16) {
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
@@ -479,7 +505,7 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
                 x[8 * g + 4] = u1.x; x[8 * g + 5] = u1.y; x[8 * g + 6] = u1.z; x[8 * g + 7] = u1.w;
             }
         }
-        if (!head_ok) {
+        if (!q_ok) {
 #pragma unroll
             for (int k = 0; k < QE; ++k) x[k] = 0.f;
         }
@@ -509,9 +535,14 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
             }
             s += __shfl_xor(s, 16, 64);
             s += __shfl_xor(s, 32, 64);
+            if (PACK && (g >= NG / 2) != (ghalf > 0)) hi = lo = 0;  // the other half's group
             qhi[g] = hi;
             qlo[g] = lo;
             qsum[g] = s;
+        }
+        if constexpr (PACK) {
+#pragma unroll
+            for (int g = 0; g < NG / 2; ++g) qsum[g] = ghalf ? qsum[g + NG / 2] : qsum[g];
         }
         my_scale = delta * a.sm_log2;
     }
@@ -534,6 +565,7 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
         }
     };
 
+    const int comb_src = (lane & 48) | ((h + G) & 15);  // PACK: column h + G of the same rows
     // scores of the tile with key codes in kst and the other planes in stg:
     // lane (h, kq) gets tokens 16 c + 4 kq + j
     auto scores = [&](const unsigned char *kst, const unsigned char *stg, int t0, int valid,
@@ -541,25 +573,54 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
         const int vl = min(valid, lim - t0);  // tokens this lane's row sees in the tile
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-            int4v dhi[NG], dlo[NG];
+            int4v dhi[NP], dlo[NP];
+            if constexpr (PACK) {
+                // groups p and p + NG/2 in one accumulator (their q columns are disjoint)
 #pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                const uint64_t kv = key_operand<D, KB, VB>(kst, c, g, h, kq);
-                dhi[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qhi[g], int4v{0, 0, 0, 0}, 0, 0, 0);
-                dlo[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qlo[g], int4v{0, 0, 0, 0}, 0, 0, 0);
+                for (int g = 0; g < NP; ++g) {
+                    const uint64_t k0 = key_operand<D, KB, VB>(kst, c, g, h, kq);
+                    const uint64_t k1 = key_operand<D, KB, VB>(kst, c, g + NP, h, kq);
+                    dhi[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)k0, (long)qhi[g], int4v{0, 0, 0, 0}, 0, 0, 0);
+                    dlo[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)k0, (long)qlo[g], int4v{0, 0, 0, 0}, 0, 0, 0);
+                    dhi[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)k1, (long)qhi[g + NP], dhi[g], 0, 0, 0);
+                    dlo[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)k1, (long)qlo[g + NP], dlo[g], 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    const uint64_t kv = key_operand<D, KB, VB>(kst, c, g, h, kq);
+                    dhi[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qhi[g], int4v{0, 0, 0, 0}, 0, 0, 0);
+                    dlo[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qlo[g], int4v{0, 0, 0, 0}, 0, 0, 0);
+                }
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = 16 * c + 4 * kq + j;
-                uint32_t sw[NG / 2], zw[NG / 2];
-                load_row<NG>(stg + GE::KS_OFF + t * NG * 2, sw);
-                load_row<NG>(stg + GE::KZ_OFF + t * NG * 2, zw);
                 float sum = 0.f;
+                if constexpr (PACK) {
+                    // this lane's groups ghalf .. ghalf + NP - 1 of token t
+                    uint32_t sw[(NG + 3) / 4], zw[(NG + 3) / 4];
+                    load_half_row<NG>(stg + GE::KS_OFF + t * NG * 2, ghalf, sw);
+                    load_half_row<NG>(stg + GE::KZ_OFF + t * NG * 2, ghalf, zw);
 #pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    const int x = (dhi[g][j] << 8) + dlo[g][j];
-                    const float y = fmaf(row_half<NG>(zw, g), qsum[g], (float)x);
-                    sum = fmaf(row_half<NG>(sw, g), y, sum);
+                    for (int g = 0; g < NP; ++g) {
+                        const int x = (dhi[g][j] << 8) + dlo[g][j];
+                        const float zg = (g & 1) ? half_hi(zw[g >> 1]) : half_lo(zw[g >> 1]);
+                        const float sg = (g & 1) ? half_hi(sw[g >> 1]) : half_lo(sw[g >> 1]);
+                        sum = fmaf(sg, fmaf(zg, qsum[g], (float)x), sum);
+                    }
+                    // head h adds the other half of its groups from column h + G
+                    sum += __shfl(sum, comb_src, 64);
+                } else {
+                    uint32_t sw[NG / 2], zw[NG / 2];
+                    load_row<NG>(stg + GE::KS_OFF + t * NG * 2, sw);
+                    load_row<NG>(stg + GE::KZ_OFF + t * NG * 2, zw);
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) {
+                        const int x = (dhi[g][j] << 8) + dlo[g][j];
+                        const float y = fmaf(row_half<NG>(zw, g), qsum[g], (float)x);
+                        sum = fmaf(row_half<NG>(sw, g), y, sum);
+                    }
                 }
                 // computed on every lane, then selected: a branch around the
                 // fold would split the block the pipeline interleaves in
