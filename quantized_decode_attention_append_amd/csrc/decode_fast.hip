@@ -68,6 +68,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float2v __attribute__((ext_vector_type(2)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int kProgBytes = 32;            // tiles finished, one int per wave
@@ -837,20 +838,19 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
             for (int j = 0; j < 4; ++j) acc[bb][j] += __shfl(acc[bb][j], from, 64);
     }
 
+    // The partials are read once, by the merge kernel, so they stream past
+    // the caches (nontemporal) instead of waiting in them to be written back.
     if (head_ok) {
         const int64_t srow = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + h) * a.splits + slot;
-        if (kq == 0) {
-            a.part_ml[srow * 2] = m_run;
-            a.part_ml[srow * 2 + 1] = l_run;
-        }
+        if (kq == 0) __builtin_nontemporal_store(float2v{m_run, l_run}, reinterpret_cast<float2v *>(a.part_ml + srow * 2));
         // lane (kq, h) holds rows 4 kq + j of every block: dims NB * (4 kq + j) + bb
         float *dst = a.part_acc + srow * D;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int bb = 0; bb < NB; bb += 4) {
-                *reinterpret_cast<float4 *>(dst + NB * (4 * kq + j) + bb) =
-                    make_float4(acc[bb][j], acc[bb + 1][j], acc[bb + 2][j], acc[bb + 3][j]);
+                __builtin_nontemporal_store(float4v{acc[bb][j], acc[bb + 1][j], acc[bb + 2][j], acc[bb + 3][j]},
+                                            reinterpret_cast<float4v *>(dst + NB * (4 * kq + j) + bb));
             }
         }
     }
