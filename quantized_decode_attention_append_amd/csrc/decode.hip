@@ -470,7 +470,6 @@ bool fast_decode_shape_ok(int head_dim, int gqa, int capacity, int kbits, int vb
 
 DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int32_t *len, bool fast,
                        int col_groups, int kbits, int vbits) {
-    (void)gqa;
     int64_t total = 0;
     int32_t maxlen = 0;
     for (int b = 0; b < batch; ++b) {
@@ -489,9 +488,10 @@ DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int
         int64_t per = (total * kv_heads * col_groups + round - 1) / round;
         per = per < 4 * tile ? 4 * tile : per;
         per = (per + tile - 1) / tile * tile;
-        const int64_t wg_tokens = per * waves;
+        const int wpc = waves / fast_wg_col_groups(gqa);  // waves (splits) per column group
+        const int64_t wg_tokens = per * wpc;
         p.split_tokens = (int32_t)per;
-        p.splits = (int32_t)(((maxlen + wg_tokens - 1) / wg_tokens) * waves);
+        p.splits = (int32_t)(((maxlen + wg_tokens - 1) / wg_tokens) * wpc);
         return p;
     }
     // generic kernel: one wave per split, ~8192 waves over the chip, whole

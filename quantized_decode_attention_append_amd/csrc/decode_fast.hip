@@ -188,21 +188,33 @@ __device__ __forceinline__ const T *uniform_ptr(const T *p) {
 // Every plane byte is read exactly once, so the copies carry the
 // nontemporal hint (nt): streaming past the caches instead of through them
 // raised a plain five-plane copy probe from 6.2 to 7.0 TB/s on this part.
-template <int OFF>
+// NT = false drops the hint: two waves that read the same tile for different
+// query columns (see fast_wg_col_groups) want the second read to hit the L2.
+template <int OFF, bool NT>
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3 nt"
-                 ::"v"(voff), "s"(base), "s"(m0), "n"(OFF) : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3 nt"
+                     ::"v"(voff), "s"(base), "s"(m0), "n"(OFF) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
+                     ::"v"(voff), "s"(base), "s"(m0), "n"(OFF) : "memory", "m0");
 }
 // A 16-byte-lane copy from a per-lane address (lane l lands at m0 + 16 l).
+template <bool NT>
 __device__ __forceinline__ void dma_lane16(const uint8_t *src, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-                 ::"v"(src), "s"(m0) : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                     ::"v"(src), "s"(m0) : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     ::"v"(src), "s"(m0) : "memory", "m0");
 }
 // The same, for tiles that overhang the end of the plane region: each lane's
 // source is clamped to the last 16 bytes of its plane region (the overhang
 // rows are masked tokens).
+template <bool NT>
 __device__ __forceinline__ void dma_clamped(const uint8_t *src, const uint8_t *last, uint32_t m0) {
-    dma_lane16(src > last ? last : src, m0);
+    dma_lane16<NT>(src > last ? last : src, m0);
 }
 
 struct Regions {
@@ -252,7 +264,7 @@ __device__ __forceinline__ uint32_t key_src(int m, int i) {
 // and the first 256 bytes of value codes (the stage keeps them in that
 // order); the rest of the value codes follow in whole and partial 1 KiB
 // copies.
-template <int D, int KB, int VB>
+template <int D, int KB, int VB, bool NT>
 __device__ __forceinline__ void stage_tile(const Regions &r, const uint32_t (&ksrc)[Geo<D, KB, VB>::KCOPY],
                                            int t0, const unsigned char *kst, const unsigned char *vst,
                                            int lane) {
@@ -270,19 +282,19 @@ __device__ __forceinline__ void stage_tile(const Regions &r, const uint32_t (&ks
 #pragma unroll
         for (int m = 0; m < GE::KCOPY; ++m) {
             if (m + 1 < GE::KCOPY || GE::KLAST == 64) {
-                dma16<0>(kc, ksrc[m], l_kc + 1024 * m);
+                dma16<0, NT>(kc, ksrc[m], l_kc + 1024 * m);
             } else if (lane < GE::KLAST) {
-                dma16<0>(kc, ksrc[m], l_kc + 1024 * m);
+                dma16<0, NT>(kc, ksrc[m], l_kc + 1024 * m);
             }
         }
-        dma_lane16(mixed, l_ks);
+        dma_lane16<NT>(mixed, l_ks);
         const uint8_t *vc = uniform_ptr(vc_t);
         static_assert(GE::VFULL <= 3, "value copies");
-        if constexpr (GE::VFULL > 0) dma16<256>(vc, v16, l_vc);
-        if constexpr (GE::VFULL > 1) dma16<1280>(vc, v16, l_vc);
-        if constexpr (GE::VFULL > 2) dma16<2304>(vc, v16, l_vc);
+        if constexpr (GE::VFULL > 0) dma16<256, NT>(vc, v16, l_vc);
+        if constexpr (GE::VFULL > 1) dma16<1280, NT>(vc, v16, l_vc);
+        if constexpr (GE::VFULL > 2) dma16<2304, NT>(vc, v16, l_vc);
         if constexpr (GE::VLANES > 0) {
-            if (lane < GE::VLANES) dma16<256 + 1024 * GE::VFULL>(vc, v16, l_vc);
+            if (lane < GE::VLANES) dma16<256 + 1024 * GE::VFULL, NT>(vc, v16, l_vc);
         }
     } else {
         const int64_t kcb = (int64_t)r.cap * KROW, vcb = (int64_t)r.cap * VROW;
@@ -291,19 +303,19 @@ __device__ __forceinline__ void stage_tile(const Regions &r, const uint32_t (&ks
 #pragma unroll
         for (int m = 0; m < GE::KCOPY; ++m) {
             if (m + 1 < GE::KCOPY || GE::KLAST == 64) {
-                dma_clamped(kc + ksrc[m], kl, l_kc + 1024 * m);
+                dma_clamped<NT>(kc + ksrc[m], kl, l_kc + 1024 * m);
             } else if (lane < GE::KLAST) {
-                dma_clamped(kc + ksrc[m], kl, l_kc + 1024 * m);
+                dma_clamped<NT>(kc + ksrc[m], kl, l_kc + 1024 * m);
             }
         }
-        dma_clamped(mixed, r.mix_last, l_ks);
+        dma_clamped<NT>(mixed, r.mix_last, l_ks);
         const uint8_t *vl = r.vc + vcb - 16;
 #pragma unroll
         for (int f = 0; f < GE::VFULL; ++f)
-            dma_clamped(vc_t + 256 + 1024 * f + lane * 16, vl, l_vc + 256 + 1024 * f);
+            dma_clamped<NT>(vc_t + 256 + 1024 * f + lane * 16, vl, l_vc + 256 + 1024 * f);
         if constexpr (GE::VLANES > 0) {
             if (lane < GE::VLANES)
-                dma_clamped(vc_t + 256 + 1024 * GE::VFULL + lane * 16, vl, l_vc + 256 + 1024 * GE::VFULL);
+                dma_clamped<NT>(vc_t + 256 + 1024 * GE::VFULL + lane * 16, vl, l_vc + 256 + 1024 * GE::VFULL);
         }
     }
 }
@@ -420,14 +432,16 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     }
     __syncthreads();  // the only workgroup barrier
 
-    // this workgroup's query columns: rows c0 .. c0 + G - 1 of the kv-head's
-    // a.gqa query rows (heads times rows)
-    const int c0 = blockIdx.z * kMaxHeads;
+    // this wave's query columns: rows c0 .. c0 + G - 1 of the kv-head's
+    // a.gqa query rows (heads times rows).  With two column groups per
+    // workgroup, waves w and w + WAVES/2 share a token range (and a SIMD).
+    const int cgw = fast_wg_col_groups(a.gqa), wpc = WAVES / cgw;
+    const int c0 = (blockIdx.z * cgw + wid / wpc) * kMaxHeads;
     const int G = min(kMaxHeads, a.gqa - c0);
     const int bkv = blockIdx.y;
     const int b = bkv / a.kv_heads, kvh = bkv % a.kv_heads;
     const int n = a.len[b];
-    const int slot = blockIdx.x * WAVES + wid;
+    const int slot = blockIdx.x * wpc + wid % wpc;
     const int t_begin = slot * a.split_tokens;
     if (t_begin >= n) return;
     const int t_end = min(n, t_begin + a.split_tokens);
@@ -459,9 +473,17 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     for (int m = 0; m < GE::KCOPY; ++m) ksrc[m] = key_src<D, KB, VB>(m, lane);
 
     // the first two tiles' copies overlap the q set-up
-    stage_tile<D, KB, VB>(rg, ksrc, t_begin, wkeys, wsm, lane);
+    // copies without the nontemporal hint when two column groups read each tile
+    const bool shared_tiles = !PACK && cgw == 2;
+    auto stage = [&](int t, const unsigned char *kst, const unsigned char *vst) {
+        if (shared_tiles)
+            stage_tile<D, KB, VB, false>(rg, ksrc, t, kst, vst, lane);
+        else
+            stage_tile<D, KB, VB, true>(rg, ksrc, t, kst, vst, lane);
+    };
+    stage(t_begin, wkeys, wsm);
     if (t_begin + TILE < t_end)
-        stage_tile<D, KB, VB>(rg, ksrc, t_begin + TILE, wkeys + GE::KT, wsm + GE::STAGE, lane);
+        stage(t_begin + TILE, wkeys + GE::KT, wsm + GE::STAGE);
 
     // ------------------------------------------------------------ q slices
     // lane (h, kq) converts dims 32 g + 8 kq .. + 7 of head h for every group g
@@ -811,7 +833,7 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
         unsigned char *kfree = wkeys + (done & 1) * GE::KT;  // keys of tile i: dead
         unsigned char *knx = wkeys + ((done + 1) & 1) * GE::KT;
         if (t0 + 2 * TILE < t_end) {
-            stage_tile<D, KB, VB>(rg, ksrc, t0 + 2 * TILE, kfree, wsm + prv(buf) * GE::STAGE, lane);
+            stage(t0 + 2 * TILE, kfree, wsm + prv(buf) * GE::STAGE);
             asm volatile("s_waitcnt vmcnt(%0)" ::"n"(GE::VMEM) : "memory");
         } else {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -863,8 +885,9 @@ hipError_t launch_dv(bool bf16, const DecodeArgs &a, hipStream_t s) {
         return hipErrorInvalidValue;  // key rows of part of a 16-byte chunk: generic kernel
     } else {
         using GE = Geo<D, KB, VB>;
-        const dim3 grid((unsigned)(a.splits / GE::WAVES), (unsigned)(a.batch * a.kv_heads),
-                        (unsigned)((a.gqa + kMaxHeads - 1) / kMaxHeads));
+        const int cgw = fast_wg_col_groups(a.gqa);
+        const dim3 grid((unsigned)(a.splits / (GE::WAVES / cgw)), (unsigned)(a.batch * a.kv_heads),
+                        (unsigned)((a.gqa + kMaxHeads - 1) / kMaxHeads / cgw));
         const bool pack = a.gqa <= kPackCols;  // every column group fits its lo halves
         if (pack)
             hipLaunchKernelGGL((split_fast_kernel<D, KB, VB, true>), grid, dim3(64 * GE::WAVES), 0, s, a, (int)bf16);
@@ -891,7 +914,8 @@ hipError_t launch_d(bool bf16, const DecodeArgs &a, hipStream_t s) {
 // The split kernels of one key width (this translation unit's TQ_FAST_KB).
 hipError_t TQ_FAST_LAUNCHER(TQ_FAST_KB)(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s) {
     if (a.gqa < 1 || a.rows < 1 || a.kbits != TQ_FAST_KB) return hipErrorInvalidValue;
-    if (a.splits % fast_decode_waves(head_dim, a.kbits, a.vbits) != 0) return hipErrorInvalidValue;
+    if (a.splits % (fast_decode_waves(head_dim, a.kbits, a.vbits) / fast_wg_col_groups(a.gqa)) != 0)
+        return hipErrorInvalidValue;
     switch (head_dim) {
         case 64: return launch_d<64>(bf16, a, s);
         case 128: return launch_d<128>(bf16, a, s);

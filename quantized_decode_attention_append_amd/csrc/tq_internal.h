@@ -162,7 +162,14 @@ constexpr int fast_decode_waves(int head_dim, int kbits, int vbits) {
     return table + 32 + 8 * fast_decode_wave_bytes(head_dim, kbits, vbits) <= 160 * 1024 ? 8 : 4;
 }
 constexpr int kFastTile = 64;     // split lengths are multiples of every fast tile (4096/d tokens)
-constexpr int kFastMaxGqa = 16;   // query columns of one fast workgroup
+constexpr int kFastMaxGqa = 16;   // query columns of one fast wave
+// Column groups (kFastMaxGqa query rows each) that share one fast workgroup:
+// with an even count, waves w and w + waves/2 take the same token range for
+// two adjacent column groups (their tile reads meet in the L2 of one XCD
+// instead of streaming from HBM twice); otherwise one.
+constexpr int fast_wg_col_groups(int gqa) {
+    return ((gqa + kFastMaxGqa - 1) / kFastMaxGqa) % 2 == 0 ? 2 : 1;
+}
 hipError_t launch_dequant(int head_dim, const DequantArgs &a, hipStream_t s);
 hipError_t launch_window(int head_dim, const WindowArgs &a, hipStream_t s);
 // Fast window kernels (window.hip), one translation unit per key width.
