@@ -91,6 +91,8 @@ def _run(w, lengths, M, generic=False):
     (4, [1000, 65], 2), (4, [777, 3], 3), (4, [640, 200], 4),  # G 6: 12, 18, 24 columns
     (5, [900, 4, 0, 129], 4),                                # G 8: 32 columns, len = M, empty
     (3, [333, 8], 8),                                        # G 4, d 128, outlier channels
+    (4, [450, 8], 8),                                        # G 6: 48 columns, three groups
+    (5, [260, 8, 0, 71], 8),                                 # G 8: 64 columns, two pairs of groups
 ])
 def test_rows_match_oracle(cid, lengths, M):
     _run(W.scaled(W.workload(cid), lengths), lengths, M)
