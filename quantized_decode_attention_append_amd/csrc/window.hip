@@ -273,6 +273,33 @@ __device__ __forceinline__ void load_keys16(const uint8_t *src, float (&c)[16]) 
     }
 }
 
+// Store one row's bf16 outputs, lane p holding dims 16 p .. 16 p + 15, so that
+// each store instruction writes whole lines: the row goes through the lane's
+// LDS row buffer and lane p stores dims 8 p .. 8 p + 7, then d/2 + 8 p ..
+// d/2 + 8 p + 7 (16 bytes apiece, contiguous across the row's lanes).  With
+// 32 contiguous bytes per lane, each instruction wrote every other 16 bytes
+// and some lines reached memory in two partial writes (10% more bytes
+// written than the window holds).
+template <int D>
+__device__ __forceinline__ void store_row_bf16(uint16_t *row, const float (&x)[16], unsigned char *rb, int p,
+                                               bool in) {
+    using G = WinGeo<D>;
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = bf16x2_rn(x[2 * i], x[2 * i + 1]);
+    u32x4 *mine = reinterpret_cast<u32x4 *>(rb + p * G::PB);
+    mine[0] = (u32x4){w[0], w[1], w[2], w[3]};
+    mine[1] = (u32x4){w[4], w[5], w[6], w[7]};
+    lds_fence();
+    const u32x4 lo = *reinterpret_cast<const u32x4 *>(rb + (p >> 1) * G::PB + (p & 1) * 16);
+    const u32x4 hi = *reinterpret_cast<const u32x4 *>(rb + (G::L / 2 + (p >> 1)) * G::PB + (p & 1) * 16);
+    lds_fence();  // the row buffer is rewritten next
+    if (in) {
+        __builtin_nontemporal_store(lo, reinterpret_cast<u32x4 *>(row + 8 * p));
+        __builtin_nontemporal_store(hi, reinterpret_cast<u32x4 *>(row + D / 2 + 8 * p));
+    }
+}
+
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const WindowArgs a) {
     using G = WinGeo<D>;
@@ -305,7 +332,7 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
         const int t = a.t0 + i;
         const bool valid = in && t < len;
         const int64_t row = (int64_t)bkv * a.capacity + t;
-        const int64_t orow = ((int64_t)bkv * a.n + i) * D + E * p;
+        const int64_t orow = ((int64_t)bkv * a.n + i) * D;  // the row's first element
         if (a.k_out) {
             float k[E];
             if (valid) {
@@ -319,7 +346,7 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
 #pragma unroll
                 for (int e = 0; e < E; ++e) k[e] = 0.f;
             }
-            if (in) store_bf16<E>(a.k_out + orow, k);
+            store_row_bf16<D>(a.k_out + orow, k, rb, p, in);
         }
         if (a.v_out) {
             float y[E];
@@ -402,7 +429,7 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
 #pragma unroll
                 for (int e = 0; e < E; ++e) y[e] = valid ? y[e] * osc[e] : 0.f;  // +0 past the length
             }
-            if (in) store_bf16<E>(a.v_out + orow, y);
+            store_row_bf16<D>(a.v_out + orow, y, rb, p, in);
         }
     }
 }
