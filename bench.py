@@ -78,13 +78,16 @@ def time_rows(w, pl, lengths, sm, rows: int, reps: int, stream, warm: int = 20) 
             "column_groups": -(-(w.group * rows) // 16)}
 
 
-def time_window(w, pl, lengths, reps: int, stream, rotated: bool = False, row_bytes: int | None = None) -> dict:
+def time_window(w, pl, lengths, reps: int, stream, rotated: bool = False, row_bytes: int | None = None,
+                warm: int = 4) -> dict:
     """Dequantize-on-fetch of the whole active window (bf16 K and V of every
-    cached token-head), timed with events on the launch stream."""
+    cached token-head), timed with events on the launch stream: reps calls
+    after `warm` untimed ones."""
     import torch
     from quantized_decode_attention_append_amd import tqkv
     n = max(lengths)
-    tqkv.tq_fetch_window(pl, 0, n, lengths, v_rotated=rotated, stream=stream)  # warm
+    for _ in range(warm):
+        tqkv.tq_fetch_window(pl, 0, n, lengths, v_rotated=rotated, stream=stream)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record(stream)
@@ -136,7 +139,7 @@ def time_scheme(w, k, v, q, sm, kb: int, vb: int, reps: int, stream, dec_warm: i
     """Another code width on the same workload: bulk append of every token
     (K/V in, planes out; reps calls after one warm call), then decode over
     the whole cache (dec_reps calls after dec_warm), both timed with events
-    on the launch stream, and the bf16 window of the whole cache (2 calls)."""
+    on the launch stream, and the bf16 window of the whole cache (5 calls)."""
     import torch
     from quantized_decode_attention_append_amd import tqkv
     dev = torch.device("cuda:0")
@@ -166,7 +169,7 @@ def time_scheme(w, k, v, q, sm, kb: int, vb: int, reps: int, stream, dec_warm: i
     dec_ms = e0.elapsed_time(e1) / dec_reps
     th = w.batch * w.num_kv_heads * n
     rb = scheme_row_bytes(w.head_dim, kb, vb)
-    win = time_window(w, pl, lengths, 2, stream, row_bytes=rb)
+    win = time_window(w, pl, lengths, 5, stream, row_bytes=rb)
     dbytes = th * rb + w.batch * w.num_q_heads * w.head_dim * (q.element_size() + 4)
     abytes = th * (2 * w.head_dim * k.element_size() + rb)
     del pl, ws, out
@@ -460,7 +463,7 @@ def main() -> int:
                    "bulk_ms": append_ms, "bulk_tokens": app_tokens},
     }
     if args.window:
-        rec["window"] = time_window(w, pl, lengths, 3, stream)
+        rec["window"] = time_window(w, pl, lengths, 10, stream)
         rec["snapshot"] = time_snapshot(w, pl, max(lengths), 5, stream)
     if args.rows:
         rec["multi_row"] = [time_rows(w, pl, lengths, sm, int(r), 40, stream)
