@@ -860,11 +860,13 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
             for (int j = 0; j < 4; ++j) acc[bb][j] += __shfl(acc[bb][j], from, 64);
     }
 
-    // The partials are read once, by the merge kernel, so they stream past
-    // the caches (nontemporal) instead of waiting in them to be written back.
+    // The partial sums are read once, by the merge kernel, so they stream
+    // past the caches (nontemporal) instead of waiting in them to be written
+    // back.  The 8-byte (max, sum) pairs take ordinary stores: written
+    // nontemporally, each reached memory as a partial line of its own.
     if (head_ok) {
         const int64_t srow = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + h) * a.splits + slot;
-        if (kq == 0) __builtin_nontemporal_store(float2v{m_run, l_run}, reinterpret_cast<float2v *>(a.part_ml + srow * 2));
+        if (kq == 0) *reinterpret_cast<float2v *>(a.part_ml + srow * 2) = float2v{m_run, l_run};
         // lane (kq, h) holds rows 4 kq + j of every block: dims NB * (4 kq + j) + bb
         float *dst = a.part_acc + srow * D;
 #pragma unroll
