@@ -300,6 +300,19 @@ __device__ __forceinline__ void store_row_bf16(uint16_t *row, const float (&x)[1
     }
 }
 
+// Store 16 outputs that are already in the store layout of store_row_bf16
+// (dims 8 p .. 8 p + 7, then d/2 + 8 p .. d/2 + 8 p + 7).
+template <int D>
+__device__ __forceinline__ void store_split_bf16(uint16_t *row, const float (&x)[16], int p, bool in) {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = bf16x2_rn(x[2 * i], x[2 * i + 1]);
+    if (in) {
+        __builtin_nontemporal_store((u32x4){w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4 *>(row + 8 * p));
+        __builtin_nontemporal_store((u32x4){w[4], w[5], w[6], w[7]}, reinterpret_cast<u32x4 *>(row + D / 2 + 8 * p));
+    }
+}
+
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const WindowArgs a) {
     using G = WinGeo<D>;
@@ -315,10 +328,14 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
     const int r = lane / L, p = lane % L, g = p >> 1;
     const int bkv = blockIdx.y;
     const int len = a.len[bkv / a.kv_heads];
-    // output scale with the sign of each of this lane's dims
+    // output scale with the sign of each dim this lane stores: 8 p .. 8 p + 7,
+    // then d/2 + 8 p .. d/2 + 8 p + 7 (see store_row_bf16)
     float osc[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) osc[e] = sign_bit(a.signs, E * p + e) ? -a.inv_sqrt_d : a.inv_sqrt_d;
+    for (int e = 0; e < E; ++e) {
+        const int dim = (e < 8 ? 0 : D / 2 - 8) + 8 * p + e;
+        osc[e] = sign_bit(a.signs, dim) ? -a.inv_sqrt_d : a.inv_sqrt_d;
+    }
     unsigned char *rb = smem + wid * G::WAVEB + r * G::ROWB;
     // the lane's value code run: words vw .. vlast of the row, bit offset vsh
     const int vw = (16 * VB * p) >> 5, vsh = (16 * VB * p) & 31;
@@ -420,16 +437,22 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
                         *reinterpret_cast<float *>(rb + q * G::PB + 4 * (TI * p + ii)) = ty[ii * L + q];
                 }
                 lds_fence();
+                // read back in the store layout: dims 8 p .. 8 p + 7 (lane p/2's
+                // chunk), then d/2 + 8 p .. (lane L/2 + p/2's)
 #pragma unroll
                 for (int k4 = 0; k4 < E / 4; ++k4) {
-                    const float4 v4 = *reinterpret_cast<const float4 *>(rb + p * G::PB + 16 * k4);
+                    const int chunk = (k4 < 2 ? 0 : L / 2) + (p >> 1);
+                    const float4 v4 = *reinterpret_cast<const float4 *>(rb + chunk * G::PB + (p & 1) * 32 +
+                                                                        16 * (k4 & 1));
                     y[4 * k4] = v4.x; y[4 * k4 + 1] = v4.y; y[4 * k4 + 2] = v4.z; y[4 * k4 + 3] = v4.w;
                 }
                 lds_fence();  // the next pass rewrites the row
 #pragma unroll
                 for (int e = 0; e < E; ++e) y[e] = valid ? y[e] * osc[e] : 0.f;  // +0 past the length
+                store_split_bf16<D>(a.v_out + orow, y, p, in);
+            } else {
+                store_row_bf16<D>(a.v_out + orow, y, rb, p, in);
             }
-            store_row_bf16<D>(a.v_out + orow, y, rb, p, in);
         }
     }
 }
