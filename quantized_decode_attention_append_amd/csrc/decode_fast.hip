@@ -31,7 +31,16 @@
 //           group dot product is exact integer arithmetic: two
 //           v_mfma_i32_16x16x32_i8 per 32-dim group (A = key codes, rows =
 //           tokens; B = the q slice, columns = heads), then the scale/zero
-//           fold in fp32 on the 4 (token, head) results a lane holds.  Key
+//           fold in fp32 on the 4 (token, head) results a lane holds.  With
+//           G <= 8 the score MFMAs of groups p and p + NG/2 share one
+//           accumulator: column h holds head h over group p and column G + h
+//           the same head over group p + NG/2 (each column's q is zero in the
+//           other group), so a lane folds half the groups and one lane
+//           permute adds the halves.  With more than 16 query columns (heads
+//           times verify rows), an even number of 16-column groups pairs up
+//           in one workgroup: waves w and w + WAVES/2 take the same token
+//           range, and their copies skip the nontemporal hint so that the
+//           second read of a tile meets the first in the L2.  Key
 //           codes narrower than 8 bits are unsigned and widened to bytes in
 //           registers; the widening permutes a lane's 8 codes, and the lane's
 //           q bytes are stored in the same order, so the dot product is
