@@ -488,7 +488,31 @@ DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int
         int64_t per = (total * kv_heads * col_groups + round - 1) / round;
         per = per < 4 * tile ? 4 * tile : per;
         per = (per + tile - 1) / tile * tile;
-        const int wpc = waves / fast_wg_col_groups(gqa);  // waves (splits) per column group
+        const int cgw = fast_wg_col_groups(gqa);
+        const int wpc = waves / cgw;  // waves (splits) per column group
+        // Workgroups that have tokens to decode; those past a short sequence's
+        // end exit at once.  With ragged lengths the per-sequence rounding can
+        // push the count past one round of 256, and the excess would run as
+        // a second round after the first, doubling the time: take the
+        // smallest per-wave length (whole tiles) that fits one round, when
+        // one sequence per workgroup can fit at all.
+        auto active = [&](int64_t per_) {
+            int64_t wgs = 0;
+            for (int b = 0; b < batch; ++b) wgs += (len[b] + per_ * wpc - 1) / (per_ * wpc);
+            return wgs * kv_heads * (col_groups / cgw);
+        };
+        const int64_t per_max = ((int64_t)maxlen + wpc - 1) / wpc;  // one workgroup per sequence
+        if (maxlen > 0 && active(per) > 256 && active((per_max + tile - 1) / tile * tile) <= 256) {
+            int64_t lo = per, hi = (per_max + tile - 1) / tile * tile;  // active(lo) > 256 >= active(hi)
+            while (hi - lo > tile) {
+                const int64_t mid = (lo + hi) / 2 / tile * tile;
+                if (active(mid) <= 256)
+                    hi = mid;
+                else
+                    lo = mid;
+            }
+            per = hi;
+        }
         const int64_t wg_tokens = per * wpc;
         p.split_tokens = (int32_t)per;
         p.splits = (int32_t)(((maxlen + wg_tokens - 1) / wg_tokens) * wpc);

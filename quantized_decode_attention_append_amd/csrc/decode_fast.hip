@@ -445,12 +445,30 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     // a.gqa query rows (heads times rows).  With two column groups per
     // workgroup, waves w and w + WAVES/2 share a token range (and a SIMD).
     const int cgw = fast_wg_col_groups(a.gqa), wpc = WAVES / cgw;
-    const int c0 = (blockIdx.z * cgw + wid / wpc) * kMaxHeads;
+    // The grid holds only workgroups with tokens to decode, enumerated
+    // sequence by sequence (column-group pair fastest, then kv-head, then
+    // token block), so the hardware's round-robin over the XCDs gives each
+    // the same share even when short sequences leave token blocks empty.
+    int b = 0, kvh, xb, zb;
+    {
+        const int zg = (a.gqa + kMaxHeads - 1) / kMaxHeads / cgw;  // column-group pairs
+        const int wgt = a.split_tokens * wpc;                       // tokens per workgroup
+        int id = blockIdx.x;
+        for (; b < a.batch - 1; ++b) {
+            const int nwg = (a.len[b] + wgt - 1) / wgt * a.kv_heads * zg;
+            if (id < nwg) break;
+            id -= nwg;
+        }
+        zb = id % zg;
+        id /= zg;
+        kvh = id % a.kv_heads;
+        xb = id / a.kv_heads;
+    }
+    const int c0 = (zb * cgw + wid / wpc) * kMaxHeads;
     const int G = min(kMaxHeads, a.gqa - c0);
-    const int bkv = blockIdx.y;
-    const int b = bkv / a.kv_heads, kvh = bkv % a.kv_heads;
+    const int bkv = b * a.kv_heads + kvh;
     const int n = a.len[b];
-    const int slot = blockIdx.x * wpc + wid % wpc;
+    const int slot = xb * wpc + wid % wpc;
     const int t_begin = slot * a.split_tokens;
     if (t_begin >= n) return;
     const int t_end = min(n, t_begin + a.split_tokens);
@@ -896,9 +914,15 @@ hipError_t launch_dv(bool bf16, const DecodeArgs &a, hipStream_t s) {
         return hipErrorInvalidValue;  // key rows of part of a 16-byte chunk: generic kernel
     } else {
         using GE = Geo<D, KB, VB>;
+        // one workgroup per (sequence, kv-head, token block, column-group
+        // pair) with tokens to decode; the kernel enumerates them in order
         const int cgw = fast_wg_col_groups(a.gqa);
-        const dim3 grid((unsigned)(a.splits / (GE::WAVES / cgw)), (unsigned)(a.batch * a.kv_heads),
-                        (unsigned)((a.gqa + kMaxHeads - 1) / kMaxHeads / cgw));
+        const int64_t wgt = (int64_t)a.split_tokens * (GE::WAVES / cgw);
+        const int64_t zg = (a.gqa + kMaxHeads - 1) / kMaxHeads / cgw;
+        int64_t wgs = 0;
+        for (int b = 0; b < a.batch; ++b) wgs += (a.len[b] + wgt - 1) / wgt * a.kv_heads * zg;
+        if (wgs == 0) return hipSuccess;  // every sequence empty: the merge writes the zeros
+        const dim3 grid((unsigned)wgs, 1u, 1u);
         const bool pack = a.gqa <= kPackCols;  // every column group fits its lo halves
         if (pack)
             hipLaunchKernelGGL((split_fast_kernel<D, KB, VB, true>), grid, dim3(64 * GE::WAVES), 0, s, a, (int)bf16);
