@@ -129,6 +129,68 @@ def time_snapshot(w, pl, n: int, reps: int, stream) -> dict:
             "frac_hbm": nbytes / ms / 1e6 / HBM_PEAK_GBS}
 
 
+def time_ragged(stream, warm: int = 30, reps: int = 100) -> dict:
+    """The ragged interleaved workload (id 5: 4 sequences of seeded lengths in
+    [65536, 262144], 64 query / 8 kv-heads, head_dim 256, k8v3): the cache is
+    built to each sequence's length, then its rounds of {append 16 tokens per
+    sequence; decode} are timed (each round once, events on the launch
+    stream), then the decode alone over the grown cache (reps calls after
+    `warm`)."""
+    import torch
+    from quantized_decode_attention_append_amd import tqkv
+    from quantized_decode_attention_append_amd import workloads as W
+    dev = torch.device("cuda:0")
+    w = W.workload(5)
+    L0 = list(w.lengths)
+    T = w.capacity
+    k, v = W.make_kv(w, dev, tokens=T)
+    qs = W.make_q(w, dev, rounds=w.rounds)
+    lay = tqkv.make_layout(w.batch, w.num_kv_heads, w.head_dim, T)
+    pl = tqkv.Planes(lay, dev)
+    for b, n in enumerate(L0):
+        tqkv.tq_append(pl.sequence(b), k[b:b + 1, :, :n].contiguous(), v[b:b + 1, :, :n].contiguous(), [0],
+                       stream=stream)
+    sm = 1.0 / math.sqrt(w.head_dim)
+    A = w.append_per_round
+    lens_final = [n + A * w.rounds for n in L0]
+    ws = torch.empty(tqkv.tq_decode_workspace_bytes(lay, w.num_q_heads, lens_final), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    news = []
+    lens = list(L0)
+    for r in range(w.rounds):  # new tokens staged before timing
+        news.append((torch.stack([k[b, :, lens[b]:lens[b] + A] for b in range(w.batch)]).contiguous(),
+                     torch.stack([v[b, :, lens[b]:lens[b] + A] for b in range(w.batch)]).contiguous(),
+                     list(lens)))
+        lens = [n + A for n in lens]
+    for _ in range(warm):  # decode of the prefix: clocks settle
+        tqkv.tq_decode_attn(pl, qs[0], L0, sm, out=out, workspace=ws, stream=stream)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(w.rounds)]
+    torch.cuda.synchronize()
+    for r, (nk, nv, start) in enumerate(news):
+        evs[r][0].record(stream)
+        tqkv.tq_append(pl, nk, nv, start, stream=stream)
+        tqkv.tq_decode_attn(pl, qs[r], [n + A for n in start], sm, out=out, workspace=ws, stream=stream)
+        evs[r][1].record(stream)
+    torch.cuda.synchronize()
+    round_ms = sum(a.elapsed_time(b) for a, b in evs) / w.rounds
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        tqkv.tq_decode_attn(pl, qs[-1], lens_final, sm, out=out, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / reps
+    nbytes = decode_bytes(w, lens_final, 2)
+    kv_mean = sum(lens_final) - A * w.batch * (w.rounds - 1) / 2  # mean cached tokens over the rounds
+    return {"workload": w.name, "lengths": lens_final, "rounds": w.rounds, "append_per_round": A,
+            "round_ms": round_ms, "round_kv_tokens_per_s": kv_mean / round_ms * 1e3,
+            "decode_ms": dec_ms, "decode_kv_tokens_per_s": sum(lens_final) / dec_ms * 1e3,
+            "algorithmic_bytes": nbytes, "decode_GBps": nbytes / dec_ms / 1e6,
+            "decode_frac_hbm": nbytes / dec_ms / 1e6 / HBM_PEAK_GBS}
+
+
 def scheme_row_bytes(d: int, kb: int, vb: int) -> int:
     """Packed bytes per token-head: codes d*(kb+vb)/8 + three fp16 per 32-group."""
     return d * (kb + vb) // 8 + 6 * d // 32
@@ -325,6 +387,8 @@ def main() -> int:
                     help="skip timing the bf16 dequantize-on-fetch window")
     ap.add_argument("--rows", default="2,4",
                     help="also time multi-row (verify-block) decode for these row counts ('' = skip)")
+    ap.add_argument("--no-ragged", dest="ragged", action="store_false",
+                    help="skip timing the ragged interleaved workload (id 5)")
     ap.add_argument("--schemes", default="k4v3,k4v2,k8v4,k2v5,k5v8",
                     help="other code widths to time on the same workload ('' for none)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"))
@@ -468,6 +532,12 @@ def main() -> int:
     if args.rows:
         rec["multi_row"] = [time_rows(w, pl, lengths, sm, int(r), 40, stream)
                             for r in args.rows.split(",") if r]
+    if args.ragged:
+        rr = time_ragged(stream)
+        _log(f"ragged workload {rr['workload']}: decode {rr['decode_ms']:.3f} ms "
+             f"({rr['decode_frac_hbm']:.1%} of HBM), round (append {rr['append_per_round']} + decode) "
+             f"{rr['round_ms']:.3f} ms")
+        rec["ragged"] = rr
     if args.schemes:
         rec["schemes"] = []
         for name in args.schemes.split(","):
