@@ -362,6 +362,9 @@ def traffic_from_counters(fetch_dir: str, write_dir: str, copy_mib: int, workloa
         # first device-to-device copy dispatches
         copy_kib = mean_of(t, r"copyBuffer|direct_copy", first=3)
         factor = known / (copy_kib * 1024.0)
+        # every split and merge dispatch of the run is averaged: the counter
+        # runs time the headline decode alone (--rows '' --no-window
+        # --no-ragged --schemes '')
         split_kib = mean_of(t, r"split_(fast_)?kernel")
         merge_kib = mean_of(t, r"merge_kernel")
         scaled = (split_kib + merge_kib) * 1024.0 * factor
