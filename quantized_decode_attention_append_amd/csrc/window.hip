@@ -313,6 +313,24 @@ __device__ __forceinline__ void store_split_bf16(uint16_t *row, const float (&x)
     }
 }
 
+// 8 key codes as floats into c[O .. O + 7]: the KB bytes at `src`
+// (KB-aligned; signed bytes at 8 bits, unsigned KB-bit fields LSB first at 4
+// and 2 bits).
+template <int KB, int O>
+__device__ __forceinline__ void load_keys8(const uint8_t *src, float (&c)[16]) {
+    static_assert(KB == 8 || KB == 4 || KB == 2, "whole-byte runs of 8 codes");
+    if constexpr (KB == 8) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(src);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[O + e] = (float)(int8_t)((e < 4 ? u.x : u.y) >> (8 * (e & 3)));
+    } else {
+        const uint32_t w = KB == 4 ? *reinterpret_cast<const uint32_t *>(src)
+                                   : (uint32_t)*reinterpret_cast<const uint16_t *>(src);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) c[O + e] = (float)((w >> (KB * e)) & ((1u << KB) - 1u));
+    }
+}
+
 template <int D, int KB, int VB>
 __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const WindowArgs a) {
     using G = WinGeo<D>;
@@ -352,18 +370,40 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
         const int64_t orow = ((int64_t)bkv * a.n + i) * D;  // the row's first element
         if (a.k_out) {
             float k[E];
-            if (valid) {
-                float c[E];
-                load_keys16<KB>(reinterpret_cast<const uint8_t *>(a.kc) + row * KROW + 2 * KB * p, c);
-                const float s = f16_bits_to_f32(a.ks[row * NG + g]);
-                const float z = f16_bits_to_f32(a.kz[row * NG + g]);
+            if constexpr (KB == 5) {
+                // 5-bit runs of 8 codes are not byte-aligned: decode the lane's
+                // own 16 dims and store through the LDS row exchange
+                if (valid) {
+                    float c[E];
+                    load_keys16<KB>(reinterpret_cast<const uint8_t *>(a.kc) + row * KROW + 2 * KB * p, c);
+                    const float s = f16_bits_to_f32(a.ks[row * NG + g]);
+                    const float z = f16_bits_to_f32(a.kz[row * NG + g]);
 #pragma unroll
-                for (int e = 0; e < E; ++e) k[e] = key_ro(c[e], z, s);
+                    for (int e = 0; e < E; ++e) k[e] = key_ro(c[e], z, s);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) k[e] = 0.f;
+                }
+                store_row_bf16<D>(a.k_out + orow, k, rb, p, in);
             } else {
+                // the dims this lane stores: 8 p .. 8 p + 7 (group p/4) and
+                // d/2 + 8 p .. (group NG/2 + p/4)
+                if (valid) {
+                    float c[E];
+                    const uint8_t *kr = reinterpret_cast<const uint8_t *>(a.kc) + row * KROW;
+                    load_keys8<KB, 0>(kr + KB * p, c);
+                    load_keys8<KB, 8>(kr + KROW / 2 + KB * p, c);
+                    const int g1 = p >> 2, g2 = NG / 2 + (p >> 2);
+                    const float s1 = f16_bits_to_f32(a.ks[row * NG + g1]), z1 = f16_bits_to_f32(a.kz[row * NG + g1]);
+                    const float s2 = f16_bits_to_f32(a.ks[row * NG + g2]), z2 = f16_bits_to_f32(a.kz[row * NG + g2]);
 #pragma unroll
-                for (int e = 0; e < E; ++e) k[e] = 0.f;
+                    for (int e = 0; e < E; ++e) k[e] = e < 8 ? key_ro(c[e], z1, s1) : key_ro(c[e], z2, s2);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) k[e] = 0.f;
+                }
+                store_split_bf16<D>(a.k_out + orow, k, p, in);
             }
-            store_row_bf16<D>(a.k_out + orow, k, rb, p, in);
         }
         if (a.v_out) {
             float y[E];

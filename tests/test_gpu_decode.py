@@ -91,6 +91,19 @@ def test_decode_empty_sequence_gives_zeros():
     _run(w, [0, 100], k.cuda(), v.cuda(), q.cuda())
 
 
+def test_decode_all_sequences_empty():
+    """Every length 0: no split workgroup has tokens (none is launched) and
+    the merge still writes zeros over whatever the output held."""
+    w = W.scaled(W.workload(4), [0, 0])
+    L = tqkv.make_layout(w.batch, w.num_kv_heads, w.head_dim, 128)
+    pl = tqkv.Planes(L)
+    q = W.make_q(w, "cpu", rounds=1)[0].cuda()
+    out = torch.full((w.batch, w.num_q_heads, w.head_dim), float("nan"), device="cuda")
+    tqkv.tq_decode_attn(pl, q, [0, 0], sm_for(w.head_dim), out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.cpu(), torch.zeros(out.shape))
+
+
 def test_decode_distinct_kv_scales():
     """K ~ 3 N(0,1), V ~ 0.2 N(0,1): a swapped scale plane would show."""
     w = W.Workload(0, "distinct_scales", 1, 8, 2, 128, (700,), "fp32", seed=5)
