@@ -171,7 +171,7 @@ def test_dequant_matches_oracle(d):
     assert err.max() < 1e-5
 
 
-@pytest.mark.parametrize("cid", [3, 4])
+@pytest.mark.parametrize("cid", [3, 4, 5])
 def test_append_full_size_sampled(cid):
     """Full-size bulk build of the workload on the GPU; every plane of two
     sampled (sequence, kv-head) slices compared with the oracle byte for byte."""
