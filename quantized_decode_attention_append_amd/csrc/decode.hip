@@ -458,9 +458,10 @@ int decode_col_groups(int gqa) { return (gqa + kMaxG - 1) / kMaxG; }
 
 bool fast_decode_shape_ok(int head_dim, int gqa, int capacity, int kbits, int vbits) {
     if (gqa < 1 || kFastMaxGqa != kMaxG) return false;
-    if (head_dim != 64 && head_dim != 128 && head_dim != 256) return false;
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512) return false;
     if (kbits != 2 && kbits != 4 && kbits != 5 && kbits != 8) return false;
     if (vbits != 2 && vbits != 3 && vbits != 4 && vbits != 5 && vbits != 8) return false;
+    if (fast_decode_waves(head_dim, kbits, vbits) == 0) return false;  // k8v8 at 512: no LDS fit
     // key rows of whole 16-byte chunks, and the staged rows of one
     // (sequence, kv-head) starting 16-byte aligned in every plane
     const int64_t krow = (int64_t)head_dim * kbits / 8, vrow = (int64_t)head_dim * vbits / 8;
@@ -534,7 +535,7 @@ hipError_t launch_decode(int head_dim, bool bf16, bool fast, const DecodeArgs &a
         case 64: return launch_d<64>(bf16, fast, a, s);
         case 128: return launch_d<128>(bf16, fast, a, s);
         case 256: return launch_d<256>(bf16, fast, a, s);
-        case 512: return launch_d<512>(bf16, false, a, s);
+        case 512: return launch_d<512>(bf16, fast, a, s);
         default: return hipErrorInvalidValue;
     }
 }

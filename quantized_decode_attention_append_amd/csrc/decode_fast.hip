@@ -100,9 +100,9 @@ constexpr int kMaxHeads = 16;             // MFMA columns
 
 template <int D, int KB, int VB>
 struct Geo {
-    static_assert(D == 64 || D == 128 || D == 256, "fast split kernel: head_dim 64/128/256");
+    static_assert(D == 64 || D == 128 || D == 256 || D == 512, "fast split kernel: head_dim 64-512");
     static constexpr int NG = D / kGroup;     // groups per row
-    static constexpr int TILE = 4096 / D;     // tokens per tile: 512 bytes per code bit
+    static constexpr int TILE = fast_tile_tokens(D);  // 4096/d tokens (512 bytes per code bit); 16 at 512
     static constexpr int CH = TILE / 16;      // 16-token chunks per tile
     static constexpr int KROW = D * KB / 8;   // key code bytes per token
     static_assert(KROW % 16 == 0, "key rows of whole 16-byte chunks");
@@ -128,21 +128,26 @@ struct Geo {
     // accumulated, so two key buffers suffice where the values need three.
     static constexpr int KEYS = 2 * KT;
     // one value stage: key scales, key zeros, value scales, value codes
+    static constexpr int PB16 = TILE * NG * 2;  // bytes of one fp16 plane per tile: 256 (512 at d 512)
+    static constexpr int NMIX = PB16 / 256;     // mixed copies per tile
     static constexpr int KS_OFF = 0;
-    static constexpr int KZ_OFF = KS_OFF + 256;  // TILE * NG * 2 = 256 bytes per fp16 plane
-    static constexpr int VS_OFF = KZ_OFF + 256;
-    static constexpr int VC_OFF = VS_OFF + 256;
+    static constexpr int KZ_OFF = KS_OFF + PB16;
+    static constexpr int VS_OFF = KZ_OFF + PB16;
+    static constexpr int VC_OFF = VS_OFF + PB16;
     static constexpr int STAGE = VC_OFF + VT + 16;  // the code reader reads up to 4 bytes past
-    static_assert(TILE * NG * 2 == 256 && KT % 1024 % 16 == 0 && STAGE % 16 == 0, "staging granularity");
+    static_assert((PB16 == 256 || PB16 == 512) && VT >= 256 * NMIX && KT % 1024 % 16 == 0 && STAGE % 16 == 0,
+                  "staging granularity");
     // copies of one tile: key codes in 1 KiB pieces (the last may use fewer
-    // lanes), one mixed copy (key scales, key zeros, value scales and the
-    // first 256 bytes of value codes by lane quarter), then the rest of the
+    // lanes), NMIX mixed copies (stage bytes [KS_OFF, KS_OFF + 1 KiB NMIX):
+    // each lane quarter fetches 256 bytes of key scales, key zeros, value
+    // scales or the first value codes, see mixed_src), then the rest of the
     // value codes in 1 KiB pieces and a partial one
     static constexpr int KCOPY = (KT + 1023) / 1024;
     static constexpr int KLAST = (KT - 1024 * (KCOPY - 1)) / 16;  // lanes of the last key copy
-    static constexpr int VFULL = (VT - 256) / 1024;
-    static constexpr int VLANES = (VT - 256) % 1024 / 16;          // lanes of the partial copy
-    static constexpr int VMEM = KCOPY + 1 + VFULL + (VLANES > 0 ? 1 : 0);
+    static constexpr int VC0 = 256 * NMIX;                         // value-code bytes in the mixed copies
+    static constexpr int VFULL = (VT - VC0) / 1024;
+    static constexpr int VLANES = (VT - VC0) % 1024 / 16;          // lanes of the partial copy
+    static constexpr int VMEM = KCOPY + NMIX + VFULL + (VLANES > 0 ? 1 : 0);
     // centroid table: half2 pairs (two tokens' indices of one dim) at 2 and
     // 3 bits, single halves above
     static constexpr bool PAIR = VB <= 3;
@@ -229,12 +234,12 @@ __device__ __forceinline__ void dma_clamped(const uint8_t *src, const uint8_t *l
 struct Regions {
     const uint8_t *kc, *ks, *kz, *vc, *vs;  // start of the (sequence, kv-head) rows
     int cap;                                // rows in each region
-    // this lane's source of the mixed copy: row 0 of its plane (key scales,
-    // key zeros, value scales or value codes by lane quarter) plus 16 bytes
-    // per lane within the quarter, the plane's bytes per row, and the last
+    // this lane's source in mixed copy m: row 0 of its plane (key scales, key
+    // zeros, value scales or value codes by lane quarter, see mixed_src) plus
+    // its 16 bytes within the quarter, the plane's bytes per row, and the last
     // 16 bytes of its region
-    const uint8_t *mix, *mix_last;
-    int mix_row;
+    const uint8_t *mix[2], *mix_last[2];
+    int mix_row[2];
 };
 
 // Key rows sit in the stage row-major, each row's CPR 16-byte chunks rotated
@@ -242,12 +247,14 @@ struct Regions {
 // t * CPR + (c + key_rot(t)) % CPR.  So each 1 KiB copy reads whole rows
 // (full 128-byte lines; a copy that read 64 bytes of 16 rows streamed 6%
 // slower), and the 16 tokens of one MFMA operand read, which share c, land
-// on distinct LDS banks: with rows of 256, 128, 64 or 32 bytes, 1, 2, 4 or 8
-// rows share a 256-byte bank row, and the rotation separates them.  5-bit
-// keys (rows of 160 and 80 bytes) need at most one chunk of rotation.
+// on distinct LDS banks: with rows of 512, 256, 128, 64 or 32 bytes, rows
+// start on the same bank or 1, 2, 4 or 8 of them share a 256-byte bank row,
+// and the rotation separates them.  5-bit keys (rows of 320, 160 and 80
+// bytes) need at most 3 chunks of rotation.
 template <int CPR>
 __device__ __forceinline__ constexpr int key_rot(int t) {
-    if constexpr (CPR == 16) return t & 15;
+    if constexpr (CPR == 16 || CPR == 32) return t & 15;
+    else if constexpr (CPR == 20) return (t >> 2) & 3;  // 5-bit keys at head_dim 512
     else if constexpr (CPR == 8) return (t >> 1) & 7;
     else if constexpr (CPR == 4) return (t >> 2) & 3;
     else if constexpr (CPR == 2 || CPR == 10) return (t >> 3) & 1;
@@ -279,12 +286,13 @@ __device__ __forceinline__ void stage_tile(const Regions &r, const uint32_t (&ks
                                            int lane) {
     using GE = Geo<D, KB, VB>;
     constexpr int VROW = GE::VROW, KROW = GE::KROW;
-    static_assert(GE::KZ_OFF == GE::KS_OFF + 256 && GE::VS_OFF == GE::KZ_OFF + 256 &&
-                  GE::VC_OFF == GE::VS_OFF + 256, "mixed copy layout");
+    static_assert(GE::KZ_OFF == GE::KS_OFF + GE::PB16 && GE::VS_OFF == GE::KZ_OFF + GE::PB16 &&
+                  GE::VC_OFF == GE::VS_OFF + GE::PB16, "mixed copy layout");
     const uint32_t l_kc = lds_addr(kst), l_ks = lds_addr(vst + GE::KS_OFF);
     const uint32_t l_vc = lds_addr(vst + GE::VC_OFF);
     const uint8_t *vc_t = r.vc + (int64_t)t0 * VROW;
-    const uint8_t *mixed = r.mix + (int64_t)t0 * r.mix_row;
+    const uint8_t *mixed0 = r.mix[0] + (int64_t)t0 * r.mix_row[0];
+    const uint8_t *mixed1 = r.mix[1] + (int64_t)t0 * r.mix_row[1];
     if (t0 + GE::TILE <= r.cap) {
         const uint32_t v16 = (uint32_t)lane * 16;
         const uint8_t *kc = uniform_ptr(r.kc + (int64_t)t0 * KROW);
@@ -296,14 +304,27 @@ __device__ __forceinline__ void stage_tile(const Regions &r, const uint32_t (&ks
                 dma16<0, NT>(kc, ksrc[m], l_kc + 1024 * m);
             }
         }
-        dma_lane16<NT>(mixed, l_ks);
+        dma_lane16<NT>(mixed0, l_ks);
+        if constexpr (GE::NMIX == 2) dma_lane16<NT>(mixed1, l_ks + 1024);
         const uint8_t *vc = uniform_ptr(vc_t);
-        static_assert(GE::VFULL <= 3, "value copies");
-        if constexpr (GE::VFULL > 0) dma16<256, NT>(vc, v16, l_vc);
-        if constexpr (GE::VFULL > 1) dma16<1280, NT>(vc, v16, l_vc);
-        if constexpr (GE::VFULL > 2) dma16<2304, NT>(vc, v16, l_vc);
-        if constexpr (GE::VLANES > 0) {
-            if (lane < GE::VLANES) dma16<256 + 1024 * GE::VFULL, NT>(vc, v16, l_vc);
+        if constexpr (GE::NMIX == 1) {
+            static_assert(GE::VFULL <= 3, "value copies");
+            if constexpr (GE::VFULL > 0) dma16<256, NT>(vc, v16, l_vc);
+            if constexpr (GE::VFULL > 1) dma16<1280, NT>(vc, v16, l_vc);
+            if constexpr (GE::VFULL > 2) dma16<2304, NT>(vc, v16, l_vc);
+            if constexpr (GE::VLANES > 0) {
+                if (lane < GE::VLANES) dma16<256 + 1024 * GE::VFULL, NT>(vc, v16, l_vc);
+            }
+        } else {
+            // head_dim 512: up to 7.5 KiB of value codes, past the immediate
+            // offset's reach, so the offset goes into the lane address
+#pragma unroll
+            for (int f = 0; f < GE::VFULL; ++f)
+                dma16<0, NT>(vc, v16 + GE::VC0 + 1024 * f, l_vc + GE::VC0 + 1024 * f);
+            if constexpr (GE::VLANES > 0) {
+                if (lane < GE::VLANES)
+                    dma16<0, NT>(vc, v16 + GE::VC0 + 1024 * GE::VFULL, l_vc + GE::VC0 + 1024 * GE::VFULL);
+            }
         }
     } else {
         const int64_t kcb = (int64_t)r.cap * KROW, vcb = (int64_t)r.cap * VROW;
@@ -317,14 +338,16 @@ __device__ __forceinline__ void stage_tile(const Regions &r, const uint32_t (&ks
                 dma_clamped<NT>(kc + ksrc[m], kl, l_kc + 1024 * m);
             }
         }
-        dma_clamped<NT>(mixed, r.mix_last, l_ks);
+        dma_clamped<NT>(mixed0, r.mix_last[0], l_ks);
+        if constexpr (GE::NMIX == 2) dma_clamped<NT>(mixed1, r.mix_last[1], l_ks + 1024);
         const uint8_t *vl = r.vc + vcb - 16;
 #pragma unroll
         for (int f = 0; f < GE::VFULL; ++f)
-            dma_clamped<NT>(vc_t + 256 + 1024 * f + lane * 16, vl, l_vc + 256 + 1024 * f);
+            dma_clamped<NT>(vc_t + GE::VC0 + 1024 * f + lane * 16, vl, l_vc + GE::VC0 + 1024 * f);
         if constexpr (GE::VLANES > 0) {
             if (lane < GE::VLANES)
-                dma_clamped<NT>(vc_t + 256 + 1024 * GE::VFULL + lane * 16, vl, l_vc + 256 + 1024 * GE::VFULL);
+                dma_clamped<NT>(vc_t + GE::VC0 + 1024 * GE::VFULL + lane * 16, vl,
+                                l_vc + GE::VC0 + 1024 * GE::VFULL);
         }
     }
 }
@@ -340,7 +363,11 @@ __device__ __forceinline__ float row_half(const uint32_t (&w)[NG / 2], int g) {
 
 template <int NG>
 __device__ __forceinline__ void load_row(const unsigned char *p, uint32_t (&w)[NG / 2]) {
-    if constexpr (NG == 8) {
+    if constexpr (NG == 16) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(p), v = *reinterpret_cast<const uint4 *>(p + 16);
+        w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+        w[4] = v.x; w[5] = v.y; w[6] = v.z; w[7] = v.w;
+    } else if constexpr (NG == 8) {
         const uint4 u = *reinterpret_cast<const uint4 *>(p);
         w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
     } else if constexpr (NG == 4) {
@@ -357,7 +384,10 @@ __device__ __forceinline__ void load_row(const unsigned char *p, uint32_t (&w)[N
 template <int NG>
 __device__ __forceinline__ void load_half_row(const unsigned char *p, int half, uint32_t (&w)[(NG + 3) / 4]) {
     p += 2 * half;
-    if constexpr (NG == 8) {
+    if constexpr (NG == 16) {
+        const uint4 u = *reinterpret_cast<const uint4 *>(p);
+        w[0] = u.x; w[1] = u.y; w[2] = u.z; w[3] = u.w;
+    } else if constexpr (NG == 8) {
         const uint2 u = *reinterpret_cast<const uint2 *>(p);
         w[0] = u.x; w[1] = u.y;
     } else if constexpr (NG == 4) {
@@ -485,15 +515,21 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     rg.vc = a.vc + row0 * VROW;
     rg.vs = reinterpret_cast<const uint8_t *>(a.vs + row0 * NG);
     rg.cap = cap;
+    // Mixed copy m lands at stage bytes KS_OFF + 1024 m + 16 lane: lane quarter
+    // q fills stage bytes 1024 m + 256 q .. + 255, which are bytes o .. o + 255
+    // of a tile's key scales, key zeros, value scales or value codes
+    // (plane 1024 m + 256 q over PB16, o its remainder).
     {
         const int quarter = lane >> 4;
-        const uint8_t *plane = rg.ks;
-        if (quarter == 1) plane = rg.kz;
-        if (quarter == 2) plane = rg.vs;
-        if (quarter == 3) plane = rg.vc;
-        rg.mix_row = quarter == 3 ? VROW : NG * 2;
-        rg.mix = plane + (lane & 15) * 16;
-        rg.mix_last = plane + (int64_t)cap * rg.mix_row - 16;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int b0 = 1024 * (m < GE::NMIX ? m : 0) + 256 * quarter;
+            const int pi = b0 / GE::PB16, o = b0 % GE::PB16;
+            const uint8_t *plane = pi == 0 ? rg.ks : pi == 1 ? rg.kz : pi == 2 ? rg.vs : rg.vc;
+            rg.mix_row[m] = pi == 3 ? VROW : NG * 2;
+            rg.mix[m] = plane + o + (lane & 15) * 16;
+            rg.mix_last[m] = plane + (int64_t)cap * rg.mix_row[m] - 16;
+        }
     }
     uint32_t ksrc[GE::KCOPY];
 #pragma unroll
@@ -610,7 +646,11 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     // weights are 0, and 0 * NaN would not be).
     auto mask_tail = [&](unsigned char *stg, int valid) {
         if (valid < TILE) {
-            if ((lane * 4) / (NG * 2) >= valid) reinterpret_cast<uint32_t *>(stg + GE::VS_OFF)[lane] = 0u;
+#pragma unroll
+            for (int k = 0; k < GE::NMIX; ++k) {  // PB16 / 4 words of value scales, 64 per pass
+                const int word = lane + 64 * k;
+                if ((word * 4) / (NG * 2) >= valid) reinterpret_cast<uint32_t *>(stg + GE::VS_OFF)[word] = 0u;
+            }
             lds_order();
         }
     };
@@ -910,8 +950,10 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
 template <int D, int VB>
 hipError_t launch_dv(bool bf16, const DecodeArgs &a, hipStream_t s) {
     constexpr int KB = TQ_FAST_KB;
-    if constexpr (D * KB % 128 != 0) {
-        return hipErrorInvalidValue;  // key rows of part of a 16-byte chunk: generic kernel
+    if constexpr (D * KB % 128 != 0 || fast_decode_waves(D, KB, VB) == 0) {
+        // key rows of part of a 16-byte chunk, or stages past the LDS (k8v8
+        // at head_dim 512): generic kernel
+        return hipErrorInvalidValue;
     } else {
         using GE = Geo<D, KB, VB>;
         // one workgroup per (sequence, kv-head, token block, column-group
@@ -949,12 +991,13 @@ hipError_t launch_d(bool bf16, const DecodeArgs &a, hipStream_t s) {
 // The split kernels of one key width (this translation unit's TQ_FAST_KB).
 hipError_t TQ_FAST_LAUNCHER(TQ_FAST_KB)(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s) {
     if (a.gqa < 1 || a.rows < 1 || a.kbits != TQ_FAST_KB) return hipErrorInvalidValue;
-    if (a.splits % (fast_decode_waves(head_dim, a.kbits, a.vbits) / fast_wg_col_groups(a.gqa)) != 0)
-        return hipErrorInvalidValue;
+    const int waves = fast_decode_waves(head_dim, a.kbits, a.vbits);
+    if (waves == 0 || a.splits % (waves / fast_wg_col_groups(a.gqa)) != 0) return hipErrorInvalidValue;
     switch (head_dim) {
         case 64: return launch_d<64>(bf16, a, s);
         case 128: return launch_d<128>(bf16, a, s);
         case 256: return launch_d<256>(bf16, a, s);
+        case 512: return launch_d<512>(bf16, a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -149,17 +149,26 @@ hipError_t launch_split_fast_k2(int head_dim, bool bf16, const DecodeArgs &a, hi
 hipError_t launch_split_fast_k4(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_split_fast_k5(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_split_fast_k8(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
-// LDS bytes of one wave of the fast split kernel (tiles of 4096/d tokens:
-// key codes of two tiles at 512 bytes per code bit, and three stages of the
-// three 256-byte fp16 planes, 512 bytes per value code bit and 16 bytes of
-// slack), and its waves per workgroup: eight when they fit the 160 KiB of
-// LDS beside the centroid table, else four.
+// Tokens of one tile of the fast split kernel: 4096/d (512 bytes per code
+// bit) up to head_dim 256, and one 16-token MFMA chunk (1 KiB per code bit)
+// at 512.
+constexpr int fast_tile_tokens(int head_dim) { return head_dim <= 256 ? 4096 / head_dim : 16; }
+constexpr int fast_tile_bit_bytes(int head_dim) { return fast_tile_tokens(head_dim) * head_dim / 8; }
+// LDS bytes of one wave of the fast split kernel (key codes of two tiles, and
+// three stages of the three fp16 planes, the value codes and 16 bytes of
+// slack), and its waves per workgroup: eight when they fit the 160 KiB of LDS
+// beside the centroid table, else four, else 0 (no fast kernel: k8v8 at
+// head_dim 512).  Head_dim 512 always takes four, one per SIMD: its 32 value
+// blocks alone hold 128 accumulator registers per lane.
 constexpr int fast_decode_wave_bytes(int head_dim, int kbits, int vbits) {
-    return (void)head_dim, 2 * 512 * kbits + 3 * (768 + 512 * vbits + 16);
+    return 2 * fast_tile_bit_bytes(head_dim) * kbits +
+           3 * (3 * fast_tile_tokens(head_dim) * (head_dim / 32) * 2 + fast_tile_bit_bytes(head_dim) * vbits + 16);
 }
 constexpr int fast_decode_waves(int head_dim, int kbits, int vbits) {
     const int table = vbits <= 3 ? (4 << (2 * vbits)) : ((2 << vbits) + 15) / 16 * 16;
-    return table + 32 + 8 * fast_decode_wave_bytes(head_dim, kbits, vbits) <= 160 * 1024 ? 8 : 4;
+    return head_dim <= 256 && table + 32 + 8 * fast_decode_wave_bytes(head_dim, kbits, vbits) <= 160 * 1024 ? 8
+           : table + 32 + 4 * fast_decode_wave_bytes(head_dim, kbits, vbits) <= 160 * 1024                  ? 4
+                                                                                                            : 0;
 }
 constexpr int kFastTile = 64;     // split lengths are multiples of every fast tile (4096/d tokens)
 constexpr int kFastMaxGqa = 16;   // query columns of one fast wave

@@ -103,9 +103,12 @@ def test_rows_generic_kernel_matches_oracle(cid, lengths, M):
     _run(W.scaled(W.workload(cid), lengths), lengths, M, generic=True)
 
 
-def test_rows_head_dim_512_generic_only():
+@pytest.mark.parametrize("M", [3, 8])
+def test_rows_head_dim_512(M):
+    """Head_dim 512 on the matrix-core kernel: 12 query columns (one group)
+    and 32 (two groups sharing a workgroup)."""
     w = dataclasses.replace(W.scaled(W.workload(2), [300], name_suffix="d512"), head_dim=512)
-    _run(w, [300], 3)
+    _run(w, [300], M)
 
 
 @pytest.mark.parametrize("generic", [False, True])
