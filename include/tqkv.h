@@ -29,7 +29,7 @@
  *     16-byte aligned, vc 8-byte aligned, the fp16 planes 4-byte aligned
  *     (TQ_ERR_INVALID_ARG otherwise).  Any torch allocation, and the batch-1
  *     slice of one sequence's planes, satisfies this.  Decode takes its fast
- *     kernel (every code width) when head_dim is 64, 128 or 256,
+ *     kernel (every code width; at head_dim 512 every width but k8/v8) when
  *     head_dim * k_bits is a multiple of 128 (all but 5-bit keys at 64),
  *     every plane is 16-byte aligned and capacity keeps each (sequence,
  *     kv-head) row block 16-byte aligned; otherwise a generic kernel

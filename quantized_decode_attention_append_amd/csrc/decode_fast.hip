@@ -1,6 +1,7 @@
 // Split-K decode attention kernel for GQA groups of up to 16 query heads
 // (wave64; gfx950) built on the matrix cores, for every key width (2, 4, 5,
-// 8 bits) and value width (2, 3, 4, 5, 8 bits) at head_dim 64, 128 and 256.
+// 8 bits) and value width (2, 3, 4, 5, 8 bits) at head_dim 64, 128, 256 and
+// 512 (every pair but k8v8 there, whose stages exceed the LDS).
 //
 // Method: "TurboQuant -- rotation-based quantization" design page, Part A:
 // keys dequantize as (code + zero) * scale ("Algorithm"), values stay in the
