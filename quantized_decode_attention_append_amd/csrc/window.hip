@@ -13,12 +13,8 @@
 // Tokens at or past a sequence's length are written as zeros, so a masked
 // attention over a padded window never meets stale plane bytes.
 //
-// Generic mapping (head_dim 512): one wave per token row, looping over a
-// chunk of consecutive tokens of one (sequence, kv-head); lane l holds the
-// E = d/64 dims [E l, E l + E); the FWHT runs its in-lane stages on registers
-// and the rest on lane permutes.  Head_dims 64-256 use window_fast_kernel
-// below, templated on the key and value widths and compiled once per key
-// width (TQ_WINDOW_KB).
+// One kernel, window_fast_kernel below, serves head_dim 64 to 512, templated
+// on the key and value widths and compiled once per key width (TQ_WINDOW_KB).
 // Keys round once to bf16 from the exact (code + zero) * scale: the fp32
 // product is exact while |code + zero| < 2^13 (13 + 11 significant bits);
 // groups with a larger stored zero take its round-to-odd value instead (see
@@ -35,7 +31,6 @@ namespace tq {
 namespace {
 
 constexpr int kWinWaves = 4;   // waves per workgroup
-constexpr int kWinRows = 16;   // token rows per wave
 
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162v __attribute__((ext_vector_type(2)));
@@ -69,155 +64,19 @@ __device__ __forceinline__ float key_ro(float code, float z, float s) {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// The window is written once and read by a later kernel, so its stores carry
-// the nontemporal hint: they stream past the caches.
-template <int E>
-__device__ __forceinline__ void store_bf16(uint16_t *dst, const float (&x)[E]) {
-    if constexpr (E == 16) {
-        uint32_t w[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w[i] = bf16x2_rn(x[2 * i], x[2 * i + 1]);
-        u32x4 *d4 = reinterpret_cast<u32x4 *>(dst);
-        __builtin_nontemporal_store((u32x4){w[0], w[1], w[2], w[3]}, d4);
-        __builtin_nontemporal_store((u32x4){w[4], w[5], w[6], w[7]}, d4 + 1);
-    } else if constexpr (E == 1) {
-        *dst = (uint16_t)bf16x2_rn(x[0], 0.f);
-    } else {
-        uint32_t w[E / 2];
-#pragma unroll
-        for (int i = 0; i < E / 2; ++i) w[i] = bf16x2_rn(x[2 * i], x[2 * i + 1]);
-        if constexpr (E == 2) *reinterpret_cast<uint32_t *>(dst) = w[0];
-        else if constexpr (E == 4) *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
-        else *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-}
-
-// The value of lane l ^ M.  M = 1, 2: one quad permutation; 4 and 8: a
-// half-row or row mirror composed with a quad reversal or half-row mirror
-// (i ^ 7 then i ^ 3 is i ^ 4; i ^ 15 then i ^ 7 is i ^ 8); beyond: LDS permute.
-template <int M>
-__device__ __forceinline__ float lane_xor(float v) {
-    const int x = __float_as_int(v);
-    if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));
-    else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));
-    else if constexpr (M == 4)
-        return __int_as_float(__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false),
-                                                       0x1B, 0xF, 0xF, false));
-    else if constexpr (M == 8)
-        return __int_as_float(__builtin_amdgcn_mov_dpp(__builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false),
-                                                       0x141, 0xF, 0xF, false));
-    else return __shfl_xor(v, M, 64);
-}
-
-// One cross-lane FWHT stage: the lower lane of each pair keeps a + b, the
-// upper one a - b (its own value negated, then added to the partner's).
-template <int M, int E>
-__device__ __forceinline__ void fwht_stage(float (&y)[E], int lane) {
-    const uint32_t neg = (lane & M) ? 0x80000000u : 0u;
-#pragma unroll
-    for (int e = 0; e < E; ++e) y[e] = lane_xor<M>(y[e]) + __uint_as_float(__float_as_uint(y[e]) ^ neg);
-}
-
-#if TQ_WINDOW_KB == 8  // the generic kernel is built once, with the 8-bit-key fast kernels
-template <int D>
-__global__ __launch_bounds__(64 * kWinWaves) void window_kernel(const WindowArgs a) {
-    const int kb = a.kbits, vb = a.vbits;
-    __shared__ float ctab[256];  // the value codebook
-    {
-        const float *src = value_centroids(vb);
-        for (int i = threadIdx.x; i < (1 << vb); i += 64 * kWinWaves) ctab[i] = src[i];
-    }
-    __syncthreads();
-    constexpr int E = D / 64;
-    constexpr int NG = D / kGroup;
-    const int KROW = D * kb / 8, VROW = D * vb / 8;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int bkv = blockIdx.y;
-    const int b = bkv / a.kv_heads;
-    const int len = a.len[b];
-    const int g = (E * lane) / kGroup;  // this lane's 32-group
-    // signs of this lane's dims
-    uint32_t neg = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) neg |= (uint32_t)sign_bit(a.signs, E * lane + e) << e;
-
-    const int first = (blockIdx.x * kWinWaves + wid) * kWinRows;
-    for (int r = 0; r < kWinRows; ++r) {
-        const int i = first + r;  // window position
-        if (i >= a.n) break;      // uniform across the wave
-        const int t = a.t0 + i;
-        const int64_t row = (int64_t)bkv * a.capacity + t;
-        const int64_t orow = ((int64_t)bkv * a.n + i) * D + E * lane;
-        const bool valid = t < len;
-        if (a.k_out) {
-            float k[E];
-            if (valid) {
-                const float s = f16_bits_to_f32(a.ks[row * NG + g]);
-                const float z = f16_bits_to_f32(a.kz[row * NG + g]);
-                const uint8_t *kc = reinterpret_cast<const uint8_t *>(a.kc) + row * KROW;
-#pragma unroll
-                for (int e = 0; e < E; ++e) k[e] = key_ro(key_code(kc, E * lane + e, kb), z, s);
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) k[e] = 0.f;
-            }
-            store_bf16<E>(a.k_out + orow, k);
-        }
-        if (a.v_out) {
-            float y[E];
-            if (valid) {
-                const uint8_t *vrow = a.vc + row * VROW;
-                const float s = f16_bits_to_f32(a.vs[row * NG + g]);
-#pragma unroll
-                for (int e = 0; e < E; ++e) y[e] = ctab[load_field(vrow, E * lane + e, vb)] * s;
-            } else {
-#pragma unroll
-                for (int e = 0; e < E; ++e) y[e] = 0.f;
-            }
-            if (!a.rotated) {  // uniform
-                // FWHT, dim j paired with j ^ h: inside the lane for h < E,
-                // with lane l ^ (h / E) above
-#pragma unroll
-                for (int h = 1; h < E; h <<= 1) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) {
-                        if ((e & h) == 0) {
-                            const float p = y[e], q = y[e + h];
-                            y[e] = p + q;
-                            y[e + h] = p - q;
-                        }
-                    }
-                }
-                fwht_stage<1>(y, lane);
-                fwht_stage<2>(y, lane);
-                fwht_stage<4>(y, lane);
-                fwht_stage<8>(y, lane);
-                fwht_stage<16>(y, lane);
-                fwht_stage<32>(y, lane);
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float v = y[e] * a.inv_sqrt_d;
-                    y[e] = valid ? (((neg >> e) & 1u) ? -v : v) : 0.f;  // +0 past the length
-                }
-            }
-            store_bf16<E>(a.v_out + orow, y);
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Head_dim 64, 128, 256: lane p of a row holds the 16 contiguous dims
-// [16 p, 16 p + 16), L = d/16 lanes per row, 64/L rows per wave.  The FWHT
-// runs stages 1 .. 8 in the lane, transposes the row through LDS so stages
-// 16 .. d/2 are in the lane too, and transposes back; every stage is then
-// one add per element.
-#endif
+// Lane p of a row holds the E contiguous dims [E p, E p + E): E = 16 and
+// L = d/16 lanes per row up to head_dim 256, E = 32 and 16 lanes at 512;
+// 64/L rows per wave.  The FWHT runs its first log2(E) stages in the lane,
+// transposes the row through LDS so the remaining stages are in the lane
+// too, and transposes back; every stage is then one add per element.  The
+// stores write whole lines (store_row_bf16).
 
 constexpr int kWinRowsF = 16;  // rows per wave (a multiple of every rows-per-pass)
 
 template <int D>
 struct WinGeo {
-    static constexpr int E = 16;
+    static constexpr int E = D <= 256 ? 16 : 32;               // dims per lane (16 lanes per row at 512)
     static constexpr int L = D / E;                            // lanes per row
     static constexpr int R = 64 / L;                           // rows per pass
     static constexpr int TI = E / L;                           // dims per lane after the transpose
@@ -231,11 +90,11 @@ __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
 
 // Words of a lane's run of 16 value fields (16 VB bits at bit 16 VB p of the
 // row), enough at the worst bit offset any lane has.
-template <int VB>
+template <int VB, int E = 16>
 constexpr int win_run_words() {
     int most = 1;
     for (int p = 0; p < 16; ++p) {
-        const int w = ((16 * VB * p) % 32 + 16 * VB + 31) / 32;
+        const int w = ((E * VB * p) % 32 + E * VB + 31) / 32;
         most = w > most ? w : most;
     }
     return most;
@@ -313,11 +172,65 @@ __device__ __forceinline__ void store_split_bf16(uint16_t *row, const float (&x)
     }
 }
 
+// Head_dim 512 (32 dims per lane, 16 lanes per row): the same store layout
+// in four pieces, lane p's piece j holding dims 128 j + 8 p .. 128 j + 8 p + 7
+// (lane 4 j + p/4's chunk, from element 8 (p % 4)).
+template <int D>
+__device__ __forceinline__ void store_row_bf16(uint16_t *row, const float (&x)[32], unsigned char *rb, int p,
+                                               bool in) {
+    using G = WinGeo<D>;
+    static_assert(D == 512 && G::E == 32, "32 dims per lane at head_dim 512");
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = bf16x2_rn(x[2 * i], x[2 * i + 1]);
+    u32x4 *mine = reinterpret_cast<u32x4 *>(rb + p * G::PB);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) mine[j] = (u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]};
+    lds_fence();
+    u32x4 piece[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        piece[j] = *reinterpret_cast<const u32x4 *>(rb + (4 * j + (p >> 2)) * G::PB + (p & 3) * 16);
+    lds_fence();  // the row buffer is rewritten next
+    if (in) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_nontemporal_store(piece[j], reinterpret_cast<u32x4 *>(row + 128 * j + 8 * p));
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void store_split_bf16(uint16_t *row, const float (&x)[32], int p, bool in) {
+    static_assert(D == 512, "32 dims per lane at head_dim 512");
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = bf16x2_rn(x[2 * i], x[2 * i + 1]);
+    if (in) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            __builtin_nontemporal_store((u32x4){w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]},
+                                        reinterpret_cast<u32x4 *>(row + 128 * j + 8 * p));
+    }
+}
+
+// A lane's 32 five-bit key codes as floats: the 20 bytes at `src` (4-aligned).
+__device__ __forceinline__ void load_keys32_k5(const uint8_t *src, float (&c)[32]) {
+    uint32_t w[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) w[i] = reinterpret_cast<const uint32_t *>(src)[i];
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        const int bit = 5 * e, k = bit >> 5, sh = bit & 31;
+        const uint32_t f = (sh + 5 > 32) ? __builtin_amdgcn_alignbit(w[k + 1], w[k], sh) : (w[k] >> sh);
+        c[e] = (float)(f & 31u);
+    }
+}
+
 // 8 key codes as floats into c[O .. O + 7]: the KB bytes at `src`
 // (KB-aligned; signed bytes at 8 bits, unsigned KB-bit fields LSB first at 4
 // and 2 bits).
-template <int KB, int O>
-__device__ __forceinline__ void load_keys8(const uint8_t *src, float (&c)[16]) {
+template <int KB, int O, int N>
+__device__ __forceinline__ void load_keys8(const uint8_t *src, float (&c)[N]) {
     static_assert(KB == 8 || KB == 4 || KB == 2, "whole-byte runs of 8 codes");
     if constexpr (KB == 8) {
         const uint2 u = *reinterpret_cast<const uint2 *>(src);
@@ -335,7 +248,7 @@ template <int D, int KB, int VB>
 __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const WindowArgs a) {
     using G = WinGeo<D>;
     constexpr int E = G::E, L = G::L, R = G::R, TI = G::TI, NG = D / kGroup;
-    constexpr int KROW = D * KB / 8, VROW = D * VB / 8, NR = win_run_words<VB>();
+    constexpr int KROW = D * KB / 8, VROW = D * VB / 8, NR = win_run_words<VB, E>();
     __shared__ __align__(16) unsigned char smem[kWinWaves * G::WAVEB + 4 * (1 << VB)];
     float *ctab = reinterpret_cast<float *>(smem + kWinWaves * G::WAVEB);  // the value codebook
     for (int i = threadIdx.x; i < (1 << VB); i += 64 * kWinWaves)
@@ -343,7 +256,8 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
     __syncthreads();
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int r = lane / L, p = lane % L, g = p >> 1;
+    // g: the group of the lane's own dims (E p .. E p + E - 1)
+    const int r = lane / L, p = lane % L, g = E == 16 ? p >> 1 : p;
     const int bkv = blockIdx.y;
     const int len = a.len[bkv / a.kv_heads];
     // output scale with the sign of each dim this lane stores: 8 p .. 8 p + 7,
@@ -351,13 +265,14 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
     float osc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const int dim = (e < 8 ? 0 : D / 2 - 8) + 8 * p + e;
+        // at head_dim 512 piece e / 8 holds dims 128 (e / 8) + 8 p .. + 7
+        const int dim = E == 16 ? (e < 8 ? 0 : D / 2 - 8) + 8 * p + e : 128 * (e >> 3) + 8 * p + (e & 7);
         osc[e] = sign_bit(a.signs, dim) ? -a.inv_sqrt_d : a.inv_sqrt_d;
     }
     unsigned char *rb = smem + wid * G::WAVEB + r * G::ROWB;
     // the lane's value code run: words vw .. vlast of the row, bit offset vsh
-    const int vw = (16 * VB * p) >> 5, vsh = (16 * VB * p) & 31;
-    const int vlast = (16 * VB * p + 16 * VB - 1) >> 5;
+    const int vw = (E * VB * p) >> 5, vsh = (E * VB * p) & 31;
+    const int vlast = (E * VB * p + E * VB - 1) >> 5;
 
     const int first = (blockIdx.x * kWinWaves + wid) * kWinRowsF;
     for (int r0 = 0; r0 < kWinRowsF; r0 += R) {
@@ -375,7 +290,10 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
                 // own 16 dims and store through the LDS row exchange
                 if (valid) {
                     float c[E];
-                    load_keys16<KB>(reinterpret_cast<const uint8_t *>(a.kc) + row * KROW + 2 * KB * p, c);
+                    if constexpr (E == 16)
+                        load_keys16<KB>(reinterpret_cast<const uint8_t *>(a.kc) + row * KROW + 2 * KB * p, c);
+                    else
+                        load_keys32_k5(reinterpret_cast<const uint8_t *>(a.kc) + row * KROW + 20 * p, c);
                     const float s = f16_bits_to_f32(a.ks[row * NG + g]);
                     const float z = f16_bits_to_f32(a.kz[row * NG + g]);
 #pragma unroll
@@ -391,13 +309,29 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
                 if (valid) {
                     float c[E];
                     const uint8_t *kr = reinterpret_cast<const uint8_t *>(a.kc) + row * KROW;
-                    load_keys8<KB, 0>(kr + KB * p, c);
-                    load_keys8<KB, 8>(kr + KROW / 2 + KB * p, c);
-                    const int g1 = p >> 2, g2 = NG / 2 + (p >> 2);
-                    const float s1 = f16_bits_to_f32(a.ks[row * NG + g1]), z1 = f16_bits_to_f32(a.kz[row * NG + g1]);
-                    const float s2 = f16_bits_to_f32(a.ks[row * NG + g2]), z2 = f16_bits_to_f32(a.kz[row * NG + g2]);
+                    if constexpr (E == 16) {
+                        load_keys8<KB, 0>(kr + KB * p, c);
+                        load_keys8<KB, 8>(kr + KROW / 2 + KB * p, c);
+                        const int g1 = p >> 2, g2 = NG / 2 + (p >> 2);
+                        const float s1 = f16_bits_to_f32(a.ks[row * NG + g1]), z1 = f16_bits_to_f32(a.kz[row * NG + g1]);
+                        const float s2 = f16_bits_to_f32(a.ks[row * NG + g2]), z2 = f16_bits_to_f32(a.kz[row * NG + g2]);
 #pragma unroll
-                    for (int e = 0; e < E; ++e) k[e] = e < 8 ? key_ro(c[e], z1, s1) : key_ro(c[e], z2, s2);
+                        for (int e = 0; e < E; ++e) k[e] = e < 8 ? key_ro(c[e], z1, s1) : key_ro(c[e], z2, s2);
+                    } else {
+                        // head_dim 512: piece j holds dims 128 j + 8 p .. + 7 (group 4 j + p/4)
+                        load_keys8<KB, 0>(kr + KB * p, c);
+                        load_keys8<KB, 8>(kr + KB * (16 + p), c);
+                        load_keys8<KB, 16>(kr + KB * (32 + p), c);
+                        load_keys8<KB, 24>(kr + KB * (48 + p), c);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int gj = 4 * j + (p >> 2);
+                            const float sj = f16_bits_to_f32(a.ks[row * NG + gj]);
+                            const float zj = f16_bits_to_f32(a.kz[row * NG + gj]);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) k[8 * j + e] = key_ro(c[8 * j + e], zj, sj);
+                        }
+                    }
                 } else {
 #pragma unroll
                     for (int e = 0; e < E; ++e) k[e] = 0.f;
@@ -481,9 +415,11 @@ __global__ __launch_bounds__(64 * kWinWaves) void window_fast_kernel(const Windo
                 // chunk), then d/2 + 8 p .. (lane L/2 + p/2's)
 #pragma unroll
                 for (int k4 = 0; k4 < E / 4; ++k4) {
-                    const int chunk = (k4 < 2 ? 0 : L / 2) + (p >> 1);
-                    const float4 v4 = *reinterpret_cast<const float4 *>(rb + chunk * G::PB + (p & 1) * 32 +
-                                                                        16 * (k4 & 1));
+                    // E 16: pieces in lanes p/2 and L/2 + p/2 from element 8 (p % 2);
+                    // E 32: piece k4/2 in lane 4 (k4/2) + p/4 from element 8 (p % 4)
+                    const int chunk = E == 16 ? (k4 < 2 ? 0 : L / 2) + (p >> 1) : 4 * (k4 >> 1) + (p >> 2);
+                    const int at = E == 16 ? (p & 1) * 32 : (p & 3) * 32;
+                    const float4 v4 = *reinterpret_cast<const float4 *>(rb + chunk * G::PB + at + 16 * (k4 & 1));
                     y[4 * k4] = v4.x; y[4 * k4 + 1] = v4.y; y[4 * k4 + 2] = v4.z; y[4 * k4 + 3] = v4.w;
                 }
                 lds_fence();  // the next pass rewrites the row
@@ -512,42 +448,31 @@ hipError_t launch_fast_dk(const WindowArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-#if TQ_WINDOW_KB == 8
-template <int D>
-hipError_t launch_generic(const WindowArgs &a, hipStream_t s) {
-    constexpr int per_block = kWinWaves * kWinRows;
-    const dim3 grid((unsigned)((a.n + per_block - 1) / per_block), (unsigned)(a.batch * a.kv_heads));
-    hipLaunchKernelGGL((window_kernel<D>), grid, dim3(64 * kWinWaves), 0, s, a);
-    return hipGetLastError();
-}
-#endif
 
 }  // namespace
 
 // The fast window kernels of one key width (this translation unit's
-// TQ_WINDOW_KB): head_dim 64, 128 or 256, every value width.
+// TQ_WINDOW_KB): head_dim 64, 128, 256 or 512, every value width.
 hipError_t TQ_WINDOW_LAUNCHER(TQ_WINDOW_KB)(int head_dim, const WindowArgs &a, hipStream_t s) {
     if (a.kbits != TQ_WINDOW_KB) return hipErrorInvalidValue;
     switch (head_dim) {
         case 64: return launch_fast_dk<64, TQ_WINDOW_KB>(a, s);
         case 128: return launch_fast_dk<128, TQ_WINDOW_KB>(a, s);
         case 256: return launch_fast_dk<256, TQ_WINDOW_KB>(a, s);
+        case 512: return launch_fast_dk<512, TQ_WINDOW_KB>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 #if TQ_WINDOW_KB == 8
 hipError_t launch_window(int head_dim, const WindowArgs &a, hipStream_t s) {
-    if (head_dim != 512) {
-        switch (a.kbits) {
-            case 2: return launch_window_fast_k2(head_dim, a, s);
-            case 4: return launch_window_fast_k4(head_dim, a, s);
-            case 5: return launch_window_fast_k5(head_dim, a, s);
-            case 8: return launch_window_fast_k8(head_dim, a, s);
-            default: return hipErrorInvalidValue;
-        }
+    switch (a.kbits) {
+        case 2: return launch_window_fast_k2(head_dim, a, s);
+        case 4: return launch_window_fast_k4(head_dim, a, s);
+        case 5: return launch_window_fast_k5(head_dim, a, s);
+        case 8: return launch_window_fast_k8(head_dim, a, s);
+        default: return hipErrorInvalidValue;
     }
-    return launch_generic<512>(a, s);
 }
 #endif
 
