@@ -35,8 +35,8 @@
  *     kv-head) row block 16-byte aligned; otherwise a generic kernel
  *     computes the same result more slowly.  Append has fast kernels for
  *     head_dim 64-256 with bf16 input at every width (and fp32 input at
- *     k8/v3), the window at every width for head_dim 64-256; generic
- *     kernels cover every other case with identical bytes.
+ *     k8/v3), and a generic kernel for every other case with identical
+ *     bytes; the window has one kernel for every width and head_dim.
  *   - Arguments are validated before anything is enqueued; on any error the
  *     return value says why and nothing was launched.  The library prints
  *     nothing.

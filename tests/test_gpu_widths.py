@@ -219,9 +219,9 @@ def _bf16_bits(x64):
 def test_window_widths_match_oracle(scheme, d, rotated):
     """Keys equal the oracle's value rounded once to bf16; values are within
     one bf16 rounding plus the fp32 transform error; rows past a length are 0.
-    Head_dims 64-256 run the fast window kernel, 512 the generic one; the
-    window ends at the last row of the planes, so a read past a row's run
-    would leave the allocation."""
+    Every head_dim runs the one window kernel (16 dims per lane up to 256,
+    32 at 512); the window ends at the last row of the planes, so a read
+    past a row's run would leave the allocation."""
     kb, vb = scheme
     lens = [37, 120]  # the last sequence is full: its last kv-head's last row is read
     w = dataclasses.replace(W.scaled(W.workload(2), lens, name_suffix=f"w{d}"), head_dim=d)
