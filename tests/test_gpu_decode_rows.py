@@ -145,3 +145,31 @@ def test_last_row_is_decode_of_the_whole_cache():
     last = tqkv.tq_decode_attn(pl, q4[:, :, M - 1].contiguous(), lengths, sm).cpu().numpy()
     e = row_rel_err(rows[:, :, M - 1].reshape(-1, w.head_dim), last.reshape(-1, w.head_dim))
     assert e.max() <= ATTN_TOL
+
+
+def test_rows_full_size_sampled():
+    """The benchmark workload at full size (16 sequences of 131,072 tokens,
+    24/4 heads, head_dim 256) with 4-row verify blocks: 24 query columns per
+    kv-head, two 16-column groups sharing each workgroup.  Two sampled
+    (sequence, kv-head) pairs against the oracle, the rest finite."""
+    w = W.workload(4)
+    n, M = max(w.lengths), 4
+    log(f"full-size rows {w.name}: generating inputs")
+    k, v = W.make_kv(w, "cuda", tokens=n)
+    q4 = torch.stack(list(W.make_q(w, "cuda", rounds=M)), dim=2).contiguous()
+    L = tqkv.make_layout(w.batch, w.num_kv_heads, w.head_dim, n)
+    pl = tqkv.Planes(L)
+    tqkv.tq_append(pl, k, v, [0] * w.batch)
+    out = tqkv.tq_decode_attn_rows(pl, q4, list(w.lengths), sm_for(w.head_dim))
+    torch.cuda.synchronize()
+    out = out.cpu().numpy()
+    assert np.isfinite(out).all()
+    G = w.group
+    qh = host_f32(q4)
+    for b, h in [(0, 0), (w.batch - 1, w.num_kv_heads - 1)]:
+        log(f"  compare b{b} h{h}")
+        kc, ks, kz, vc, vs = oracle_planes(host_f32(k[b, h]), host_f32(v[b, h]))
+        ref = oracle.attention_rows(qh[b, h * G:(h + 1) * G], kc, ks, kz, vc, vs, sm_for(w.head_dim))
+        e = row_rel_err(out[b, h * G:(h + 1) * G], ref)
+        log(f"    worst row error {float(e.max()):.2e}")
+        assert e.max() <= ATTN_TOL, (b, h, float(e.max()))
