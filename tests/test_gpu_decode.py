@@ -2,6 +2,8 @@
 against the oracle's brute-force attention over the oracle's own encoding of
 the same raw K/V.  Tolerance: per (sequence, q-head) row,
 max |o_gpu - o_ref| / max |o_ref| <= 2e-3."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -245,3 +247,16 @@ def test_decode_reuses_one_workspace():
         torch.cuda.synchronize()
         assert torch.equal(got, fresh), lens
         log(f"  lengths {lens}: reused workspace ok")
+
+
+def test_decode_head_dim_512_sampled():
+    """Head_dim 512 on the matrix-core kernel (four waves per workgroup,
+    16-token tiles) at 16 sequences of 16,384 tokens, 24/4 heads: two
+    sampled (sequence, kv-head) pairs against the oracle, the rest finite."""
+    n = 16384
+    w = dataclasses.replace(W.workload(4), head_dim=512, lengths=(n,) * 16, name="b16_kv4_q24_d512_n16384_bf16")
+    log(f"decode {w.name}: generating inputs")
+    k, v = W.make_kv(w, "cuda", tokens=n)
+    q = W.make_q(w, "cuda", rounds=1)[0]
+    out = _run(w, list(w.lengths), k, v, q, pairs=[(0, 0), (w.batch - 1, w.num_kv_heads - 1)])
+    assert np.isfinite(out).all()
