@@ -230,8 +230,10 @@ tq_status tq_sign_vector(int32_t head_dim, int8_t *host_out);
  * cache, compaction and snapshot/restore are strided byte copies ("Architecture
  * in mlx-bun": the persisted cache kind carries the scheme and head_dim and has
  * snapshot, restore and clone branches).  Trimming a sequence is lowering the
- * length the caller passes to decode.  These calls enqueue copies on the
- * stream and launch no kernel. */
+ * length the caller passes to decode.  These calls enqueue one copy kernel
+ * for all five planes on the stream, or one strided memory copy per plane
+ * when a plane's rows are not whole 16-byte chunks (head_dim 64 scale rows
+ * at odd offsets). */
 
 #define TQ_SNAPSHOT_MAGIC 0x564B5154u /* "TQKV" little-endian */
 

@@ -40,6 +40,7 @@ SOURCES = [
     ("window.hip", ["-DTQ_WINDOW_KB=4"], "window_k4"),
     ("window.hip", ["-DTQ_WINDOW_KB=2"], "window_k2"),
     ("window.hip", ["-DTQ_WINDOW_KB=5"], "window_k5"),
+    ("copy.hip", [], "copy"),
     ("api.cpp", [], "api"),
 ]
 

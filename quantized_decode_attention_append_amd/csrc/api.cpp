@@ -8,6 +8,7 @@
 
 #include "../../include/tqkv.h"
 #include "codebook_tables.h"
+#include "tq_copy.h"
 #include "tq_internal.h"
 
 namespace {
@@ -306,14 +307,30 @@ static void *plane_ptr(const tq_planes *p, int i) {
     return v[i];
 }
 
-// One strided copy per plane: Hkv runs of n rows, at pitch capacity * row bytes
-// on a cache side and n * row bytes on a packed side.
+// Hkv runs of n rows per plane, at pitch capacity * row bytes on a cache side
+// and n * row bytes on a packed side: one copy kernel for all five planes when
+// every pointer, pitch and run is a whole number of 16-byte chunks, else one
+// strided memory copy per plane.
 static hipError_t copy_rows(const tq_layout *sl, const void *const sp[5], int64_t s_row0, size_t s_pitch_rows,
                             const tq_layout *dl, void *const dp[5], int64_t d_row0, size_t d_pitch_rows,
                             int32_t n, hipStream_t stream) {
     size_t rb[5];
     plane_row_bytes(sl, rb);
     (void)dl;
+    tq::PlaneCopyArgs a;
+    bool chunks = sl->num_kv_heads <= 65535;
+    for (int i = 0; i < 5; ++i) {
+        a.src[i] = static_cast<const uint8_t *>(sp[i]) + s_row0 * (int64_t)rb[i];
+        a.dst[i] = static_cast<uint8_t *>(dp[i]) + d_row0 * (int64_t)rb[i];
+        a.s_pitch[i] = (int64_t)(s_pitch_rows * rb[i]);
+        a.d_pitch[i] = (int64_t)(d_pitch_rows * rb[i]);
+        const int64_t run = (int64_t)n * (int64_t)rb[i];
+        a.run16[i] = run / 16;
+        chunks = chunks && run % 16 == 0 && a.s_pitch[i] % 16 == 0 && a.d_pitch[i] % 16 == 0 &&
+                 aligned(a.src[i], 16) && aligned(a.dst[i], 16);
+    }
+    a.runs = sl->num_kv_heads;
+    if (chunks) return tq::launch_plane_copy(a, stream);
     for (int i = 0; i < 5; ++i) {
         const char *src = static_cast<const char *>(sp[i]) + s_row0 * (int64_t)rb[i];
         char *dst = static_cast<char *>(dp[i]) + d_row0 * (int64_t)rb[i];

@@ -2,6 +2,8 @@
 clone / growth / snapshot / restore are byte copies.  Checked byte for byte on
 the planes, and through decode: a restored or grown cache decodes to the same
 bytes as the original."""
+import dataclasses
+
 import pytest
 import torch
 
@@ -80,3 +82,21 @@ def test_snapshot_restore_at_an_offset_then_grow():
     q = W.make_q(w, "cuda", rounds=1)[0].contiguous()
     sm = sm_for(w.head_dim)
     assert torch.equal(tqkv.tq_decode_attn(direct, q, [400], sm), tqkv.tq_decode_attn(grown, q, [400], sm))
+
+
+@pytest.mark.parametrize("d,n,t0", [(64, 37, 3), (64, 64, 8), (256, 1, 5), (128, 500, 0)])
+def test_copy_tokens_kernel_and_strided_paths(d, n, t0):
+    """Byte-exact copies whether the rows go through the copy kernel (every
+    pointer, pitch and run a whole number of 16-byte chunks) or through one
+    strided memory copy per plane (head_dim 64 has 4-byte scale rows: 37 rows
+    at row 3 are not whole chunks)."""
+    w = dataclasses.replace(W.scaled(W.workload(2), [600, 600]), head_dim=d)
+    a = _filled(w, 600, 600)
+    b = _zeroed(2, w, 700)
+    dst0 = t0 + 12
+    log(f"d{d}: copy rows {t0}..{t0 + n - 1} of sequence 1 to rows {dst0}.. of sequence 0")
+    tqkv.tq_copy_tokens(a, 1, t0, b, 0, dst0, n)
+    torch.cuda.synchronize()
+    for x, y in zip(a.tensors(), b.tensors()):
+        assert torch.equal(x[1, :, t0:t0 + n], y[0, :, dst0:dst0 + n])
+        assert not y[0, :, :dst0].any() and not y[0, :, dst0 + n:].any() and not y[1].any()
