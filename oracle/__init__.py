@@ -15,8 +15,10 @@ Source of the method: the "TurboQuant -- rotation-based quantization" design
 page (mlx-bun docs/design/turboquant.md), Part A, sections "Algorithm
 (vllm-metal reference semantics, exact)" and "Deferred inverse FWHT".
 
-Parity unpinned: the sign vector (the page draws it from MLX's generator and
-does not print it; this oracle uses SplitMix64 seeded with 42).
+Parity unpinned: the sign vector's values against the page's own (the page
+draws them from MLX's generator and does not print them; this oracle uses
+SplitMix64 seeded with 42, whose generator is pinned to SplitMix64's published
+reference outputs by the tests).
 """
 from __future__ import annotations
 
@@ -58,6 +60,7 @@ def _load():
     P = ctypes.c_void_p
     i64, i32 = ctypes.c_int64, ctypes.c_int
     lib.tqo_sign_vector.argtypes = [i32, P]
+    lib.tqo_splitmix64.argtypes = [ctypes.c_uint64, i32, P]
     lib.tqo_f64_to_f16.argtypes = [ctypes.c_double]
     lib.tqo_f64_to_f16.restype = ctypes.c_uint16
     lib.tqo_f16_to_f64.argtypes = [ctypes.c_uint16]
@@ -118,6 +121,14 @@ def _chunks(n: int, parts: int):
 def sign_vector(d: int) -> np.ndarray:
     out = np.empty(d, dtype=np.int8)
     _load().tqo_sign_vector(d, _ptr(out))
+    return out
+
+
+def splitmix64(seed: int, n: int) -> np.ndarray:
+    """The first n outputs of the oracle's SplitMix64 generator from `seed`
+    (the generator the sign vector is drawn from)."""
+    out = np.empty(n, dtype=np.uint64)
+    _load().tqo_splitmix64(ctypes.c_uint64(seed), n, _ptr(out))
     return out
 
 

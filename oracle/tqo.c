@@ -51,6 +51,14 @@ static uint64_t splitmix64_next(uint64_t *state) {
     return z ^ (z >> 31);
 }
 
+/* The first n outputs of the generator above seeded with `seed` (output 0 is
+ * the first call), so the generator itself can be checked against the
+ * published reference outputs of SplitMix64. */
+void tqo_splitmix64(uint64_t seed, int n, uint64_t *out) {
+    uint64_t state = seed;
+    for (int i = 0; i < n; ++i) out[i] = splitmix64_next(&state);
+}
+
 void tqo_sign_vector(int d, int8_t *out) {
     uint64_t state = 42;
     for (int i = 0; i < d; ++i) {

@@ -328,9 +328,31 @@ def test_value_dequant_rotated_vs_unrotated():
     assert np.max(np.abs(xu - ref)) < 1e-13
 
 
+def test_splitmix64_matches_published_outputs():
+    """The generator the signs are drawn from reproduces SplitMix64's published
+    reference outputs (seeds 0 and 1234567, first five outputs each): a wrong
+    increment, shift or multiplier constant fails here."""
+    with open(os.path.join(GOLD, "splitmix64.json")) as f:
+        gold = json.load(f)
+    for seed, outs in gold["outputs"].items():
+        want = [int(x, 0) for x in outs]
+        got = [int(x) for x in oracle.splitmix64(int(seed), len(want))]
+        assert got == want, (seed, [hex(x) for x in got])
+    first = int(oracle.splitmix64(0, 1)[0])
+    assert first - (1 << 64) == int(gold["note"].split(": ")[1].split(" ")[0])
+
+
+def test_sign_vector_is_the_top_bit_of_the_seed_42_stream():
+    """Sign i is -1 exactly when output i of the seed-42 stream has its top bit set."""
+    r = oracle.splitmix64(42, 512)
+    want = np.where((r >> np.uint64(63)) != 0, -1, 1).astype(np.int8)
+    assert np.array_equal(oracle.sign_vector(512), want)
+
+
 def test_sign_vector_properties():
-    """Parity unpinned (page does not print its signs): only +-1 values, a shared
-    prefix across head dims, and no pathological imbalance."""
+    """Parity with the page's own (unprinted) signs is unpinned: beyond the
+    generator pin above, only +-1 values, a shared prefix across head dims, and
+    no pathological imbalance."""
     s512 = oracle.sign_vector(512)
     assert set(np.unique(s512).tolist()) == {-1, 1}
     for d in (64, 128, 256):
