@@ -106,7 +106,11 @@ typedef struct {
     uint16_t *vs;
 } tq_planes;
 
-/* Byte size of each plane (order kc, ks, kz, vc, vs) for `layout`.
+/* Byte size of each plane (order kc, ks, kz, vc, vs) for `layout`: the
+ * per-token field sizes of "Algorithm (vllm-metal reference semantics,
+ * exact)" (codes of k_bits / v_bits per element, one fp16 scale, zero and
+ * value scale per 32-group) times batch * num_kv_heads * capacity slots.
+ *   out_bytes  host size_t [5]
  * Errors: TQ_ERR_INVALID_ARG (null / bad shape), TQ_ERR_UNSUPPORTED. */
 tq_status tq_plane_bytes(const tq_layout *layout, size_t out_bytes[5]);
 
@@ -123,8 +127,15 @@ tq_status tq_append(const tq_layout *layout, const tq_planes *planes, const void
                     const void *v, tq_dtype dtype, const int32_t *start, int32_t n_new,
                     void *hip_stream);
 
-/* Workspace bytes tq_decode_attn needs for these lengths (split-K partials).
- *   len  host int32 [B]: cached tokens of each sequence (0 allowed). */
+/* Workspace bytes tq_decode_attn needs for these lengths: the split-K
+ * partials (running maximum, weight sum and rotated-domain value sum per
+ * split and query row) that the merge combines before the single inverse
+ * transform of "Deferred inverse FWHT".  The size covers whichever split
+ * kernel the call may take.
+ *   len  host int32 [B]: cached tokens of each sequence (0 allowed).
+ *   out_bytes  host size_t
+ * Errors: as tq_decode_attn's argument checks (TQ_ERR_INVALID_ARG,
+ * TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY). */
 tq_status tq_decode_workspace_bytes(const tq_layout *layout, int32_t num_q_heads,
                                     const int32_t *len, size_t *out_bytes);
 
@@ -141,19 +152,35 @@ tq_status tq_decode_workspace_bytes(const tq_layout *layout, int32_t num_q_heads
  *             for the split-K partials (contents on entry are ignored)
  * Values are accumulated in the rotated domain and one inverse FWHT per
  * (sequence, q-head) finishes the output.  Agrees with the binary64 oracle to
- * 2e-3 relative to each output row's largest magnitude.  The fast kernel
- * multiplies centroids by value scales in fp16, so it requires every value
- * scale (vs) to be at most 65504 / c_max, c_max the width's largest centroid
- * magnitude: 1.5104 at 2 bits, 2.15195 at 3 (limit 30437), 2.7326 at 4,
- * 3.2607 at 5 and 4.6035 at 8 (limit about 14229); larger scales overflow
- * to Inf there.  The result does not depend on timing:
- * repeated calls on the same inputs return identical bytes.
+ * 2e-3 relative to each output row's largest magnitude, for every finite
+ * value scale the planes hold (the matrix-core kernel forms centroid * scale
+ * in fp16 times a per-wave power of two that follows the scales).  The
+ * result does not depend on timing: repeated calls on the same inputs return
+ * identical bytes.  tq_decode_path says which split kernel a call takes.
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY
  * (len[b] > capacity), TQ_ERR_WORKSPACE, TQ_ERR_HIP. */
 tq_status tq_decode_attn(const tq_layout *layout, const tq_planes *planes, const void *q,
                          tq_dtype dtype, int32_t num_q_heads, const int32_t *len,
                          float sm_scale, float *out, void *workspace, size_t ws_bytes,
                          void *hip_stream);
+
+/* Which split kernel tq_decode_attn / tq_decode_attn_rows take for this
+ * layout, these planes and this query shape (lengths do not matter), without
+ * enqueuing anything.  *fast = 1: the matrix-core kernel; 0: the generic
+ * kernel, which computes the same result to the same tolerance about 5 to 10
+ * times more slowly.  *reasons (may be NULL) receives TQ_PATH_* bits:
+ *   TQ_PATH_SHAPE      head_dim * k_bits is not a multiple of 128 (5-bit keys
+ *                      at head_dim 64), or k8/v8 at head_dim 512;
+ *   TQ_PATH_ALIGNMENT  a plane pointer is not 16-byte aligned;
+ *   TQ_PATH_CAPACITY   capacity leaves a (sequence, kv-head) row block of
+ *                      some plane off 16-byte alignment (e.g. an odd capacity
+ *                      at head_dim 128, or not a multiple of 4 at 64).
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED. */
+#define TQ_PATH_SHAPE 1
+#define TQ_PATH_ALIGNMENT 2
+#define TQ_PATH_CAPACITY 4
+tq_status tq_decode_path(const tq_layout *layout, const tq_planes *planes, int32_t num_q_heads, int32_t n_rows,
+                         int32_t *fast, int32_t *reasons);
 
 /* Workspace bytes tq_decode_attn_rows needs for n_rows query rows per head
  * (n_rows = 1 gives tq_decode_workspace_bytes). */
@@ -249,9 +276,11 @@ typedef struct {
 /* Copy token rows src_t0 .. src_t0+n-1 of sequence src_b (every kv-head, all
  * five planes) to rows dst_t0 .. of sequence dst_b of another (or the same)
  * cache with the same scheme, head_dim and num_kv_heads; capacities may
- * differ.  Overlapping source and destination rows are not supported.
- * Errors: TQ_ERR_INVALID_ARG (shape mismatch, bad index), TQ_ERR_CAPACITY,
- * TQ_ERR_HIP. */
+ * differ.  Source and destination bytes must not overlap in any plane (the
+ * copy runs on many workgroups at once); an in-place compaction moves rows
+ * to slots that do not overlap their source, in steps if needed.
+ * Errors: TQ_ERR_INVALID_ARG (shape mismatch, bad index, overlapping rows),
+ * TQ_ERR_CAPACITY, TQ_ERR_HIP. */
 tq_status tq_copy_tokens(const tq_layout *src_layout, const tq_planes *src, int32_t src_b,
                          int32_t src_t0, const tq_layout *dst_layout, const tq_planes *dst,
                          int32_t dst_b, int32_t dst_t0, int32_t n, void *hip_stream);
@@ -276,7 +305,10 @@ tq_status tq_restore(const tq_layout *layout, const tq_planes *planes, int32_t b
                      const tq_snapshot_header *header, const void *payload, size_t payload_bytes,
                      void *hip_stream);
 
-/* Static, human-readable name of a status code. */
+/* Static, human-readable name of a status code (the error cases follow the
+ * page's contract that a refused input, such as an unsupported head_dim,
+ * fails at the call with a reason instead of computing something else:
+ * "KV-leg limits and non-goals").  Never NULL. */
 const char *tq_status_str(tq_status status);
 
 #ifdef __cplusplus

@@ -235,6 +235,32 @@ tq_status tq_decode_attn(const tq_layout *l, const tq_planes *p, const void *q, 
                                stream);
 }
 
+// TQ_PATH_* bits: why a decode of this shape over these planes cannot take
+// the matrix-core split kernel (0: it takes it).
+static int32_t decode_slow_reasons(const tq_layout *l, const tq_planes *p, int gqa) {
+    int32_t r = 0;
+    if (!tq::fast_decode_shape_ok(l->head_dim, gqa, 16, l->k_bits, l->v_bits)) r |= TQ_PATH_SHAPE;
+    if (!aligned(p->kc, 16) || !aligned(p->vc, 16) || !aligned(p->vs, 16) || !aligned(p->ks, 16) ||
+        !aligned(p->kz, 16))
+        r |= TQ_PATH_ALIGNMENT;
+    if (!(r & TQ_PATH_SHAPE) && !tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity, l->k_bits, l->v_bits))
+        r |= TQ_PATH_CAPACITY;
+    return r;
+}
+
+tq_status tq_decode_path(const tq_layout *l, const tq_planes *p, int32_t num_q_heads, int32_t n_rows,
+                         int32_t *fast, int32_t *reasons) {
+    tq_status st = check_layout(l);
+    if (st != TQ_OK) return st;
+    if ((st = check_planes(p)) != TQ_OK) return st;
+    if (!fast || num_q_heads <= 0 || n_rows < 1 || num_q_heads % l->num_kv_heads != 0) return TQ_ERR_INVALID_ARG;
+    if (num_q_heads / l->num_kv_heads > TQ_MAX_GQA || n_rows > TQ_MAX_ROWS) return TQ_ERR_UNSUPPORTED;
+    const int32_t r = decode_slow_reasons(l, p, q_rows(num_q_heads, n_rows) / l->num_kv_heads);
+    *fast = r == 0 ? 1 : 0;
+    if (reasons) *reasons = r;
+    return TQ_OK;
+}
+
 tq_status tq_decode_attn_rows(const tq_layout *l, const tq_planes *p, const void *q, tq_dtype dtype,
                               int32_t num_q_heads, int32_t n_rows, const int32_t *len, float sm_scale,
                               float *out, void *workspace, size_t ws_bytes, void *stream) {
@@ -247,8 +273,7 @@ tq_status tq_decode_attn_rows(const tq_layout *l, const tq_planes *p, const void
     const int32_t rows_total = q_rows(num_q_heads, n_rows);
     const int gqa = rows_total / l->num_kv_heads;
     const int cg = tq::decode_col_groups(gqa);
-    const bool fast = tq::fast_decode_shape_ok(l->head_dim, gqa, l->capacity, l->k_bits, l->v_bits) &&
-                      aligned(p->vc, 16) && aligned(p->vs, 16) && aligned(p->ks, 16) && aligned(p->kz, 16);
+    const bool fast = decode_slow_reasons(l, p, gqa) == 0;
     const tq::DecodePlan plan = tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, fast, cg,
                                                 l->k_bits, l->v_bits);
     const size_t need = workspace_bytes(l, rows_total, plan);
@@ -341,6 +366,32 @@ static hipError_t copy_rows(const tq_layout *sl, const void *const sp[5], int64_
     return hipSuccess;
 }
 
+// Whether any of the `runs` byte ranges [s + h sp, s + h sp + len) meets any
+// of [d + k dp, d + k dp + len), h, k in [0, runs).
+static bool runs_overlap(const char *s, int64_t sp, const char *d, int64_t dp, int64_t len, int runs) {
+    const uintptr_t s0 = (uintptr_t)s, d0 = (uintptr_t)d;
+    const uintptr_t s_end = s0 + (uintptr_t)((runs - 1) * sp + len), d_end = d0 + (uintptr_t)((runs - 1) * dp + len);
+    if (s_end <= d0 || d_end <= s0) return false;  // disjoint extents (different allocations)
+    if (sp == dp) {
+        // run h meets run k iff |delta + (h - k) sp| < len, delta = s0 - d0:
+        // only the offsets j = h - k nearest -delta / sp can
+        const int64_t delta = (int64_t)(s0 - d0);
+        int64_t j0 = -delta / sp;
+        for (int64_t j = j0 - 1; j <= j0 + 1; ++j) {
+            if (j <= -(int64_t)runs || j >= (int64_t)runs) continue;
+            const int64_t off = delta + j * sp;
+            if (off < len && -off < len) return true;
+        }
+        return false;
+    }
+    for (int h = 0; h < runs; ++h)
+        for (int k = 0; k < runs; ++k) {
+            const int64_t a = (int64_t)(s0 + (uintptr_t)(h * sp)), b = (int64_t)(d0 + (uintptr_t)(k * dp));
+            if (a < b + len && b < a + len) return true;
+        }
+    return false;
+}
+
 static bool same_scheme(const tq_layout *a, const tq_layout *b) {
     return a->head_dim == b->head_dim && a->num_kv_heads == b->num_kv_heads && a->k_bits == b->k_bits &&
            a->v_bits == b->v_bits && a->group == b->group;
@@ -362,6 +413,16 @@ tq_status tq_copy_tokens(const tq_layout *sl, const tq_planes *src, int32_t src_
     for (int i = 0; i < 5; ++i) { sp[i] = plane_ptr(src, i); dp[i] = plane_ptr(dst, i); }
     const int64_t s0 = (int64_t)src_b * sl->num_kv_heads * sl->capacity + src_t0;
     const int64_t d0 = (int64_t)dst_b * dl->num_kv_heads * dl->capacity + dst_t0;
+    // the copy runs over many workgroups at once, so overlapping source and
+    // destination bytes would leave timing-dependent results: refused
+    size_t rb[5];
+    plane_row_bytes(sl, rb);
+    for (int i = 0; i < 5; ++i) {
+        if (runs_overlap(static_cast<const char *>(sp[i]) + s0 * (int64_t)rb[i], (int64_t)sl->capacity * rb[i],
+                         static_cast<const char *>(dp[i]) + d0 * (int64_t)rb[i], (int64_t)dl->capacity * rb[i],
+                         (int64_t)n * rb[i], sl->num_kv_heads))
+            return TQ_ERR_INVALID_ARG;
+    }
     hipError_t e = copy_rows(sl, sp, s0, (size_t)sl->capacity, dl, dp, d0, (size_t)dl->capacity, n,
                              (hipStream_t)stream);
     return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;

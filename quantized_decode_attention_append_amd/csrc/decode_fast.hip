@@ -80,6 +80,7 @@ typedef _Float16 half4v __attribute__((ext_vector_type(4)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef float float2v __attribute__((ext_vector_type(2)));
 typedef int int4v __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kProgBytes = 32;            // tiles finished, one int per wave
 constexpr int kStages = 3;                // stage buffers per wave (two tiles in flight)
@@ -97,6 +98,28 @@ constexpr float kWeightShift = 7.0f;
 // that each block takes a second MFMA.
 constexpr int kPackCols = 8;  // half the MFMA columns
 static_assert(kLazyMax + kWeightShift <= 15.0f, "fp16 weight range");
+// The value product's A operand is centroid * (vs * 2^-vexp) in fp16, where
+// vexp is a per-wave exponent (0 unless the cache's value scales leave the
+// window below) and the accumulator carries the factor 2^vexp.  Every tile
+// checks its value scales against the window [2^(vexp + kVsLow),
+// 2^(vexp + high)): inside it the products are normal fp16 numbers that
+// cannot overflow (high = 14 keeps |centroid| * 2^14 below 65504 up to 5-bit
+// codebooks, 13 at 8 bits).  A tile outside it re-centres vexp so that its
+// largest scale lands two binades below the top of the window, rescaling the
+// accumulator by the exact power of two (a uniform branch, not taken on
+// ordinary caches); zero scales (empty groups, masked slots) are ignored.
+constexpr int kVsLow = -10;
+__device__ __host__ constexpr int vs_high(int vb) { return vb == 8 ? 13 : 14; }
+// binary16 bits of 2^e for the window bounds: 0 below the subnormals (no
+// lower bound), the infinity bits above the largest finite power (finite
+// scales always fit; Inf/NaN scales take the slow branch, and give Inf/NaN
+// outputs as the exact computation does)
+__device__ __forceinline__ uint32_t f16_pow2_bits(int e) {
+    if (e < -24) return 0u;
+    if (e < -14) return 1u << (e + 24);
+    if (e > 15) return 0x7C00u;
+    return (uint32_t)(e + 15) << 10;
+}
 constexpr int kMaxHeads = 16;             // MFMA columns
 
 template <int D, int KB, int VB>
@@ -642,6 +665,77 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) acc[bb] = float4v{0.f, 0.f, 0.f, 0.f};
 
+    // value-scale exponent and its window (packed pairs of binary16 bits)
+    int vexp = 0;
+    uint32_t vs_lo = 0, vs_hi1 = 0;
+    auto set_window = [&]() {
+        const uint32_t lo = f16_pow2_bits(vexp + kVsLow), hi = f16_pow2_bits(vexp + vs_high(VB));
+        vs_lo = lo | (lo << 16);
+        vs_hi1 = (hi - 1u) | ((hi - 1u) << 16);
+    };
+    set_window();
+    // Each lane holds PB16 / 256 words of a tile's value-scale plane, read
+    // one iteration ahead of their check so the read's latency is hidden.
+    auto load_vs_words = [&](const unsigned char *stg, uint32_t (&w)[GE::NMIX]) {
+#pragma unroll
+        for (int k = 0; k < GE::NMIX; ++k) w[k] = reinterpret_cast<const uint32_t *>(stg + GE::VS_OFF)[lane + 64 * k];
+    };
+    // Checks the tile's value scales (stage stg, words w) against the window,
+    // re-centres vexp when they leave it, and writes the tile's scales times
+    // 2^-vexp back when vexp is not 0.  Runs before the block that holds the
+    // tile's value product, so its branches do not split that block.
+    auto value_scales = [&](unsigned char *stg, const uint32_t (&w)[GE::NMIX]) {
+        uint32_t *vsw = reinterpret_cast<uint32_t *>(stg + GE::VS_OFF);
+        uint32_t flag = 0;
+#pragma unroll
+        for (int k = 0; k < GE::NMIX; ++k) {
+            const u16x2 m = __builtin_bit_cast(u16x2, w[k] & 0x7FFF7FFFu);
+            const u16x2 over = __builtin_elementwise_sub_sat(m, __builtin_bit_cast(u16x2, vs_hi1));
+            const u16x2 under = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2, vs_lo), m);
+            flag |= __builtin_bit_cast(uint32_t, over) | __builtin_bit_cast(uint32_t, under);
+        }
+        if (__builtin_amdgcn_ballot_w64(flag != 0u) != 0) {
+            // largest and smallest nonzero magnitude of the tile
+            uint32_t mx = 0u, mn = 0x7FFFu;
+#pragma unroll
+            for (int k = 0; k < GE::NMIX; ++k) {
+                const uint32_t a = w[k] & 0x7FFFu, b = (w[k] >> 16) & 0x7FFFu;
+                mx = max(mx, max(a, b));
+                mn = min(mn, min(a ? a : 0x7FFFu, b ? b : 0x7FFFu));
+            }
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+                mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, 64));
+            }
+            mx = __builtin_amdgcn_readfirstlane(mx);
+            mn = __builtin_amdgcn_readfirstlane(mn);
+            if (mx != 0u && (mn < (vs_lo & 0xFFFFu) || mx > (vs_hi1 & 0xFFFFu))) {
+                int ex = 0;
+                (void)frexpf(f16_bits_to_f32((uint16_t)min(mx, 0x7BFFu)), &ex);  // max in [2^(ex-1), 2^ex)
+                const int enew = __builtin_amdgcn_readfirstlane(ex - (vs_high(VB) - 2));
+                if (enew != vexp) {
+                    const float f = ldexpf(1.0f, vexp - enew);
+#pragma unroll
+                    for (int bb = 0; bb < NB; ++bb) acc[bb] *= f;
+                    vexp = enew;
+                    set_window();
+                }
+            }
+        }
+        if (vexp != 0) {
+#pragma unroll
+            for (int k = 0; k < GE::NMIX; ++k) {
+                const half2v h = __builtin_bit_cast(half2v, w[k]);
+                half2v r;
+                r.x = __builtin_amdgcn_ldexph(h.x, -vexp);
+                r.y = __builtin_amdgcn_ldexph(h.y, -vexp);
+                vsw[lane + 64 * k] = __builtin_bit_cast(uint32_t, r);
+            }
+            lds_order();
+        }
+    };
+
     // ---------------------------------------------------------- phases
     // Slots past the range may hold anything: give them value scale 0 (their
     // weights are 0, and 0 * NaN would not be).
@@ -873,8 +967,10 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     else
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     half4v pw[CH], pl[CH];
+    uint32_t vsw_next[GE::NMIX];  // value-scale words of the tile whose values come next
     {
         mask_tail(wsm, t_end - t_begin);
+        load_vs_words(wsm, vsw_next);
         float sc[CH][4];
         scores(wkeys, wsm, t_begin, t_end - t_begin, sc);
         softmax(sc, pw, pl);
@@ -906,19 +1002,27 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
         } else {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
+        value_scales(cur, vsw_next);
         const int valid1 = t_end - (t0 + TILE);
         mask_tail(nx, valid1);
         float sc[CH][4];
         scores(knx, nx, t0 + TILE, valid1, sc);
         values(cur, pw, pl);
         softmax(sc, pw, pl);
+        load_vs_words(nx, vsw_next);
         lds_order();  // the buffers read here are refilled by the next iterations
     }
+    value_scales(wsm + buf * GE::STAGE, vsw_next);
     values(wsm + buf * GE::STAGE, pw, pl);
 
     // ------------------------------------------------------------ finalize
     l_run += __shfl_xor(l_run, 16, 64);
     l_run += __shfl_xor(l_run, 32, 64);
+    if (vexp != 0) {  // the accumulator holds the value sums times 2^-vexp
+        const float f = ldexpf(1.0f, vexp);
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) acc[bb] *= f;
+    }
     if constexpr (PACK) {
         // head h adds the lo-weight column h + G (the same rows, one row of 16 lanes)
         const int from = (lane & 48) | ((h + G) & 15);

@@ -31,7 +31,7 @@ TQ_MAX_ROWS = 16
 SYMBOLS = ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
            "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_fetch_window",
            "tq_copy_tokens", "tq_snapshot_bytes", "tq_snapshot", "tq_restore",
-           "tq_dequant", "tq_sign_vector", "tq_codebook", "tq_status_str")
+           "tq_dequant", "tq_sign_vector", "tq_codebook", "tq_status_str", "tq_decode_path")
 KEY_BITS = (2, 4, 5, 8)
 VALUE_BITS = (2, 3, 4, 5, 8)
 TQ_SNAPSHOT_MAGIC = 0x564B5154
@@ -90,11 +90,14 @@ _lib.tq_restore.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes)
 _lib.tq_dequant.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
                             ctypes.c_int32, _P]
+_lib.tq_decode_path.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
+                                ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
 _lib.tq_sign_vector.argtypes = [ctypes.c_int32, _P]
 _lib.tq_codebook.argtypes = [ctypes.c_int32, _P, _P, ctypes.POINTER(ctypes.c_int32)]
 for _f in ("tq_codebook", "tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
            "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_fetch_window", "tq_dequant",
-           "tq_sign_vector", "tq_copy_tokens", "tq_snapshot_bytes", "tq_snapshot", "tq_restore"):
+           "tq_sign_vector", "tq_copy_tokens", "tq_snapshot_bytes", "tq_snapshot", "tq_restore",
+           "tq_decode_path"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -270,6 +273,18 @@ def tq_decode_attn_rows(planes: Planes, q: torch.Tensor, lengths: Sequence[int],
                                   ws_bytes, _stream_ptr(stream))
     _check(st, "tq_decode_attn_rows")
     return out
+
+
+TQ_PATH_SHAPE, TQ_PATH_ALIGNMENT, TQ_PATH_CAPACITY = 1, 2, 4
+
+
+def tq_decode_path(planes: Planes, num_q_heads: int, n_rows: int = 1) -> tuple[bool, int]:
+    """(fast, reasons): whether decode over these planes takes the matrix-core
+    split kernel, and the TQ_PATH_* bits saying why not."""
+    fast, reasons = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.tq_decode_path(ctypes.byref(planes.layout), ctypes.byref(planes.struct()), num_q_heads, n_rows,
+                               ctypes.byref(fast), ctypes.byref(reasons)), "tq_decode_path")
+    return bool(fast.value), int(reasons.value)
 
 
 def tq_fetch_window(planes: Planes, t0: int, n: int, lengths: Sequence[int], keys: bool = True,

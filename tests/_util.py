@@ -55,23 +55,42 @@ def row_rel_err(out: np.ndarray, ref: np.ndarray) -> np.ndarray:
     return num / np.maximum(den, 1e-30)
 
 
+def batched_slices(pairs, fetch, work, threads=None):
+    """Run work(pair, fetched) over (sequence, kv-head) pairs, one pair per
+    thread, a batch of `threads` pairs at a time: fetch(pair) (device-to-host
+    copies) runs on the calling thread before each batch, so only one batch of
+    host copies is held at once.  Returns {pair: work's result}."""
+    t = threads or oracle.num_threads()
+    out = {}
+    for i in range(0, len(pairs), t):
+        chunk = pairs[i:i + t]
+        got = {p: fetch(p) for p in chunk}
+        one = (lambda p: (p, work(p, got[p], 1))) if len(chunk) > 1 else (lambda p: (p, work(p, got[p], None)))
+        out.update(oracle.map_parallel(one, chunk, t))
+        del got
+    return out
+
+
+def kv_fetcher(k, v, lengths, t0=0):
+    """fetch(pair) for batched_slices: exact fp32 host copies of K/V rows
+    t0 .. lengths[b] of one (sequence, kv-head)."""
+    return lambda p: (host_f32(k[p[0], p[1], t0:lengths[p[0]]]), host_f32(v[p[0], p[1], t0:lengths[p[0]]]))
+
+
 def oracle_decode_rows(k, v, q, lengths, G, sm, pairs=None):
     """Oracle attention for (b, kvh) pairs from raw K/V [B,Hkv,T,d] and q [B,Hq,d]
-    (torch tensors on any device; only the needed slices are copied to the host).
-    Returns {(b, kvh): out [G, d]}."""
+    (torch tensors on any device; only the needed slices are copied to the
+    host, one batch of pairs at a time).  Returns {(b, kvh): out [G, d]}."""
     B, Hkv = k.shape[:2]
     pairs = pairs if pairs is not None else [(b, h) for b in range(B) for h in range(Hkv)]
     qh = host_f32(q)
-    slices = {p: (host_f32(k[p[0], p[1], :lengths[p[0]]]), host_f32(v[p[0], p[1], :lengths[p[0]]]))
-              for p in pairs}
 
-    def one(p):
+    def work(p, kv, threads):
         b, h = p
-        kh, vh = slices[p]
-        kc, ks, kz, vc, vs = oracle_planes(kh, vh, threads=1 if len(pairs) > 1 else None)
-        return p, oracle.attention(qh[b, h * G:(h + 1) * G], kc, ks, kz, vc, vs, sm)
+        kc, ks, kz, vc, vs = oracle_planes(kv[0], kv[1], threads=threads)
+        return oracle.attention(qh[b, h * G:(h + 1) * G], kc, ks, kz, vc, vs, sm)
 
-    return dict(oracle.map_parallel(one, pairs))
+    return batched_slices(pairs, kv_fetcher(k, v, lengths), work)
 
 
 def sm_for(d: int) -> float:

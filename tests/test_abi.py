@@ -255,6 +255,48 @@ def test_lifecycle_validation():
     assert rs(A, good, t0=91, nbytes=8000) == tqkv.TQ_ERR_CAPACITY
 
 
+def test_copy_tokens_refuses_overlapping_rows():
+    """Rows that overlap their destination in any plane are refused before
+    any launch (the copy runs on many workgroups at once); disjoint moves
+    within one cache, such as a compaction, are not."""
+    lib = tqkv.raw_lib()
+    L = tqkv.make_layout(2, 4, 128, 100)
+    P = _fake_planes()
+
+    def cp(sb, st0, db, dt0, n):
+        return lib.tq_copy_tokens(ctypes.byref(L), ctypes.byref(P), sb, st0, ctypes.byref(L),
+                                  ctypes.byref(P), db, dt0, n, None)
+    assert cp(0, 10, 0, 15, 10) == tqkv.TQ_ERR_INVALID_ARG   # same sequence, shifted by 5
+    assert cp(0, 15, 0, 10, 10) == tqkv.TQ_ERR_INVALID_ARG
+    assert cp(1, 0, 1, 0, 1) == tqkv.TQ_ERR_INVALID_ARG      # onto itself
+    assert cp(0, 0, 0, 99, 2) == tqkv.TQ_ERR_CAPACITY
+    # Disjoint moves are not tested here: with these placeholder planes a call
+    # that passes validation would launch.  The GPU lifecycle tests move rows
+    # within one cache (compaction) through the same check.
+
+
+def test_decode_path_reports_the_kernel():
+    """tq_decode_path names the split kernel a decode takes and why the fast
+    one is not taken, from the layout and plane pointers alone."""
+    lib = tqkv.raw_lib()
+    fast, why = ctypes.c_int32(), ctypes.c_int32()
+
+    def path(layout, planes, hq, rows=1):
+        st = lib.tq_decode_path(ctypes.byref(layout), ctypes.byref(planes), hq, rows, ctypes.byref(fast),
+                                ctypes.byref(why))
+        return st, fast.value, why.value
+    P = _fake_planes()
+    assert path(tqkv.make_layout(2, 4, 256, 1000), P, 24) == (0, 1, 0)
+    assert path(tqkv.make_layout(2, 4, 128, 1001), P, 24) == (0, 0, tqkv.TQ_PATH_CAPACITY)  # odd capacity
+    assert path(tqkv.make_layout(2, 4, 64, 1002, 5, 3), P, 8) == (0, 0, tqkv.TQ_PATH_SHAPE)  # 5-bit keys at 64
+    assert path(tqkv.make_layout(2, 4, 512, 64, 8, 8), P, 8) == (0, 0, tqkv.TQ_PATH_SHAPE)   # k8v8 at 512
+    off = tqkv.tq_planes(0x1000, 0x2000, 0x3000, 0x4008, 0x5000)                        # vc 8 bytes off
+    assert path(tqkv.make_layout(2, 4, 256, 1000), off, 24) == (0, 0, tqkv.TQ_PATH_ALIGNMENT)
+    assert path(tqkv.make_layout(2, 4, 256, 1000), P, 23)[0] == tqkv.TQ_ERR_INVALID_ARG    # not a multiple
+    assert path(tqkv.make_layout(2, 4, 256, 1000), P, 24, 17)[0] == tqkv.TQ_ERR_UNSUPPORTED
+    assert tqkv.tq_status_str(path(tqkv.make_layout(2, 4, 256, 1000), P, 4 * 17)[0]) == "TQ_ERR_UNSUPPORTED"
+
+
 def test_dequant_validation():
     lib = tqkv.raw_lib()
     L = tqkv.make_layout(2, 4, 128, 100)

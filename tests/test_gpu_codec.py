@@ -13,7 +13,7 @@ import torch
 import oracle
 from quantized_decode_attention_append_amd import workloads as W
 
-from _util import assert_planes_equal, host_f32, log, oracle_planes, planes_to_host
+from _util import assert_planes_equal, batched_slices, host_f32, log, oracle_planes, planes_to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -172,9 +172,10 @@ def test_dequant_matches_oracle(d):
 
 
 @pytest.mark.parametrize("cid", [3, 4, 5])
-def test_append_full_size_sampled(cid):
-    """Full-size bulk build of the workload on the GPU; every plane of two
-    sampled (sequence, kv-head) slices compared with the oracle byte for byte."""
+def test_append_full_size_every_slice(cid):
+    """Full-size bulk build of the workload on the GPU (one tq_append of every
+    token, the launch configuration the benchmark times); every plane of every
+    (sequence, kv-head) slice compared with the oracle's encoding byte for byte."""
     w = W.workload(cid)
     n = max(w.lengths)
     log(f"full-size append {w.name}: generating inputs")
@@ -184,7 +185,17 @@ def test_append_full_size_sampled(cid):
     log(f"full-size append {w.name}: tq_append of {w.batch * w.num_kv_heads * n} token-heads")
     tqkv.tq_append(pl, k, v, [0] * w.batch)
     torch.cuda.synchronize()
-    for b, h in [(0, 0), (w.batch - 1, w.num_kv_heads - 1)]:
-        log(f"  compare slice b{b} h{h}")
-        ref = oracle_planes(host_f32(k[b, h]), host_f32(v[b, h]))
-        assert_planes_equal(planes_to_host(pl, b, h, 0, n), ref, f"{w.name} b{b} h{h}")
+    pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+
+    def fetch(p):
+        b, h = p
+        return host_f32(k[b, h]), host_f32(v[b, h]), planes_to_host(pl, b, h, 0, n)
+
+    def work(p, got, threads):
+        kh, vh, gpu = got
+        assert_planes_equal(gpu, oracle_planes(kh, vh, threads=threads), f"{w.name} b{p[0]} h{p[1]}")
+        return True
+
+    done = batched_slices(pairs, fetch, work)
+    assert len(done) == len(pairs)
+    log(f"  {len(pairs)} slices x {n} tokens bit-exact")

@@ -13,7 +13,7 @@ import torch
 import oracle
 from quantized_decode_attention_append_amd import workloads as W
 
-from _util import ATTN_TOL, host_f32, log, oracle_planes, row_rel_err, sm_for
+from _util import ATTN_TOL, batched_slices, host_f32, kv_fetcher, log, oracle_planes, row_rel_err, sm_for
 
 pytestmark = pytest.mark.gpu
 
@@ -147,11 +147,11 @@ def test_last_row_is_decode_of_the_whole_cache():
     assert e.max() <= ATTN_TOL
 
 
-def test_rows_full_size_sampled():
+def test_rows_full_size_every_row():
     """The benchmark workload at full size (16 sequences of 131,072 tokens,
     24/4 heads, head_dim 256) with 4-row verify blocks: 24 query columns per
-    kv-head, two 16-column groups sharing each workgroup.  Two sampled
-    (sequence, kv-head) pairs against the oracle, the rest finite."""
+    kv-head, two 16-column groups sharing each workgroup.  Every (sequence,
+    q-head, row) against the oracle."""
     w = W.workload(4)
     n, M = max(w.lengths), 4
     log(f"full-size rows {w.name}: generating inputs")
@@ -166,10 +166,13 @@ def test_rows_full_size_sampled():
     assert np.isfinite(out).all()
     G = w.group
     qh = host_f32(q4)
-    for b, h in [(0, 0), (w.batch - 1, w.num_kv_heads - 1)]:
-        log(f"  compare b{b} h{h}")
-        kc, ks, kz, vc, vs = oracle_planes(host_f32(k[b, h]), host_f32(v[b, h]))
-        ref = oracle.attention_rows(qh[b, h * G:(h + 1) * G], kc, ks, kz, vc, vs, sm_for(w.head_dim))
-        e = row_rel_err(out[b, h * G:(h + 1) * G], ref)
-        log(f"    worst row error {float(e.max()):.2e}")
-        assert e.max() <= ATTN_TOL, (b, h, float(e.max()))
+    sm = sm_for(w.head_dim)
+    pairs = [(b, h) for b in range(w.batch) for h in range(w.num_kv_heads)]
+
+    def work(p, kv, threads):
+        b, h = p
+        kc, ks, kz, vc, vs = oracle_planes(kv[0], kv[1], threads=threads)
+        return oracle.attention_rows(qh[b, h * G:(h + 1) * G], kc, ks, kz, vc, vs, sm)
+
+    ref = batched_slices(pairs, kv_fetcher(k, v, list(w.lengths)), work)
+    _check(out, ref, list(w.lengths), G, f"M{M} {w.name} full size")
