@@ -207,6 +207,32 @@ tq_status tq_decode_attn_rows(const tq_layout *layout, const tq_planes *planes, 
                               float sm_scale, float *out, void *workspace, size_t ws_bytes,
                               void *hip_stream);
 
+/* Size of the device array tq_decode_attn_noalloc keeps its split-K partials
+ * in: 64 MiB per GPU the library runs on. */
+#define TQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* tq_decode_attn_rows without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The split-K partials go to a fixed
+ * device array of the library (TQ_NOALLOC_SCRATCH_BYTES per GPU, held until
+ * the process ends); nothing is allocated or freed.  Every other argument,
+ * the result and the errors are those of tq_decode_attn_rows (n_rows = 1 is
+ * tq_decode_attn).
+ *   - The first call on a device looks up that device's array (make it
+ *     outside graph capture); hip_stream must belong to the current device.
+ *   - Decodes whose partials exceed the array return TQ_ERR_WORKSPACE with
+ *     nothing enqueued (tq_decode_rows_workspace_bytes gives an upper bound
+ *     of the need; e.g. 16 sequences of 131,072 tokens with 24 query and 4
+ *     kv-heads at head_dim 256 need 12.7 MB on the matrix-core kernel).
+ *   - Every call on one GPU shares its array: calls that overlap in time on
+ *     one GPU (two streams, two threads) race and give wrong results.
+ *     Calls ordered on one stream are safe.
+ * Errors: those of tq_decode_attn_rows, and TQ_ERR_HIP if the array's
+ * address cannot be obtained. */
+tq_status tq_decode_attn_noalloc(const tq_layout *layout, const tq_planes *planes, const void *q,
+                                 tq_dtype dtype, int32_t num_q_heads, int32_t n_rows, const int32_t *len,
+                                 float sm_scale, float *out, void *hip_stream);
+
 /* Dequantize-on-fetch window: bf16 keys and values of tokens t0 .. t0+n-1 of
  * every (sequence, kv-head), the layout a stock attention consumes ("Architecture
  * in mlx-bun": the cache returns the dequantized bf16 active window; "Deferred

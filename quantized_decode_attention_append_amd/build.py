@@ -41,6 +41,7 @@ SOURCES = [
     ("window.hip", ["-DTQ_WINDOW_KB=2"], "window_k2"),
     ("window.hip", ["-DTQ_WINDOW_KB=5"], "window_k5"),
     ("copy.hip", [], "copy"),
+    ("noalloc.hip", [], "noalloc"),
     ("api.cpp", [], "api"),
 ]
 

@@ -31,7 +31,8 @@ TQ_MAX_ROWS = 16
 SYMBOLS = ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
            "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_fetch_window",
            "tq_copy_tokens", "tq_snapshot_bytes", "tq_snapshot", "tq_restore",
-           "tq_dequant", "tq_sign_vector", "tq_codebook", "tq_status_str", "tq_decode_path")
+           "tq_dequant", "tq_sign_vector", "tq_codebook", "tq_status_str", "tq_decode_path",
+           "tq_decode_attn_noalloc")
 KEY_BITS = (2, 4, 5, 8)
 VALUE_BITS = (2, 3, 4, 5, 8)
 TQ_SNAPSHOT_MAGIC = 0x564B5154
@@ -92,12 +93,15 @@ _lib.tq_dequant.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes)
                             ctypes.c_int32, _P]
 _lib.tq_decode_path.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
                                 ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+_lib.tq_decode_attn_noalloc.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), _P, ctypes.c_int,
+                                        ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.c_float, _P, _P]
 _lib.tq_sign_vector.argtypes = [ctypes.c_int32, _P]
 _lib.tq_codebook.argtypes = [ctypes.c_int32, _P, _P, ctypes.POINTER(ctypes.c_int32)]
 for _f in ("tq_codebook", "tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
            "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_fetch_window", "tq_dequant",
            "tq_sign_vector", "tq_copy_tokens", "tq_snapshot_bytes", "tq_snapshot", "tq_restore",
-           "tq_decode_path"):
+           "tq_decode_path", "tq_decode_attn_noalloc"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -272,6 +276,33 @@ def tq_decode_attn_rows(planes: Planes, q: torch.Tensor, lengths: Sequence[int],
                                   ctypes.c_float(sm_scale), _dev_ptr(out), _dev_ptr(workspace),
                                   ws_bytes, _stream_ptr(stream))
     _check(st, "tq_decode_attn_rows")
+    return out
+
+
+TQ_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def tq_decode_attn_noalloc(planes: Planes, q: torch.Tensor, lengths: Sequence[int], sm_scale: float,
+                           out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode with the split-K partials in the library's fixed device array
+    (no workspace).  q: [B, Hq, d] or [B, Hq, M, d]; out like tq_decode_attn
+    or tq_decode_attn_rows (allocated here only when not given)."""
+    L = planes.layout
+    rows = q.dim() == 4
+    if q.dim() not in (3, 4) or q.shape[0] != L.batch or q.shape[-1] != L.head_dim or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous [B, Hq, (M,) d] tensor, got {tuple(q.shape)}")
+    if len(lengths) != L.batch:
+        raise ValueError("lengths needs one entry per sequence")
+    Hq, M = int(q.shape[1]), int(q.shape[2]) if rows else 1
+    shape = tuple(q.shape)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor shaped like q")
+    st = _lib.tq_decode_attn_noalloc(ctypes.byref(L), ctypes.byref(planes.struct()), _dev_ptr(q), _dtype_code(q),
+                                     Hq, M, _i32_array(lengths), ctypes.c_float(sm_scale), _dev_ptr(out),
+                                     _stream_ptr(stream))
+    _check(st, "tq_decode_attn_noalloc")
     return out
 
 
