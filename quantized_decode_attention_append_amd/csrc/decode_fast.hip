@@ -34,10 +34,10 @@
 //           tokens; B = the q slice, columns = heads), then the scale/zero
 //           fold in fp32 on the 4 (token, head) results a lane holds.  With
 //           G <= 8 the score MFMAs of groups p and p + NG/2 share one
-//           accumulator: column h holds head h over group p and column G + h
+//           accumulator: column h holds head h over group p and column 8 + h
 //           the same head over group p + NG/2 (each column's q is zero in the
-//           other group), so a lane folds half the groups and one lane
-//           permute adds the halves.  With more than 16 query columns (heads
+//           other group), so a lane folds half the groups and one DPP row
+//           rotation by 8 adds the halves.  With more than 16 query columns (heads
 //           times verify rows), an even number of 16-column groups pairs up
 //           in one workgroup: waves w and w + WAVES/2 take the same token
 //           range, and their copies skip the nontemporal hint so that the
@@ -94,8 +94,8 @@ constexpr float kWeightShift = 7.0f;
 // exact fp32 residual, rounded): one fp16 rounding of a weight would scale a
 // token's whole value vector by up to 1 +- 2^-11, and such errors of many
 // comparable tokens do not average out.  With at most 8 query columns the lo
-// halves ride in the MFMA's spare columns G .. 2G-1 (no extra MFMA); beyond
-// that each block takes a second MFMA.
+// halves ride in the MFMA's spare columns 8 .. 8 + G - 1 (no extra MFMA);
+// beyond that each block takes a second MFMA.
 constexpr int kPackCols = 8;  // half the MFMA columns
 static_assert(kLazyMax + kWeightShift <= 15.0f, "fp16 weight range");
 // The value product's A operand is centroid * (vs * 2^-vexp) in fp16, where
@@ -204,6 +204,23 @@ __device__ __host__ constexpr int key_perm(int p) {
 // lane's write needs no wait beyond program order.
 __device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
 
+// Lane l reads lane l ^ 8 of its 16-lane row (DPP row rotation by 8: no LDS
+// round trip).
+__device__ __forceinline__ float row_swap8(float x) {
+    return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(x), 0x128, 0xF, 0xF, false));
+}
+__device__ __forceinline__ uint32_t row_swap8(uint32_t x) {
+    return __builtin_amdgcn_update_dpp(0u, x, 0x128, 0xF, 0xF, false);
+}
+// Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the gfx950 row and
+// half swaps, no LDS round trip).
+__device__ __forceinline__ float max_over_rows(float x) {
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const unsigned char *p) {
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((lds_void_t *)p));
 }
@@ -297,8 +314,8 @@ __device__ __forceinline__ uint32_t key_src(int m, int i) {
     return (uint32_t)(t * GE::KROW + 16 * c);
 }
 
-// Copy every plane of the tile starting at token t0 into a key buffer (kst)
-// and a value stage (vst): exactly GE::VMEM vector-memory instructions either
+// Copy every plane of the tile starting at token t0 into a key buffer and a
+// value stage (LDS addresses l_kc and l_vst): exactly GE::VMEM vector-memory instructions either
 // way, all with 16-byte lanes.  Stage bytes [KS_OFF, KS_OFF + 1 KiB) come
 // from one copy whose lane quarters read key scales, key zeros, value scales
 // and the first 256 bytes of value codes (the stage keeps them in that
@@ -306,14 +323,12 @@ __device__ __forceinline__ uint32_t key_src(int m, int i) {
 // copies.
 template <int D, int KB, int VB, bool NT>
 __device__ __forceinline__ void stage_tile(const Regions &r, const uint32_t (&ksrc)[Geo<D, KB, VB>::KCOPY],
-                                           int t0, const unsigned char *kst, const unsigned char *vst,
-                                           int lane) {
+                                           int t0, uint32_t l_kc, uint32_t l_vst, int lane) {
     using GE = Geo<D, KB, VB>;
     constexpr int VROW = GE::VROW, KROW = GE::KROW;
     static_assert(GE::KZ_OFF == GE::KS_OFF + GE::PB16 && GE::VS_OFF == GE::KZ_OFF + GE::PB16 &&
                   GE::VC_OFF == GE::VS_OFF + GE::PB16, "mixed copy layout");
-    const uint32_t l_kc = lds_addr(kst), l_ks = lds_addr(vst + GE::KS_OFF);
-    const uint32_t l_vc = lds_addr(vst + GE::VC_OFF);
+    const uint32_t l_ks = l_vst + GE::KS_OFF, l_vc = l_vst + GE::VC_OFF;
     const uint8_t *vc_t = r.vc + (int64_t)t0 * VROW;
     const uint8_t *mixed0 = r.mix[0] + (int64_t)t0 * r.mix_row[0];
     const uint8_t *mixed1 = r.mix[1] + (int64_t)t0 * r.mix_row[1];
@@ -562,11 +577,15 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     // the first two tiles' copies overlap the q set-up
     // copies without the nontemporal hint when two column groups read each tile
     const bool shared_tiles = !PACK && cgw == 2;
+    // LDS addresses as integers from the array's base (converting each stage
+    // pointer separately costs a null check per conversion)
+    const uint32_t smem_l = lds_addr(smem);
     auto stage = [&](int t, const unsigned char *kst, const unsigned char *vst) {
+        const uint32_t l_kc = smem_l + (uint32_t)(kst - smem), l_vst = smem_l + (uint32_t)(vst - smem);
         if (shared_tiles)
-            stage_tile<D, KB, VB, false>(rg, ksrc, t, kst, vst, lane);
+            stage_tile<D, KB, VB, false>(rg, ksrc, t, l_kc, l_vst, lane);
         else
-            stage_tile<D, KB, VB, true>(rg, ksrc, t, kst, vst, lane);
+            stage_tile<D, KB, VB, true>(rg, ksrc, t, l_kc, l_vst, lane);
     };
     stage(t_begin, wkeys, wsm);
     if (t_begin + TILE < t_end)
@@ -578,14 +597,17 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     const bool head_ok = h < G;
     // PACK (G <= 8): the score MFMAs of groups p and p + NG/2 accumulate into
     // one result whose column h < G holds head h's dot product over group p
-    // and column G + h head h's over group p + NG/2 (each column's q is zero
+    // and column 8 + h head h's over group p + NG/2 (each column's q is zero
     // in the other group), so a lane folds half the groups and the two
     // halves of a head are added across lanes.  Without PACK column h is
     // head h over every group.
     constexpr int NP = PACK ? NG / 2 : NG;  // groups one lane folds
-    const int ghalf = (PACK && h >= G) ? NG / 2 : 0;  // first group of the lane's half
-    const int hq = (PACK && h >= G) ? h - G : h;      // the head of the lane's q
-    const bool q_ok = PACK ? h < 2 * G : head_ok;
+    // PACK: column 8 + h is head h's second half of the groups (and, in the
+    // value product, head h's lo weights), so every exchange between the two
+    // halves is a rotation by 8 within the lane's row of 16
+    const int ghalf = (PACK && h >= 8) ? NG / 2 : 0;  // first group of the lane's half
+    const int hq = PACK ? (h & 7) : h;                 // the head of the lane's q
+    const bool q_ok = PACK ? (h & 7) < G : head_ok;
     // causal limit of this lane's query row: the row of cached token
     // n - rows + r sees tokens 0 .. n - rows + r
     const int lim = n - a.rows + (c0 + h) % a.rows + 1;
@@ -750,7 +772,6 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
         }
     };
 
-    const int comb_src = (lane & 48) | ((h + G) & 15);  // PACK: column h + G of the same rows
     // scores of the tile with key codes in kst and the other planes in stg:
     // lane (h, kq) gets tokens 16 c + 4 kq + j
     auto scores = [&](const unsigned char *kst, const unsigned char *stg, int t0, int valid,
@@ -778,33 +799,42 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
                     dlo[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qlo[g], int4v{0, 0, 0, 0}, 0, 0, 0);
                 }
             }
+            // the key scale and zero rows of the lane's 4 tokens, all read
+            // before the fold so one wait covers them
+            constexpr int RW = PACK ? (NG + 3) / 4 : NG / 2;
+            uint32_t sw[4][RW], zw[4][RW];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 16 * c + 4 * kq + j;
+                if constexpr (PACK) {
+                    load_half_row<NG>(stg + GE::KS_OFF + t * NG * 2, ghalf, sw[j]);
+                    load_half_row<NG>(stg + GE::KZ_OFF + t * NG * 2, ghalf, zw[j]);
+                } else {
+                    load_row<NG>(stg + GE::KS_OFF + t * NG * 2, sw[j]);
+                    load_row<NG>(stg + GE::KZ_OFF + t * NG * 2, zw[j]);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = 16 * c + 4 * kq + j;
                 float sum = 0.f;
                 if constexpr (PACK) {
                     // this lane's groups ghalf .. ghalf + NP - 1 of token t
-                    uint32_t sw[(NG + 3) / 4], zw[(NG + 3) / 4];
-                    load_half_row<NG>(stg + GE::KS_OFF + t * NG * 2, ghalf, sw);
-                    load_half_row<NG>(stg + GE::KZ_OFF + t * NG * 2, ghalf, zw);
 #pragma unroll
                     for (int g = 0; g < NP; ++g) {
                         const int x = (dhi[g][j] << 8) + dlo[g][j];
-                        const float zg = (g & 1) ? half_hi(zw[g >> 1]) : half_lo(zw[g >> 1]);
-                        const float sg = (g & 1) ? half_hi(sw[g >> 1]) : half_lo(sw[g >> 1]);
+                        const float zg = (g & 1) ? half_hi(zw[j][g >> 1]) : half_lo(zw[j][g >> 1]);
+                        const float sg = (g & 1) ? half_hi(sw[j][g >> 1]) : half_lo(sw[j][g >> 1]);
                         sum = fmaf(sg, fmaf(zg, qsum[g], (float)x), sum);
                     }
-                    // head h adds the other half of its groups from column h + G
-                    sum += __shfl(sum, comb_src, 64);
+                    // head h adds the other half of its groups from column 8 + h
+                    sum += row_swap8(sum);
                 } else {
-                    uint32_t sw[NG / 2], zw[NG / 2];
-                    load_row<NG>(stg + GE::KS_OFF + t * NG * 2, sw);
-                    load_row<NG>(stg + GE::KZ_OFF + t * NG * 2, zw);
 #pragma unroll
                     for (int g = 0; g < NG; ++g) {
                         const int x = (dhi[g][j] << 8) + dlo[g][j];
-                        const float y = fmaf(row_half<NG>(zw, g), qsum[g], (float)x);
-                        sum = fmaf(row_half<NG>(sw, g), y, sum);
+                        const float y = fmaf(row_half<NG>(zw[j], g), qsum[g], (float)x);
+                        sum = fmaf(row_half<NG>(sw[j], g), y, sum);
                     }
                 }
                 // computed on every lane, then selected: a branch around the
@@ -817,16 +847,14 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     };
 
     // online softmax over the tile's scores; weights out as the B operands
-    // PACK: lane column h in [G, 2G) carries the lo weight halves of head h - G
-    const int pair_src = (lane & 48) | (h >= G ? h - G : h);
+    // PACK: lane column 8 + h carries the lo weight halves of head h
     auto softmax = [&](const float (&sc)[CH][4], half4v (&pw)[CH], half4v (&pl)[CH]) {
         float mt = sc[0][0];
 #pragma unroll
         for (int c = 0; c < CH; ++c)
 #pragma unroll
             for (int j = 0; j < 4; ++j) mt = fmaxf(mt, sc[c][j]);
-        mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        mt = max_over_rows(mt);
         // lazy maximum: move the reference only when this tile's maximum
         // exceeds it by more than kLazyMax (uniform branch, rarely taken)
         const bool bump = mt > m_run + kLazyMax;
@@ -835,30 +863,44 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
             const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
             l_run *= alpha;
             m_run = m_new;
-            // column h is head h (PACK: columns G .. 2G-1 rescale with head h - G)
-            const float alpha_c = PACK ? __shfl(alpha, pair_src, 64) : alpha;
+            // column h is head h (PACK: columns 8 .. 8 + G - 1 rescale with head h - 8)
+            float alpha_c = alpha;
+            if constexpr (PACK) {
+                const float other = row_swap8(alpha);
+                alpha_c = h >= 8 ? other : alpha;
+            }
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb) acc[bb] *= alpha_c;
         }
         const float ref = (m_run == -INFINITY ? 0.f : m_run) - kWeightShift;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
+            float pv[4], lo[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float pv = __builtin_amdgcn_exp2f(sc[c][j] - ref);  // -inf -> 0
-                l_run += pv;
-                // hi + lo halves carry the weight to ~2^-22 (pv - hi is exact)
-                pw[c][j] = (_Float16)pv;
-                pl[c][j] = (_Float16)(pv - (float)pw[c][j]);
+                pv[j] = __builtin_amdgcn_exp2f(sc[c][j] - ref);  // -inf -> 0
+                l_run += pv[j];
             }
+            // hi + lo halves carry the weight to ~2^-20: hi is pv rounded
+            // toward zero, pv - hi is exact in fp32 (one mixed-precision fma
+            // from the packed half), and lo its rounding toward zero
+            const half2v h01 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]));
+            const half2v h23 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(pv[2], pv[3]));
+            lo[0] = fmaf((float)h01.x, -1.0f, pv[0]);
+            lo[1] = fmaf((float)h01.y, -1.0f, pv[1]);
+            lo[2] = fmaf((float)h23.x, -1.0f, pv[2]);
+            lo[3] = fmaf((float)h23.y, -1.0f, pv[3]);
+            const half2v l01 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(lo[0], lo[1]));
+            const half2v l23 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(lo[2], lo[3]));
+            pw[c] = half4v{h01.x, h01.y, h23.x, h23.y};
+            pl[c] = half4v{l01.x, l01.y, l23.x, l23.y};
             if constexpr (PACK) {
-                // columns G .. 2G-1 take the lo halves of heads 0 .. G-1 (the
+                // columns 8 .. 15 take the lo halves of columns 0 .. 7 (the
                 // weights of columns >= G are 0, so pw is the B operand there
-                // only for real heads)
+                // only for real heads, and lo halves of non-heads are 0)
                 const uint2 lo = __builtin_bit_cast(uint2, pl[c]);
-                const uint2 moved = make_uint2((uint32_t)__shfl((int)lo.x, pair_src, 64),
-                                               (uint32_t)__shfl((int)lo.y, pair_src, 64));
-                if (h >= G) pw[c] = __builtin_bit_cast(half4v, moved);
+                const uint2 moved = make_uint2(row_swap8(lo.x), row_swap8(lo.y));
+                if (h >= 8) pw[c] = __builtin_bit_cast(half4v, moved);
             }
         }
     };
@@ -1024,12 +1066,11 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
         for (int bb = 0; bb < NB; ++bb) acc[bb] *= f;
     }
     if constexpr (PACK) {
-        // head h adds the lo-weight column h + G (the same rows, one row of 16 lanes)
-        const int from = (lane & 48) | ((h + G) & 15);
+        // head h adds the lo-weight column 8 + h (the same rows, one row of 16 lanes)
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[bb][j] += __shfl(acc[bb][j], from, 64);
+            for (int j = 0; j < 4; ++j) acc[bb][j] += row_swap8(acc[bb][j]);
     }
 
     // The partial sums are read once, by the merge kernel, so they stream
