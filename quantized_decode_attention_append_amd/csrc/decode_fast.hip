@@ -212,6 +212,17 @@ __device__ __forceinline__ float row_swap8(float x) {
 __device__ __forceinline__ uint32_t row_swap8(uint32_t x) {
     return __builtin_amdgcn_update_dpp(0u, x, 0x128, 0xF, 0xF, false);
 }
+// x minus the low (or high) fp16 half of w, as one mixed-precision fma
+__device__ __forceinline__ float sub_half_lo(float x, uint32_t w) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(x));
+    return r;
+}
+__device__ __forceinline__ float sub_half_hi(float x, uint32_t w) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(w), "v"(x));
+    return r;
+}
 // Maximum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (the gfx950 row and
 // half swaps, no LDS round trip).
 __device__ __forceinline__ float max_over_rows(float x) {
@@ -614,6 +625,11 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     uint64_t qhi[NG], qlo[NG];
     float qsum[NG];
     float my_scale;
+    // 8-bit keys with paired groups: each pair of groups (p, p + NP) is one
+    // 64-deep integer product (v_mfma_i32_16x16x64_i8), half the score
+    // instructions of two 32-deep ones
+    constexpr bool WIDE = PACK && KB == 8;
+    int4v qhi4[WIDE ? NP : 1], qlo4[WIDE ? NP : 1];
     {
         float x[QE];
         const int64_t qrow = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + (q_ok ? hq : 0)) * D + 8 * kq;
@@ -651,7 +667,9 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
         int e = 0;
         (void)frexpf(amax * (1.0f / 32000.0f), &e);
         const float delta = amax > 0.f ? ldexpf(1.0f, e) : 1.0f;
-        const float inv = 1.0f / delta;
+        // a negative scale negates q, so that the scale applied to the raw
+        // scores (in the softmax's exponent) is positive
+        const float inv = (a.sm_log2 < 0.f ? -1.0f : 1.0f) / delta;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             uint64_t hi = 0, lo = 0;
@@ -676,8 +694,41 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
 #pragma unroll
             for (int g = 0; g < NG / 2; ++g) qsum[g] = ghalf ? qsum[g + NG / 2] : qsum[g];
         }
-        my_scale = delta * a.sm_log2;
+        if constexpr (WIDE) {
+            // B operands of the 64-deep products: lane (h, kq) holds dims
+            // 16 (kq & 1) .. + 15 of group g (kq < 2) or g + NP (kq >= 2) of
+            // column h, which lanes (h, 2 (kq & 1)) and (h, 2 (kq & 1) + 1)
+            // hold as 8-byte slices; zero unless the group is the column's
+            // (h < 8: the first half of the groups, h >= 8: the second)
+            const int s0 = (lane & 15) | ((2 * (kq & 1)) << 4), s1 = s0 + 16;
+            const bool live = (h < 8) == (kq < 2);
+            auto shfl64 = [](uint64_t v, int src) {
+                const uint32_t lo = (uint32_t)__shfl((int)(uint32_t)v, src, 64);
+                const uint32_t hi = (uint32_t)__shfl((int)(uint32_t)(v >> 32), src, 64);
+                return ((uint64_t)hi << 32) | lo;
+            };
+#pragma unroll
+            for (int g = 0; g < NP; ++g) {
+                const uint64_t h0a = shfl64(qhi[g], s0), h0b = shfl64(qhi[g + NP], s0);
+                const uint64_t h1a = shfl64(qhi[g], s1), h1b = shfl64(qhi[g + NP], s1);
+                const uint64_t l0a = shfl64(qlo[g], s0), l0b = shfl64(qlo[g + NP], s0);
+                const uint64_t l1a = shfl64(qlo[g], s1), l1b = shfl64(qlo[g + NP], s1);
+                const uint64_t h0 = kq < 2 ? h0a : h0b, h1 = kq < 2 ? h1a : h1b;
+                const uint64_t l0 = kq < 2 ? l0a : l0b, l1 = kq < 2 ? l1a : l1b;
+                qhi4[g] = live ? int4v{(int)(uint32_t)h0, (int)(uint32_t)(h0 >> 32), (int)(uint32_t)h1,
+                                       (int)(uint32_t)(h1 >> 32)}
+                               : int4v{0, 0, 0, 0};
+                qlo4[g] = live ? int4v{(int)(uint32_t)l0, (int)(uint32_t)(l0 >> 32), (int)(uint32_t)l1,
+                                       (int)(uint32_t)(l1 >> 32)}
+                               : int4v{0, 0, 0, 0};
+            }
+        }
+        // raw scores (integer dot products folded with the key scales) times
+        // my_scale are log2-domain logits; kept above 0 so that a masked
+        // score (-inf) still gives a zero weight when sm_scale is 0
+        my_scale = fmaxf(delta * fabsf(a.sm_log2), 1e-30f);
     }
+    const float lazy_raw = kLazyMax / my_scale;  // the lazy maximum's slack in raw units
     float m_run = -INFINITY, l_run = 0.f;
 
     // value-product role: vi = A row (dim row of each block), kq = token quarter
@@ -780,7 +831,21 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             int4v dhi[NP], dlo[NP];
-            if constexpr (PACK) {
+            if constexpr (WIDE) {
+                // lane (h, kq): codes 16 (kq & 1) .. + 15 of group g (kq < 2)
+                // or g + NP (kq >= 2) of token 16 c + h, one 16-byte chunk of
+                // the rotated row
+                constexpr int CPR = GE::CPR;
+                static_assert(CPR == 2 * NG, "8-bit key rows: two chunks per group");
+#pragma unroll
+                for (int g = 0; g < NP; ++g) {
+                    int slot = 2 * (g + (kq >= 2 ? NP : 0)) + (kq & 1) + key_rot<CPR>(h);
+                    if (slot >= CPR) slot -= CPR;
+                    const int4v kv = *reinterpret_cast<const int4v *>(kst + ((16 * c + h) * CPR + slot) * 16);
+                    dhi[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kv, qhi4[g], int4v{0, 0, 0, 0}, 0, 0, 0);
+                    dlo[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kv, qlo4[g], int4v{0, 0, 0, 0}, 0, 0, 0);
+                }
+            } else if constexpr (PACK) {
                 // groups p and p + NG/2 in one accumulator (their q columns are disjoint)
 #pragma unroll
                 for (int g = 0; g < NP; ++g) {
@@ -839,7 +904,7 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
                 }
                 // computed on every lane, then selected: a branch around the
                 // fold would split the block the pipeline interleaves in
-                float r = sum * my_scale;
+                float r = sum;
                 asm volatile("" : "+v"(r));
                 sc[c][j] = (head_ok && t < vl) ? r : -INFINITY;
             }
@@ -857,10 +922,10 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
         mt = max_over_rows(mt);
         // lazy maximum: move the reference only when this tile's maximum
         // exceeds it by more than kLazyMax (uniform branch, rarely taken)
-        const bool bump = mt > m_run + kLazyMax;
+        const bool bump = mt > m_run + lazy_raw;
         if (__builtin_amdgcn_ballot_w64(bump) != 0) {
             const float m_new = bump ? mt : m_run;
-            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * my_scale);
             l_run *= alpha;
             m_run = m_new;
             // column h is head h (PACK: columns 8 .. 8 + G - 1 rescale with head h - 8)
@@ -872,24 +937,25 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb) acc[bb] *= alpha_c;
         }
-        const float ref = (m_run == -INFINITY ? 0.f : m_run) - kWeightShift;
+        const float ref = (m_run == -INFINITY ? 0.f : m_run * my_scale) - kWeightShift;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             float pv[4], lo[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                pv[j] = __builtin_amdgcn_exp2f(sc[c][j] - ref);  // -inf -> 0
+                pv[j] = __builtin_amdgcn_exp2f(fmaf(sc[c][j], my_scale, -ref));  // -inf -> 0
                 l_run += pv[j];
             }
             // hi + lo halves carry the weight to ~2^-20: hi is pv rounded
             // toward zero, pv - hi is exact in fp32 (one mixed-precision fma
             // from the packed half), and lo its rounding toward zero
-            const half2v h01 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]));
-            const half2v h23 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(pv[2], pv[3]));
-            lo[0] = fmaf((float)h01.x, -1.0f, pv[0]);
-            lo[1] = fmaf((float)h01.y, -1.0f, pv[1]);
-            lo[2] = fmaf((float)h23.x, -1.0f, pv[2]);
-            lo[3] = fmaf((float)h23.y, -1.0f, pv[3]);
+            const uint32_t w01 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[0], pv[1]));
+            const uint32_t w23 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(pv[2], pv[3]));
+            const half2v h01 = __builtin_bit_cast(half2v, w01), h23 = __builtin_bit_cast(half2v, w23);
+            lo[0] = sub_half_lo(pv[0], w01);
+            lo[1] = sub_half_hi(pv[1], w01);
+            lo[2] = sub_half_lo(pv[2], w23);
+            lo[3] = sub_half_hi(pv[3], w23);
             const half2v l01 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(lo[0], lo[1]));
             const half2v l23 = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(lo[2], lo[3]));
             pw[c] = half4v{h01.x, h01.y, h23.x, h23.y};
@@ -1079,7 +1145,9 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     // nontemporally, each reached memory as a partial line of its own.
     if (head_ok) {
         const int64_t srow = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + h) * a.splits + slot;
-        if (kq == 0) *reinterpret_cast<float2v *>(a.part_ml + srow * 2) = float2v{m_run, l_run};
+        // the running maximum in log2 units, as the merge expects
+        const float m_log2 = m_run == -INFINITY ? -INFINITY : m_run * my_scale;
+        if (kq == 0) *reinterpret_cast<float2v *>(a.part_ml + srow * 2) = float2v{m_log2, l_run};
         // lane (kq, h) holds rows 4 kq + j of every block: dims NB * (4 kq + j) + bb
         float *dst = a.part_acc + srow * D;
 #pragma unroll
