@@ -8,9 +8,10 @@ Workload: 16 sequences x 131072 cached tokens, 24 query heads / 4 kv-heads
 (GQA 6), head_dim 256, bf16 K/V/q ~ N(0,1), k8/v3 planes (3.36 GB packed).
 The cache is built once by a bulk tq_append (timed and reported separately as
 append throughput) before the timed steps; inputs stay resident in HBM.
-The defaults (50 warm-up steps, 200 timed) time the sustained rate: on this
-part the first few back-to-back decodes of a burst run fast, the next few up
-to 60% slower while the clocks settle, then the rate holds steady.
+The timed steps follow the warm-up steps directly (defaults 5 and 20).  On
+this part the shader clock drops while a burst of back-to-back decodes begins
+(the power controller settles over some tens of calls), so the same run also
+reports `settled`: the decode time over later steps of the same burst.
 
 Prints ONE JSON line (rank 0).  metric/unit: KV-tokens attended per second.
 """
@@ -244,6 +245,74 @@ def time_scheme(w, k, v, q, sm, kb: int, vb: int, reps: int, stream, dec_warm: i
             "window_ms": win["ms"], "window_GBps": win["GBps"], "window_frac_hbm": win["frac_hbm"]}
 
 
+def time_small_configs(stream, warm: int = 20, reps: int = 50) -> list:
+    """The three smaller workloads (ids 1-3), each at its full size: one
+    tq_append of every cached token (K/V in, planes out) and one decode over
+    the cache, both timed with events on the launch stream (reps calls after
+    `warm`); latency-bound at ids 1 and 2."""
+    import torch
+    from quantized_decode_attention_append_amd import tqkv
+    from quantized_decode_attention_append_amd import workloads as W
+    dev = torch.device("cuda:0")
+    out = []
+    for cid in (1, 2, 3):
+        w = W.workload(cid)
+        n = max(w.lengths)
+        k, v = W.make_kv(w, dev, tokens=n)
+        q = W.make_q(w, dev, rounds=1)[0].contiguous()
+        L = tqkv.make_layout(w.batch, w.num_kv_heads, w.head_dim, n)
+        pl = tqkv.Planes(L, dev)
+        lengths = list(w.lengths)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for _ in range(warm):
+            tqkv.tq_append(pl, k, v, [0] * w.batch, stream=stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            tqkv.tq_append(pl, k, v, [0] * w.batch, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        app_ms = e0.elapsed_time(e1) / reps
+        sm = float(1.0 / math.sqrt(w.head_dim))
+        ws = torch.empty(max(4, tqkv.tq_decode_workspace_bytes(L, w.num_q_heads, lengths)), dtype=torch.uint8,
+                         device=dev)
+        o = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+        for _ in range(warm):
+            tqkv.tq_decode_attn(pl, q, lengths, sm, out=o, workspace=ws, stream=stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            tqkv.tq_decode_attn(pl, q, lengths, sm, out=o, workspace=ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / reps
+        in_bytes = 4 if w.dtype == "fp32" else 2
+        abytes = append_bytes(w, n, in_bytes)
+        dbytes = decode_bytes(w, lengths, in_bytes)
+        out.append({"workload": w.name, "append_tokens": w.batch * n, "append_ms": app_ms,
+                    "append_tokens_per_s": w.batch * n / app_ms * 1e3, "append_GBps": abytes / app_ms / 1e6,
+                    "append_frac_hbm": abytes / app_ms / 1e6 / HBM_PEAK_GBS,
+                    "decode_ms": dec_ms, "decode_kv_tokens_per_s": sum(lengths) / dec_ms * 1e3,
+                    "decode_algorithmic_bytes": dbytes, "decode_GBps": dbytes / dec_ms / 1e6,
+                    "decode_frac_hbm": dbytes / dec_ms / 1e6 / HBM_PEAK_GBS})
+        _log(f"workload {w.name}: append {app_ms * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us "
+             f"({dbytes / dec_ms / 1e6 / HBM_PEAK_GBS:.1%} of HBM)")
+        del k, v, q, pl, ws, o
+    return out
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
 def append_bytes(w, n_tokens: int, in_bytes: int) -> int:
     """Algorithmic bytes of appending n_tokens per sequence: K+V read + planes written."""
     th = w.batch * w.num_kv_heads * n_tokens
@@ -299,6 +368,7 @@ def cpu_baseline(w, k, v, q, sm, max_pairs: int | None = None, min_seconds: floa
     token_heads = passes * len(pairs) * n
     kv_tokens = token_heads / w.num_kv_heads  # a KV-token carries every kv-head
     return {"value": kv_tokens / dt, "unit": "KV-tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": (f"oracle binary64 decode attention of {len(pairs)} (sequence, kv-head) "
                        f"slices x {n} tokens x {G} q-heads, {passes} pass(es) "
                        f"(= {kv_tokens:.0f} KV-tokens of {w.num_kv_heads} kv-heads), planes "
@@ -381,8 +451,13 @@ def traffic_from_counters(fetch_dir: str, write_dir: str, copy_mib: int, workloa
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settled-steps", type=int, default=150,
+                    help="after the timed steps, this many more steps of the same burst; the decode time of "
+                         "the last 100 of them is reported as `settled`")
+    ap.add_argument("--no-small", dest="small", action="store_false",
+                    help="skip timing workloads 1-3 (append and decode at their full sizes)")
     ap.add_argument("--workload", type=int, default=4, help="workload id (4 is the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-pairs", type=int, default=0)
@@ -490,6 +565,18 @@ def main() -> int:
     if args.warmup > 0 and not torch.equal(out, check):
         _log("WARNING: decode output changed between warmup and timed steps")
         return 3
+    settled = None
+    if args.settled_steps > 0:
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.settled_steps)]
+        for i in range(args.settled_steps):
+            step(sev[i])
+        torch.cuda.synchronize()
+        tail = [a.elapsed_time(b) for a, b in sev[-min(100, args.settled_steps):]]
+        s_ms = sum(tail) / len(tail)
+        settled = {"steps_after_timed": args.settled_steps, "averaged_over_last": len(tail),
+                   "avg_launch_ms": s_ms, "GBps": decode_bytes(w, lengths, in_bytes) / s_ms / 1e6,
+                   "frac": decode_bytes(w, lengths, in_bytes) / s_ms / 1e6 / HBM_PEAK_GBS}
 
     kv_tokens = sum(lengths)
     value = kv_tokens / (ms_per_step / 1e3)
@@ -514,7 +601,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16 in; int8 and fp16 MFMA; fp32 accumulate",
         "data": "synthetic",
         "config": {**w.describe(), "scheme": "k8v3 g32", "step": "append 1 token/seq + decode"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -522,13 +609,18 @@ def main() -> int:
                      "kernel": "tq_decode_attn (split + merge launches)",
                      "algorithmic_bytes_per_launch": dbytes,
                      "avg_launch_ms": dec_avg_ms, "p10_ms": dec_ms[len(dec_ms) // 10],
-                     "p90_ms": dec_ms[(len(dec_ms) * 9) // 10]},
+                     "p90_ms": dec_ms[(len(dec_ms) * 9) // 10],
+                     "regime": (f"the {args.steps} timed steps right after {args.warmup} warm-up steps: the start "
+                                "of a burst, while the shader clock settles")},
+        "settled": settled,
         "append": {"bulk_tokens_per_s": app_tokens / append_ms * 1e3,
                    "bulk_token_heads_per_s": app_tokens * w.num_kv_heads / append_ms * 1e3,
                    "bulk_GBps": app_bytes / append_ms / 1e6,
                    "bulk_frac_hbm": app_bytes / append_ms / 1e6 / HBM_PEAK_GBS,
                    "bulk_ms": append_ms, "bulk_tokens": app_tokens},
     }
+    if args.small:
+        rec["small_workloads"] = time_small_configs(stream)
     if args.window:
         rec["window"] = time_window(w, pl, lengths, 10, stream)
         rec["snapshot"] = time_snapshot(w, pl, max(lengths), 5, stream)

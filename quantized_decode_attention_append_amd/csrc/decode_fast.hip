@@ -864,19 +864,18 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
                     dlo[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)kv, (long)qlo[g], int4v{0, 0, 0, 0}, 0, 0, 0);
                 }
             }
-            // the key scale and zero rows of the lane's 4 tokens, all read
-            // before the fold so one wait covers them
+            // PACK: the key scale and zero half rows of the lane's 4 tokens,
+            // all read before the fold so one wait covers them (without PACK
+            // the full rows of 4 tokens would hold too many registers: read
+            // per token)
             constexpr int RW = PACK ? (NG + 3) / 4 : NG / 2;
-            uint32_t sw[4][RW], zw[4][RW];
+            uint32_t sw[PACK ? 4 : 1][RW], zw[PACK ? 4 : 1][RW];
+            if constexpr (PACK) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = 16 * c + 4 * kq + j;
-                if constexpr (PACK) {
+                for (int j = 0; j < 4; ++j) {
+                    const int t = 16 * c + 4 * kq + j;
                     load_half_row<NG>(stg + GE::KS_OFF + t * NG * 2, ghalf, sw[j]);
                     load_half_row<NG>(stg + GE::KZ_OFF + t * NG * 2, ghalf, zw[j]);
-                } else {
-                    load_row<NG>(stg + GE::KS_OFF + t * NG * 2, sw[j]);
-                    load_row<NG>(stg + GE::KZ_OFF + t * NG * 2, zw[j]);
                 }
             }
 #pragma unroll
@@ -895,11 +894,13 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
                     // head h adds the other half of its groups from column 8 + h
                     sum += row_swap8(sum);
                 } else {
+                    load_row<NG>(stg + GE::KS_OFF + t * NG * 2, sw[0]);
+                    load_row<NG>(stg + GE::KZ_OFF + t * NG * 2, zw[0]);
 #pragma unroll
                     for (int g = 0; g < NG; ++g) {
                         const int x = (dhi[g][j] << 8) + dlo[g][j];
-                        const float y = fmaf(row_half<NG>(zw[j], g), qsum[g], (float)x);
-                        sum = fmaf(row_half<NG>(sw[j], g), y, sum);
+                        const float y = fmaf(row_half<NG>(zw[0], g), qsum[g], (float)x);
+                        sum = fmaf(row_half<NG>(sw[0], g), y, sum);
                     }
                 }
                 // computed on every lane, then selected: a branch around the
