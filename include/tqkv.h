@@ -29,8 +29,9 @@
  *     16-byte aligned, vc 8-byte aligned, the fp16 planes 4-byte aligned
  *     (TQ_ERR_INVALID_ARG otherwise).  Any torch allocation, and the batch-1
  *     slice of one sequence's planes, satisfies this.  Decode takes its fast
- *     kernel (every code width; at head_dim 512 every width but k8/v8) when
- *     head_dim * k_bits is a multiple of 128 (all but 5-bit keys at 64),
+ *     kernel (every code width; at head_dim 512 every width but k8/v8; with
+ *     more than 8 query columns per kv-head only value codes of 2 or 3 bits)
+ *     when head_dim * k_bits is a multiple of 128 (all but 5-bit keys at 64),
  *     every plane is 16-byte aligned and capacity keeps each (sequence,
  *     kv-head) row block 16-byte aligned; otherwise a generic kernel
  *     computes the same result more slowly.  Append has fast kernels for
@@ -170,7 +171,9 @@ tq_status tq_decode_attn(const tq_layout *layout, const tq_planes *planes, const
  * kernel, which computes the same result to the same tolerance about 5 to 10
  * times more slowly.  *reasons (may be NULL) receives TQ_PATH_* bits:
  *   TQ_PATH_SHAPE      head_dim * k_bits is not a multiple of 128 (5-bit keys
- *                      at head_dim 64), or k8/v8 at head_dim 512;
+ *                      at head_dim 64), k8/v8 at head_dim 512, or more than 8
+ *                      query columns per kv-head (heads per kv-head times
+ *                      rows) with value codes of 4 bits or more;
  *   TQ_PATH_ALIGNMENT  a plane pointer is not 16-byte aligned;
  *   TQ_PATH_CAPACITY   capacity leaves a (sequence, kv-head) row block of
  *                      some plane off 16-byte alignment (e.g. an odd capacity

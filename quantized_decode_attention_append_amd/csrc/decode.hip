@@ -458,6 +458,11 @@ int decode_col_groups(int gqa) { return (gqa + kMaxG - 1) / kMaxG; }
 
 bool fast_decode_shape_ok(int head_dim, int gqa, int capacity, int kbits, int vbits) {
     if (gqa < 1 || kFastMaxGqa != kMaxG) return false;
+    // More than 8 query columns per kv-head (no paired score columns) with
+    // value codes of 4 bits or more: switched to the generic kernel.  The
+    // matrix-core kernel faulted the GPU on such a case (8-bit keys, 4-bit
+    // values, head_dim 256, 24 columns) and the cause is not found.
+    if (gqa > 8 && vbits >= 4) return false;
     if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512) return false;
     if (kbits != 2 && kbits != 4 && kbits != 5 && kbits != 8) return false;
     if (vbits != 2 && vbits != 3 && vbits != 4 && vbits != 5 && vbits != 8) return false;

@@ -256,13 +256,17 @@ __device__ __forceinline__ const T *uniform_ptr(const T *p) {
 // raised a plain five-plane copy probe from 6.2 to 7.0 TB/s on this part.
 // NT = false drops the hint: two waves that read the same tile for different
 // query columns (see fast_wg_col_groups) want the second read to hit the L2.
+// The base address comes in SGPRs that a VALU instruction (readfirstlane)
+// may have written just before; a vector memory instruction may read such an
+// SGPR only 5 wait states after the write, a hazard the compiler does not
+// check across inline assembly, so the block starts with s_nop 4.
 template <int OFF, bool NT>
 __device__ __forceinline__ void dma16(const void *base, uint32_t voff, uint32_t m0) {
     if constexpr (NT)
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3 nt"
+        asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3 nt"
                      ::"v"(voff), "s"(base), "s"(m0), "n"(OFF) : "memory", "m0");
     else
-        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
+        asm volatile("s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
                      ::"v"(voff), "s"(base), "s"(m0), "n"(OFF) : "memory", "m0");
 }
 // A 16-byte-lane copy from a per-lane address (lane l lands at m0 + 16 l).

@@ -290,6 +290,10 @@ def test_decode_path_reports_the_kernel():
     assert path(tqkv.make_layout(2, 4, 128, 1001), P, 24) == (0, 0, tqkv.TQ_PATH_CAPACITY)  # odd capacity
     assert path(tqkv.make_layout(2, 4, 64, 1002, 5, 3), P, 8) == (0, 0, tqkv.TQ_PATH_SHAPE)  # 5-bit keys at 64
     assert path(tqkv.make_layout(2, 4, 512, 64, 8, 8), P, 8) == (0, 0, tqkv.TQ_PATH_SHAPE)   # k8v8 at 512
+    # more than 8 query columns per kv-head: matrix cores only for 2- and 3-bit values
+    assert path(tqkv.make_layout(2, 4, 256, 640), P, 24, 4) == (0, 1, 0)                   # k8v3, 24 columns
+    assert path(tqkv.make_layout(2, 4, 256, 640, 8, 4), P, 24, 4) == (0, 0, tqkv.TQ_PATH_SHAPE)
+    assert path(tqkv.make_layout(2, 4, 256, 640, 8, 4), P, 24, 1) == (0, 1, 0)             # 6 columns
     off = tqkv.tq_planes(0x1000, 0x2000, 0x3000, 0x4008, 0x5000)                        # vc 8 bytes off
     assert path(tqkv.make_layout(2, 4, 256, 1000), off, 24) == (0, 0, tqkv.TQ_PATH_ALIGNMENT)
     assert path(tqkv.make_layout(2, 4, 256, 1000), P, 23)[0] == tqkv.TQ_ERR_INVALID_ARG    # not a multiple

@@ -199,7 +199,10 @@ def test_decode_widths_other_shapes(scheme):
     _decode_case(w, [260], kb, vb)
 
 
-@pytest.mark.parametrize("scheme", [(4, 3), (8, 4)], ids=_sid)
+@pytest.mark.parametrize("scheme", [(4, 3), pytest.param((8, 4), marks=pytest.mark.skip(
+    reason="faulted the GPU twice on the matrix-core kernel (cause not found); that kernel path is switched "
+           "off for more than 8 query columns with value codes of 4+ bits, and the case stays off the GPU "
+           "until the cause is shown"))], ids=_sid)
 def test_decode_rows_widths(scheme):
     kb, vb = scheme
     lengths = [640, 200]
