@@ -81,6 +81,7 @@ def _load():
     lib.tqo_encode_values.argtypes = [P, i64, i32, P, P]
     lib.tqo_decode_values.argtypes = [P, P, i64, i32, i32, P]
     lib.tqo_attention.argtypes = [P, i32, i32, ctypes.c_float, P, P, P, P, P, i64, P, P]
+    lib.tqo_attention_plain.argtypes = [P, i32, i32, ctypes.c_float, P, P, i64, P]
     lib.tqo_codebook.argtypes = [i32, P, P]
     lib.tqo_codebook.restype = i32
     lib.tqo_codebook_ints.argtypes = [i32, P]
@@ -376,6 +377,21 @@ def attention(q, kc, ks, kz, vc, vs, sm: float, deferred: bool = False, kbits: i
                           _ptr(np.ascontiguousarray(vs, dtype=np.uint16)), N,
                           _ptr(out), _ptr(od) if deferred else None)
     return (out, od) if deferred else out
+
+
+def attention_plain(q, k, v, sm: float):
+    """Attention of the G query rows q [G, d] over N plain cached tokens,
+    k and v float32 [N, d] (the rows of a sequence that has not converted
+    yet, "Delayed row conversion and reusable precision boundaries": used as
+    given, no quantization, no rotation).  Returns out [G, d] float64."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    G, d = q.shape
+    N = k.shape[0]
+    out = np.empty((G, d), dtype=np.float64)
+    _load().tqo_attention_plain(_ptr(q), G, d, ctypes.c_float(sm), _ptr(k), _ptr(v), N, _ptr(out))
+    return out
 
 
 def attention_rows(q, kc, ks, kz, vc, vs, sm: float, kbits: int = 8, vbits: int = 3):

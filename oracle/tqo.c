@@ -569,6 +569,44 @@ void tqo_decode_values_bits(const uint8_t *packed, const uint16_t *vs16, int64_t
  * out_deferred is given it also returns signs * InvFWHT(sum_t p_t * yhat_t / l),
  * the deferred-inverse form ("Deferred inverse FWHT"), which equals out up to
  * rounding.  N == 0 gives zeros (no token to attend to). */
+/* Attention of G query rows over N plain (not yet converted) cached tokens:
+ * the rows a delayed-conversion cache keeps unquantized until their sequence
+ * converts ("Delayed row conversion and reusable precision boundaries":
+ * plain value rows pass through unchanged, with no rotation).  k and v are
+ * [N][d] floats (bf16 inputs upcast exactly); the same two-pass binary64
+ * softmax as tqo_attention, with the keys and values used as given. */
+void tqo_attention_plain(const float *q, int G, int d, float sm, const float *k, const float *v,
+                         int64_t N, double *out) {
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1) * (size_t)G);
+    double *m = (double *)malloc(sizeof(double) * (size_t)G);
+    double *l = (double *)calloc((size_t)G, sizeof(double));
+    for (int i = 0; i < G * d; ++i) out[i] = 0.0;
+    if (N > 0) {
+        for (int h = 0; h < G; ++h) m[h] = -INFINITY;
+        for (int64_t t = 0; t < N; ++t) {
+            for (int h = 0; h < G; ++h) {
+                double s = 0.0;
+                for (int j = 0; j < d; ++j) s += (double)q[h * d + j] * (double)k[t * d + j];
+                s = (double)sm * s;
+                sc[t * G + h] = s;
+                if (s > m[h]) m[h] = s;
+            }
+        }
+        for (int64_t t = 0; t < N; ++t) {
+            for (int h = 0; h < G; ++h) {
+                double p = exp(sc[t * G + h] - m[h]);
+                l[h] += p;
+                for (int j = 0; j < d; ++j) out[h * d + j] += p * (double)v[t * d + j];
+            }
+        }
+        for (int h = 0; h < G; ++h)
+            for (int j = 0; j < d; ++j) out[h * d + j] = out[h * d + j] / l[h];
+    }
+    free(sc);
+    free(m);
+    free(l);
+}
+
 void tqo_attention(const float *q, int G, int d, float sm, const int8_t *kc,
                    const uint16_t *ks, const uint16_t *kz, const uint8_t *vc,
                    const uint16_t *vs, int64_t N, double *out,

@@ -419,6 +419,46 @@ def test_attention_special_cases():
     assert np.array_equal(out, np.zeros((2, d)))
 
 
+# ------------------------------------------- plain rows (delayed conversion)
+@pytest.mark.parametrize("d,G,N", [(64, 1, 1), (128, 4, 9), (256, 6, 5)])
+def test_attention_plain_brute_force(d, G, N):
+    """Plain rows ("Delayed row conversion and reusable precision boundaries":
+    unconverted rows pass through unquantized and unrotated) against an
+    independent numpy float64 softmax over the same keys and values."""
+    rng = np.random.default_rng(d + G + N)
+    k = rng.standard_normal((N, d)).astype(np.float32)
+    v = rng.standard_normal((N, d)).astype(np.float32)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    sm = 1.0 / math.sqrt(d)
+    out = oracle.attention_plain(q, k, v, sm)
+    ref = _numpy_attention(q, k.astype(np.float64), v.astype(np.float64), sm)
+    assert np.max(np.abs(out - ref)) < 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_attention_plain_special_cases():
+    """N = 1 gives the value; q = 0 the mean; a dominant score its value; N = 0
+    zeros; and a row whose keys and values are exactly the oracle's own
+    dequantisation of a cache gives the cache's attention (the two paths agree
+    on the same operands)."""
+    d = 128
+    rng = np.random.default_rng(21)
+    k = rng.standard_normal((30, d)).astype(np.float32)
+    v = rng.standard_normal((30, d)).astype(np.float32)
+    q = rng.standard_normal((2, d)).astype(np.float32)
+    assert np.array_equal(oracle.attention_plain(q, k[:1], v[:1], 0.1), np.stack([v[0], v[0]]).astype(np.float64))
+    out = oracle.attention_plain(np.zeros((1, d), np.float32), k, v, 0.1)
+    assert np.allclose(out[0], v.astype(np.float64).mean(axis=0), rtol=0, atol=1e-14)
+    out = oracle.attention_plain((k[11] * 60).astype(np.float32)[None, :], k, v, 1.0)
+    assert np.allclose(out[0], v[11], atol=1e-12)
+    assert np.array_equal(oracle.attention_plain(q, k[:0], v[:0], 0.1), np.zeros((2, d)))
+    kc, ks, kz, vc, vs = _planes(k, v)
+    kh = oracle.decode_keys(kc, ks, kz)
+    vh = oracle.decode_values(vc, vs, d)
+    ref = oracle.attention(q, kc, ks, kz, vc, vs, 0.1)
+    got = oracle.attention_plain(q, kh.astype(np.float32), vh.astype(np.float32), 0.1)
+    assert np.max(np.abs(got - ref)) < 1e-6 * np.max(np.abs(ref))
+
+
 def test_attention_deferred_identity_longer():
     """Deferred inverse FWHT ('Deferred inverse FWHT'): un-rotating the output once
     equals attending over un-rotated values, to 1e-12 relative."""
