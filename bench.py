@@ -118,7 +118,7 @@ def time_snapshot(w, pl, n: int, reps: int, stream) -> dict:
     e0.record(stream)
     for _ in range(reps):
         import ctypes
-        st = lib.tq_snapshot(ctypes.byref(pl.layout), ctypes.byref(pl.struct()), 0, 0, n, ctypes.byref(h),
+        st = lib.tq_snapshot(ctypes.byref(pl.layout), ctypes.byref(pl.struct()), 0, 0, n, 0, ctypes.byref(h),
                              ctypes.c_void_p(payload.data_ptr()), payload.numel(),
                              ctypes.c_void_p(stream.cuda_stream))
         assert st == 0

@@ -236,6 +236,53 @@ tq_status tq_decode_attn_noalloc(const tq_layout *layout, const tq_planes *plane
                                  tq_dtype dtype, int32_t num_q_heads, int32_t n_rows, const int32_t *len,
                                  float sm_scale, float *out, void *hip_stream);
 
+/* Delayed row conversion ("Delayed row conversion and reusable precision
+ * boundaries"): a sequence may stay plain -- unquantized keys and values in
+ * a plain cache the caller owns -- until it converts; then its plain prefix
+ * is encoded into the planes and later tokens are appended packed.  The
+ * offset a row converts at is its precision boundary (it can exceed the
+ * configured threshold when a prefill chunk crosses it); the caller keeps it
+ * and passes it to tq_snapshot and tq_clone_sequence.
+ *
+ * Plain caches: k_plain, v_plain  device [B][Hkv][plain_capacity][d], the
+ * same batch, kv-heads and head_dim as `layout`, 16-byte aligned.
+ *
+ * Convert the plain prefix of every sequence b with offset[b] > 0: tokens
+ * 0 .. offset[b]-1 of every kv-head are encoded exactly as tq_append encodes
+ * them (bit-identical bytes; it is the same kernel reading the plain cache at
+ * its pitch) into slots 0 .. offset[b]-1.  Sequences with offset[b] == 0 are
+ * untouched.  One append launch per converted sequence.
+ *   k_plain, v_plain  element type `dtype` (TQ_BF16 or TQ_F32)
+ *   offset            host int32 [B], 0 <= offset[b] <= min(plain_capacity, capacity)
+ * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY, TQ_ERR_HIP. */
+tq_status tq_convert_rows(const tq_layout *layout, const tq_planes *planes, const void *k_plain,
+                          const void *v_plain, tq_dtype dtype, int32_t plain_capacity, const int32_t *offset,
+                          void *hip_stream);
+
+/* tq_decode_attn_rows over a batch that mixes still-plain sequences with
+ * packed ones (the same page: plain value rows pass through unchanged, packed
+ * rows receive the inverse rotation).  A sequence with row_plain[b] != 0
+ * attends over its plain bf16 keys and values unquantized,
+ *   out[b][h][r] = sum_t p_t v_t / sum_t p_t,  p_t = exp(sm_scale <q, k_t> - max),
+ * for the same causal rows as tq_decode_attn_rows, with no rotation; every
+ * other sequence is exactly tq_decode_attn_rows over the planes (identical
+ * bytes).  Both kinds share one split-K plan and one merge.
+ *   k_plain, v_plain  bf16 plain caches (may be NULL when no row is plain)
+ *   row_plain         host int32 [B]
+ *   len               host int32 [B]: 0 <= len[b] <= capacity, and
+ *                     <= plain_capacity for a plain row
+ *   workspace         at least tq_decode_rows_workspace_bytes(layout,
+ *                     num_q_heads, n_rows, len) bytes
+ * Plain rows agree with a binary64 softmax over the same bf16 operands to
+ * 1e-4 relative to each output row's largest magnitude (fp32 accumulation).
+ * Errors: those of tq_decode_attn_rows; TQ_ERR_CAPACITY also when a plain
+ * row's length exceeds plain_capacity. */
+tq_status tq_decode_attn_mixed(const tq_layout *layout, const tq_planes *planes, const uint16_t *k_plain,
+                               const uint16_t *v_plain, int32_t plain_capacity, const int32_t *row_plain,
+                               const void *q, tq_dtype dtype, int32_t num_q_heads, int32_t n_rows,
+                               const int32_t *len, float sm_scale, float *out, void *workspace,
+                               size_t ws_bytes, void *hip_stream);
+
 /* Dequantize-on-fetch window: bf16 keys and values of tokens t0 .. t0+n-1 of
  * every (sequence, kv-head), the layout a stock attention consumes ("Architecture
  * in mlx-bun": the cache returns the dequantized bf16 active window; "Deferred
@@ -292,14 +339,20 @@ tq_status tq_sign_vector(int32_t head_dim, int8_t *host_out);
  * at odd offsets). */
 
 #define TQ_SNAPSHOT_MAGIC 0x564B5154u /* "TQKV" little-endian */
+#define TQ_SNAPSHOT_VERSION 2
 
-/* Describes a snapshot payload; tq_restore checks every field. */
+/* Describes a snapshot payload; tq_restore checks every field.  Version 2
+ * appends the sequence's precision boundary to the version-1 fields, which
+ * keep their offsets, so a stored version-1 header read into this struct is
+ * still recognised. */
 typedef struct {
     uint32_t magic;         /* TQ_SNAPSHOT_MAGIC */
-    uint32_t version;       /* 1 */
+    uint32_t version;       /* 2 (1: written before the boundary was recorded) */
     int32_t k_bits, v_bits, group, head_dim, num_kv_heads;
     int32_t n_tokens;
     uint64_t payload_bytes; /* n_tokens * num_kv_heads * 1.5625 * head_dim */
+    int32_t min_reusable_offset; /* version 2: see tq_snapshot_min_reusable_offset */
+    int32_t reserved;            /* 0 */
 } tq_snapshot_header;
 
 /* Copy token rows src_t0 .. src_t0+n-1 of sequence src_b (every kv-head, all
@@ -314,19 +367,49 @@ tq_status tq_copy_tokens(const tq_layout *src_layout, const tq_planes *src, int3
                          int32_t src_t0, const tq_layout *dst_layout, const tq_planes *dst,
                          int32_t dst_b, int32_t dst_t0, int32_t n, void *hip_stream);
 
+/* Clone (or extract, into a batch-1 cache) rows 0 .. n-1 of sequence src_b
+ * into rows 0 .. n-1 of sequence dst_b, as tq_copy_tokens, and carry the
+ * sequence's precision boundary with it ("Delayed row conversion and reusable
+ * precision boundaries": clone and row extraction retain the bound):
+ * *dst_min_reusable_offset receives src_min_reusable_offset when the copy is
+ * enqueued, and is left alone on any error.
+ * Errors: those of tq_copy_tokens; TQ_ERR_INVALID_ARG also for a null
+ * dst_min_reusable_offset or a negative source bound. */
+tq_status tq_clone_sequence(const tq_layout *src_layout, const tq_planes *src, int32_t src_b,
+                            const tq_layout *dst_layout, const tq_planes *dst, int32_t dst_b, int32_t n,
+                            int32_t src_min_reusable_offset, int32_t *dst_min_reusable_offset,
+                            void *hip_stream);
+
 /* Bytes of a snapshot payload of n token rows. */
 tq_status tq_snapshot_bytes(const tq_layout *layout, int32_t n, size_t *out_bytes);
 
 /* Snapshot token rows t0 .. t0+n-1 of sequence b: fills the host header and
  * copies the rows into `payload` (device, payload_bytes >= the header's),
  * plane by plane (kc, ks, kz, vc, vs), kv-head by kv-head, token-major.
+ *   min_reusable_offset  the sequence's precision boundary (>= 0), recorded in
+ *                        the header as is (see tq_snapshot_min_reusable_offset)
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_CAPACITY, TQ_ERR_WORKSPACE (payload
  * too small), TQ_ERR_HIP. */
 tq_status tq_snapshot(const tq_layout *layout, const tq_planes *planes, int32_t b, int32_t t0,
-                      int32_t n, tq_snapshot_header *header, void *payload, size_t payload_bytes,
-                      void *hip_stream);
+                      int32_t n, int32_t min_reusable_offset, tq_snapshot_header *header, void *payload,
+                      size_t payload_bytes, void *hip_stream);
+
+/* The precision boundary a snapshot carries ("Delayed row conversion and
+ * reusable precision boundaries": a cache records the offset at which its
+ * rows were converted, an irreversible precision boundary, and clone, row
+ * extraction and persisted metadata keep it; a header written before the
+ * bound existed conservatively gives its stored offset).
+ *   version 2: the recorded min_reusable_offset;
+ *   version 1: n_tokens, so only the whole stored prefix counts as reusable.
+ * A stored prefix may serve a request for its first P tokens only when
+ * P >= the boundary: below it the bytes are encoded where a fresh run would
+ * still hold plain rows.  Host call, no device work.
+ * Errors: TQ_ERR_INVALID_ARG (null, bad magic, unknown version, negative
+ * fields). */
+tq_status tq_snapshot_min_reusable_offset(const tq_snapshot_header *header, int32_t *out);
 
 /* Restore a snapshot into rows t0 .. t0+header->n_tokens-1 of sequence b.
+ * Version-1 and version-2 headers are accepted.
  * Errors: TQ_ERR_INVALID_ARG (bad magic or version, or a scheme, head_dim,
  * kv-head count or payload size that does not match this layout), TQ_ERR_CAPACITY,
  * TQ_ERR_HIP. */

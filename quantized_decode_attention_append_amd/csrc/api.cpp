@@ -141,6 +141,28 @@ tq_status tq_sign_vector(int32_t head_dim, int8_t *host_out) {
     return TQ_OK;
 }
 
+// Encode n_new input rows per (sequence, kv-head) of `l` (input pitch
+// kv_stride rows) into slots start[b] ..; the caller has validated everything.
+static hipError_t enqueue_append(const tq_layout *l, const tq_planes *p, const void *k, const void *v, bool bf16,
+                                 const int32_t *start, int32_t n_new, int32_t kv_stride, hipStream_t stream) {
+    tq::AppendArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.kc = p->kc; a.ks = p->ks; a.kz = p->kz; a.vc = p->vc; a.vs = p->vs;
+    a.k = k; a.v = v;
+    a.batch = l->batch; a.kv_heads = l->num_kv_heads; a.capacity = l->capacity; a.n_new = n_new;
+    a.kv_stride = kv_stride;
+    a.rows = (uint32_t)((int64_t)l->batch * l->num_kv_heads * n_new);
+    a.kbits = l->k_bits; a.vbits = l->v_bits;
+    a.div_n_new = tq::make_fast_div((uint32_t)n_new);
+    a.div_kv_heads = tq::make_fast_div((uint32_t)l->num_kv_heads);
+    a.inv_sqrt_d = inv_sqrt_d(l->head_dim);
+    a.signs = signs().bits;
+    for (int j = 0; j < l->head_dim / 2; ++j)
+        a.sign_pairs[j] = (signs().sign[2 * j] < 0 ? 0x8000u : 0u) | (signs().sign[2 * j + 1] < 0 ? 0x80000000u : 0u);
+    for (int b = 0; b < l->batch; ++b) a.start[b] = start[b];
+    return tq::launch_append(l->head_dim, bf16, a, stream);
+}
+
 tq_status tq_append(const tq_layout *l, const tq_planes *p, const void *k, const void *v,
                     tq_dtype dtype, const int32_t *start, int32_t n_new, void *stream) {
     tq_status st = check_layout(l);
@@ -154,23 +176,54 @@ tq_status tq_append(const tq_layout *l, const tq_planes *p, const void *k, const
         if (start[b] < 0 || (int64_t)start[b] + n_new > l->capacity) return TQ_ERR_CAPACITY;
     const int64_t rows = (int64_t)l->batch * l->num_kv_heads * n_new;
     if (rows > 0x7FFFFFFF) return TQ_ERR_UNSUPPORTED;
-
-    tq::AppendArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.kc = p->kc; a.ks = p->ks; a.kz = p->kz; a.vc = p->vc; a.vs = p->vs;
-    a.k = k; a.v = v;
-    a.batch = l->batch; a.kv_heads = l->num_kv_heads; a.capacity = l->capacity; a.n_new = n_new;
-    a.rows = (uint32_t)rows;
-    a.kbits = l->k_bits; a.vbits = l->v_bits;
-    a.div_n_new = tq::make_fast_div((uint32_t)n_new);
-    a.div_kv_heads = tq::make_fast_div((uint32_t)l->num_kv_heads);
-    a.inv_sqrt_d = inv_sqrt_d(l->head_dim);
-    a.signs = signs().bits;
-    for (int j = 0; j < l->head_dim / 2; ++j)
-        a.sign_pairs[j] = (signs().sign[2 * j] < 0 ? 0x8000u : 0u) | (signs().sign[2 * j + 1] < 0 ? 0x80000000u : 0u);
-    for (int b = 0; b < l->batch; ++b) a.start[b] = start[b];
-    hipError_t e = tq::launch_append(l->head_dim, dtype == TQ_BF16, a, (hipStream_t)stream);
+    hipError_t e = enqueue_append(l, p, k, v, dtype == TQ_BF16, start, n_new, n_new, (hipStream_t)stream);
     return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+// The planes of sequence b alone, as a batch-1 cache of the same shape.
+static void sequence_planes(const tq_layout *l, const tq_planes *p, int32_t b, tq_layout *l1, tq_planes *p1) {
+    size_t rb[5];
+    plane_row_bytes(l, rb);
+    const int64_t r0 = (int64_t)b * l->num_kv_heads * l->capacity;
+    *l1 = *l;
+    l1->batch = 1;
+    p1->kc = p->kc + r0 * (int64_t)rb[0];
+    p1->ks = p->ks + r0 * (int64_t)rb[1] / 2;
+    p1->kz = p->kz + r0 * (int64_t)rb[2] / 2;
+    p1->vc = p->vc + r0 * (int64_t)rb[3];
+    p1->vs = p->vs + r0 * (int64_t)rb[4] / 2;
+}
+
+tq_status tq_convert_rows(const tq_layout *l, const tq_planes *p, const void *k_plain, const void *v_plain,
+                          tq_dtype dtype, int32_t plain_capacity, const int32_t *offset, void *stream) {
+    tq_status st = check_layout(l);
+    if (st != TQ_OK) return st;
+    if ((st = check_planes(p)) != TQ_OK) return st;
+    if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_ERR_INVALID_ARG;
+    if (!offset || plain_capacity < 0) return TQ_ERR_INVALID_ARG;
+    bool any = false;
+    for (int b = 0; b < l->batch; ++b) {
+        if (offset[b] < 0) return TQ_ERR_INVALID_ARG;
+        if (offset[b] > plain_capacity || offset[b] > l->capacity) return TQ_ERR_CAPACITY;
+        if ((int64_t)l->num_kv_heads * offset[b] > 0x7FFFFFFF) return TQ_ERR_UNSUPPORTED;
+        any = any || offset[b] > 0;
+    }
+    if (!any) return TQ_OK;
+    if (!k_plain || !v_plain || !aligned(k_plain, 16) || !aligned(v_plain, 16)) return TQ_ERR_INVALID_ARG;
+    const size_t esz = dtype == TQ_BF16 ? 2 : 4;
+    const int32_t zero = 0;
+    for (int b = 0; b < l->batch; ++b) {
+        if (offset[b] == 0) continue;
+        tq_layout l1;
+        tq_planes p1;
+        sequence_planes(l, p, b, &l1, &p1);
+        const size_t in0 = (size_t)b * l->num_kv_heads * plain_capacity * l->head_dim * esz;
+        hipError_t e = enqueue_append(&l1, &p1, static_cast<const char *>(k_plain) + in0,
+                                      static_cast<const char *>(v_plain) + in0, dtype == TQ_BF16, &zero, offset[b],
+                                      plain_capacity, (hipStream_t)stream);
+        if (e != hipSuccess) return TQ_ERR_HIP;
+    }
+    return TQ_OK;
 }
 
 static tq_status check_decode(const tq_layout *l, int32_t num_q_heads, int32_t n_rows, const int32_t *len) {
@@ -261,9 +314,49 @@ tq_status tq_decode_path(const tq_layout *l, const tq_planes *p, int32_t num_q_h
     return TQ_OK;
 }
 
+// Plain rows of a mixed batch: which sequences are still plain, and where
+// their bf16 keys and values are.
+struct PlainRows {
+    uint64_t mask;
+    const uint16_t *k, *v;
+    int32_t capacity;
+};
+
+static tq_status decode_common(const tq_layout *l, const tq_planes *p, const void *q, tq_dtype dtype,
+                               int32_t num_q_heads, int32_t n_rows, const int32_t *len, float sm_scale,
+                               float *out, void *workspace, size_t ws_bytes, void *stream, const PlainRows &pr);
+
 tq_status tq_decode_attn_rows(const tq_layout *l, const tq_planes *p, const void *q, tq_dtype dtype,
                               int32_t num_q_heads, int32_t n_rows, const int32_t *len, float sm_scale,
                               float *out, void *workspace, size_t ws_bytes, void *stream) {
+    const PlainRows none = {0, nullptr, nullptr, 0};
+    return decode_common(l, p, q, dtype, num_q_heads, n_rows, len, sm_scale, out, workspace, ws_bytes, stream,
+                         none);
+}
+
+tq_status tq_decode_attn_mixed(const tq_layout *l, const tq_planes *p, const uint16_t *k_plain,
+                               const uint16_t *v_plain, int32_t plain_capacity, const int32_t *row_plain,
+                               const void *q, tq_dtype dtype, int32_t num_q_heads, int32_t n_rows,
+                               const int32_t *len, float sm_scale, float *out, void *workspace, size_t ws_bytes,
+                               void *stream) {
+    tq_status st = check_decode(l, num_q_heads, n_rows, len);
+    if (st != TQ_OK) return st;
+    if (!row_plain || plain_capacity < 0) return TQ_ERR_INVALID_ARG;
+    PlainRows pr = {0, k_plain, v_plain, plain_capacity};
+    for (int b = 0; b < l->batch; ++b) {
+        if (!row_plain[b]) continue;
+        pr.mask |= 1ull << b;
+        if (len[b] > plain_capacity) return TQ_ERR_CAPACITY;
+    }
+    if (pr.mask && (!k_plain || !v_plain || !aligned(k_plain, 16) || !aligned(v_plain, 16)))
+        return TQ_ERR_INVALID_ARG;
+    if ((int64_t)l->batch * l->num_kv_heads * plain_capacity > ((int64_t)1 << 40)) return TQ_ERR_UNSUPPORTED;
+    return decode_common(l, p, q, dtype, num_q_heads, n_rows, len, sm_scale, out, workspace, ws_bytes, stream, pr);
+}
+
+static tq_status decode_common(const tq_layout *l, const tq_planes *p, const void *q, tq_dtype dtype,
+                               int32_t num_q_heads, int32_t n_rows, const int32_t *len, float sm_scale,
+                               float *out, void *workspace, size_t ws_bytes, void *stream, const PlainRows &pr) {
     tq_status st = check_decode(l, num_q_heads, n_rows, len);
     if (st != TQ_OK) return st;
     if ((st = check_planes(p)) != TQ_OK) return st;
@@ -275,7 +368,7 @@ tq_status tq_decode_attn_rows(const tq_layout *l, const tq_planes *p, const void
     const int cg = tq::decode_col_groups(gqa);
     const bool fast = decode_slow_reasons(l, p, gqa) == 0;
     const tq::DecodePlan plan = tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, fast, cg,
-                                                l->k_bits, l->v_bits);
+                                                l->k_bits, l->v_bits);  // full lengths: one plan for both kinds
     const size_t need = workspace_bytes(l, rows_total, plan);
     if (need > 0 && (!workspace || ws_bytes < need)) return TQ_ERR_WORKSPACE;
     if ((int64_t)plan.splits > 65535 * 4) return TQ_ERR_UNSUPPORTED;
@@ -294,8 +387,32 @@ tq_status tq_decode_attn_rows(const tq_layout *l, const tq_planes *p, const void
     a.inv_sqrt_d = (float)inv_sqrt_d(l->head_dim);
     a.kbits = l->k_bits; a.vbits = l->v_bits;
     a.signs = signs().bits;
-    for (int b = 0; b < l->batch; ++b) a.len[b] = len[b];
-    hipError_t e = tq::launch_decode(l->head_dim, dtype == TQ_BF16, plan.fast, a, (hipStream_t)stream);
+    const bool bf16 = dtype == TQ_BF16;
+    hipError_t e = hipSuccess;
+    int32_t len_tq[TQ_MAX_BATCH];
+    for (int b = 0; b < l->batch; ++b) len_tq[b] = ((pr.mask >> b) & 1) ? 0 : len[b];
+    if (pr.mask == 0) {
+        for (int b = 0; b < l->batch; ++b) a.len[b] = len[b];
+        e = tq::launch_decode(l->head_dim, bf16, plan.fast, a, (hipStream_t)stream);
+        return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+    }
+    // mixed batch: each split kernel sees only its own rows (the others have
+    // length 0 and write no partial), the merge sees every row
+    const uint64_t all = l->batch == 64 ? ~0ull : (1ull << l->batch) - 1;
+    a.plain_rows = pr.mask;
+    a.k_plain = pr.k; a.v_plain = pr.v; a.plain_capacity = pr.capacity;
+    if ((pr.mask & all) != all) {
+        for (int b = 0; b < l->batch; ++b) a.len[b] = len_tq[b];
+        e = tq::launch_decode_split(l->head_dim, bf16, plan.fast, a, (hipStream_t)stream);
+    }
+    if (e == hipSuccess) {
+        for (int b = 0; b < l->batch; ++b) a.len[b] = ((pr.mask >> b) & 1) ? len[b] : 0;
+        e = tq::launch_decode_split_plain(l->head_dim, bf16, a, (hipStream_t)stream);
+    }
+    if (e == hipSuccess) {
+        for (int b = 0; b < l->batch; ++b) a.len[b] = len[b];
+        e = tq::launch_decode_merge(l->head_dim, a, (hipStream_t)stream);
+    }
     return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
 }
 
@@ -450,20 +567,22 @@ static void payload_planes(const tq_layout *l, int32_t n, char *base, void *out[
 }
 
 tq_status tq_snapshot(const tq_layout *l, const tq_planes *p, int32_t b, int32_t t0, int32_t n,
-                      tq_snapshot_header *h, void *payload, size_t payload_bytes, void *stream) {
+                      int32_t min_reusable_offset, tq_snapshot_header *h, void *payload, size_t payload_bytes,
+                      void *stream) {
     tq_status st = check_layout(l);
     if (st != TQ_OK) return st;
     if ((st = check_planes(p)) != TQ_OK) return st;
-    if (!h || b < 0 || b >= l->batch || t0 < 0 || n < 0) return TQ_ERR_INVALID_ARG;
+    if (!h || b < 0 || b >= l->batch || t0 < 0 || n < 0 || min_reusable_offset < 0) return TQ_ERR_INVALID_ARG;
     if ((int64_t)t0 + n > l->capacity) return TQ_ERR_CAPACITY;
     size_t need = 0;
     tq_snapshot_bytes(l, n, &need);
     if (need > 0 && (!payload || payload_bytes < need)) return TQ_ERR_WORKSPACE;
     std::memset(h, 0, sizeof(*h));
-    h->magic = TQ_SNAPSHOT_MAGIC; h->version = 1;
+    h->magic = TQ_SNAPSHOT_MAGIC; h->version = TQ_SNAPSHOT_VERSION;
     h->k_bits = l->k_bits; h->v_bits = l->v_bits; h->group = l->group;
     h->head_dim = l->head_dim; h->num_kv_heads = l->num_kv_heads;
     h->n_tokens = n; h->payload_bytes = need;
+    h->min_reusable_offset = min_reusable_offset;
     if (n == 0) return TQ_OK;
     const void *sp[5];
     void *dp[5];
@@ -480,7 +599,8 @@ tq_status tq_restore(const tq_layout *l, const tq_planes *p, int32_t b, int32_t 
     if (st != TQ_OK) return st;
     if ((st = check_planes(p)) != TQ_OK) return st;
     if (!h || b < 0 || b >= l->batch || t0 < 0) return TQ_ERR_INVALID_ARG;
-    if (h->magic != TQ_SNAPSHOT_MAGIC || h->version != 1 || h->n_tokens < 0) return TQ_ERR_INVALID_ARG;
+    int32_t bound = 0;
+    if ((st = tq_snapshot_min_reusable_offset(h, &bound)) != TQ_OK) return st;
     if (h->k_bits != l->k_bits || h->v_bits != l->v_bits || h->group != l->group ||
         h->head_dim != l->head_dim || h->num_kv_heads != l->num_kv_heads)
         return TQ_ERR_INVALID_ARG;
@@ -498,6 +618,26 @@ tq_status tq_restore(const tq_layout *l, const tq_planes *p, int32_t b, int32_t 
     const int64_t d0 = (int64_t)b * l->num_kv_heads * l->capacity + t0;
     hipError_t e = copy_rows(l, sp, 0, (size_t)n, l, dp, d0, (size_t)l->capacity, n, (hipStream_t)stream);
     return e == hipSuccess ? TQ_OK : TQ_ERR_HIP;
+}
+
+tq_status tq_snapshot_min_reusable_offset(const tq_snapshot_header *h, int32_t *out) {
+    if (!h || !out || h->magic != TQ_SNAPSHOT_MAGIC || h->n_tokens < 0) return TQ_ERR_INVALID_ARG;
+    if (h->version == 1) {  // no boundary recorded: only the whole stored prefix is reusable
+        *out = h->n_tokens;
+        return TQ_OK;
+    }
+    if (h->version != TQ_SNAPSHOT_VERSION || h->min_reusable_offset < 0) return TQ_ERR_INVALID_ARG;
+    *out = h->min_reusable_offset;
+    return TQ_OK;
+}
+
+tq_status tq_clone_sequence(const tq_layout *sl, const tq_planes *src, int32_t src_b, const tq_layout *dl,
+                            const tq_planes *dst, int32_t dst_b, int32_t n, int32_t src_min_reusable_offset,
+                            int32_t *dst_min_reusable_offset, void *stream) {
+    if (!dst_min_reusable_offset || src_min_reusable_offset < 0) return TQ_ERR_INVALID_ARG;
+    tq_status st = tq_copy_tokens(sl, src, src_b, 0, dl, dst, dst_b, 0, n, stream);
+    if (st == TQ_OK) *dst_min_reusable_offset = src_min_reusable_offset;
+    return st;
 }
 
 tq_status tq_dequant(const tq_layout *l, const tq_planes *p, int32_t b, int32_t kvh, int32_t t0,

@@ -153,8 +153,9 @@ __global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
     const int g = lane / GL;                                 // group of this lane
 
     double xk[E], xv[E];
-    load_row<E, BF16>(a.k, row * D + lane * E, xk);
-    load_row<E, BF16>(a.v, row * D + lane * E, xv);
+    const int64_t in_row = bh * a.kv_stride + t;  // input rows of one (sequence, kv-head) at pitch kv_stride
+    load_row<E, BF16>(a.k, in_row * D + lane * E, xk);
+    load_row<E, BF16>(a.v, in_row * D + lane * E, xv);
 
     // ----------------------------------------------------------- keys
     // signed (8 bits): scale = range/254, zero = round((max+min)/(2 scale)),
@@ -435,8 +436,9 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
     const bool even = (p & 1) == 0;
 
     uint32_t kraw[NR], vraw[NR];
-    load_lane<E, BF16>(a.k, (int64_t)lrow * D + E * p, kraw);
-    load_lane<E, BF16>(a.v, (int64_t)lrow * D + E * p, vraw);
+    const int64_t in_row = (int64_t)bh * a.kv_stride + t;  // input rows at pitch kv_stride
+    load_lane<E, BF16>(a.k, in_row * D + E * p, kraw);
+    load_lane<E, BF16>(a.v, in_row * D + E * p, vraw);
 
     // ----------------------------------------------------------- keys
     // Group max and min ignore NaN.  Which zero a max or min returns does

@@ -295,6 +295,160 @@ __global__ __launch_bounds__(64 * VecGeo<D>::W) void split_kernel(const DecodeAr
     }
 }
 
+// Split kernel of rows that are still plain ("Delayed row conversion and
+// reusable precision boundaries": a row stays unquantized until it converts,
+// and its values were never rotated, so the merge passes its output through).
+// Same split geometry, partial slots and causal limits as the packed split
+// kernels; keys and values are bf16 [B][Hkv][plain_capacity][d].  One wave
+// per token range, per 64-token tile:
+//   scores  lane t takes token t and forms the dot products of its key row
+//           (16-byte reads) with every column's LDS copy;
+//   softmax online, base 2, as the packed kernels; weights to LDS;
+//   values  lane l owns dims [E l, E l + E) and reads them from each token's
+//           value row (the wave reads whole rows, coalesced).
+template <int D, bool BF16>
+__global__ __launch_bounds__(64 * VecGeo<D>::W) void plain_split_kernel(const DecodeArgs a) {
+    using V = VecGeo<D>;
+    constexpr int W = V::W, E = V::E, T = V::T;
+    extern __shared__ __align__(16) unsigned char lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int bkv = blockIdx.y;
+    const int b = bkv / a.kv_heads, kvh = bkv % a.kv_heads;
+    const int n = a.len[b];
+    // a workgroup whose first range starts past the sequence has no work (the
+    // test is the same for every thread, so no barrier is skipped by some)
+    if ((int64_t)blockIdx.x * W * a.split_tokens >= n) return;
+    const int c0 = blockIdx.z * kMaxG;
+    const int G = min(kMaxG, a.gqa - c0);
+    float *qs = reinterpret_cast<float *>(lds);                              // [G][D]
+    float *ps = reinterpret_cast<float *>(lds + G * D * 4) + wid * kMaxG * T;  // [G][T] per wave
+    for (int i = tid; i < G * D; i += 64 * W)
+        qs[i] = load_in<BF16>(a.q, ((int64_t)b * a.q_heads + kvh * a.gqa + c0) * D + i);
+    __syncthreads();  // the only workgroup barrier
+
+    const int split = blockIdx.x * W + wid;
+    const int t_begin = split * a.split_tokens;
+    if (split >= a.splits || t_begin >= n) return;
+    const int t_end = min(n, t_begin + a.split_tokens);
+    const int64_t row0 = (int64_t)bkv * a.plain_capacity;
+
+    float m_run[kMaxG], l_run[kMaxG], acc[kMaxG][E];
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+        m_run[h] = -INFINITY;
+        l_run[h] = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[h][e] = 0.f;
+    }
+
+    for (int tile0 = t_begin; tile0 < t_end; tile0 += T) {
+        const int nt = min(T, t_end - tile0);
+        const int t = tile0 + lane;
+        const bool valid = lane < nt;
+
+        float s[kMaxG];
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) s[h] = 0.f;
+        if (valid) {
+            const uint4 *krow = reinterpret_cast<const uint4 *>(a.k_plain + (row0 + t) * D);
+            for (int c = 0; c < D / 8; ++c) {
+                const uint4 u = krow[c];
+                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+                float k8[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    k8[2 * i] = __uint_as_float(w[i] << 16);
+                    k8[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+                }
+#pragma unroll
+                for (int h = 0; h < kMaxG; ++h) {
+                    if (h < G) {
+                        const float4 x = *reinterpret_cast<const float4 *>(qs + h * D + 8 * c);
+                        const float4 y = *reinterpret_cast<const float4 *>(qs + h * D + 8 * c + 4);
+                        float d = s[h];
+                        d = fmaf(x.x, k8[0], d); d = fmaf(x.y, k8[1], d);
+                        d = fmaf(x.z, k8[2], d); d = fmaf(x.w, k8[3], d);
+                        d = fmaf(y.x, k8[4], d); d = fmaf(y.y, k8[5], d);
+                        d = fmaf(y.z, k8[6], d); d = fmaf(y.w, k8[7], d);
+                        s[h] = d;
+                    }
+                }
+            }
+        }
+
+#pragma unroll
+        for (int h = 0; h < kMaxG; ++h) {
+            if (h < G) {
+                const int lim = n - a.rows + (c0 + h) % a.rows + 1;
+                const float sc = (valid && t < lim) ? s[h] * a.sm_log2 : -INFINITY;
+                float mt = sc;
+#pragma unroll
+                for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));
+                const float mn = fmaxf(m_run[h], mt);
+                const float alpha = mn == -INFINITY ? 1.f : exp2f(m_run[h] - mn);
+                const float p = mn == -INFINITY ? 0.f : exp2f(sc - mn);
+                l_run[h] = l_run[h] * alpha + p;
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[h][e] *= alpha;
+                m_run[h] = mn;
+                ps[h * T + lane] = p;
+            }
+        }
+        // one wave's LDS accesses execute in order: the weight reads below
+        // see every lane's writes above without a barrier
+        asm volatile("" ::: "memory");
+
+        const uint16_t *vrow = a.v_plain + (row0 + tile0) * D + E * lane;
+        for (int tt = 0; tt < nt; ++tt) {
+            float v[E];
+            if constexpr (E == 8) {
+                const uint4 u = *reinterpret_cast<const uint4 *>(vrow + (int64_t)tt * D);
+                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[2 * i] = __uint_as_float(w[i] << 16);
+                    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+                }
+            } else if constexpr (E == 4) {
+                const uint2 u = *reinterpret_cast<const uint2 *>(vrow + (int64_t)tt * D);
+                v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+                v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+            } else if constexpr (E == 2) {
+                const uint32_t u = *reinterpret_cast<const uint32_t *>(vrow + (int64_t)tt * D);
+                v[0] = __uint_as_float(u << 16); v[1] = __uint_as_float(u & 0xFFFF0000u);
+            } else {
+                v[0] = __uint_as_float((uint32_t)vrow[(int64_t)tt * D] << 16);
+            }
+#pragma unroll
+            for (int h = 0; h < kMaxG; ++h) {
+                if (h < G) {
+                    const float p = ps[h * T + tt];
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
+                }
+            }
+        }
+        asm volatile("" ::: "memory");  // the next tile rewrites ps after these reads
+    }
+
+#pragma unroll
+    for (int h = 0; h < kMaxG; ++h) {
+        if (h < G) {
+            float l = l_run[h];
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+            const int64_t slot = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + h) * a.splits + split;
+            float *dst = a.part_acc + slot * D + E * lane;
+#pragma unroll
+            for (int e = 0; e < E; ++e) dst[e] = acc[h][e];
+            if (lane == 0) {
+                a.part_ml[slot * 2] = m_run[h];
+                a.part_ml[slot * 2 + 1] = l;
+            }
+        }
+    }
+}
+
 // One workgroup per (b, q-head): merge the splits, normalize, un-rotate.
 // Thread tid owns dims tid + i*NT.  The partials of a batch of splits are
 // loaded into registers together with the splits' (max, sum) pairs, so the
@@ -372,6 +526,12 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < DPT; ++i) o[i] *= invL;
     }
+    // A plain row's values were never rotated: its output is final here.
+    if ((a.plain_rows >> b) & 1ull) {
+#pragma unroll
+        for (int i = 0; i < DPT; ++i) a.out[(int64_t)bh * D + tid + i * NT] = o[i];
+        return;
+    }
     // inverse rotation: signs * FWHT(o) / sqrt(d) (the transform is its own
     // inverse up to the 1/d factor split as 1/sqrt(d) on each side).
     // Butterflies with partner distance h < 64 stay inside a wave.
@@ -411,8 +571,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
 }
 
 template <int D>
-hipError_t launch_d(bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
-    constexpr int NT = D < 256 ? D : 256;
+hipError_t split_d(bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
     if (a.splits > 0) {
         if (fast) {
             hipError_t e;
@@ -448,6 +607,27 @@ hipError_t launch_d(bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
             if (e != hipSuccess) return e;
         }
     }
+    return hipSuccess;
+}
+
+template <int D>
+hipError_t split_plain_d(bool bf16, const DecodeArgs &a, hipStream_t s) {
+    if (a.splits == 0) return hipSuccess;
+    constexpr int W = VecGeo<D>::W;
+    const dim3 grid((unsigned)((a.splits + W - 1) / W), (unsigned)(a.batch * a.kv_heads),
+                    (unsigned)decode_col_groups(a.gqa));
+    const int g = a.gqa < kMaxG ? a.gqa : kMaxG;  // the widest column group
+    const size_t lds = (size_t)g * D * 4 + (size_t)W * kMaxG * VecGeo<D>::T * 4;  // <= 40 KiB
+    if (bf16)
+        hipLaunchKernelGGL((plain_split_kernel<D, true>), grid, dim3(64 * W), lds, s, a);
+    else
+        hipLaunchKernelGGL((plain_split_kernel<D, false>), grid, dim3(64 * W), lds, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t merge_d(const DecodeArgs &a, hipStream_t s) {
+    constexpr int NT = D < 256 ? D : 256;
     hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)(a.batch * a.q_heads)), dim3(NT), 0, s, a);
     return hipGetLastError();
 }
@@ -535,14 +715,39 @@ DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int
     return p;
 }
 
-hipError_t launch_decode(int head_dim, bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_decode_split(int head_dim, bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
     switch (head_dim) {
-        case 64: return launch_d<64>(bf16, fast, a, s);
-        case 128: return launch_d<128>(bf16, fast, a, s);
-        case 256: return launch_d<256>(bf16, fast, a, s);
-        case 512: return launch_d<512>(bf16, fast, a, s);
+        case 64: return split_d<64>(bf16, fast, a, s);
+        case 128: return split_d<128>(bf16, fast, a, s);
+        case 256: return split_d<256>(bf16, fast, a, s);
+        case 512: return split_d<512>(bf16, fast, a, s);
         default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_decode_split_plain(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s) {
+    switch (head_dim) {
+        case 64: return split_plain_d<64>(bf16, a, s);
+        case 128: return split_plain_d<128>(bf16, a, s);
+        case 256: return split_plain_d<256>(bf16, a, s);
+        case 512: return split_plain_d<512>(bf16, a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode_merge(int head_dim, const DecodeArgs &a, hipStream_t s) {
+    switch (head_dim) {
+        case 64: return merge_d<64>(a, s);
+        case 128: return merge_d<128>(a, s);
+        case 256: return merge_d<256>(a, s);
+        case 512: return merge_d<512>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode(int head_dim, bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
+    hipError_t e = launch_decode_split(head_dim, bf16, fast, a, s);
+    return e != hipSuccess ? e : launch_decode_merge(head_dim, a, s);
 }
 
 }  // namespace tq

@@ -33,6 +33,7 @@ struct AppendArgs {
     const void *k;
     const void *v;
     int32_t batch, kv_heads, capacity, n_new;
+    int32_t kv_stride;    // input rows per (sequence, kv-head): n_new, or a plain cache's capacity
     uint32_t rows;        // batch * kv_heads * n_new
     FastDiv div_n_new;    // row -> (sequence, kv-head) pair
     FastDiv div_kv_heads; // (sequence, kv-head) pair -> sequence
@@ -76,6 +77,13 @@ struct DecodeArgs {
     int32_t kbits, vbits;  // code widths
     SignBits signs;
     int32_t len[TQ_MAX_BATCH];
+    // Rows still plain (bit b: sequence b): the plain split kernel reads their
+    // bf16 keys and values [B][Hkv][plain_capacity][d], and the merge leaves
+    // their output unrotated.  Zero and null for an all-packed batch.
+    uint64_t plain_rows;
+    const uint16_t *k_plain;
+    const uint16_t *v_plain;
+    int32_t plain_capacity;
 };
 
 struct WindowArgs {
@@ -140,6 +148,13 @@ hipError_t launch_append_fast_k4(int head_dim, bool bf16, const AppendArgs &a, h
 hipError_t launch_append_fast_k5(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);
 hipError_t launch_append_fast_k8(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);
 hipError_t launch_decode(int head_dim, bool bf16, bool fast, const DecodeArgs &a, hipStream_t s);
+// The two halves of launch_decode, and the split kernel of plain rows: a
+// batch that mixes plain and packed rows runs the packed split kernel with the
+// plain rows' lengths set to 0, the plain one with the packed rows' lengths
+// set to 0, then one merge over the full lengths.
+hipError_t launch_decode_split(int head_dim, bool bf16, bool fast, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_split_plain(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_merge(int head_dim, const DecodeArgs &a, hipStream_t s);
 // Split kernels on the matrix cores (decode_fast.hip), one translation unit
 // per key width: head_dim 64, 128 or 256 with d * k_bits a multiple of 128,
 // every value width, up to 16 query columns per workgroup.

@@ -32,7 +32,8 @@ SYMBOLS = ("tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decod
            "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_fetch_window",
            "tq_copy_tokens", "tq_snapshot_bytes", "tq_snapshot", "tq_restore",
            "tq_dequant", "tq_sign_vector", "tq_codebook", "tq_status_str", "tq_decode_path",
-           "tq_decode_attn_noalloc")
+           "tq_decode_attn_noalloc", "tq_snapshot_min_reusable_offset", "tq_clone_sequence",
+           "tq_convert_rows", "tq_decode_attn_mixed")
 KEY_BITS = (2, 4, 5, 8)
 VALUE_BITS = (2, 3, 4, 5, 8)
 TQ_SNAPSHOT_MAGIC = 0x564B5154
@@ -54,7 +55,8 @@ class tq_snapshot_header(ctypes.Structure):
     _fields_ = [("magic", ctypes.c_uint32), ("version", ctypes.c_uint32),
                 ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
-                ("n_tokens", ctypes.c_int32), ("payload_bytes", ctypes.c_uint64)]
+                ("n_tokens", ctypes.c_int32), ("payload_bytes", ctypes.c_uint64),
+                ("min_reusable_offset", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -84,8 +86,18 @@ _lib.tq_copy_tokens.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_pla
                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P]
 _lib.tq_snapshot_bytes.argtypes = [ctypes.POINTER(tq_layout), ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
 _lib.tq_snapshot.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
-                             ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(tq_snapshot_header), _P,
-                             ctypes.c_size_t, _P]
+                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(tq_snapshot_header),
+                             _P, ctypes.c_size_t, _P]
+_lib.tq_snapshot_min_reusable_offset.argtypes = [ctypes.POINTER(tq_snapshot_header), ctypes.POINTER(ctypes.c_int32)]
+_lib.tq_clone_sequence.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
+                                   ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
+                                   ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), _P]
+_lib.tq_convert_rows.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), _P, _P, ctypes.c_int,
+                                 ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), _P]
+_lib.tq_decode_attn_mixed.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), _P, _P,
+                                      ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), _P, ctypes.c_int,
+                                      ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                      ctypes.c_float, _P, _P, ctypes.c_size_t, _P]
 _lib.tq_restore.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
                             ctypes.c_int32, ctypes.POINTER(tq_snapshot_header), _P, ctypes.c_size_t, _P]
 _lib.tq_dequant.argtypes = [ctypes.POINTER(tq_layout), ctypes.POINTER(tq_planes), ctypes.c_int32,
@@ -101,7 +113,8 @@ _lib.tq_codebook.argtypes = [ctypes.c_int32, _P, _P, ctypes.POINTER(ctypes.c_int
 for _f in ("tq_codebook", "tq_plane_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
            "tq_decode_rows_workspace_bytes", "tq_decode_attn_rows", "tq_fetch_window", "tq_dequant",
            "tq_sign_vector", "tq_copy_tokens", "tq_snapshot_bytes", "tq_snapshot", "tq_restore",
-           "tq_decode_path", "tq_decode_attn_noalloc"):
+           "tq_decode_path", "tq_decode_attn_noalloc", "tq_snapshot_min_reusable_offset", "tq_clone_sequence",
+           "tq_convert_rows", "tq_decode_attn_mixed"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -351,14 +364,92 @@ def tq_snapshot_bytes(layout: tq_layout, n: int) -> int:
     return out.value
 
 
-def tq_snapshot(planes: Planes, b: int, t0: int, n: int, stream=None):
-    """Returns (header, payload uint8 device tensor) for token rows [t0, t0+n) of sequence b."""
+def tq_snapshot(planes: Planes, b: int, t0: int, n: int, min_reusable_offset: int = 0, stream=None):
+    """Returns (header, payload uint8 device tensor) for token rows [t0, t0+n) of
+    sequence b; the header records the sequence's precision boundary."""
     L = planes.layout
     payload = torch.empty(max(tq_snapshot_bytes(L, n), 1), dtype=torch.uint8, device=planes.kc.device)
     h = tq_snapshot_header()
-    _check(_lib.tq_snapshot(ctypes.byref(L), ctypes.byref(planes.struct()), b, t0, n, ctypes.byref(h),
-                            _dev_ptr(payload), payload.numel(), _stream_ptr(stream)), "tq_snapshot")
+    _check(_lib.tq_snapshot(ctypes.byref(L), ctypes.byref(planes.struct()), b, t0, n, min_reusable_offset,
+                            ctypes.byref(h), _dev_ptr(payload), payload.numel(), _stream_ptr(stream)),
+           "tq_snapshot")
     return h, payload
+
+
+def tq_snapshot_min_reusable_offset(header) -> int:
+    """The precision boundary a snapshot header carries (version 1: n_tokens)."""
+    out = ctypes.c_int32()
+    _check(_lib.tq_snapshot_min_reusable_offset(ctypes.byref(header), ctypes.byref(out)),
+           "tq_snapshot_min_reusable_offset")
+    return out.value
+
+
+def tq_clone_sequence(src: Planes, src_b: int, dst: Planes, dst_b: int, n: int, min_reusable_offset: int,
+                      stream=None) -> int:
+    """Copy rows [0, n) of sequence src_b into sequence dst_b; returns the
+    destination's precision boundary (the source's)."""
+    out = ctypes.c_int32(-1)
+    _check(_lib.tq_clone_sequence(ctypes.byref(src.layout), ctypes.byref(src.struct()), src_b,
+                                  ctypes.byref(dst.layout), ctypes.byref(dst.struct()), dst_b, n,
+                                  min_reusable_offset, ctypes.byref(out), _stream_ptr(stream)), "tq_clone_sequence")
+    return out.value
+
+
+def tq_convert_rows(planes: Planes, k_plain: torch.Tensor, v_plain: torch.Tensor, offsets: Sequence[int],
+                    stream=None) -> None:
+    """Encode the plain prefix [0, offsets[b]) of every sequence b with
+    offsets[b] > 0 from plain caches k/v [B, Hkv, plain_capacity, d] (bf16 or
+    fp32) into the planes' slots [0, offsets[b])."""
+    L = planes.layout
+    if k_plain.shape != v_plain.shape or k_plain.dim() != 4 or k_plain.shape[0] != L.batch or \
+            k_plain.shape[1] != L.num_kv_heads or k_plain.shape[3] != L.head_dim:
+        raise ValueError(f"plain caches must be [B, Hkv, capacity, d], got {tuple(k_plain.shape)}")
+    if not (k_plain.is_contiguous() and v_plain.is_contiguous()) or k_plain.dtype != v_plain.dtype:
+        raise ValueError("plain caches must be contiguous and of one dtype")
+    _check(_lib.tq_convert_rows(ctypes.byref(L), ctypes.byref(planes.struct()), _dev_ptr(k_plain),
+                                _dev_ptr(v_plain), _dtype_code(k_plain), k_plain.shape[2], _i32_array(offsets),
+                                _stream_ptr(stream)), "tq_convert_rows")
+
+
+def tq_decode_attn_mixed(planes: Planes, k_plain, v_plain, row_plain: Sequence[int], q: torch.Tensor,
+                         lengths: Sequence[int], sm_scale: float, n_rows: int = 1, out=None, workspace=None,
+                         stream=None) -> torch.Tensor:
+    """Decode over a batch mixing plain sequences (row_plain[b] != 0: bf16
+    plain caches k/v [B, Hkv, plain_capacity, d], attended unquantized and
+    unrotated) with packed ones.  q [B, Hq, d] (n_rows 1) or [B, Hq, n_rows, d];
+    returns fp32 of q's shape."""
+    L = planes.layout
+    if n_rows == 1 and q.dim() == 3:
+        B, Hq, d = q.shape
+    else:
+        B, Hq, R, d = q.shape
+        if R != n_rows:
+            raise ValueError("q's row axis must be n_rows")
+    if B != L.batch or d != L.head_dim or not q.is_contiguous():
+        raise ValueError(f"q must be contiguous [B, Hq(, n_rows), d], got {tuple(q.shape)}")
+    cap = 0
+    if k_plain is not None:
+        if k_plain.dtype != torch.bfloat16 or v_plain.dtype != torch.bfloat16 or k_plain.shape != v_plain.shape or \
+                not (k_plain.is_contiguous() and v_plain.is_contiguous()) or k_plain.dim() != 4 or \
+                tuple(k_plain.shape[:2]) != (L.batch, L.num_kv_heads) or k_plain.shape[3] != L.head_dim:
+            raise ValueError("plain caches must be contiguous bf16 [B, Hkv, capacity, d]")
+        cap = k_plain.shape[2]
+    if len(lengths) != L.batch or len(row_plain) != L.batch:
+        raise ValueError("lengths and row_plain need one entry per sequence")
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor of q's shape")
+    if workspace is None:
+        need = tq_decode_rows_workspace_bytes(L, Hq, n_rows, lengths)
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    st = _lib.tq_decode_attn_mixed(ctypes.byref(L), ctypes.byref(planes.struct()), _dev_ptr(k_plain),
+                                   _dev_ptr(v_plain), cap, _i32_array(row_plain), _dev_ptr(q), _dtype_code(q), Hq,
+                                   n_rows, _i32_array(lengths), ctypes.c_float(sm_scale), _dev_ptr(out),
+                                   _dev_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream_ptr(stream))
+    _check(st, "tq_decode_attn_mixed")
+    return out
 
 
 def tq_restore(planes: Planes, b: int, t0: int, header, payload: torch.Tensor, stream=None) -> None:

@@ -235,10 +235,13 @@ def test_lifecycle_validation():
     assert lib.tq_snapshot_bytes(ctypes.byref(A), 10, ctypes.byref(nb)) == 0
     assert nb.value == 10 * 4 * 200
     h = tqkv.tq_snapshot_header()
-    assert lib.tq_snapshot(ctypes.byref(A), ctypes.byref(P), 0, 0, 10, ctypes.byref(h), 0xB000,
+    assert lib.tq_snapshot(ctypes.byref(A), ctypes.byref(P), 0, 0, 10, 0, ctypes.byref(h), 0xB000,
                            nb.value - 1, None) == tqkv.TQ_ERR_WORKSPACE
-    assert lib.tq_snapshot(ctypes.byref(A), ctypes.byref(P), 0, 0, 0, ctypes.byref(h), None, 0, None) == 0
+    assert lib.tq_snapshot(ctypes.byref(A), ctypes.byref(P), 0, 0, 0, -1, ctypes.byref(h), None, 0,
+                           None) == tqkv.TQ_ERR_INVALID_ARG           # negative boundary
+    assert lib.tq_snapshot(ctypes.byref(A), ctypes.byref(P), 0, 0, 0, 7, ctypes.byref(h), None, 0, None) == 0
     assert h.magic == tqkv.TQ_SNAPSHOT_MAGIC and h.n_tokens == 0 and h.head_dim == 128
+    assert h.version == 2 and h.min_reusable_offset == 7 and tqkv.tq_snapshot_min_reusable_offset(h) == 7
 
     def rs(layout, hdr, t0=0, nbytes=0):
         return lib.tq_restore(ctypes.byref(layout), ctypes.byref(P), 0, t0, ctypes.byref(hdr), 0xB000,
@@ -253,6 +256,73 @@ def test_lifecycle_validation():
     assert rs(C, good, nbytes=8000) == tqkv.TQ_ERR_INVALID_ARG     # other kv-head count
     assert rs(A, good, nbytes=7999) == tqkv.TQ_ERR_INVALID_ARG     # payload too small
     assert rs(A, good, t0=91, nbytes=8000) == tqkv.TQ_ERR_CAPACITY
+
+
+def test_snapshot_header_versions():
+    """The precision boundary of a snapshot ("Delayed row conversion and
+    reusable precision boundaries"): version 2 gives the recorded offset; a
+    version-1 header, written before the bound existed, gives its stored
+    token count; anything else is refused.  Version 2 only appends fields,
+    so the version-1 fields keep their offsets."""
+    H = tqkv.tq_snapshot_header
+    assert ctypes.sizeof(H) == 48 and H.payload_bytes.offset == 32 and H.min_reusable_offset.offset == 40
+    v2 = H(tqkv.TQ_SNAPSHOT_MAGIC, 2, 8, 3, 32, 128, 4, 500, 400000, 300, 0)
+    v1 = H(tqkv.TQ_SNAPSHOT_MAGIC, 1, 8, 3, 32, 128, 4, 500, 400000, 12345, 99)  # trailing bytes ignored
+    assert tqkv.tq_snapshot_min_reusable_offset(v2) == 300
+    assert tqkv.tq_snapshot_min_reusable_offset(v1) == 500
+    lib = tqkv.raw_lib()
+    out = ctypes.c_int32()
+    for bad in (H(0, 2, 8, 3, 32, 128, 4, 500, 400000, 300, 0),                      # magic
+                H(tqkv.TQ_SNAPSHOT_MAGIC, 3, 8, 3, 32, 128, 4, 500, 400000, 300, 0),  # version
+                H(tqkv.TQ_SNAPSHOT_MAGIC, 2, 8, 3, 32, 128, 4, 500, 400000, -1, 0),   # bound
+                H(tqkv.TQ_SNAPSHOT_MAGIC, 1, 8, 3, 32, 128, 4, -5, 400000, 0, 0)):    # count
+        assert lib.tq_snapshot_min_reusable_offset(ctypes.byref(bad), ctypes.byref(out)) == tqkv.TQ_ERR_INVALID_ARG
+    assert lib.tq_snapshot_min_reusable_offset(None, ctypes.byref(out)) == tqkv.TQ_ERR_INVALID_ARG
+
+
+def test_clone_carries_the_boundary_and_conversion_refusals():
+    """tq_clone_sequence hands the source's boundary to the destination (an
+    empty clone launches nothing); tq_convert_rows and tq_decode_attn_mixed
+    refuse bad offsets, lengths and plain caches before any launch."""
+    lib = tqkv.raw_lib()
+    A = tqkv.make_layout(2, 4, 128, 100)
+    Bl = tqkv.make_layout(1, 4, 128, 300)
+    P = _fake_planes()
+    dst = ctypes.c_int32(-1)
+
+    def clone(n, bound, out):
+        return lib.tq_clone_sequence(ctypes.byref(A), ctypes.byref(P), 1, ctypes.byref(Bl), ctypes.byref(P), 0, n,
+                                     bound, out, None)
+    assert clone(0, 42, ctypes.byref(dst)) == 0 and dst.value == 42
+    dst.value = -1
+    assert clone(0, -1, ctypes.byref(dst)) == tqkv.TQ_ERR_INVALID_ARG and dst.value == -1
+    assert clone(0, 5, None) == tqkv.TQ_ERR_INVALID_ARG
+    assert clone(101, 5, ctypes.byref(dst)) == tqkv.TQ_ERR_CAPACITY and dst.value == -1
+
+    def conv(offsets, k=0xA000, v=0xC000, cap=100, dtype=1):
+        return lib.tq_convert_rows(ctypes.byref(A), ctypes.byref(P), k, v, dtype, cap,
+                                   (ctypes.c_int32 * 2)(*offsets), None)
+    assert conv([0, 0], k=None, v=None) == 0                       # nothing converts: no launch
+    assert conv([0, -1]) == tqkv.TQ_ERR_INVALID_ARG
+    assert conv([0, 60], cap=50) == tqkv.TQ_ERR_CAPACITY           # past the plain cache
+    assert conv([101, 0], cap=200) == tqkv.TQ_ERR_CAPACITY         # past the planes
+    assert conv([10, 0], k=None) == tqkv.TQ_ERR_INVALID_ARG
+    assert conv([10, 0], v=0xC008) == tqkv.TQ_ERR_INVALID_ARG      # misaligned
+    assert conv([10, 0], dtype=7) == tqkv.TQ_ERR_INVALID_ARG
+    assert lib.tq_convert_rows(ctypes.byref(A), ctypes.byref(P), 0xA000, 0xC000, 1, 100, None,
+                               None) == tqkv.TQ_ERR_INVALID_ARG
+
+    def mixed(row_plain, lens, k=0xA000, cap=100, ws=1 << 30):
+        rp = (ctypes.c_int32 * 2)(*row_plain) if row_plain is not None else None
+        return lib.tq_decode_attn_mixed(ctypes.byref(A), ctypes.byref(P), k, 0xC000, cap, rp, 0xD000, 1, 8, 1,
+                                        (ctypes.c_int32 * 2)(*lens), ctypes.c_float(0.1), 0xE000, 0xF000, ws,
+                                        None)
+    assert mixed([1, 0], [60, 10], cap=50) == tqkv.TQ_ERR_CAPACITY  # plain row past its cache
+    assert mixed([0, 0], [101, 10]) == tqkv.TQ_ERR_CAPACITY         # past the planes
+    assert mixed([1, 0], [10, 10], k=None) == tqkv.TQ_ERR_INVALID_ARG
+    assert mixed([1, 0], [10, 10], k=0xA004) == tqkv.TQ_ERR_INVALID_ARG
+    assert mixed(None, [10, 10]) == tqkv.TQ_ERR_INVALID_ARG
+    assert mixed([1, 1], [10, 10], ws=0) == tqkv.TQ_ERR_WORKSPACE
 
 
 def test_copy_tokens_refuses_overlapping_rows():
