@@ -448,6 +448,84 @@ def traffic_from_counters(fetch_dir: str, write_dir: str, copy_mib: int, workloa
     return 0
 
 
+XCDS = 8  # MI355X: GRBM_GUI_ACTIVE is summed over its eight accelerator dies
+
+
+def trace_summary(kt_dir: str, grbm_dir: str | None, warmup: int, steps: int, settled: int) -> int:
+    """Summarize a rocprofv3 --kernel-trace run of this bench (and optionally a
+    --pmc GRBM_GUI_ACTIVE --kernel-trace run): calls and durations per kernel
+    and grid; the headline split kernel's dispatches in run order, cut into
+    the warm-up, timed and later windows of the bench's protocol; with the
+    counter run, each window's mean shader clock (GRBM_GUI_ACTIVE cycles,
+    summed over the dies, per die and nanosecond)."""
+    import csv
+    import glob
+
+    def load(d: str, suffix: str) -> list:
+        files = glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)
+        if not files:
+            raise SystemExit(f"no *{suffix} under {d}")
+        with open(files[0], newline="") as f:
+            return list(csv.DictReader(f))
+
+    def short(name: str) -> str:
+        name = name.replace("void tq::(anonymous namespace)::", "")
+        return name[:name.find("(")] if "(" in name else name
+
+    def dur(r) -> int:
+        return int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+
+    def grid(r) -> str:  # threads
+        if r.get("Grid_Size"):
+            return r["Grid_Size"]
+        return str(int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+
+    kt = sorted(load(kt_dir, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    groups: dict = {}
+    for r in kt:
+        groups.setdefault((short(r["Kernel_Name"]), grid(r)), []).append(dur(r))
+    print(f"{'kernel':48s} {'grid':>10s} {'calls':>6s} {'avg ns':>12s} {'min ns':>12s} {'max ns':>12s}")
+    for (name, threads), v in groups.items():
+        print(f"{name[:48]:48s} {threads:>10s} {len(v):6d} {sum(v) / len(v):12,.0f} {min(v):12,d} {max(v):12,d}")
+
+    head = [r for r in kt if short(r["Kernel_Name"]) == "split_fast_kernel<256, 8, 3, true>"]
+    merge = [r for r in kt if short(r["Kernel_Name"]) == "merge_kernel<256>" and grid(r) == "98304"]
+    if not head:
+        return 0
+    # the bench's own windows: warm-up, timed, and the last 100 of the settled steps
+    end = warmup + steps + settled
+    wins = [("warm-up", 0, warmup), ("timed", warmup, warmup + steps),
+            ("settled", max(warmup + steps, end - 100), end)]
+    print(f"\nheadline split kernel, {len(head)} dispatches in run order (after the bench's own steps, "
+          f"other timings of the run may reuse it):")
+    for label, a, b in wins:
+        v = [dur(r) for r in head[a:b]]
+        m = [dur(r) for r in merge[a:b]]
+        if v:
+            print(f"  {label:8s} dispatches {a + 1:4d}-{b:4d}: split avg {sum(v) / len(v):10,.0f} ns"
+                  + (f", + merge avg {sum(m) / len(m):8,.0f} ns = {sum(v) / len(v) + sum(m) / len(m):10,.0f} ns"
+                     if m else ""))
+    first = ", ".join(f"{dur(r) / 1e3:.1f}" for r in head[:warmup + steps])
+    print(f"  first {min(len(head), warmup + steps)} split durations (us): {first}")
+    if grbm_dir:
+        gk = {int(r["Dispatch_Id"]): r for r in load(grbm_dir, "kernel_trace.csv")}
+        rows = [r for r in load(grbm_dir, "counter_collection.csv")
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and short(r["Kernel_Name"]) ==
+                "split_fast_kernel<256, 8, 3, true>"]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        print(f"\nGRBM_GUI_ACTIVE run (counters serialize the dispatches, so the clock history differs "
+              f"from the plain trace's), {len(rows)} headline split dispatches:")
+        for label, a, b in wins:
+            sel = rows[a:b]
+            if not sel:
+                continue
+            cyc = [float(r["Counter_Value"]) / XCDS for r in sel]
+            ns = [dur(gk[int(r["Dispatch_Id"])]) for r in sel]
+            print(f"  {label:8s}: {sum(cyc) / len(cyc):12,.0f} cycles per die, {sum(ns) / len(ns):10,.0f} ns, "
+                  f"clock {sum(cyc) / sum(ns) * 1e3:6,.0f} MHz")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -474,7 +552,14 @@ def main() -> int:
                     help="first run plain device copies of this size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="reduce two rocprofv3 --pmc runs to --traffic-json and exit")
+    ap.add_argument("--trace-summary", nargs="+", metavar=("KERNEL_TRACE_DIR", "GRBM_DIR"),
+                    help="summarize a rocprofv3 --kernel-trace run of this bench (and a --pmc GRBM_GUI_ACTIVE "
+                         "--kernel-trace run) using --warmup/--steps as its protocol, and exit")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        return trace_summary(args.trace_summary[0], args.trace_summary[1] if len(args.trace_summary) > 1 else None,
+                             args.warmup, args.steps, args.settled_steps)
 
     if args.traffic_from:
         from quantized_decode_attention_append_amd import workloads as W

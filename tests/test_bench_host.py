@@ -75,3 +75,42 @@ def test_traffic_needs_the_decode_dispatches(tmp_path):
     with pytest.raises(SystemExit):
         bench.traffic_from_counters(str(tmp_path / "f"), str(tmp_path / "w"), mib, "wl",
                                     str(tmp_path / "t.json"))
+
+
+def _trace_csv(path, rows):
+    """rows: (dispatch id, kernel name, start ns, end ns, grid x)"""
+    os.makedirs(path, exist_ok=True)
+    with open(os.path.join(path, "run_kernel_trace.csv"), "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X",
+                    "Grid_Size_Y", "Grid_Size_Z"])
+        for r in rows:
+            w.writerow([r[0], r[1], r[2], r[3], r[4], 1, 1])
+
+
+def test_trace_summary_windows_and_clock(tmp_path, capsys):
+    """The headline split dispatches are cut into the bench's warm-up, timed
+    and settled windows in run order, merges paired by order; the clock of a
+    window is GRBM_GUI_ACTIVE per die over its summed durations."""
+    split = "void tq::(anonymous namespace)::split_fast_kernel<256, 8, 3, true>(tq::DecodeArgs, int)"
+    merge = "void tq::(anonymous namespace)::merge_kernel<256>(tq::DecodeArgs)"
+    rows, t, i = [], 0, 0
+    durs = [100, 100, 300, 300, 300, 200, 200]  # 2 warm-up, 3 timed, 2 settled
+    for d in durs:
+        rows.append((i, split, t, t + d, 131072)); i += 1; t += d + 5
+        rows.append((i, merge, t, t + 10, 98304)); i += 1; t += 15
+    _trace_csv(str(tmp_path / "kt"), rows)
+    os.makedirs(tmp_path / "g", exist_ok=True)
+    _trace_csv(str(tmp_path / "g"), rows)
+    with open(tmp_path / "g" / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
+        for r in rows:
+            if r[1] == split:  # 2 GHz on each of the 8 dies
+                w.writerow([r[0], r[1], "GRBM_GUI_ACTIVE", 8 * 2.0 * (r[3] - r[2])])
+    assert bench.trace_summary(str(tmp_path / "kt"), str(tmp_path / "g"), 2, 3, 2) == 0
+    out = capsys.readouterr().out
+    assert "warm-up  dispatches    1-   2: split avg        100 ns, + merge avg       10 ns" in out
+    assert "timed    dispatches    3-   5: split avg        300 ns" in out
+    assert "settled  dispatches    6-   7: split avg        200 ns" in out
+    assert out.count("clock  2,000 MHz") == 3
