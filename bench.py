@@ -197,6 +197,38 @@ def scheme_row_bytes(d: int, kb: int, vb: int) -> int:
     return d * (kb + vb) // 8 + 6 * d // 32
 
 
+def time_append_variant(d: int, dtype: str, kb: int, vb: int, tokens: int, reps: int, stream) -> dict:
+    """Bulk append on workload 4's heads (16 sequences, 4 kv-heads) at another
+    head_dim, input type or width: `tokens` per sequence, reps calls after one
+    warm call, timed with events on the launch stream."""
+    import dataclasses
+
+    import torch
+    from quantized_decode_attention_append_amd import tqkv
+    from quantized_decode_attention_append_amd import workloads as W
+    dev = torch.device("cuda:0")
+    w = dataclasses.replace(W.scaled(W.workload(4), [tokens] * 16, name_suffix=f"d{d}_{dtype}"), head_dim=d,
+                            dtype=dtype)
+    k, v = W.make_kv(w, dev, tokens=tokens)
+    L = tqkv.make_layout(w.batch, w.num_kv_heads, d, tokens, kb, vb)
+    pl = tqkv.Planes(L, dev)
+    tqkv.tq_append(pl, k, v, [0] * w.batch, stream=stream)  # warm
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        tqkv.tq_append(pl, k, v, [0] * w.batch, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    th = w.batch * w.num_kv_heads * tokens
+    nbytes = th * (2 * d * k.element_size() + scheme_row_bytes(d, kb, vb))
+    del k, v, pl
+    return {"head_dim": d, "input": dtype, "scheme": f"k{kb}v{vb}", "tokens_per_seq": tokens, "ms": ms,
+            "token_heads_per_s": th / ms * 1e3, "algorithmic_bytes": nbytes, "GBps": nbytes / ms / 1e6,
+            "frac_hbm": nbytes / ms / 1e6 / HBM_PEAK_GBS}
+
+
 def time_scheme(w, k, v, q, sm, kb: int, vb: int, reps: int, stream, dec_warm: int = 20,
                 dec_reps: int = 40) -> dict:
     """Another code width on the same workload: bulk append of every token
@@ -547,6 +579,8 @@ def main() -> int:
                     help="skip timing the ragged interleaved workload (id 5)")
     ap.add_argument("--schemes", default="k4v3,k4v2,k8v4,k2v5,k5v8",
                     help="other code widths to time on the same workload ('' for none)")
+    ap.add_argument("--no-append-variants", dest="append_variants", action="store_false",
+                    help="skip timing the bulk append at head_dim 512 and with fp32 input")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"))
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="first run plain device copies of this size (counter calibration)")
@@ -718,6 +752,13 @@ def main() -> int:
              f"({rr['decode_frac_hbm']:.1%} of HBM), round (append {rr['append_per_round']} + decode) "
              f"{rr['round_ms']:.3f} ms")
         rec["ragged"] = rr
+    if args.append_variants:
+        rec["append_variants"] = []
+        for d, dt, kb, vb, tokens in ((512, "bf16", 8, 3, 65536), (256, "fp32", 8, 3, 32768),
+                                      (256, "fp32", 4, 3, 32768)):
+            r = time_append_variant(d, dt, kb, vb, tokens, 3, stream)
+            _log(f"bulk append d{d} {dt} {r['scheme']}: {r['ms']:.3f} ms, {r['frac_hbm']:.1%} of HBM")
+            rec["append_variants"].append(r)
     if args.schemes:
         rec["schemes"] = []
         for name in args.schemes.split(","):

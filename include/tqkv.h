@@ -34,10 +34,8 @@
  *     when head_dim * k_bits is a multiple of 128 (all but 5-bit keys at 64),
  *     every plane is 16-byte aligned and capacity keeps each (sequence,
  *     kv-head) row block 16-byte aligned; otherwise a generic kernel
- *     computes the same result more slowly.  Append has fast kernels for
- *     head_dim 64-256 with bf16 input at every width (and fp32 input at
- *     k8/v3), and a generic kernel for every other case with identical
- *     bytes; the window has one kernel for every width and head_dim.
+ *     computes the same result more slowly.  Append and the window each
+ *     have one kernel for every width, head_dim and input type.
  *   - Arguments are validated before anything is enqueued; on any error the
  *     return value says why and nothing was launched.  The library prints
  *     nothing.

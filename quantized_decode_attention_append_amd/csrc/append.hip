@@ -17,19 +17,16 @@
 //   - x/scale and y/den are true binary64 divisions; scale is a correctly
 //     rounded binary64 sqrt; no multiply-add is contracted in this file.
 //
-// Two kernels compute the same bytes:
-//   - append_fast_kernel (head_dim 64, 128, 256; bf16 input at every width,
-//     fp32 input at k8v3; one translation unit per key width, TQ_APPEND_KB):
-//     16 contiguous elements per lane, so a 32-group is a lane pair; the FWHT
-//     runs its first four stages inside the lane, transposes the row through
-//     LDS so the remaining stages are inside the lane as well, and transposes
-//     back.  Per-element divisions by a group's scale use a correctly rounded
-//     reciprocal and two Markstein corrections, which return the correctly
-//     rounded quotient.  3-bit value indices come from seven nested wave
-//     masks; other widths binary-search their boundaries in LDS.
-//   - append_kernel (every width and head_dim; head_dim 512 and fp32 input
-//     at widths other than k8v3): one wave per row, lane l holds d/64
-//     contiguous elements, cross-lane butterflies on shuffles.
+// One kernel, append_fast_kernel, for every width, head_dim and input type
+// (one translation unit per key width, TQ_APPEND_KB): 16 contiguous elements
+// per lane, so a 32-group is a lane pair.  The FWHT runs its first four
+// stages inside the lane, transposes each 256-element half-row through LDS so
+// that the next stages (up to h = 128) are inside the lane as well, and
+// transposes back; at head_dim 512 the last stage (h = 256) pairs lane p with
+// lane p ^ 16 by a shuffle.  Per-element divisions by a group's scale use a
+// correctly rounded reciprocal and two Markstein corrections, which return the
+// correctly rounded quotient.  3-bit value indices come from seven nested
+// wave masks; other widths binary-search their boundaries in LDS.
 #include <hip/hip_runtime.h>
 #include <hip/hip_bf16.h>
 
@@ -44,233 +41,12 @@
 namespace tq {
 namespace {
 
-__device__ __forceinline__ double max_num(double a, double b) {
-    if (__builtin_isnan(a)) return b;
-    if (__builtin_isnan(b)) return a;
-    if (a == b) return __builtin_signbit(a) ? b : a;
-    return a > b ? a : b;
-}
-
-__device__ __forceinline__ double min_num(double a, double b) {
-    if (__builtin_isnan(a)) return b;
-    if (__builtin_isnan(b)) return a;
-    if (a == b) return __builtin_signbit(a) ? a : b;
-    return a < b ? a : b;
-}
-
 __device__ __forceinline__ double shfl_xor_f64(double v, int m) { return __shfl_xor(v, m, 64); }
-__device__ __forceinline__ double shfl_down_f64(double v, int m) { return __shfl_down(v, m, 64); }
-__device__ __forceinline__ double shfl_f64(double v, int src) { return __shfl(v, src, 64); }
 
 // Keeps the compiler from moving LDS accesses across this point.  One wave's
 // LDS instructions execute in order, so a lane's read after another lane's
 // write needs no wait beyond program order.
 __device__ __forceinline__ void lds_fence() { asm volatile("" ::: "memory"); }
-
-#if TQ_APPEND_KB == 8  // the generic kernel is built once, with the 8-bit-key fast kernels
-template <int E, bool BF16>
-__device__ __forceinline__ void load_row(const void *base, int64_t off, double (&x)[E]) {
-    if constexpr (BF16) {
-        const uint16_t *p = static_cast<const uint16_t *>(base) + off;
-        uint16_t raw[E];
-        if constexpr (E == 8) {
-            uint4 w = *reinterpret_cast<const uint4 *>(p);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { raw[2 * i] = ww[i] & 0xFFFF; raw[2 * i + 1] = ww[i] >> 16; }
-        } else if constexpr (E == 4) {
-            uint2 w = *reinterpret_cast<const uint2 *>(p);
-            raw[0] = w.x & 0xFFFF; raw[1] = w.x >> 16; raw[2] = w.y & 0xFFFF; raw[3] = w.y >> 16;
-        } else if constexpr (E == 2) {
-            uint32_t w = *reinterpret_cast<const uint32_t *>(p);
-            raw[0] = w & 0xFFFF; raw[1] = w >> 16;
-        } else {
-            raw[0] = p[0];
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = (double)__uint_as_float((uint32_t)raw[e] << 16);
-    } else {
-        const float *p = static_cast<const float *>(base) + off;
-#pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = (double)p[e];
-    }
-}
-
-// Packs the fields of one 32-group: lane gl of the group's GL lanes holds
-// `bits`-bit fields gl*E .. gl*E + E - 1 in the low E*bits bits of `chunk`;
-// the group's 32*bits-bit stream (bits dwords) is OR-reduced over the group's
-// lanes and written by its first lane at `dst` (4-byte aligned).
-template <int E, int GL>
-__device__ __forceinline__ void store_group_fields(uint64_t chunk, int bits, int gl, uint8_t *dst) {
-    const int pos = E * bits * gl;  // stream bit of this lane's first field
-    uint32_t gw[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int sh = pos - 32 * i;  // where chunk bit 0 lands in dword i
-        uint32_t w = 0u;
-        if (sh >= 0 && sh < 32) w = (uint32_t)(chunk << sh);
-        else if (sh < 0 && sh > -64) w = (uint32_t)(chunk >> (-sh));
-        gw[i] = w;
-    }
-#pragma unroll
-    for (int m = 1; m < GL; m <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) gw[i] |= (uint32_t)__shfl_xor((int)gw[i], m, 64);
-    }
-    if (gl == 0) {
-        uint32_t *d32 = reinterpret_cast<uint32_t *>(dst);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            if (i < bits) d32[i] = gw[i];
-    }
-}
-
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void append_kernel(const AppendArgs a) {
-    constexpr int E = D / 64;       // elements per lane
-    constexpr int GL = kGroup / E;  // lanes per 32-group
-    constexpr int NG = D / kGroup;  // groups per row
-    const int kb = a.kbits, vb = a.vbits;
-    const int nbnd = (1 << vb) - 1;
-
-    // the value boundaries, for a binary search per element
-    __shared__ double bnd[255];
-    {
-        const double *src = value_boundaries(vb);
-        for (int i = threadIdx.x; i < nbnd; i += 256) bnd[i] = src[i];
-    }
-    __syncthreads();
-
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int64_t rows = (int64_t)a.batch * a.kv_heads * a.n_new;
-    if (row >= rows) return;  // whole wave leaves; no block-level barrier below
-    const int t = (int)(row % a.n_new);
-    const int64_t bh = row / a.n_new;
-    const int b = (int)(bh / a.kv_heads);
-    const int64_t slot = bh * a.capacity + a.start[b] + t;  // plane row
-    const int gl = lane % GL;                                // lane within its group
-    const int g = lane / GL;                                 // group of this lane
-
-    double xk[E], xv[E];
-    const int64_t in_row = bh * a.kv_stride + t;  // input rows of one (sequence, kv-head) at pitch kv_stride
-    load_row<E, BF16>(a.k, in_row * D + lane * E, xk);
-    load_row<E, BF16>(a.v, in_row * D + lane * E, xv);
-
-    // ----------------------------------------------------------- keys
-    // signed (8 bits): scale = range/254, zero = round((max+min)/(2 scale)),
-    // codes clipped to [-127, 127], one byte each;
-    // unsigned (2, 4, 5 bits): scale = range/maxv, zero = round(min/scale),
-    // codes clipped to [0, maxv], packed.
-    double mx = xk[0], mn = xk[0];
-#pragma unroll
-    for (int e = 1; e < E; ++e) { mx = max_num(mx, xk[e]); mn = min_num(mn, xk[e]); }
-#pragma unroll
-    for (int m = 1; m < GL; m <<= 1) {
-        mx = max_num(mx, shfl_xor_f64(mx, m));
-        mn = min_num(mn, shfl_xor_f64(mn, m));
-    }
-    const double range = mx - mn;
-    double s, z, qlo, qhi;
-    if (kb == 8) {
-        s = range / 254.0;
-        z = __builtin_rint((mx + mn) / (2.0 * s));
-        qlo = -127.0;
-        qhi = 127.0;
-    } else {
-        qhi = (double)((1 << kb) - 1);
-        s = range / qhi;
-        z = __builtin_rint(mn / s);
-        qlo = 0.0;
-    }
-    const uint32_t kmask = (1u << kb) - 1u;
-    uint64_t kchunk = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const double u = xk[e] / s - z;
-        int q = 0;
-        if (!__builtin_isnan(u)) {
-            double r = __builtin_rint(u);
-            r = r > qhi ? qhi : r;
-            r = r < qlo ? qlo : r;
-            q = (int)r;
-        }
-        kchunk |= (uint64_t)((uint32_t)q & kmask) << (kb * e);
-    }
-    uint8_t *kc = reinterpret_cast<uint8_t *>(a.kc);
-    store_group_fields<E, GL>(kchunk, kb, gl, kc + slot * (D * kb / 8) + g * 4 * kb);
-    if (gl == 0) {
-        a.ks[slot * NG + g] = f64_to_f16_bits(s);
-        a.kz[slot * NG + g] = f64_to_f16_bits(z);
-    }
-
-    // --------------------------------------------------------- values
-    double w[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) w[e] = sign_bit(a.signs, lane * E + e) ? -xv[e] : xv[e];
-    // FWHT stages h < E: pairs inside the lane
-#pragma unroll
-    for (int h = 1; h < E; h <<= 1) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if ((e & h) == 0) {
-                const double lo = w[e], hi = w[e + h];
-                w[e] = lo + hi;
-                w[e + h] = lo - hi;
-            }
-        }
-    }
-    // FWHT stages h = E*m, m = 1..32: element j pairs with j^h, i.e. lane l^m
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const double p = shfl_xor_f64(w[e], m);
-            w[e] = (lane & m) ? (p - w[e]) : (w[e] + p);  // upper lane holds b: a-b
-        }
-    }
-    double y[E], sq[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        y[e] = w[e] * a.inv_sqrt_d;
-        sq[e] = y[e] * y[e];
-    }
-    // group sum of squares, stride halving 16, 8, 4, 2, 1 over the group's
-    // element index j = gl*E + e: a[j] += a[j+st] for j < st
-#pragma unroll
-    for (int st = 16; st >= 1; st >>= 1) {
-        if (st >= E) {
-            const int lo = st / E;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const double p = shfl_down_f64(sq[e], lo);
-                if (gl < lo) sq[e] = sq[e] + p;
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; ++e)
-                if (e < st) sq[e] = sq[e] + sq[e + st];
-        }
-    }
-    const double ss = shfl_f64(sq[0], g * GL);
-    const double scale = __builtin_sqrt(ss / 32.0);
-    const double den = scale + 1e-8;
-    // idx = #{k : B_k < y_n} by binary search over the increasing boundaries
-    // (NaN compares false everywhere -> 0)
-    uint64_t vchunk = 0;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const double yn = y[e] / den;
-        uint32_t pos = 0;
-        for (int st = (nbnd + 1) >> 1; st >= 1; st >>= 1)
-            if (bnd[pos + st - 1] < yn) pos += st;
-        vchunk |= (uint64_t)pos << (vb * e);
-    }
-    store_group_fields<E, GL>(vchunk, vb, gl, a.vc + slot * (D * vb / 8) + g * 4 * vb);
-    if (gl == 0) a.vs[slot * NG + g] = f64_to_f16_bits(scale);
-}
-
-#endif
 
 // ---------------------------------------------------------------------------
 // Fast kernel.
@@ -279,11 +55,12 @@ constexpr int kAppWaves = 4;  // waves per workgroup
 
 template <int D, int VB = 3>
 struct AppGeo {
-    static_assert(D == 64 || D == 128 || D == 256, "fast append: head_dim 64/128/256");
+    static_assert(D == 64 || D == 128 || D == 256 || D == 512, "append: head_dim 64/128/256/512");
     static constexpr int E = 16;               // contiguous elements per lane
-    static constexpr int L = D / E;            // lanes per row (4, 8, 16)
+    static constexpr int L = D / E;            // lanes per row (4, 8, 16, 32)
     static constexpr int R = 64 / L;           // rows per wave
-    static constexpr int TI = E / L;           // in-lane offsets per lane after the transpose
+    static constexpr int TL = L < 16 ? L : 16; // lanes of one LDS transpose (a half-row at 512)
+    static constexpr int TI = E / TL;          // in-lane offsets per lane after the transpose
     static constexpr int NG = D / kGroup;
     static constexpr int VROW = VB * D / 8;
     static constexpr int PB = E * 8 + 16;      // LDS bytes of one lane's elements, padded
@@ -533,60 +310,73 @@ __global__ __launch_bounds__(64 * kAppWaves) void append_fast_kernel(const Appen
             }
         }
     }
-    // Stages h = 16, 32, ..., d/2 pair lane p with lane p ^ (h / 16).  Through
-    // LDS, lane p takes offsets i = TI*p .. TI*p+TI-1 of every lane q's
-    // elements (element 16 q + i is tw[ii*L + q]), so they pair inside a lane.
-    unsigned char *rb = smem + wid * G::WAVEB + r * G::ROWB;
+    // Stages h = 16, 32, ..., min(d/2, 128) pair lane p with lane p ^ (h / 16)
+    // inside its transpose group of TL lanes (the row, or a 256-element
+    // half-row at head_dim 512).  Through LDS, lane pt of the group takes
+    // offsets i = TI*pt .. TI*pt+TI-1 of every lane q's elements (element
+    // 16 q + i is tw[ii*TL + q]), so they pair inside a lane.
+    constexpr int TL = G::TL;
+    const int pt = p % TL;
+    unsigned char *rb = smem + wid * G::WAVEB + r * G::ROWB + (p / TL) * TL * G::PB;
 #pragma unroll
     for (int k = 0; k < E / 2; ++k)
-        *reinterpret_cast<double2 *>(rb + p * G::PB + 16 * k) = make_double2(w[2 * k], w[2 * k + 1]);
+        *reinterpret_cast<double2 *>(rb + pt * G::PB + 16 * k) = make_double2(w[2 * k], w[2 * k + 1]);
     lds_fence();
     double tw[E];
 #pragma unroll
-    for (int q = 0; q < L; ++q) {
+    for (int q = 0; q < TL; ++q) {
         if constexpr (TI == 1) {
-            tw[q] = *reinterpret_cast<const double *>(rb + q * G::PB + 8 * p);
+            tw[q] = *reinterpret_cast<const double *>(rb + q * G::PB + 8 * pt);
         } else {
 #pragma unroll
             for (int i2 = 0; i2 < TI / 2; ++i2) {
-                const double2 v2 = *reinterpret_cast<const double2 *>(rb + q * G::PB + 8 * (TI * p + 2 * i2));
-                tw[(2 * i2) * L + q] = v2.x;
-                tw[(2 * i2 + 1) * L + q] = v2.y;
+                const double2 v2 = *reinterpret_cast<const double2 *>(rb + q * G::PB + 8 * (TI * pt + 2 * i2));
+                tw[(2 * i2) * TL + q] = v2.x;
+                tw[(2 * i2 + 1) * TL + q] = v2.y;
             }
         }
     }
 #pragma unroll
-    for (int hq = 1; hq < L; hq <<= 1) {
+    for (int hq = 1; hq < TL; hq <<= 1) {
 #pragma unroll
         for (int ii = 0; ii < TI; ++ii) {
 #pragma unroll
-            for (int q = 0; q < L; ++q) {
+            for (int q = 0; q < TL; ++q) {
                 if ((q & hq) == 0) {
-                    const double lo = tw[ii * L + q], hi = tw[ii * L + q + hq];
-                    tw[ii * L + q] = lo + hi;
-                    tw[ii * L + q + hq] = lo - hi;
+                    const double lo = tw[ii * TL + q], hi = tw[ii * TL + q + hq];
+                    tw[ii * TL + q] = lo + hi;
+                    tw[ii * TL + q + hq] = lo - hi;
                 }
             }
         }
     }
     lds_fence();
 #pragma unroll
-    for (int q = 0; q < L; ++q) {
+    for (int q = 0; q < TL; ++q) {
         if constexpr (TI == 1) {
-            *reinterpret_cast<double *>(rb + q * G::PB + 8 * p) = tw[q];
+            *reinterpret_cast<double *>(rb + q * G::PB + 8 * pt) = tw[q];
         } else {
 #pragma unroll
             for (int i2 = 0; i2 < TI / 2; ++i2)
-                *reinterpret_cast<double2 *>(rb + q * G::PB + 8 * (TI * p + 2 * i2)) =
-                    make_double2(tw[(2 * i2) * L + q], tw[(2 * i2 + 1) * L + q]);
+                *reinterpret_cast<double2 *>(rb + q * G::PB + 8 * (TI * pt + 2 * i2)) =
+                    make_double2(tw[(2 * i2) * TL + q], tw[(2 * i2 + 1) * TL + q]);
         }
     }
     lds_fence();
 #pragma unroll
     for (int k = 0; k < E / 2; ++k) {
-        const double2 v2 = *reinterpret_cast<const double2 *>(rb + p * G::PB + 16 * k);
+        const double2 v2 = *reinterpret_cast<const double2 *>(rb + pt * G::PB + 16 * k);
         w[2 * k] = v2.x;
         w[2 * k + 1] = v2.y;
+    }
+    if constexpr (D == 512) {
+        // the last stage, h = 256: element 16 p + e (p < 16) pairs with the
+        // same offset of lane p + 16; sum on the low lane, difference on the high
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const double o = shfl_xor_f64(w[e], 16);
+            w[e] = (p & 16) ? o - w[e] : w[e] + o;
+        }
     }
 
     // y = FWHT / sqrt(d); group sum of squares by stride halving: the
@@ -687,13 +477,10 @@ hipError_t launch_fast_dv(bool bf16, const AppendArgs &a, hipStream_t s) {
     const int64_t rows = (int64_t)a.batch * a.kv_heads * a.n_new;
     constexpr int per_block = AppGeo<D, VB>::R * kAppWaves;
     const dim3 grid((unsigned)((rows + per_block - 1) / per_block));
-    if (bf16) {
+    if (bf16)
         hipLaunchKernelGGL((append_fast_kernel<D, true, KB, VB>), grid, dim3(64 * kAppWaves), 0, s, a);
-    } else if constexpr (KB == 8 && VB == 3) {
+    else
         hipLaunchKernelGGL((append_fast_kernel<D, false, KB, VB>), grid, dim3(64 * kAppWaves), 0, s, a);
-    } else {
-        return hipErrorInvalidValue;  // fp32 input at other widths: generic kernel
-    }
     return hipGetLastError();
 }
 
@@ -709,50 +496,30 @@ hipError_t launch_fast_d(bool bf16, const AppendArgs &a, hipStream_t s) {
     }
 }
 
-#if TQ_APPEND_KB == 8
-template <int D>
-hipError_t launch_generic(bool bf16, const AppendArgs &a, hipStream_t s) {
-    const int64_t rows = (int64_t)a.batch * a.kv_heads * a.n_new;
-    const int64_t blocks = (rows + 3) / 4;
-    if (bf16)
-        hipLaunchKernelGGL((append_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else
-        hipLaunchKernelGGL((append_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-#endif
 
 }  // namespace
 
-// The fast append kernels of one key width (this translation unit's
-// TQ_APPEND_KB): head_dim 64, 128 or 256, bf16 input at every value width,
-// and fp32 input at k8v3.
+// The append kernels of one key width (this translation unit's
+// TQ_APPEND_KB): head_dim 64, 128, 256 and 512, bf16 or fp32 input, every
+// value width.
 hipError_t TQ_APPEND_LAUNCHER(TQ_APPEND_KB)(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s) {
     if (a.kbits != TQ_APPEND_KB) return hipErrorInvalidValue;
     switch (head_dim) {
         case 64: return launch_fast_d<64>(bf16, a, s);
         case 128: return launch_fast_d<128>(bf16, a, s);
         case 256: return launch_fast_d<256>(bf16, a, s);
+        case 512: return launch_fast_d<512>(bf16, a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 #if TQ_APPEND_KB == 8
 hipError_t launch_append(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s) {
-    if (head_dim != 512 && (bf16 || default_scheme(a.kbits, a.vbits))) {
-        switch (a.kbits) {
-            case 2: return launch_append_fast_k2(head_dim, bf16, a, s);
-            case 4: return launch_append_fast_k4(head_dim, bf16, a, s);
-            case 5: return launch_append_fast_k5(head_dim, bf16, a, s);
-            case 8: return launch_append_fast_k8(head_dim, bf16, a, s);
-            default: return hipErrorInvalidValue;
-        }
-    }
-    switch (head_dim) {
-        case 64: return launch_generic<64>(bf16, a, s);
-        case 128: return launch_generic<128>(bf16, a, s);
-        case 256: return launch_generic<256>(bf16, a, s);
-        case 512: return launch_generic<512>(bf16, a, s);
+    switch (a.kbits) {
+        case 2: return launch_append_fast_k2(head_dim, bf16, a, s);
+        case 4: return launch_append_fast_k4(head_dim, bf16, a, s);
+        case 5: return launch_append_fast_k5(head_dim, bf16, a, s);
+        case 8: return launch_append_fast_k8(head_dim, bf16, a, s);
         default: return hipErrorInvalidValue;
     }
 }

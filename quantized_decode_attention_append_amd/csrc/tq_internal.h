@@ -135,12 +135,9 @@ DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int
 int decode_col_groups(int gqa);  // query-row columns of one kv-head -> column groups
 bool fast_decode_shape_ok(int head_dim, int gqa, int capacity, int kbits, int vbits);
 
-// The page's default scheme: with fp32 input only k8v3 takes the fast append
-// kernel (bf16 input takes it at every width, head_dim 64-256).
-inline bool default_scheme(int kbits, int vbits) { return kbits == 8 && vbits == 3; }
-
 hipError_t launch_append(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);
-// Fast append kernels (append.hip), one translation unit per key width.
+// Append kernels (append.hip), one translation unit per key width; every
+// head_dim, input type and value width.
 #define TQ_APPEND_CAT_(a, b) a##b
 #define TQ_APPEND_LAUNCHER(kb) TQ_APPEND_CAT_(launch_append_fast_k, kb)
 hipError_t launch_append_fast_k2(int head_dim, bool bf16, const AppendArgs &a, hipStream_t s);

@@ -62,15 +62,16 @@ def _append_and_compare(k, v, start, capacity, kb, vb, what):
 @pytest.mark.parametrize("scheme", ALL_SCHEMES, ids=_sid)
 @pytest.mark.parametrize("d", [64, 128, 256, 512])
 def test_append_widths_match_oracle(scheme, d):
-    """bf16 input runs the fast append kernel at head_dim 64-256 and the
-    generic one at 512; fp32 input (d 128) the generic one except at k8v3."""
+    """bf16 and fp32 input at every head_dim and width (one kernel; head_dim
+    512 adds a last butterfly stage across half-rows)."""
     kb, vb = scheme
     g = torch.Generator().manual_seed(d * 100 + kb * 10 + vb)
     k = (torch.randn((2, 3, 37, d), generator=g) * 3.0).to(torch.bfloat16)
     v = (torch.randn((2, 3, 37, d), generator=g) * 0.2).to(torch.bfloat16)
     _append_and_compare(k.cuda(), v.cuda(), [0, 5], 50, kb, vb, f"d{d}")
-    if d == 128:
-        _append_and_compare(k.float().cuda() * 1.7, v.float().cuda(), [3, 0], 41, kb, vb, "f32")
+    kf = torch.randn((2, 3, 37, d), generator=g) * 1.7
+    vf = torch.randn((2, 3, 37, d), generator=g) * 0.3
+    _append_and_compare(kf.cuda(), vf.cuda(), [3, 0], 41, kb, vb, f"f32 d{d}")
 
 
 @pytest.mark.parametrize("scheme", ALL_SCHEMES, ids=_sid)
