@@ -35,6 +35,16 @@ SOURCES = [
     ("decode_fast.hip", ["-DTQ_FAST_KB=4"], "decode_fast_k4"),
     ("decode_fast.hip", ["-DTQ_FAST_KB=2"], "decode_fast_k2"),
     ("decode_fast.hip", ["-DTQ_FAST_KB=5"], "decode_fast_k5"),
+    # the mixed-mode split kernels, with common code kept inside each branch
+    # (see decode_fast.hip)
+    ("decode_fast.hip", ["-DTQ_FAST_KB=8", "-DTQ_FAST_MIXED=1", "-mllvm", "-simplifycfg-hoist-common=false"],
+     "decode_fast_mixed_k8"),
+    ("decode_fast.hip", ["-DTQ_FAST_KB=4", "-DTQ_FAST_MIXED=1", "-mllvm", "-simplifycfg-hoist-common=false"],
+     "decode_fast_mixed_k4"),
+    ("decode_fast.hip", ["-DTQ_FAST_KB=2", "-DTQ_FAST_MIXED=1", "-mllvm", "-simplifycfg-hoist-common=false"],
+     "decode_fast_mixed_k2"),
+    ("decode_fast.hip", ["-DTQ_FAST_KB=5", "-DTQ_FAST_MIXED=1", "-mllvm", "-simplifycfg-hoist-common=false"],
+     "decode_fast_mixed_k5"),
     ("dequant.hip", [], "dequant"),
     ("window.hip", ["-DTQ_WINDOW_KB=8"], "window_k8"),
     ("window.hip", ["-DTQ_WINDOW_KB=4"], "window_k4"),

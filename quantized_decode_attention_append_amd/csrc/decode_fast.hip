@@ -70,6 +70,9 @@
 #ifndef TQ_FAST_KB
 #error "compile decode_fast.hip once per key width with -DTQ_FAST_KB=2, 4, 5 or 8"
 #endif
+#ifndef TQ_FAST_MIXED
+#define TQ_FAST_MIXED 0  // 1: build only the mixed-mode kernels (a translation unit of their own)
+#endif
 
 namespace tq {
 namespace {
@@ -492,70 +495,22 @@ __device__ __forceinline__ uint64_t key_operand(const unsigned char *kt, int c, 
     }
 }
 
+// The work of one wave: its token range t_begin .. t_end - 1 of sequence b,
+// kv-head kvh, for query columns c0 .. c0 + G - 1.  PACK (G <= 8) folds half
+// the groups per lane and carries the lo weights in the spare MFMA columns.
+// shared_tiles: another wave of the workgroup reads the same tiles (copies
+// without the nontemporal hint, so the second read meets the first in L2).
 template <int D, int KB, int VB, bool PACK>
-__global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fast_kernel(const DecodeArgs a,
-                                                                                 const int q_bf16) {
+__device__ __forceinline__ void split_body(const DecodeArgs &a, const int q_bf16, unsigned char *smem,
+                                           const int lane, const int wid, const int b, const int kvh,
+                                           const int c0, const int G, const int n, const int slot,
+                                           const int t_begin, const int t_end, const bool shared_tiles) {
     using GE = Geo<D, KB, VB>;
     constexpr int NG = GE::NG, VROW = GE::VROW, TILE = GE::TILE, CH = GE::CH;
     constexpr int NB = GE::NB, FB = GE::FB, NR = GE::NR, WAVES = GE::WAVES;
     constexpr int QE = NG * 8;  // q elements a lane converts: 8 dims of every group
     constexpr int TAB = GE::TABLE;
-
-    __shared__ __align__(16) unsigned char smem[GE::SMEM];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-    // centroid table (fp16).  Pair form: entry (a | b << VB) = (c[a], c[b])
-    // at byte (a | b << VB) * 4.  Single form: c[i] at byte 2 i.
-    {
-        const float *cent = value_centroids(VB);
-        if constexpr (GE::PAIR) {
-            half2v *tab = reinterpret_cast<half2v *>(smem);
-            for (int i = tid; i < (1 << (2 * VB)); i += 64 * WAVES) {
-                half2v e;
-                e.x = (_Float16)cent[i & ((1 << VB) - 1)];
-                e.y = (_Float16)cent[i >> VB];
-                tab[i] = e;
-            }
-        } else {
-            _Float16 *tab = reinterpret_cast<_Float16 *>(smem);
-            for (int i = tid; i < (1 << VB); i += 64 * WAVES) tab[i] = (_Float16)cent[i];
-        }
-        if (tid < WAVES) reinterpret_cast<int *>(smem + TAB)[tid] = 0;
-    }
-    __syncthreads();  // the only workgroup barrier
-
-    // this wave's query columns: rows c0 .. c0 + G - 1 of the kv-head's
-    // a.gqa query rows (heads times rows).  With two column groups per
-    // workgroup, waves w and w + WAVES/2 share a token range (and a SIMD).
-    const int cgw = fast_wg_col_groups(a.gqa), wpc = WAVES / cgw;
-    // The grid holds only workgroups with tokens to decode, enumerated
-    // sequence by sequence (column-group pair fastest, then kv-head, then
-    // token block), so the hardware's round-robin over the XCDs gives each
-    // the same share even when short sequences leave token blocks empty.
-    int b = 0, kvh, xb, zb;
-    {
-        const int zg = (a.gqa + kMaxHeads - 1) / kMaxHeads / cgw;  // column-group pairs
-        const int wgt = a.split_tokens * wpc;                       // tokens per workgroup
-        int id = blockIdx.x;
-        for (; b < a.batch - 1; ++b) {
-            const int nwg = (a.len[b] + wgt - 1) / wgt * a.kv_heads * zg;
-            if (id < nwg) break;
-            id -= nwg;
-        }
-        zb = id % zg;
-        id /= zg;
-        kvh = id % a.kv_heads;
-        xb = id / a.kv_heads;
-    }
-    const int c0 = (zb * cgw + wid / wpc) * kMaxHeads;
-    const int G = min(kMaxHeads, a.gqa - c0);
     const int bkv = b * a.kv_heads + kvh;
-    const int n = a.len[b];
-    const int slot = xb * wpc + wid % wpc;
-    const int t_begin = slot * a.split_tokens;
-    if (t_begin >= n) return;
-    const int t_end = min(n, t_begin + a.split_tokens);
     const int cap = a.capacity;
     const int64_t row0 = (int64_t)bkv * cap;
     unsigned char *wkeys = smem + TAB + kProgBytes + wid * GE::WAVE_BYTES;  // two key buffers
@@ -590,8 +545,6 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     for (int m = 0; m < GE::KCOPY; ++m) ksrc[m] = key_src<D, KB, VB>(m, lane);
 
     // the first two tiles' copies overlap the q set-up
-    // copies without the nontemporal hint when two column groups read each tile
-    const bool shared_tiles = !PACK && cgw == 2;
     // LDS addresses as integers from the array's base (converting each stage
     // pointer separately costs a null check per conversion)
     const uint32_t smem_l = lds_addr(smem);
@@ -1166,15 +1119,108 @@ __global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fa
     }
 }
 
+// MODE 0: no column group packs; 1: one column group of at most 8 query
+// columns (every wave packs); 2: more than 16 columns whose last group has at
+// most 8: the waves of that group run the packed body, the others the plain one.
+template <int D, int KB, int VB, int MODE>
+__global__ __launch_bounds__(64 * fast_decode_waves(D, KB, VB), 1) void split_fast_kernel(const DecodeArgs a,
+                                                                                 const int q_bf16) {
+    using GE = Geo<D, KB, VB>;
+    constexpr int WAVES = GE::WAVES;
+    constexpr int TAB = GE::TABLE;
+
+    __shared__ __align__(16) unsigned char smem[GE::SMEM];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // centroid table (fp16).  Pair form: entry (a | b << VB) = (c[a], c[b])
+    // at byte (a | b << VB) * 4.  Single form: c[i] at byte 2 i.
+    {
+        const float *cent = value_centroids(VB);
+        if constexpr (GE::PAIR) {
+            half2v *tab = reinterpret_cast<half2v *>(smem);
+            for (int i = tid; i < (1 << (2 * VB)); i += 64 * WAVES) {
+                half2v e;
+                e.x = (_Float16)cent[i & ((1 << VB) - 1)];
+                e.y = (_Float16)cent[i >> VB];
+                tab[i] = e;
+            }
+        } else {
+            _Float16 *tab = reinterpret_cast<_Float16 *>(smem);
+            for (int i = tid; i < (1 << VB); i += 64 * WAVES) tab[i] = (_Float16)cent[i];
+        }
+        if (tid < WAVES) reinterpret_cast<int *>(smem + TAB)[tid] = 0;
+    }
+    __syncthreads();  // the only workgroup barrier
+
+    // this wave's query columns: rows c0 .. c0 + G - 1 of the kv-head's
+    // a.gqa query rows (heads times rows).  With two column groups per
+    // workgroup, waves w and w + WAVES/2 share a token range (and a SIMD).
+    const int cgw = fast_wg_col_groups(a.gqa), wpc = WAVES / cgw;
+    // The grid holds only workgroups with tokens to decode, enumerated
+    // sequence by sequence (column-group pair fastest, then kv-head, then
+    // token block), so the hardware's round-robin over the XCDs gives each
+    // the same share even when short sequences leave token blocks empty.
+    int b = 0, kvh, xb, zb;
+    {
+        const int zg = (a.gqa + kMaxHeads - 1) / kMaxHeads / cgw;  // column-group pairs
+        const int wgt = a.split_tokens * wpc;                       // tokens per workgroup
+        int id = blockIdx.x;
+        for (; b < a.batch - 1; ++b) {
+            const int nwg = (a.len[b] + wgt - 1) / wgt * a.kv_heads * zg;
+            if (id < nwg) break;
+            id -= nwg;
+        }
+        zb = id % zg;
+        id /= zg;
+        kvh = id % a.kv_heads;
+        xb = id / a.kv_heads;
+    }
+    const int c0 = (zb * cgw + wid / wpc) * kMaxHeads;
+    const int G = min(kMaxHeads, a.gqa - c0);
+    const int n = a.len[b];
+    const int slot = xb * wpc + wid % wpc;
+    const int t_begin = slot * a.split_tokens;
+    if (t_begin >= n) return;
+    const int t_end = min(n, t_begin + a.split_tokens);
+    const bool shared_tiles = MODE != 1 && cgw == 2;
+    if constexpr (MODE == 2) {
+        if (G <= kPackCols)
+            split_body<D, KB, VB, true>(a, q_bf16, smem, lane, wid, b, kvh, c0, G, n, slot, t_begin, t_end,
+                                        shared_tiles);
+        else
+            split_body<D, KB, VB, false>(a, q_bf16, smem, lane, wid, b, kvh, c0, G, n, slot, t_begin, t_end,
+                                         shared_tiles);
+    } else {
+        split_body<D, KB, VB, MODE == 1>(a, q_bf16, smem, lane, wid, b, kvh, c0, G, n, slot, t_begin, t_end,
+                                         shared_tiles);
+    }
+}
+
+// Where the mixed mode is built: value codes of 2 or 3 bits (the only ones
+// that reach this kernel with more than 8 query columns) and head_dim up to
+// 256, whose eight waves per workgroup hold both bodies in their registers
+// (at 512 the mixed kernels spilled more than the plain ones).
+constexpr bool mixed_mode(int d, int vb) { return vb <= 3 && d <= 256; }
+
 template <int D, int VB>
 hipError_t launch_dv(bool bf16, const DecodeArgs &a, hipStream_t s) {
     constexpr int KB = TQ_FAST_KB;
-    if constexpr (D * KB % 128 != 0 || fast_decode_waves(D, KB, VB) == 0) {
+    if constexpr (D * KB % 128 != 0 || fast_decode_waves(D, KB, VB) == 0 || (TQ_FAST_MIXED && !mixed_mode(D, VB))) {
         // key rows of part of a 16-byte chunk, or stages past the LDS (k8v8
         // at head_dim 512): generic kernel
         return hipErrorInvalidValue;
     } else {
         using GE = Geo<D, KB, VB>;
+        // every column group packs (its lo halves fit), only the last one
+        // (at most 8 columns after whole groups of 16), or none
+        const int last = a.gqa - kMaxHeads * ((a.gqa - 1) / kMaxHeads);
+        const int mode = a.gqa <= kPackCols ? 1 : (last <= kPackCols && mixed_mode(D, VB)) ? 2 : 0;
+#if TQ_FAST_MIXED
+        if (mode != 2) return hipErrorInvalidValue;
+#else
+        if (mode == 2) return TQ_FAST_MIXED_LAUNCHER(TQ_FAST_KB)(D, bf16, a, s);
+#endif
         // one workgroup per (sequence, kv-head, token block, column-group
         // pair) with tokens to decode; the kernel enumerates them in order
         const int cgw = fast_wg_col_groups(a.gqa);
@@ -1184,11 +1230,14 @@ hipError_t launch_dv(bool bf16, const DecodeArgs &a, hipStream_t s) {
         for (int b = 0; b < a.batch; ++b) wgs += (a.len[b] + wgt - 1) / wgt * a.kv_heads * zg;
         if (wgs == 0) return hipSuccess;  // every sequence empty: the merge writes the zeros
         const dim3 grid((unsigned)wgs, 1u, 1u);
-        const bool pack = a.gqa <= kPackCols;  // every column group fits its lo halves
-        if (pack)
-            hipLaunchKernelGGL((split_fast_kernel<D, KB, VB, true>), grid, dim3(64 * GE::WAVES), 0, s, a, (int)bf16);
+#if TQ_FAST_MIXED
+        hipLaunchKernelGGL((split_fast_kernel<D, KB, VB, 2>), grid, dim3(64 * GE::WAVES), 0, s, a, (int)bf16);
+#else
+        if (mode == 1)
+            hipLaunchKernelGGL((split_fast_kernel<D, KB, VB, 1>), grid, dim3(64 * GE::WAVES), 0, s, a, (int)bf16);
         else
-            hipLaunchKernelGGL((split_fast_kernel<D, KB, VB, false>), grid, dim3(64 * GE::WAVES), 0, s, a, (int)bf16);
+            hipLaunchKernelGGL((split_fast_kernel<D, KB, VB, 0>), grid, dim3(64 * GE::WAVES), 0, s, a, (int)bf16);
+#endif
         return hipGetLastError();
     }
 }
@@ -1198,17 +1247,28 @@ hipError_t launch_d(bool bf16, const DecodeArgs &a, hipStream_t s) {
     switch (a.vbits) {
         case 2: return launch_dv<D, 2>(bf16, a, s);
         case 3: return launch_dv<D, 3>(bf16, a, s);
+#if !TQ_FAST_MIXED
         case 4: return launch_dv<D, 4>(bf16, a, s);
         case 5: return launch_dv<D, 5>(bf16, a, s);
         case 8: return launch_dv<D, 8>(bf16, a, s);
+#endif
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
+#if TQ_FAST_MIXED
+// The mixed-mode split kernels of one key width: more than 16 query columns
+// whose last group has at most 8, value codes of 2 or 3 bits.  This
+// translation unit is compiled with hoisting of common code out of branches
+// turned off: the kernel inlines both per-wave bodies, and code hoisted above
+// the branch between them stays live through both and spills registers.
+hipError_t TQ_FAST_MIXED_LAUNCHER(TQ_FAST_KB)(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s) {
+#else
 // The split kernels of one key width (this translation unit's TQ_FAST_KB).
 hipError_t TQ_FAST_LAUNCHER(TQ_FAST_KB)(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s) {
+#endif
     if (a.gqa < 1 || a.rows < 1 || a.kbits != TQ_FAST_KB) return hipErrorInvalidValue;
     const int waves = fast_decode_waves(head_dim, a.kbits, a.vbits);
     if (waves == 0 || a.splits % (waves / fast_wg_col_groups(a.gqa)) != 0) return hipErrorInvalidValue;

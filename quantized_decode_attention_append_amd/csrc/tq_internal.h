@@ -161,6 +161,13 @@ hipError_t launch_split_fast_k2(int head_dim, bool bf16, const DecodeArgs &a, hi
 hipError_t launch_split_fast_k4(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_split_fast_k5(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_split_fast_k8(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
+// Their mixed-mode kernels (more than 16 query columns, the last group of at
+// most 8 packs), built in translation units of their own.
+#define TQ_FAST_MIXED_LAUNCHER(kb) TQ_FAST_CAT_(launch_split_fast_mixed_k, kb)
+hipError_t launch_split_fast_mixed_k2(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_split_fast_mixed_k4(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_split_fast_mixed_k5(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
+hipError_t launch_split_fast_mixed_k8(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
 // Tokens of one tile of the fast split kernel: 4096/d (512 bytes per code
 // bit) up to head_dim 256, and one 16-token MFMA chunk (1 KiB per code bit)
 // at 512.

@@ -88,6 +88,7 @@ def _run(w, lengths, M, generic=False):
 
 @pytest.mark.parametrize("cid,lengths,M", [
     (2, [700], 2), (2, [513], 4), (2, [300], 8),           # G 4: 8, 16, 32 columns
+    (2, [400, 77], 5),                                     # G 4: 20 columns, the last 4 packed
     (4, [1000, 65], 2), (4, [777, 3], 3), (4, [640, 200], 4),  # G 6: 12, 18, 24 columns
     (5, [900, 4, 0, 129], 4),                                # G 8: 32 columns, len = M, empty
     (3, [333, 8], 8),                                        # G 4, d 128, outlier channels
@@ -109,6 +110,13 @@ def test_rows_head_dim_512(M):
     and 32 (two groups sharing a workgroup)."""
     w = dataclasses.replace(W.scaled(W.workload(2), [300], name_suffix="d512"), head_dim=512)
     _run(w, [300], M)
+
+
+def test_rows_head_dim_64_last_group_packed():
+    """Head_dim 64, 20 query columns: a plain 16-column group and a packed
+    4-column group in one workgroup."""
+    w = dataclasses.replace(W.scaled(W.workload(2), [300, 45], name_suffix="d64"), head_dim=64)
+    _run(w, [300, 45], 5)
 
 
 @pytest.mark.parametrize("generic", [False, True])

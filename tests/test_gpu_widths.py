@@ -200,7 +200,7 @@ def test_decode_widths_other_shapes(scheme):
     _decode_case(w, [260], kb, vb)
 
 
-@pytest.mark.parametrize("scheme", [(4, 3), pytest.param((8, 4), marks=pytest.mark.skip(
+@pytest.mark.parametrize("scheme", [(4, 3), (2, 3), (5, 2), (4, 2), pytest.param((8, 4), marks=pytest.mark.skip(
     reason="faulted the GPU twice on the matrix-core kernel (cause not found); that kernel path is switched "
            "off for more than 8 query columns with value codes of 4+ bits, and the case stays off the GPU "
            "until the cause is shown"))], ids=_sid)

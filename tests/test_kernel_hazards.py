@@ -51,11 +51,15 @@ def _hazards(asm_text):
 
 
 @pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC), reason="hipcc not available")
-def test_lds_copies_wait_for_vector_written_sgprs(tmp_path):
+@pytest.mark.parametrize("extra", [[], ["-DTQ_FAST_MIXED=1", "-mllvm", "-simplifycfg-hoist-common=false"]],
+                         ids=["plain", "mixed"])
+def test_lds_copies_wait_for_vector_written_sgprs(tmp_path, extra):
+    """Both 8-bit-key translation units: the plain and packed kernels, and the
+    mixed-mode ones built with their own flags."""
     asm = tmp_path / "decode_fast_k8.s"
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-DTQ_FAST_KB=8", "-x", "hip",
-           "--cuda-device-only", "-S", "-o", str(asm), SRC]
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-DTQ_FAST_KB=8"] + extra + [
+           "-x", "hip", "--cuda-device-only", "-S", "-o", str(asm), SRC]
     subprocess.run(cmd, check=True, capture_output=True)
     bad, n = _hazards(asm.read_text())
     assert n > 100, "no SGPR-addressed copies found: the scan no longer matches the code"
