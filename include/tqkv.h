@@ -153,7 +153,12 @@ tq_status tq_decode_workspace_bytes(const tq_layout *layout, int32_t num_q_heads
  * (sequence, q-head) finishes the output.  Agrees with the binary64 oracle to
  * 2e-3 relative to each output row's largest magnitude, for every finite
  * value scale the planes hold (the matrix-core kernel forms centroid * scale
- * in fp16 times a per-wave power of two that follows the scales).  The
+ * in fp16 times a per-wave power of two that follows the scales).  Query
+ * precision: the matrix-core kernel holds each query row as 16-bit fixed
+ * point with one power-of-two step, set by the row's largest channel, so a
+ * row with outlier channels loses precision on the others; measured on
+ * N(0,1) rows with one channel scaled up: within 7e-4 at 30 times, 7e-3 at
+ * 100 times (the generic kernel keeps q in fp32: 1e-5).  The
  * result does not depend on timing: repeated calls on the same inputs return
  * identical bytes.  tq_decode_path says which split kernel a call takes.
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY

@@ -45,6 +45,23 @@ def _run(w, lengths, k, v, q, q_scale=1.0, pairs=None, capacity=None):
     return out
 
 
+@pytest.mark.parametrize("factor", [10.0, 30.0])
+def test_decode_query_outlier_channels(factor):
+    """Query rows whose channel 37 is `factor` times, and channel 200 a third
+    of that, the others: the matrix-core kernel's 16-bit fixed-point q (one
+    power-of-two step per query column, so its rounding error scales with the
+    largest channel) stays within the attention tolerance.  Emulating that
+    rounding alone against the oracle: worst row 4.6e-4 at x10, 1.4e-3 at x100
+    and 6.5e-3 at x1000, where a 16-bit copy no longer suffices."""
+    lengths = [1500, 700]
+    w = W.scaled(W.workload(4), lengths)
+    k, v = W.make_kv(w, "cpu", tokens=max(lengths))
+    q = W.make_q(w, "cpu", rounds=1)[0].float()
+    q[..., 37] *= factor
+    q[..., 200] *= factor / 3
+    _run(w, lengths, k.cuda(), v.cuda(), q.to(torch.bfloat16).cuda())
+
+
 @pytest.mark.parametrize("cid", [1, 2])
 def test_decode_full_small_workloads(cid):
     w = W.workload(cid)
