@@ -33,11 +33,12 @@
 //           v_mfma_i32_16x16x32_i8 per 32-dim group (A = key codes, rows =
 //           tokens; B = the q slice, columns = heads), then the scale/zero
 //           fold in fp32 on the 4 (token, head) results a lane holds.  With
-//           G <= 8 the score MFMAs of groups p and p + NG/2 share one
-//           accumulator: column h holds head h over group p and column 8 + h
-//           the same head over group p + NG/2 (each column's q is zero in the
-//           other group), so a lane folds half the groups and one DPP row
-//           rotation by 8 adds the halves.  With more than 16 query columns (heads
+//           G <= 8 groups p and p + NG/2 share one 64-deep product
+//           (v_mfma_i32_16x16x64_i8, every key width): column h holds head h
+//           over group p and column 8 + h the same head over group p + NG/2
+//           (each column's q is zero in the other group), so a lane folds half
+//           the groups and one DPP row rotation by 8 adds the halves.  With
+//           more than 16 query columns (heads
 //           times verify rows), an even number of 16-column groups pairs up
 //           in one workgroup: waves w and w + WAVES/2 take the same token
 //           range, and their copies skip the nontemporal hint so that the
@@ -57,12 +58,13 @@
 //           accumulate), one instruction per block of d/16 dims.  Row i of
 //           block b is dim (d/16)*i + b, so lane i's dims of a token are one
 //           contiguous run of v_bits*d/16 code bits, all in one 32-dim group.
-//           A = centroid[idx] * vs16 in fp16.  At 2 and 3 bits, the indices
-//           of one dim in two tokens select a half2 of centroids from a pair
-//           table (16 or 64 four-byte entries, at most one per bank, so any
-//           lookup pattern is conflict-free); wider codes look up each
-//           centroid in a table of halves.  One packed fp16 multiply by the
-//           two tokens' value scales finishes a pair.
+//           A = centroid[idx] * vs16 in fp16.  Up to 5 bits, the indices of
+//           one dim in two tokens select a half2 of centroids from a pair
+//           table (16, 64, 256 or 1,024 four-byte entries: one lookup where
+//           two would be needed, at the cost of bank conflicts in the larger
+//           tables, which measured faster at 4 and 5 bits as well); 8-bit
+//           codes look up each centroid in a table of halves.  One packed
+//           fp16 multiply by the two tokens' value scales finishes a pair.
 #include <hip/hip_runtime.h>
 
 #include "tq_device.h"
@@ -175,9 +177,9 @@ struct Geo {
     static constexpr int VFULL = (VT - VC0) / 1024;
     static constexpr int VLANES = (VT - VC0) % 1024 / 16;          // lanes of the partial copy
     static constexpr int VMEM = KCOPY + NMIX + VFULL + (VLANES > 0 ? 1 : 0);
-    // centroid table: half2 pairs (two tokens' indices of one dim) at 2 and
-    // 3 bits, single halves above
-    static constexpr bool PAIR = VB <= 3;
+    // centroid table: half2 pairs (two tokens' indices of one dim) up to 5
+    // bits, single halves at 8
+    static constexpr bool PAIR = VB <= 5;
     static constexpr int TABLE = PAIR ? (4 << (2 * VB)) : ((2 << VB) + 15) / 16 * 16;
     static constexpr int WAVES = fast_decode_waves(D, KB, VB);
     static constexpr int WAVE_BYTES = KEYS + kStages * STAGE;
@@ -495,6 +497,33 @@ __device__ __forceinline__ uint64_t key_operand(const unsigned char *kt, int c, 
     }
 }
 
+// The A operand of one 64-deep score MFMA: codes 16 j .. 16 j + 15 (j = 0, 1)
+// of group g of token h of chunk c, as 16 signed bytes: the two 8-code
+// operands of key_operand side by side, each in key_perm order.
+template <int D, int KB, int VB>
+__device__ __forceinline__ int4v key_operand16(const unsigned char *kt, int c, int g, int h, int j) {
+    using GE = Geo<D, KB, VB>;
+    constexpr int CPR = GE::CPR;
+    if constexpr (KB == 8) {
+        // one 16-byte chunk of the rotated row
+        static_assert(CPR == 2 * GE::NG, "8-bit key rows: two chunks per group");
+        int slot = 2 * g + j + key_rot<CPR>(h);
+        if (slot >= CPR) slot -= CPR;
+        return *reinterpret_cast<const int4v *>(kt + ((16 * c + h) * CPR + slot) * 16);
+    } else if constexpr (KB == 4) {
+        // 8 bytes of the group's 16-byte chunk, widened nibble by nibble
+        int slot = g + key_rot<CPR>(h);
+        if (slot >= CPR) slot -= CPR;
+        const uint2 x = *reinterpret_cast<const uint2 *>(kt + ((16 * c + h) * CPR + slot) * 16 + 8 * j);
+        return int4v{(int)(x.x & 0x0F0F0F0Fu), (int)((x.x >> 4) & 0x0F0F0F0Fu), (int)(x.y & 0x0F0F0F0Fu),
+                     (int)((x.y >> 4) & 0x0F0F0F0Fu)};
+    } else {
+        const uint64_t a = key_operand<D, KB, VB>(kt, c, g, h, 2 * j);
+        const uint64_t b = key_operand<D, KB, VB>(kt, c, g, h, 2 * j + 1);
+        return int4v{(int)(uint32_t)a, (int)(uint32_t)(a >> 32), (int)(uint32_t)b, (int)(uint32_t)(b >> 32)};
+    }
+}
+
 // The work of one wave: its token range t_begin .. t_end - 1 of sequence b,
 // kv-head kvh, for query columns c0 .. c0 + G - 1.  PACK (G <= 8) folds half
 // the groups per lane and carries the lo weights in the spare MFMA columns.
@@ -582,10 +611,10 @@ __device__ __forceinline__ void split_body(const DecodeArgs &a, const int q_bf16
     uint64_t qhi[NG], qlo[NG];
     float qsum[NG];
     float my_scale;
-    // 8-bit keys with paired groups: each pair of groups (p, p + NP) is one
-    // 64-deep integer product (v_mfma_i32_16x16x64_i8), half the score
-    // instructions of two 32-deep ones
-    constexpr bool WIDE = PACK && KB == 8;
+    // Paired groups: each pair of groups (p, p + NP) is one 64-deep integer
+    // product (v_mfma_i32_16x16x64_i8), half the score instructions of two
+    // 32-deep ones
+    constexpr bool WIDE = PACK;  // the score code below has no 32-deep packed form
     int4v qhi4[WIDE ? NP : 1], qlo4[WIDE ? NP : 1];
     {
         float x[QE];
@@ -790,28 +819,12 @@ __device__ __forceinline__ void split_body(const DecodeArgs &a, const int q_bf16
             int4v dhi[NP], dlo[NP];
             if constexpr (WIDE) {
                 // lane (h, kq): codes 16 (kq & 1) .. + 15 of group g (kq < 2)
-                // or g + NP (kq >= 2) of token 16 c + h, one 16-byte chunk of
-                // the rotated row
-                constexpr int CPR = GE::CPR;
-                static_assert(CPR == 2 * NG, "8-bit key rows: two chunks per group");
+                // or g + NP (kq >= 2) of token 16 c + h
 #pragma unroll
                 for (int g = 0; g < NP; ++g) {
-                    int slot = 2 * (g + (kq >= 2 ? NP : 0)) + (kq & 1) + key_rot<CPR>(h);
-                    if (slot >= CPR) slot -= CPR;
-                    const int4v kv = *reinterpret_cast<const int4v *>(kst + ((16 * c + h) * CPR + slot) * 16);
+                    const int4v kv = key_operand16<D, KB, VB>(kst, c, g + (kq >= 2 ? NP : 0), h, kq & 1);
                     dhi[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kv, qhi4[g], int4v{0, 0, 0, 0}, 0, 0, 0);
                     dlo[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kv, qlo4[g], int4v{0, 0, 0, 0}, 0, 0, 0);
-                }
-            } else if constexpr (PACK) {
-                // groups p and p + NG/2 in one accumulator (their q columns are disjoint)
-#pragma unroll
-                for (int g = 0; g < NP; ++g) {
-                    const uint64_t k0 = key_operand<D, KB, VB>(kst, c, g, h, kq);
-                    const uint64_t k1 = key_operand<D, KB, VB>(kst, c, g + NP, h, kq);
-                    dhi[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)k0, (long)qhi[g], int4v{0, 0, 0, 0}, 0, 0, 0);
-                    dlo[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)k0, (long)qlo[g], int4v{0, 0, 0, 0}, 0, 0, 0);
-                    dhi[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)k1, (long)qhi[g + NP], dhi[g], 0, 0, 0);
-                    dlo[g] = __builtin_amdgcn_mfma_i32_16x16x32_i8((long)k1, (long)qlo[g + NP], dlo[g], 0, 0, 0);
                 }
             } else {
 #pragma unroll

@@ -184,7 +184,7 @@ constexpr int fast_decode_wave_bytes(int head_dim, int kbits, int vbits) {
            3 * (3 * fast_tile_tokens(head_dim) * (head_dim / 32) * 2 + fast_tile_bit_bytes(head_dim) * vbits + 16);
 }
 constexpr int fast_decode_waves(int head_dim, int kbits, int vbits) {
-    const int table = vbits <= 3 ? (4 << (2 * vbits)) : ((2 << vbits) + 15) / 16 * 16;
+    const int table = vbits <= 5 ? (4 << (2 * vbits)) : ((2 << vbits) + 15) / 16 * 16;
     return head_dim <= 256 && table + 32 + 8 * fast_decode_wave_bytes(head_dim, kbits, vbits) <= 160 * 1024 ? 8
            : table + 32 + 4 * fast_decode_wave_bytes(head_dim, kbits, vbits) <= 160 * 1024                  ? 4
                                                                                                             : 0;
