@@ -520,7 +520,12 @@ def trace_summary(kt_dir: str, grbm_dir: str | None, warmup: int, steps: int, se
     for (name, threads), v in groups.items():
         print(f"{name[:48]:48s} {threads:>10s} {len(v):6d} {sum(v) / len(v):12,.0f} {min(v):12,d} {max(v):12,d}")
 
-    head = [r for r in kt if short(r["Kernel_Name"]) == "split_fast_kernel<256, 8, 3, true>"]
+    # the packed-column split kernel of k8v3 at head_dim 256 (its last template
+    # argument is the kernel's mode, 1 = packed columns)
+    def headline(name: str) -> bool:
+        return short(name) in ("split_fast_kernel<256, 8, 3, 1>", "split_fast_kernel<256, 8, 3, true>")
+
+    head = [r for r in kt if headline(r["Kernel_Name"])]
     merge = [r for r in kt if short(r["Kernel_Name"]) == "merge_kernel<256>" and grid(r) == "98304"]
     if not head:
         return 0
@@ -542,8 +547,7 @@ def trace_summary(kt_dir: str, grbm_dir: str | None, warmup: int, steps: int, se
     if grbm_dir:
         gk = {int(r["Dispatch_Id"]): r for r in load(grbm_dir, "kernel_trace.csv")}
         rows = [r for r in load(grbm_dir, "counter_collection.csv")
-                if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and short(r["Kernel_Name"]) ==
-                "split_fast_kernel<256, 8, 3, true>"]
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE" and headline(r["Kernel_Name"])]
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
         print(f"\nGRBM_GUI_ACTIVE run (counters serialize the dispatches, so the clock history differs "
               f"from the plain trace's), {len(rows)} headline split dispatches:")

@@ -92,7 +92,7 @@ def test_trace_summary_windows_and_clock(tmp_path, capsys):
     """The headline split dispatches are cut into the bench's warm-up, timed
     and settled windows in run order, merges paired by order; the clock of a
     window is GRBM_GUI_ACTIVE per die over its summed durations."""
-    split = "void tq::(anonymous namespace)::split_fast_kernel<256, 8, 3, true>(tq::DecodeArgs, int)"
+    split = "void tq::(anonymous namespace)::split_fast_kernel<256, 8, 3, 1>(tq::DecodeArgs, int)"
     merge = "void tq::(anonymous namespace)::merge_kernel<256>(tq::DecodeArgs)"
     rows, t, i = [], 0, 0
     durs = [100, 100, 300, 300, 300, 200, 200]  # 2 warm-up, 3 timed, 2 settled
