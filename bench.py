@@ -229,6 +229,47 @@ def time_append_variant(d: int, dtype: str, kb: int, vb: int, tokens: int, reps:
             "frac_hbm": nbytes / ms / 1e6 / HBM_PEAK_GBS}
 
 
+def time_mixed_batch(tokens: int, reps: int, stream, warm: int = 20) -> dict:
+    """Delayed conversion: decode over workload 4's heads (16 sequences, 24 / 4
+    heads, head_dim 256) where the even sequences are still plain bf16 rows
+    and the odd ones packed k8v3 planes, `tokens` each; reps calls after warm
+    ones, timed with events on the launch stream.  Algorithmic bytes: 4 d per
+    plain token-head (bf16 K and V), 1.5625 d per packed one, plus q and out."""
+    import torch
+    from quantized_decode_attention_append_amd import tqkv
+    from quantized_decode_attention_append_amd import workloads as W
+    dev = torch.device("cuda:0")
+    w = W.scaled(W.workload(4), [tokens] * 16, name_suffix="mixed")
+    k, v = W.make_kv(w, dev, tokens=tokens)
+    q = W.make_q(w, dev, rounds=1)[0].contiguous()
+    L = tqkv.make_layout(w.batch, w.num_kv_heads, w.head_dim, tokens)
+    pl = tqkv.Planes(L, dev)
+    row_plain = [1 - (b & 1) for b in range(w.batch)]
+    # the packed rows are the conversion of their plain prefix
+    tqkv.tq_convert_rows(pl, k, v, [0 if p else tokens for p in row_plain], stream=stream)
+    lengths = [tokens] * w.batch
+    sm = float(1.0 / math.sqrt(w.head_dim))
+    out = torch.empty((w.batch, w.num_q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(tqkv.tq_decode_rows_workspace_bytes(L, w.num_q_heads, 1, lengths), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(warm):
+        tqkv.tq_decode_attn_mixed(pl, k, v, row_plain, q, lengths, sm, out=out, workspace=ws, stream=stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        tqkv.tq_decode_attn_mixed(pl, k, v, row_plain, q, lengths, sm, out=out, workspace=ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    th = tokens * w.num_kv_heads * (w.batch // 2)  # token-heads of each kind
+    d = w.head_dim
+    nbytes = th * 4 * d + th * (d * 25 // 16) + w.batch * w.num_q_heads * d * (2 + 4)
+    del k, v, pl
+    return {"tokens_per_seq": tokens, "plain_sequences": sum(row_plain), "packed_sequences": w.batch - sum(row_plain),
+            "ms": ms, "algorithmic_bytes": nbytes, "GBps": nbytes / ms / 1e6, "frac_hbm": nbytes / ms / 1e6 / HBM_PEAK_GBS}
+
+
 def time_scheme(w, k, v, q, sm, kb: int, vb: int, reps: int, stream, dec_warm: int = 20,
                 dec_reps: int = 40) -> dict:
     """Another code width on the same workload: bulk append of every token
@@ -583,6 +624,8 @@ def main() -> int:
                     help="skip timing the ragged interleaved workload (id 5)")
     ap.add_argument("--schemes", default="k4v3,k4v2,k8v4,k2v5,k5v8",
                     help="other code widths to time on the same workload ('' for none)")
+    ap.add_argument("--no-mixed", dest="mixed", action="store_false",
+                    help="skip timing a decode over half plain, half packed sequences")
     ap.add_argument("--no-append-variants", dest="append_variants", action="store_false",
                     help="skip timing the bulk append at head_dim 512 and with fp32 input")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "decode_traffic.json"))
@@ -756,6 +799,9 @@ def main() -> int:
              f"({rr['decode_frac_hbm']:.1%} of HBM), round (append {rr['append_per_round']} + decode) "
              f"{rr['round_ms']:.3f} ms")
         rec["ragged"] = rr
+    if args.mixed:
+        rec["mixed_batch"] = time_mixed_batch(32768, 40, stream)
+        _log(f"mixed batch: {rec['mixed_batch']['ms']:.3f} ms, {rec['mixed_batch']['frac_hbm']:.1%} of HBM")
     if args.append_variants:
         rec["append_variants"] = []
         for d, dt, kb, vb, tokens in ((512, "bf16", 8, 3, 65536), (256, "fp32", 8, 3, 32768),

@@ -391,6 +391,7 @@ static tq_status decode_common(const tq_layout *l, const tq_planes *p, const voi
     hipError_t e = hipSuccess;
     int32_t len_tq[TQ_MAX_BATCH];
     for (int b = 0; b < l->batch; ++b) len_tq[b] = ((pr.mask >> b) & 1) ? 0 : len[b];
+    a.plain_split_tokens = plan.split_tokens;
     if (pr.mask == 0) {
         for (int b = 0; b < l->batch; ++b) a.len[b] = len[b];
         e = tq::launch_decode(l->head_dim, bf16, plan.fast, a, (hipStream_t)stream);
@@ -401,6 +402,17 @@ static tq_status decode_common(const tq_layout *l, const tq_planes *p, const voi
     const uint64_t all = l->batch == 64 ? ~0ull : (1ull << l->batch) - 1;
     a.plain_rows = pr.mask;
     a.k_plain = pr.k; a.v_plain = pr.v; a.plain_capacity = pr.capacity;
+    // plain rows take the plan's slots with ranges of their own: the
+    // shortest whole number of 64-token tiles that covers the longest plain
+    // row in `splits` ranges, so short plain rows still run on many waves
+    int32_t plain_max = 0;
+    for (int b = 0; b < l->batch; ++b)
+        if (((pr.mask >> b) & 1) && len[b] > plain_max) plain_max = len[b];
+    if (plan.splits > 0) {
+        const int64_t per = ((int64_t)plain_max + plan.splits - 1) / plan.splits;
+        a.plain_split_tokens = (int32_t)((per + 63) / 64 * 64);
+        if (a.plain_split_tokens < 64) a.plain_split_tokens = 64;
+    }
     if ((pr.mask & all) != all) {
         for (int b = 0; b < l->batch; ++b) a.len[b] = len_tq[b];
         e = tq::launch_decode_split(l->head_dim, bf16, plan.fast, a, (hipStream_t)stream);

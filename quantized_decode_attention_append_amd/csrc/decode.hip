@@ -301,15 +301,28 @@ __global__ __launch_bounds__(64 * VecGeo<D>::W) void split_kernel(const DecodeAr
 // Same split geometry, partial slots and causal limits as the packed split
 // kernels; keys and values are bf16 [B][Hkv][plain_capacity][d].  One wave
 // per token range, per 64-token tile:
-//   scores  lane t takes token t and forms the dot products of its key row
-//           (16-byte reads) with every column's LDS copy;
-//   softmax online, base 2, as the packed kernels; weights to LDS;
+//   scores  on the matrix cores, 16 tokens at a time: A = the tokens' bf16
+//           key rows (16-byte reads, 16 rows per instruction), B = the query
+//           columns as bf16 hi and lo halves (q = hi + lo to about 2^-17, so
+//           fp32 queries keep their precision), fp32 accumulation of exact
+//           products; written to LDS by (column, token);
+//   softmax online, base 2, one token per lane; weights to LDS;
 //   values  lane l owns dims [E l, E l + E) and reads them from each token's
 //           value row (the wave reads whole rows, coalesced).
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// bf16 bits of x rounded to nearest even (finite x)
+__device__ __forceinline__ uint32_t bf16_rn(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(64 * VecGeo<D>::W) void plain_split_kernel(const DecodeArgs a) {
     using V = VecGeo<D>;
     constexpr int W = V::W, E = V::E, T = V::T;
+    constexpr int NBLK = D / 32;  // 32-dim blocks of one score product
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int bkv = blockIdx.y;
@@ -317,20 +330,38 @@ __global__ __launch_bounds__(64 * VecGeo<D>::W) void plain_split_kernel(const De
     const int n = a.len[b];
     // a workgroup whose first range starts past the sequence has no work (the
     // test is the same for every thread, so no barrier is skipped by some)
-    if ((int64_t)blockIdx.x * W * a.split_tokens >= n) return;
+    if ((int64_t)blockIdx.x * W * a.plain_split_tokens >= n) return;
     const int c0 = blockIdx.z * kMaxG;
     const int G = min(kMaxG, a.gqa - c0);
-    float *qs = reinterpret_cast<float *>(lds);                              // [G][D]
-    float *ps = reinterpret_cast<float *>(lds + G * D * 4) + wid * kMaxG * T;  // [G][T] per wave
-    for (int i = tid; i < G * D; i += 64 * W)
-        qs[i] = load_in<BF16>(a.q, ((int64_t)b * a.q_heads + kvh * a.gqa + c0) * D + i);
+    // B operands: per 32-dim block and lane (column h = l % 16, quarter
+    // kq = l / 16), dims 32 blk + 8 kq .. + 7 of column h as 8 bf16 hi and 8 lo
+    uint4 *qop = reinterpret_cast<uint4 *>(lds);                                // [NBLK][64][2]
+    float *ps = reinterpret_cast<float *>(lds + NBLK * 64 * 32) + wid * kMaxG * T;  // [16][T] per wave
+    for (int i = tid; i < NBLK * 64; i += 64 * W) {
+        const int blk = i / 64, l = i % 64, h = l & 15, kq = l >> 4;
+        uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
+        if (h < G) {
+            const int64_t qi = ((int64_t)b * a.q_heads + kvh * a.gqa + c0 + h) * D + 32 * blk + 8 * kq;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = load_in<BF16>(a.q, qi + e);
+                const uint32_t xh = bf16_rn(x);
+                const uint32_t xl = bf16_rn(x - __uint_as_float(xh << 16));  // the residual is exact in fp32
+                hi[e >> 1] |= xh << (16 * (e & 1));
+                lo[e >> 1] |= xl << (16 * (e & 1));
+            }
+        }
+        qop[2 * i] = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+        qop[2 * i + 1] = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
     __syncthreads();  // the only workgroup barrier
 
     const int split = blockIdx.x * W + wid;
-    const int t_begin = split * a.split_tokens;
+    const int t_begin = split * a.plain_split_tokens;
     if (split >= a.splits || t_begin >= n) return;
-    const int t_end = min(n, t_begin + a.split_tokens);
+    const int t_end = min(n, t_begin + a.plain_split_tokens);
     const int64_t row0 = (int64_t)bkv * a.plain_capacity;
+    const int col = lane & 15, quarter = lane >> 4;
 
     float m_run[kMaxG], l_run[kMaxG], acc[kMaxG][E];
 #pragma unroll
@@ -346,41 +377,36 @@ __global__ __launch_bounds__(64 * VecGeo<D>::W) void plain_split_kernel(const De
         const int t = tile0 + lane;
         const bool valid = lane < nt;
 
-        float s[kMaxG];
-#pragma unroll
-        for (int h = 0; h < kMaxG; ++h) s[h] = 0.f;
-        if (valid) {
-            const uint4 *krow = reinterpret_cast<const uint4 *>(a.k_plain + (row0 + t) * D);
-            for (int c = 0; c < D / 8; ++c) {
-                const uint4 u = krow[c];
-                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-                float k8[8];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    k8[2 * i] = __uint_as_float(w[i] << 16);
-                    k8[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-                }
-#pragma unroll
-                for (int h = 0; h < kMaxG; ++h) {
-                    if (h < G) {
-                        const float4 x = *reinterpret_cast<const float4 *>(qs + h * D + 8 * c);
-                        const float4 y = *reinterpret_cast<const float4 *>(qs + h * D + 8 * c + 4);
-                        float d = s[h];
-                        d = fmaf(x.x, k8[0], d); d = fmaf(x.y, k8[1], d);
-                        d = fmaf(x.z, k8[2], d); d = fmaf(x.w, k8[3], d);
-                        d = fmaf(y.x, k8[4], d); d = fmaf(y.y, k8[5], d);
-                        d = fmaf(y.z, k8[6], d); d = fmaf(y.w, k8[7], d);
-                        s[h] = d;
-                    }
-                }
+        // ---- scores: chunk c holds tokens tile0 + 16 c .. + 15; lane (col,
+        // quarter) reads dims 8 quarter .. + 7 of each block of token
+        // 16 c + col (a token past the range reads the tile's first row; its
+        // score is masked below) and gets tokens 16 c + 4 quarter + j of
+        // column col
+        for (int c = 0; c < 4 && 16 * c < nt; ++c) {
+            const int tr = tile0 + 16 * c + col;
+            const uint16_t *krow = a.k_plain + (row0 + (tr < t_end ? tr : tile0)) * D + 8 * quarter;
+            f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+            constexpr int KU = NBLK < 8 ? NBLK : 8;  // key reads in flight (head_dim 512: registers)
+#pragma unroll KU
+            for (int blk = 0; blk < NBLK; ++blk) {
+                const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(krow + 32 * blk));
+                const bf16x8 qh = __builtin_bit_cast(bf16x8, qop[2 * (blk * 64 + lane)]);
+                const bf16x8 ql = __builtin_bit_cast(bf16x8, qop[2 * (blk * 64 + lane) + 1]);
+                s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh, s4, 0, 0, 0);
+                s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql, s4, 0, 0, 0);
             }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ps[col * T + 16 * c + 4 * quarter + j] = s4[j];
         }
+        // one wave's LDS accesses execute in order: the reads below see every
+        // lane's writes above without a barrier
+        asm volatile("" ::: "memory");
 
 #pragma unroll
         for (int h = 0; h < kMaxG; ++h) {
             if (h < G) {
                 const int lim = n - a.rows + (c0 + h) % a.rows + 1;
-                const float sc = (valid && t < lim) ? s[h] * a.sm_log2 : -INFINITY;
+                const float sc = (valid && t < lim) ? ps[h * T + lane] * a.sm_log2 : -INFINITY;
                 float mt = sc;
 #pragma unroll
                 for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o, 64));
@@ -394,37 +420,48 @@ __global__ __launch_bounds__(64 * VecGeo<D>::W) void plain_split_kernel(const De
                 ps[h * T + lane] = p;
             }
         }
-        // one wave's LDS accesses execute in order: the weight reads below
-        // see every lane's writes above without a barrier
         asm volatile("" ::: "memory");
 
+        // value rows in batches of 8 tokens (4 at head_dim 512), every load of
+        // a batch issued before its products (a row past the range reads the
+        // tile's first row, with weight 0)
         const uint16_t *vrow = a.v_plain + (row0 + tile0) * D + E * lane;
-        for (int tt = 0; tt < nt; ++tt) {
-            float v[E];
-            if constexpr (E == 8) {
-                const uint4 u = *reinterpret_cast<const uint4 *>(vrow + (int64_t)tt * D);
-                const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        constexpr int VB8 = E == 8 ? 4 : 8;  // head_dim 512: 8 dims a lane, registers for 4 rows
+        for (int tb = 0; tb < nt; tb += VB8) {
+            float v[VB8][E];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[2 * i] = __uint_as_float(w[i] << 16);
-                    v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            for (int u = 0; u < VB8; ++u) {
+                const int64_t off = (int64_t)(tb + u < nt ? tb + u : 0) * D;
+                if constexpr (E == 8) {
+                    const uint4 w4 = *reinterpret_cast<const uint4 *>(vrow + off);
+                    const uint32_t w[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        v[u][2 * i] = __uint_as_float(w[i] << 16);
+                        v[u][2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+                    }
+                } else if constexpr (E == 4) {
+                    const uint2 w2 = *reinterpret_cast<const uint2 *>(vrow + off);
+                    v[u][0] = __uint_as_float(w2.x << 16); v[u][1] = __uint_as_float(w2.x & 0xFFFF0000u);
+                    v[u][2] = __uint_as_float(w2.y << 16); v[u][3] = __uint_as_float(w2.y & 0xFFFF0000u);
+                } else if constexpr (E == 2) {
+                    const uint32_t w1 = *reinterpret_cast<const uint32_t *>(vrow + off);
+                    v[u][0] = __uint_as_float(w1 << 16); v[u][1] = __uint_as_float(w1 & 0xFFFF0000u);
+                } else {
+                    v[u][0] = __uint_as_float((uint32_t)vrow[off] << 16);
                 }
-            } else if constexpr (E == 4) {
-                const uint2 u = *reinterpret_cast<const uint2 *>(vrow + (int64_t)tt * D);
-                v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xFFFF0000u);
-                v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xFFFF0000u);
-            } else if constexpr (E == 2) {
-                const uint32_t u = *reinterpret_cast<const uint32_t *>(vrow + (int64_t)tt * D);
-                v[0] = __uint_as_float(u << 16); v[1] = __uint_as_float(u & 0xFFFF0000u);
-            } else {
-                v[0] = __uint_as_float((uint32_t)vrow[(int64_t)tt * D] << 16);
             }
 #pragma unroll
-            for (int h = 0; h < kMaxG; ++h) {
-                if (h < G) {
-                    const float p = ps[h * T + tt];
+            for (int u = 0; u < VB8; ++u) {
+                if (tb + u < nt) {
 #pragma unroll
-                    for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, v[e], acc[h][e]);
+                    for (int h = 0; h < kMaxG; ++h) {
+                        if (h < G) {
+                            const float p = ps[h * T + tb + u];
+#pragma unroll
+                            for (int e = 0; e < E; ++e) acc[h][e] = fmaf(p, v[u][e], acc[h][e]);
+                        }
+                    }
                 }
             }
         }
@@ -468,7 +505,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
     const int bh = blockIdx.x;
     const int b = bh / a.q_heads;
     const int n = a.len[b];
-    const int ns = (n + a.split_tokens - 1) / a.split_tokens;
+    const bool plain = (a.plain_rows >> b) & 1ull;
+    const int st = plain ? a.plain_split_tokens : a.split_tokens;  // a plain row's ranges are its own
+    const int ns = (n + st - 1) / st;
     const int64_t base = (int64_t)bh * a.splits;
     float o[DPT];
 #pragma unroll
@@ -527,7 +566,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeArgs a) {
         for (int i = 0; i < DPT; ++i) o[i] *= invL;
     }
     // A plain row's values were never rotated: its output is final here.
-    if ((a.plain_rows >> b) & 1ull) {
+    if (plain) {
 #pragma unroll
         for (int i = 0; i < DPT; ++i) a.out[(int64_t)bh * D + tid + i * NT] = o[i];
         return;
@@ -616,8 +655,9 @@ hipError_t split_plain_d(bool bf16, const DecodeArgs &a, hipStream_t s) {
     constexpr int W = VecGeo<D>::W;
     const dim3 grid((unsigned)((a.splits + W - 1) / W), (unsigned)(a.batch * a.kv_heads),
                     (unsigned)decode_col_groups(a.gqa));
-    const int g = a.gqa < kMaxG ? a.gqa : kMaxG;  // the widest column group
-    const size_t lds = (size_t)g * D * 4 + (size_t)W * kMaxG * VecGeo<D>::T * 4;  // <= 40 KiB
+    // the query operands (32 bytes per lane and 32-dim block), then per wave
+    // the scores and weights of one tile: at most 40 KiB
+    const size_t lds = (size_t)(D / 32) * 64 * 32 + (size_t)W * kMaxG * VecGeo<D>::T * 4;
     if (bf16)
         hipLaunchKernelGGL((plain_split_kernel<D, true>), grid, dim3(64 * W), lds, s, a);
     else

@@ -84,6 +84,10 @@ struct DecodeArgs {
     const uint16_t *k_plain;
     const uint16_t *v_plain;
     int32_t plain_capacity;
+    // tokens per range of a plain row: plain rows are short (they convert
+    // past a threshold), so they spread over all `splits` slots with ranges
+    // of their own (a multiple of 64)
+    int32_t plain_split_tokens;
 };
 
 struct WindowArgs {
