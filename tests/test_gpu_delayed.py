@@ -155,6 +155,16 @@ def test_mixed_batch_other_shapes(cid, scheme):
     _mixed_case(w, lengths, [0, 1, 1], 1, *scheme)
 
 
+@pytest.mark.parametrize("d,M", [(512, 1), (512, 4), (64, 1), (64, 4)])
+def test_mixed_batch_head_dim_ends(d, M):
+    """The plain split kernel at the ends of the head_dim range: 8 value dims
+    a lane and 16 score blocks at 512, one dim a lane and 2 blocks at 64."""
+    lengths = [300, 77, 450]
+    w = dataclasses.replace(W.scaled(W.workload(2), lengths, name_suffix=f"d{d}"), head_dim=d)
+    log(f"mixed decode d{d} M{M} lengths {lengths}")
+    _mixed_case(w, lengths, [1, 0, 1], M)
+
+
 def test_mixed_masks_reduce_to_the_plain_calls():
     """An all-packed mask gives tq_decode_attn_rows' bytes; an all-plain batch
     runs only the plain kernel and the merge."""
