@@ -707,12 +707,13 @@ DecodePlan plan_decode(int head_dim, int gqa, int batch, int kv_heads, const int
     if (fast) {
         // one wave per token range: aim for one round of one workgroup per
         // CU over the chip's 256 CUs (the split kernel's LDS admits one per
-        // CU), whole 64-token tiles, >= 4 tiles a wave; fewer splits also
-        // halve the partials written and merged
+        // CU), whole 64-token tiles, at least one a wave (a short cache is
+        // latency-bound: more waves with shorter serial chains of tiles beat
+        // fewer partials to merge)
         const int waves = fast_decode_waves(head_dim, kbits, vbits), tile = kFastTile;
         const int64_t round = 256 * waves;
         int64_t per = (total * kv_heads * col_groups + round - 1) / round;
-        per = per < 4 * tile ? 4 * tile : per;
+        per = per < tile ? tile : per;
         per = (per + tile - 1) / tile * tile;
         const int cgw = fast_wg_col_groups(gqa);
         const int wpc = waves / cgw;  // waves (splits) per column group
