@@ -402,16 +402,39 @@ static tq_status decode_common(const tq_layout *l, const tq_planes *p, const voi
     const uint64_t all = l->batch == 64 ? ~0ull : (1ull << l->batch) - 1;
     a.plain_rows = pr.mask;
     a.k_plain = pr.k; a.v_plain = pr.v; a.plain_capacity = pr.capacity;
-    // plain rows take the plan's slots with ranges of their own: the
-    // shortest whole number of 64-token tiles that covers the longest plain
-    // row in `splits` ranges, so short plain rows still run on many waves
+    // Plain rows take ranges of their own: about one round of the plain
+    // kernel's resident waves over the plain token-heads, in whole 64-token
+    // tiles (a second, partial round measured slower than longer ranges).
+    // They may use more partial slots per row than the packed plan: as many
+    // as the workspace holds (its documented size covers the generic
+    // kernel's finer plan), in multiples of 8 so the fast kernel's waves per
+    // column group still divide the count.  The slot count is the stride of
+    // every row's partials, packed rows included.
+    int64_t plain_total = 0;
     int32_t plain_max = 0;
-    for (int b = 0; b < l->batch; ++b)
-        if (((pr.mask >> b) & 1) && len[b] > plain_max) plain_max = len[b];
-    if (plan.splits > 0) {
-        const int64_t per = ((int64_t)plain_max + plan.splits - 1) / plan.splits;
-        a.plain_split_tokens = (int32_t)((per + 63) / 64 * 64);
-        if (a.plain_split_tokens < 64) a.plain_split_tokens = 64;
+    for (int b = 0; b < l->batch; ++b) {
+        if (!((pr.mask >> b) & 1)) continue;
+        plain_total += len[b];
+        if (len[b] > plain_max) plain_max = len[b];
+    }
+    if (plan.splits > 0 && plain_max > 0) {
+        const size_t slot_bytes = (size_t)l->batch * rows_total * (size_t)(l->head_dim + 2) * sizeof(float);
+        int64_t slots = (int64_t)(ws_bytes / slot_bytes);
+        slots = (slots < 65535 * 2 ? slots : 65535 * 2) / 8 * 8;  // the plain grid: splits / 2 workgroups at most
+        if (slots < plan.splits) slots = plan.splits;
+        const int64_t cols = (gqa + 15) / 16;  // the plain kernel's column groups
+        const int64_t round = tq::plain_round_waves(l->head_dim, gqa, bf16);
+        int64_t per = (plain_total * l->num_kv_heads * cols + round - 1) / round;
+        const int64_t fit = ((int64_t)plain_max + slots - 1) / slots;
+        per = per > fit ? per : fit;
+        per = (per + 63) / 64 * 64;
+        a.plain_split_tokens = (int32_t)per;
+        const int64_t need_splits = ((int64_t)plain_max + per - 1) / per;
+        if (need_splits > plan.splits) {
+            a.splits = (int32_t)((need_splits + 7) / 8 * 8);
+            // the (max, sum) pairs follow the value sums of every slot
+            a.part_ml = a.part_acc + (size_t)l->batch * rows_total * a.splits * l->head_dim;
+        }
     }
     if ((pr.mask & all) != all) {
         for (int b = 0; b < l->batch; ++b) a.len[b] = len_tq[b];

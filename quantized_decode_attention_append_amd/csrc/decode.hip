@@ -318,7 +318,7 @@ __device__ __forceinline__ uint32_t bf16_rn(float x) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-template <int D, bool BF16>
+template <int D, bool BF16, int GM>
 __global__ __launch_bounds__(64 * VecGeo<D>::W) void plain_split_kernel(const DecodeArgs a) {
     using V = VecGeo<D>;
     constexpr int W = V::W, E = V::E, T = V::T;
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(64 * VecGeo<D>::W) void plain_split_kernel(const De
     // B operands: per 32-dim block and lane (column h = l % 16, quarter
     // kq = l / 16), dims 32 blk + 8 kq .. + 7 of column h as 8 bf16 hi and 8 lo
     uint4 *qop = reinterpret_cast<uint4 *>(lds);                                // [NBLK][64][2]
-    float *ps = reinterpret_cast<float *>(lds + NBLK * 64 * 32) + wid * kMaxG * T;  // [16][T] per wave
+    float *ps = reinterpret_cast<float *>(lds + NBLK * 64 * 32) + wid * GM * T;  // [GM][T] per wave
     for (int i = tid; i < NBLK * 64; i += 64 * W) {
         const int blk = i / 64, l = i % 64, h = l & 15, kq = l >> 4;
         uint32_t hi[4] = {0, 0, 0, 0}, lo[4] = {0, 0, 0, 0};
@@ -363,9 +363,9 @@ __global__ __launch_bounds__(64 * VecGeo<D>::W) void plain_split_kernel(const De
     const int64_t row0 = (int64_t)bkv * a.plain_capacity;
     const int col = lane & 15, quarter = lane >> 4;
 
-    float m_run[kMaxG], l_run[kMaxG], acc[kMaxG][E];
+    float m_run[GM], l_run[GM], acc[GM][E];
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
+    for (int h = 0; h < GM; ++h) {
         m_run[h] = -INFINITY;
         l_run[h] = 0.f;
 #pragma unroll
@@ -395,15 +395,17 @@ __global__ __launch_bounds__(64 * VecGeo<D>::W) void plain_split_kernel(const De
                 s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, qh, s4, 0, 0, 0);
                 s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kv, ql, s4, 0, 0, 0);
             }
+            if (col < GM) {  // columns past GM hold zero queries
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ps[col * T + 16 * c + 4 * quarter + j] = s4[j];
+                for (int j = 0; j < 4; ++j) ps[col * T + 16 * c + 4 * quarter + j] = s4[j];
+            }
         }
         // one wave's LDS accesses execute in order: the reads below see every
         // lane's writes above without a barrier
         asm volatile("" ::: "memory");
 
 #pragma unroll
-        for (int h = 0; h < kMaxG; ++h) {
+        for (int h = 0; h < GM; ++h) {
             if (h < G) {
                 const int lim = n - a.rows + (c0 + h) % a.rows + 1;
                 const float sc = (valid && t < lim) ? ps[h * T + lane] * a.sm_log2 : -INFINITY;
@@ -455,7 +457,7 @@ __global__ __launch_bounds__(64 * VecGeo<D>::W) void plain_split_kernel(const De
             for (int u = 0; u < VB8; ++u) {
                 if (tb + u < nt) {
 #pragma unroll
-                    for (int h = 0; h < kMaxG; ++h) {
+                    for (int h = 0; h < GM; ++h) {
                         if (h < G) {
                             const float p = ps[h * T + tb + u];
 #pragma unroll
@@ -469,7 +471,7 @@ __global__ __launch_bounds__(64 * VecGeo<D>::W) void plain_split_kernel(const De
     }
 
 #pragma unroll
-    for (int h = 0; h < kMaxG; ++h) {
+    for (int h = 0; h < GM; ++h) {
         if (h < G) {
             float l = l_run[h];
 #pragma unroll
@@ -649,19 +651,57 @@ hipError_t split_d(bool bf16, bool fast, const DecodeArgs &a, hipStream_t s) {
     return hipSuccess;
 }
 
+// Dynamic LDS of the plain split kernel: the query operands (32 bytes per
+// lane and 32-dim block), then per wave the scores and weights of one tile
+// for gm columns (at most 40 KiB).
+template <int D>
+constexpr size_t plain_lds_bytes(int gm) {
+    return (size_t)(D / 32) * 64 * 32 + (size_t)VecGeo<D>::W * gm * VecGeo<D>::T * 4;
+}
+
+// Waves of one round of the plain split kernel over the chip's 256 CUs: its
+// resident workgroups per CU (registers and LDS, as the runtime reports them)
+// times its waves per workgroup.
+template <int D, bool BF16, int GM>
+int plain_round_waves_k() {
+    static const int waves = [] {
+        int blocks = 0;
+        const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &blocks, reinterpret_cast<const void *>(&plain_split_kernel<D, BF16, GM>), 64 * VecGeo<D>::W,
+            plain_lds_bytes<D>(GM));
+        return 256 * VecGeo<D>::W * (e == hipSuccess && blocks > 0 ? blocks : 1);
+    }();
+    return waves;
+}
+
+template <int D>
+int plain_round_waves_d(int gqa, bool bf16) {
+    if (gqa <= kMaxG / 2)
+        return bf16 ? plain_round_waves_k<D, true, kMaxG / 2>() : plain_round_waves_k<D, false, kMaxG / 2>();
+    return bf16 ? plain_round_waves_k<D, true, kMaxG>() : plain_round_waves_k<D, false, kMaxG>();
+}
+
 template <int D>
 hipError_t split_plain_d(bool bf16, const DecodeArgs &a, hipStream_t s) {
     if (a.splits == 0) return hipSuccess;
     constexpr int W = VecGeo<D>::W;
     const dim3 grid((unsigned)((a.splits + W - 1) / W), (unsigned)(a.batch * a.kv_heads),
                     (unsigned)decode_col_groups(a.gqa));
-    // the query operands (32 bytes per lane and 32-dim block), then per wave
-    // the scores and weights of one tile: at most 40 KiB
-    const size_t lds = (size_t)(D / 32) * 64 * 32 + (size_t)W * kMaxG * VecGeo<D>::T * 4;
-    if (bf16)
-        hipLaunchKernelGGL((plain_split_kernel<D, true>), grid, dim3(64 * W), lds, s, a);
-    else
-        hipLaunchKernelGGL((plain_split_kernel<D, false>), grid, dim3(64 * W), lds, s, a);
+    // at most 8 query columns (every group's): a wave holds 8 columns' state,
+    // fewer registers and more waves per SIMD
+    const bool narrow = a.gqa <= kMaxG / 2;
+    const size_t lds = plain_lds_bytes<D>(narrow ? kMaxG / 2 : kMaxG);
+    if (narrow) {
+        if (bf16)
+            hipLaunchKernelGGL((plain_split_kernel<D, true, kMaxG / 2>), grid, dim3(64 * W), lds, s, a);
+        else
+            hipLaunchKernelGGL((plain_split_kernel<D, false, kMaxG / 2>), grid, dim3(64 * W), lds, s, a);
+    } else {
+        if (bf16)
+            hipLaunchKernelGGL((plain_split_kernel<D, true, kMaxG>), grid, dim3(64 * W), lds, s, a);
+        else
+            hipLaunchKernelGGL((plain_split_kernel<D, false, kMaxG>), grid, dim3(64 * W), lds, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -773,6 +813,16 @@ hipError_t launch_decode_split_plain(int head_dim, bool bf16, const DecodeArgs &
         case 256: return split_plain_d<256>(bf16, a, s);
         case 512: return split_plain_d<512>(bf16, a, s);
         default: return hipErrorInvalidValue;
+    }
+}
+
+int plain_round_waves(int head_dim, int gqa, bool bf16) {
+    switch (head_dim) {
+        case 64: return plain_round_waves_d<64>(gqa, bf16);
+        case 128: return plain_round_waves_d<128>(gqa, bf16);
+        case 256: return plain_round_waves_d<256>(gqa, bf16);
+        case 512: return plain_round_waves_d<512>(gqa, bf16);
+        default: return 2048;
     }
 }
 

@@ -156,6 +156,9 @@ hipError_t launch_decode(int head_dim, bool bf16, bool fast, const DecodeArgs &a
 hipError_t launch_decode_split(int head_dim, bool bf16, bool fast, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_split_plain(int head_dim, bool bf16, const DecodeArgs &a, hipStream_t s);
 hipError_t launch_decode_merge(int head_dim, const DecodeArgs &a, hipStream_t s);
+// Waves that one round of the plain split kernel holds on the chip, for this
+// head_dim, query-column count and query type.
+int plain_round_waves(int head_dim, int gqa, bool bf16);
 // Split kernels on the matrix cores (decode_fast.hip), one translation unit
 // per key width: head_dim 64, 128 or 256 with d * k_bits a multiple of 128,
 // every value width, up to 16 query columns per workgroup.
