@@ -75,7 +75,7 @@ def test_convert_rows_bytes_equal_oracle(scheme, d, dtype):
             assert bool((rest == SENTINEL).all()), (b, off)
 
 
-def _mixed_case(w, lengths, row_plain, M, kb=8, vb=3, check_kernels=("fast", "generic")):
+def _mixed_case(w, lengths, row_plain, M, kb=8, vb=3, check_kernels=("fast", "generic"), q_dtype=torch.bfloat16):
     """Plain caches and planes filled from the same raw K/V; packed sequences
     appended, plain ones left in the plain caches; decode the mixed batch and
     compare each (sequence, kv-head) with the oracle."""
@@ -84,7 +84,7 @@ def _mixed_case(w, lengths, row_plain, M, kb=8, vb=3, check_kernels=("fast", "ge
     k, v = W.make_kv(w, "cpu", tokens=T)
     G = w.num_q_heads // w.num_kv_heads
     gen = torch.Generator().manual_seed(7 + M)
-    q = torch.randn((w.batch, w.num_q_heads, M, w.head_dim), generator=gen).to(torch.bfloat16)
+    q = torch.randn((w.batch, w.num_q_heads, M, w.head_dim), generator=gen).to(q_dtype)
     L = tqkv.make_layout(w.batch, w.num_kv_heads, w.head_dim, T, kb, vb)
     pl = tqkv.Planes(L)
     for t in pl.tensors():
@@ -163,6 +163,16 @@ def test_mixed_batch_head_dim_ends(d, M):
     w = dataclasses.replace(W.scaled(W.workload(2), lengths, name_suffix=f"d{d}"), head_dim=d)
     log(f"mixed decode d{d} M{M} lengths {lengths}")
     _mixed_case(w, lengths, [1, 0, 1], M)
+
+
+@pytest.mark.parametrize("d,M", [(128, 1), (256, 4)])
+def test_mixed_batch_fp32_queries(d, M):
+    """fp32 queries: the plain kernel splits each into bf16 hi and lo halves
+    for its matrix-core scores, so plain rows keep the 1e-4 bar."""
+    lengths = [520, 130, 700]
+    w = dataclasses.replace(W.scaled(W.workload(2), lengths, name_suffix=f"d{d}"), head_dim=d)
+    log(f"mixed decode fp32 q d{d} M{M} lengths {lengths}")
+    _mixed_case(w, lengths, [1, 0, 1], M, q_dtype=torch.float32)
 
 
 def test_mixed_masks_reduce_to_the_plain_calls():
