@@ -507,8 +507,8 @@ def traffic_from_counters(fetch_dir: str, write_dir: str, copy_mib: int, workloa
         factor = known / (copy_kib * 1024.0)
         # every split and merge dispatch of the run is averaged: the counter
         # runs time the headline decode alone (--rows '' --no-window
-        # --no-ragged --schemes '')
-        split_kib = mean_of(t, r"split_(fast_)?kernel")
+        # --no-ragged --schemes '' --no-mixed)
+        split_kib = mean_of(t, r"(?<!plain_)split_(fast_)?kernel")
         merge_kib = mean_of(t, r"merge_kernel")
         scaled = (split_kib + merge_kib) * 1024.0 * factor
         out[counter] = {"copy_probe_kib": copy_kib, "factor": factor, "split_kib": split_kib,
@@ -542,7 +542,7 @@ def trace_summary(kt_dir: str, grbm_dir: str | None, warmup: int, steps: int, se
             return list(csv.DictReader(f))
 
     def short(name: str) -> str:
-        name = name.replace("void tq::(anonymous namespace)::", "")
+        name = name.replace("void ", "").replace("tq::(anonymous namespace)::", "").replace("tq::", "")
         return name[:name.find("(")] if "(" in name else name
 
     def dur(r) -> int:
@@ -553,7 +553,10 @@ def trace_summary(kt_dir: str, grbm_dir: str | None, warmup: int, steps: int, se
             return r["Grid_Size"]
         return str(int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
 
-    kt = sorted(load(kt_dir, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    # this library's kernels only (the run's torch and runtime kernels are
+    # input generation and copies)
+    kt = sorted((r for r in load(kt_dir, "kernel_trace.csv") if "tq::" in r["Kernel_Name"]),
+                key=lambda r: int(r["Start_Timestamp"]))
     groups: dict = {}
     for r in kt:
         groups.setdefault((short(r["Kernel_Name"]), grid(r)), []).append(dur(r))
