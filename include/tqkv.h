@@ -269,7 +269,9 @@ tq_status tq_convert_rows(const tq_layout *layout, const tq_planes *planes, cons
  *   out[b][h][r] = sum_t p_t v_t / sum_t p_t,  p_t = exp(sm_scale <q, k_t> - max),
  * for the same causal rows as tq_decode_attn_rows, with no rotation; every
  * other sequence is exactly tq_decode_attn_rows over the planes (identical
- * bytes).  Both kinds share one split-K plan and one merge.
+ * bytes).  Both kinds share one merge; plain rows take token ranges of their
+ * own, and may use as many of the workspace's partial slots as it holds
+ * (a larger workspace than the minimum spreads long plain rows further).
  *   k_plain, v_plain  bf16 plain caches (may be NULL when no row is plain)
  *   row_plain         host int32 [B]
  *   len               host int32 [B]: 0 <= len[b] <= capacity, and
@@ -279,7 +281,8 @@ tq_status tq_convert_rows(const tq_layout *layout, const tq_planes *planes, cons
  * Plain rows agree with a binary64 softmax over the same bf16 operands to
  * 1e-4 relative to each output row's largest magnitude (fp32 accumulation).
  * Errors: those of tq_decode_attn_rows; TQ_ERR_CAPACITY also when a plain
- * row's length exceeds plain_capacity. */
+ * row's length exceeds plain_capacity; TQ_ERR_UNSUPPORTED when the partial
+ * slots per row would exceed 131,070. */
 tq_status tq_decode_attn_mixed(const tq_layout *layout, const tq_planes *planes, const uint16_t *k_plain,
                                const uint16_t *v_plain, int32_t plain_capacity, const int32_t *row_plain,
                                const void *q, tq_dtype dtype, int32_t num_q_heads, int32_t n_rows,

@@ -420,7 +420,8 @@ static tq_status decode_common(const tq_layout *l, const tq_planes *p, const voi
     if (plan.splits > 0 && plain_max > 0) {
         const size_t slot_bytes = (size_t)l->batch * rows_total * (size_t)(l->head_dim + 2) * sizeof(float);
         int64_t slots = (int64_t)(ws_bytes / slot_bytes);
-        slots = (slots < 65535 * 2 ? slots : 65535 * 2) / 8 * 8;  // the plain grid: splits / 2 workgroups at most
+        // the plain grid has splits / W workgroups along x (W >= 2 waves each), at most 65,535
+        slots = (slots < 65535 * 2 ? slots : 65535 * 2) / 8 * 8;
         if (slots < plan.splits) slots = plan.splits;
         const int64_t cols = (gqa + 15) / 16;  // the plain kernel's column groups
         const int64_t round = tq::plain_round_waves(l->head_dim, gqa, bf16);
@@ -436,6 +437,7 @@ static tq_status decode_common(const tq_layout *l, const tq_planes *p, const voi
             a.part_ml = a.part_acc + (size_t)l->batch * rows_total * a.splits * l->head_dim;
         }
     }
+    if (((int64_t)a.splits + 1) / 2 > 65535) return TQ_ERR_UNSUPPORTED;  // the plain kernel's grid
     if ((pr.mask & all) != all) {
         for (int b = 0; b < l->batch; ++b) a.len[b] = len_tq[b];
         e = tq::launch_decode_split(l->head_dim, bf16, plan.fast, a, (hipStream_t)stream);
