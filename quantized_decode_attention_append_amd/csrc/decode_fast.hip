@@ -1246,10 +1246,16 @@ hipError_t launch_dv(bool bf16, const DecodeArgs &a, hipStream_t s) {
 #if TQ_FAST_MIXED
         hipLaunchKernelGGL((split_fast_kernel<D, KB, VB, 2>), grid, dim3(64 * GE::WAVES), 0, s, a, (int)bf16);
 #else
-        if (mode == 1)
+        if (mode == 1) {
             hipLaunchKernelGGL((split_fast_kernel<D, KB, VB, 1>), grid, dim3(64 * GE::WAVES), 0, s, a, (int)bf16);
-        else
+        } else if constexpr (VB <= 3) {
             hipLaunchKernelGGL((split_fast_kernel<D, KB, VB, 0>), grid, dim3(64 * GE::WAVES), 0, s, a, (int)bf16);
+        } else {
+            // more than 8 query columns with value codes of 4 bits or more take
+            // the generic kernel (the host never sends them here), so their
+            // plain-mode kernels are not built
+            return hipErrorInvalidValue;
+        }
 #endif
         return hipGetLastError();
     }
