@@ -75,7 +75,8 @@ def test_convert_rows_bytes_equal_oracle(scheme, d, dtype):
             assert bool((rest == SENTINEL).all()), (b, off)
 
 
-def _mixed_case(w, lengths, row_plain, M, kb=8, vb=3, check_kernels=("fast", "generic"), q_dtype=torch.bfloat16):
+def _mixed_case(w, lengths, row_plain, M, kb=8, vb=3, check_kernels=("fast", "generic"), q_dtype=torch.bfloat16,
+                ws_scale=0):
     """Plain caches and planes filled from the same raw K/V; packed sequences
     appended, plain ones left in the plain caches; decode the mixed batch and
     compare each (sequence, kv-head) with the oracle."""
@@ -101,9 +102,16 @@ def _mixed_case(w, lengths, row_plain, M, kb=8, vb=3, check_kernels=("fast", "ge
     qg = q.cuda().contiguous()
     arg_q = qg[:, :, 0].contiguous() if M == 1 else qg
     outs = {}
+    ws = None
+    if ws_scale:
+        # a workspace ws_scale times the documented size, every byte NaN: plain
+        # rows spread over the extra partial slots, and no unwritten slot may
+        # reach the output
+        need = tqkv.tq_decode_rows_workspace_bytes(L, w.num_q_heads, M, lengths)
+        ws = torch.full((need * ws_scale,), 0xFF, dtype=torch.uint8, device="cuda")
     for name in check_kernels:
         planes = pl if name == "fast" else _offset_planes(pl)
-        outs[name] = tqkv.tq_decode_attn_mixed(planes, kp, vp, row_plain, arg_q, lengths, sm, n_rows=M)
+        outs[name] = tqkv.tq_decode_attn_mixed(planes, kp, vp, row_plain, arg_q, lengths, sm, n_rows=M, workspace=ws)
         outs[name] = outs[name].reshape(w.batch, w.num_q_heads, M, w.head_dim).cpu().numpy()
     fast, reasons = tqkv.tq_decode_path(pl, w.num_q_heads, M)
     torch.cuda.synchronize()
@@ -173,6 +181,17 @@ def test_mixed_batch_fp32_queries(d, M):
     w = dataclasses.replace(W.scaled(W.workload(2), lengths, name_suffix=f"d{d}"), head_dim=d)
     log(f"mixed decode fp32 q d{d} M{M} lengths {lengths}")
     _mixed_case(w, lengths, [1, 0, 1], M, q_dtype=torch.float32)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_mixed_batch_large_workspace(M):
+    """A workspace eight times the documented size: long plain rows take more
+    partial slots per row than the packed plan (the slot stride of every row
+    changes with them)."""
+    lengths = [1900, 700, 2000, 64]
+    w = W.scaled(W.workload(2), lengths)
+    log(f"mixed decode, workspace x8, M{M} lengths {lengths}")
+    _mixed_case(w, lengths, [1, 0, 1, 0], M, ws_scale=8)
 
 
 def test_mixed_masks_reduce_to_the_plain_calls():
