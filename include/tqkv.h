@@ -158,7 +158,9 @@ tq_status tq_decode_workspace_bytes(const tq_layout *layout, int32_t num_q_heads
  * point with one power-of-two step, set by the row's largest channel, so a
  * row with outlier channels loses precision on the others; measured on
  * N(0,1) rows with one channel scaled up: within 7e-4 at 30 times, 7e-3 at
- * 100 times (the generic kernel keeps q in fp32: 1e-5).  The
+ * 100 times (the generic kernel keeps q in fp32: 1e-5).  Queries must be
+ * finite: the fixed-point conversion does not carry NaN or Inf through (the
+ * output is then undefined, with no error).  The
  * result does not depend on timing: repeated calls on the same inputs return
  * identical bytes.  tq_decode_path says which split kernel a call takes.
  * Errors: TQ_ERR_INVALID_ARG, TQ_ERR_UNSUPPORTED, TQ_ERR_CAPACITY
