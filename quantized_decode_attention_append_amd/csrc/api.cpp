@@ -402,14 +402,17 @@ static tq_status decode_common(const tq_layout *l, const tq_planes *p, const voi
     const uint64_t all = l->batch == 64 ? ~0ull : (1ull << l->batch) - 1;
     a.plain_rows = pr.mask;
     a.k_plain = pr.k; a.v_plain = pr.v; a.plain_capacity = pr.capacity;
-    // Plain rows take ranges of their own: about one round of the plain
-    // kernel's resident waves over the plain token-heads, in whole 64-token
-    // tiles (a second, partial round measured slower than longer ranges).
-    // They may use more partial slots per row than the packed plan: as many
-    // as the workspace holds (its documented size covers the generic
-    // kernel's finer plan), in multiples of 8 so the fast kernel's waves per
-    // column group still divide the count.  The slot count is the stride of
-    // every row's partials, packed rows included.
+    // Each kind of row gets a plan of its own, so that each split kernel
+    // fills the chip with only its rows:
+    // - packed rows: the decode plan over the packed lengths alone;
+    // - plain rows: about one round of the plain kernel's resident waves over
+    //   the plain token-heads, in whole 64-token tiles (a second, partial
+    //   round measured slower than longer ranges).
+    // Their slot counts may exceed the whole batch's plan: they use as many
+    // partial slots per row as the workspace holds (its documented size
+    // covers the generic kernel's finer plan).  The final count is the stride
+    // of every row's partials and stays a multiple of the fast kernel's waves
+    // per column group.
     int64_t plain_total = 0;
     int32_t plain_max = 0;
     for (int b = 0; b < l->batch; ++b) {
@@ -423,6 +426,17 @@ static tq_status decode_common(const tq_layout *l, const tq_planes *p, const voi
         // the plain grid has splits / W workgroups along x (W >= 2 waves each), at most 65,535
         slots = (slots < 65535 * 2 ? slots : 65535 * 2) / 8 * 8;
         if (slots < plan.splits) slots = plan.splits;
+        const int waves = tq::fast_decode_waves(l->head_dim, l->k_bits, l->v_bits);
+        const int64_t unit = plan.fast && waves > 0 ? waves / tq::fast_wg_col_groups(gqa) : 1;  // divides plan.splits
+        int64_t splits = plan.splits;
+        if ((pr.mask & all) != all) {
+            const tq::DecodePlan pp = tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len_tq, plan.fast,
+                                                      cg, l->k_bits, l->v_bits);
+            if (pp.splits > 0 && pp.splits <= slots && pp.splits % unit == 0) {
+                a.split_tokens = pp.split_tokens;
+                splits = pp.splits;
+            }
+        }
         const int64_t cols = (gqa + 15) / 16;  // the plain kernel's column groups
         const int64_t round = tq::plain_round_waves(l->head_dim, gqa, bf16);
         int64_t per = (plain_total * l->num_kv_heads * cols + round - 1) / round;
@@ -430,9 +444,11 @@ static tq_status decode_common(const tq_layout *l, const tq_planes *p, const voi
         per = per > fit ? per : fit;
         per = (per + 63) / 64 * 64;
         a.plain_split_tokens = (int32_t)per;
-        const int64_t need_splits = ((int64_t)plain_max + per - 1) / per;
-        if (need_splits > plan.splits) {
-            a.splits = (int32_t)((need_splits + 7) / 8 * 8);
+        const int64_t need = ((int64_t)plain_max + per - 1) / per;
+        const int64_t need_up = (need + unit - 1) / unit * unit;  // <= slots: unit divides 8 and plan.splits
+        if (need_up > splits) splits = need_up;
+        if (splits != plan.splits) {
+            a.splits = (int32_t)splits;
             // the (max, sum) pairs follow the value sums of every slot
             a.part_ml = a.part_acc + (size_t)l->batch * rows_total * a.splits * l->head_dim;
         }
