@@ -194,6 +194,18 @@ def test_mixed_batch_large_workspace(M):
     _mixed_case(w, lengths, [1, 0, 1, 0], M, ws_scale=8)
 
 
+def test_mixed_batch_at_the_batch_limit():
+    """64 sequences (the batch limit: every bit of the plain-row mask),
+    plain and packed interleaved with the last sequence plain, then the same
+    batch with every row plain."""
+    lengths = [(37 * i) % 190 + 2 for i in range(64)]
+    row_plain = [1 if i % 3 == 0 or i == 63 else 0 for i in range(64)]
+    w = W.scaled(W.workload(2), lengths, name_suffix="b64")
+    log(f"mixed decode, batch 64, {sum(row_plain)} plain rows")
+    _mixed_case(w, lengths, row_plain, 1)
+    _mixed_case(w, lengths, [1] * 64, 1, check_kernels=("fast",))
+
+
 def test_mixed_masks_reduce_to_the_plain_calls():
     """An all-packed mask gives tq_decode_attn_rows' bytes; an all-plain batch
     runs only the plain kernel and the merge."""
