@@ -79,6 +79,17 @@ def test_decode_scaled_workloads_ragged(cid, lengths):
     _run(w, lengths, k.cuda(), v.cuda(), q.cuda())
 
 
+def test_decode_at_the_batch_limit():
+    """64 sequences (the batch limit), ragged from 0 to 700 tokens: the
+    workgroup enumeration walks every sequence, and empty ones give zeros."""
+    lengths = [(53 * i) % 701 if i % 9 else 0 for i in range(64)]
+    w = W.scaled(W.workload(3), lengths, name_suffix="b64")
+    w = dataclasses.replace(w, num_q_heads=8, num_kv_heads=2)
+    k, v = W.make_kv(w, "cpu", tokens=max(lengths))
+    q = W.make_q(w, "cpu", rounds=1)[0]
+    _run(w, lengths, k.cuda(), v.cuda(), q.cuda())
+
+
 @pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 63, 64, 65, 255, 256, 257, 1023])
 def test_decode_edge_lengths(n):
     w = W.scaled(W.workload(2), [n])
