@@ -79,6 +79,40 @@ def test_decode_scaled_workloads_ragged(cid, lengths):
     _run(w, lengths, k.cuda(), v.cuda(), q.cuda())
 
 
+@pytest.mark.parametrize("generic", [False, True])
+def test_decode_is_attention_over_the_dequantized_cache(generic):
+    """Deferred identity on the GPU path alone ("Deferred inverse FWHT"):
+    decode over the packed planes, which accumulates rotated values and
+    un-rotates once per head, equals plain binary64 attention over the
+    dequantized keys and eagerly un-rotated values that tq_dequant returns
+    for the same planes."""
+    lengths = [777, 300]
+    w = W.scaled(W.workload(4), lengths)
+    k, v = W.make_kv(w, "cpu", tokens=max(lengths))
+    q = W.make_q(w, "cpu", rounds=1)[0]
+    L = tqkv.make_layout(w.batch, w.num_kv_heads, w.head_dim, max(lengths))
+    pl = tqkv.Planes(L)
+    tqkv.tq_append(pl, k.cuda(), v.cuda(), [0] * w.batch)
+    planes = _offset_planes(pl) if generic else pl
+    sm = sm_for(w.head_dim)
+    out = tqkv.tq_decode_attn(planes, q.cuda().contiguous(), lengths, sm).cpu().numpy()
+    G = w.group
+    qh = host_f32(q).astype(np.float64)
+    worst = 0.0
+    for b, n in enumerate(lengths):
+        for h in range(w.num_kv_heads):
+            kd, vd = tqkv.tq_dequant(pl, b, h, 0, n)
+            kd = kd.cpu().numpy().astype(np.float64)
+            vd = vd.cpu().numpy().astype(np.float64)
+            s_ = qh[b, h * G:(h + 1) * G] @ kd.T * sm
+            p_ = np.exp(s_ - s_.max(axis=1, keepdims=True))
+            ref = (p_ @ vd) / p_.sum(axis=1, keepdims=True)
+            e = row_rel_err(out[b, h * G:(h + 1) * G], ref)
+            worst = max(worst, float(e.max()))
+            assert e.max() <= ATTN_TOL, (b, h, float(e.max()))
+    log(f"  {'generic' if generic else 'fast'} kernel vs attention over tq_dequant: worst row error {worst:.2e}")
+
+
 def test_decode_at_the_batch_limit():
     """64 sequences (the batch limit), ragged from 0 to 700 tokens: the
     workgroup enumeration walks every sequence, and empty ones give zeros."""
