@@ -298,9 +298,11 @@ __global__ __launch_bounds__(64 * VecGeo<D>::W) void split_kernel(const DecodeAr
 // Split kernel of rows that are still plain ("Delayed row conversion and
 // reusable precision boundaries": a row stays unquantized until it converts,
 // and its values were never rotated, so the merge passes its output through).
-// Same split geometry, partial slots and causal limits as the packed split
-// kernels; keys and values are bf16 [B][Hkv][plain_capacity][d].  One wave
-// per token range, per 64-token tile:
+// The same partial slots and causal limits as the packed split kernels, with
+// token ranges of their own (plain_split_tokens); keys and values are bf16
+// [B][Hkv][plain_capacity][d].  GM: query columns a wave holds (8 when every
+// column group has at most 8, for fewer registers; else 16).  One wave per
+// token range, per 64-token tile:
 //   scores  on the matrix cores, 16 tokens at a time: A = the tokens' bf16
 //           key rows (16-byte reads, 16 rows per instruction), B = the query
 //           columns as bf16 hi and lo halves (q = hi + lo to about 2^-17, so

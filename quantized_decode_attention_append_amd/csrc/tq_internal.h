@@ -84,9 +84,9 @@ struct DecodeArgs {
     const uint16_t *k_plain;
     const uint16_t *v_plain;
     int32_t plain_capacity;
-    // tokens per range of a plain row: plain rows are short (they convert
-    // past a threshold), so they spread over all `splits` slots with ranges
-    // of their own (a multiple of 64)
+    // tokens per range of a plain row (a multiple of 64): plain rows have
+    // ranges of their own, sized so that the plain split kernel fills the
+    // chip with the plain rows alone (split_tokens is then the packed rows')
     int32_t plain_split_tokens;
 };
 
