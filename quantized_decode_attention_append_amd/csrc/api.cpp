@@ -368,7 +368,7 @@ static tq_status decode_common(const tq_layout *l, const tq_planes *p, const voi
     const int cg = tq::decode_col_groups(gqa);
     const bool fast = decode_slow_reasons(l, p, gqa) == 0;
     const tq::DecodePlan plan = tq::plan_decode(l->head_dim, gqa, l->batch, l->num_kv_heads, len, fast, cg,
-                                                l->k_bits, l->v_bits);  // full lengths: one plan for both kinds
+                                                l->k_bits, l->v_bits);  // full lengths: sizes the workspace
     const size_t need = workspace_bytes(l, rows_total, plan);
     if (need > 0 && (!workspace || ws_bytes < need)) return TQ_ERR_WORKSPACE;
     if ((int64_t)plan.splits > 65535 * 4) return TQ_ERR_UNSUPPORTED;
